@@ -1,0 +1,165 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) hot path of DeepSeek Sparse
+ * Attention (DSA): lightning indexer -> top-k selector -> attention over the
+ * selected KV rows.
+ *
+ * The operation is the one described in "DeepSeek-V3.2-Exp 稀疏注意力机制(DSA)
+ * 技术深度解析：从原理到 TaoToken API 实测效率提升" (sheratonhq.com), section 1:
+ * a light indexer with few heads, index_head_dim 128, ReLU instead of softmax
+ * and FP8 arithmetic scores every history token of each query; a top-k
+ * selector keeps the k highest-scoring KV; the main attention then looks only
+ * at that subset, so its cost falls from O(n^2) to O(n*k).  "DeepSeek-V4 百万
+ * token 上下文的工程实现" (blog.hotdry.top), section "从 O(N²) 到 O(N・k)", names the
+ * same two stages (Lightning Indexer, then a fine-grained selector).
+ *
+ * Definitions used by every entry point (per sequence b, query row t):
+ *   pos(t)   last visible key: q_pos[b*n_q+t] if q_pos is given, else
+ *            n_k - n_q + t (queries are the last n_q tokens of the sequence,
+ *            the query's own position included).  Keys s > pos(t) are history
+ *            of no one and never scored or selected.
+ *   I[t,s] = sum_h w[t,h] * ReLU( q_I[t,h] . k_I[s] )   for s <= pos(t).
+ *            With FP8 inputs q_I = sq[t]*code, k_I = sk[s]*code, so
+ *            I = sq*sk * sum_h w*ReLU(code.code) exactly (scales are > 0).
+ *   top-k    m = min(top_k, pos(t)+1) keys with the highest I; among equal I
+ *            the lower position wins; -0.0 equals +0.0.
+ *   attn     for each query head h (kv head g = h / (q_heads/kv_heads)):
+ *            z_j = softmax_scale * q[t,h].k[s_j,g] over the kept rows s_j,
+ *            out = sum_j softmax(z)_j * v[s_j,g], lse = log sum_j exp(z_j).
+ *            In latent mode (kv_latent = 1, kv_heads = 1) the value is the
+ *            first d_v entries of the key row.
+ *
+ * Memory and ownership.  Every pointer inside dsa_problem_t and every output
+ * pointer is DEVICE memory owned by the caller, contiguous and row-major in
+ * the layouts given below; the library keeps no pointer after a call returns,
+ * never allocates, frees or copies between host and device, and never
+ * synchronises.  All work is enqueued on `stream` (0 = the null stream); the
+ * call returns once it is enqueued.  The dsa_problem_t struct itself is host
+ * memory, read only during the call.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * an invalid call returns a negative status and enqueues nothing.
+ * DSA_E_DEVICE reports a failed launch (the HIP error text is in
+ * dsa_last_error()).  Data-dependent cases are defined, not errors: an idx
+ * entry that is negative, > pos(t) or >= n_k is skipped by dsa_sparse_attn,
+ * and a row with no valid entry gets out = 0 and lse = -inf.  The library
+ * never prints and never aborts.  Calls are thread-safe as long as concurrent
+ * calls do not share output or workspace memory; dsa_last_error() is
+ * per-thread.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same typedef as HIP's own header, so both may be included together. */
+typedef struct ihipStream_t *hipStream_t;
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_E_INVALID = -1,      /* null required pointer, non-positive size, bad combination */
+    DSA_E_UNSUPPORTED = -2,  /* valid problem outside what this build implements */
+    DSA_E_WORKSPACE = -3,    /* workspace missing or smaller than dsa_workspace_bytes() */
+    DSA_E_DEVICE = -4        /* a HIP launch failed; see dsa_last_error() */
+} dsa_status_t;
+
+typedef enum {
+    DSA_F32 = 0,             /* IEEE binary32 */
+    DSA_BF16 = 1,            /* bfloat16 */
+    DSA_FP8_E4M3 = 2         /* OCP FP8 E4M3 (bias 7, max 448, no inf) + fp32 scale per token row */
+} dsa_dtype_t;
+
+typedef enum {
+    DSA_OP_INDEX_SCORES = 0,
+    DSA_OP_TOPK = 1,
+    DSA_OP_SPARSE_ATTN = 2,
+    DSA_OP_PREFILL = 3,
+    DSA_OP_DECODE = 4
+} dsa_op_t;
+
+/* One problem: B sequences, each with n_q query rows and n_k key rows. */
+typedef struct {
+    int32_t batch;            /* B >= 1 */
+    int32_t n_q;              /* query rows per sequence, 1 <= n_q <= n_k */
+    int32_t n_k;              /* key rows per sequence, n_k <= 2^24 */
+    const int32_t *q_pos;     /* [B*n_q] last visible key of each query, or NULL */
+
+    /* lightning indexer */
+    int32_t idx_heads;        /* H_I, 1..64 (16 in the pages' configuration) */
+    int32_t idx_dim;          /* index_head_dim; must be 128 */
+    int32_t idx_dtype;        /* dsa_dtype_t of iq and ik */
+    const void *iq;           /* [B, n_q, H_I, idx_dim] */
+    const float *iq_scale;    /* [B, n_q] one scale per query row (FP8 only, else NULL) */
+    const void *ik;           /* [B, n_k, idx_dim] */
+    const float *ik_scale;    /* [B, n_k] one scale per key row (FP8 only, else NULL) */
+    const float *iw;          /* [B, n_q, H_I] fp32 head weights w[t,h] */
+
+    /* main attention */
+    int32_t q_heads;          /* Hq >= 1 */
+    int32_t kv_heads;         /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t d_qk;             /* 64, 128, or 576 (latent) */
+    int32_t d_v;              /* 64, 128, or 512 (latent) */
+    int32_t kv_latent;        /* 1: v is NULL, value = first d_v entries of the k row */
+    int32_t attn_dtype;       /* DSA_F32 or DSA_BF16, for q, k, v and out */
+    const void *q;            /* [B, n_q, Hq, d_qk] */
+    const void *k;            /* [B, n_k, Hkv, d_qk] */
+    const void *v;            /* [B, n_k, Hkv, d_v], NULL when kv_latent */
+    float softmax_scale;      /* > 0, e.g. 1/sqrt(d_qk) */
+
+    int32_t top_k;            /* k, 1..8192 */
+} dsa_problem_t;
+
+/* DSA_ABI_VERSION of the loaded library. */
+int dsa_abi_version(void);
+
+/* Workspace bytes that entry point `op` needs for problem `p` (0 if none).
+ * Returns (size_t)-1 if the problem is invalid for that op; the reason is in
+ * dsa_last_error(). */
+size_t dsa_workspace_bytes(int op, const dsa_problem_t *p);
+
+/* Indexer scores, unfused: scores[b][t][s] = I[t,s] (fp32) for s <= pos(t) and
+ * -inf for s > pos(t).  scores: [B, n_q, n_k] fp32.  Uses the iq/ik/iw fields. */
+dsa_status_t dsa_index_scores(const dsa_problem_t *p, float *scores, hipStream_t stream);
+
+/* Top-k selector, unfused.  scores: [B, n_q, n_k] fp32 as written by
+ * dsa_index_scores (entries past pos(t) are ignored whatever they hold);
+ * idx: [B, n_q, top_k] int32, the m = min(top_k, pos(t)+1) kept positions in
+ * ascending order, then -1.  Among equal scores the lower position wins. */
+dsa_status_t dsa_topk(const dsa_problem_t *p, const float *scores, int32_t *idx,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Attention over the selected rows only, unfused.  idx: [B, n_q, kk] int32 with
+ * kk = p->top_k (any entries; invalid ones skipped); out: [B, n_q, Hq, d_v] in
+ * attn_dtype; lse: [B, n_q, Hq] fp32 natural-log sum-exp, or NULL. */
+dsa_status_t dsa_sparse_attn(const dsa_problem_t *p, const int32_t *idx, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Fused prefill: indexer, top-k and sparse attention for every query row.  The
+ * full [n_q, n_k] score matrix is never held in memory: scores are produced
+ * and consumed one bounded block of query rows at a time inside the
+ * workspace.  idx_out: [B, n_q, top_k] or NULL (then kept in the workspace). */
+dsa_status_t dsa_prefill(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Fused decode: as dsa_prefill for n_q == 1 (one new token per sequence whose
+ * own key row is already the last cached row, unless q_pos says otherwise). */
+dsa_status_t dsa_decode(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *dsa_status_str(dsa_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

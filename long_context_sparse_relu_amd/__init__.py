@@ -1,0 +1,278 @@
+"""Python binding of libdsa, the gfx950 DeepSeek Sparse Attention hot path.
+
+Argument marshalling only: every step of the path (indexer scores, top-k
+selection, sparse attention) runs in the HIP kernels behind the C ABI in
+``include/dsa.h``.  PyTorch supplies device memory and the current stream.  If
+``libdsa.so`` has not been built the first call raises; there is no fallback.
+
+The entry points mirror the C ABI: ``index_scores``, ``topk``, ``sparse_attn``,
+``prefill`` and ``decode``, plus ``workspace_bytes``.  Build the problem once
+with :func:`make_problem` (it checks shapes, dtypes and devices and keeps the
+tensors alive) and pass it to any of them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE = 0, -1, -2, -3, -4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE = 0, 1, 2, 3, 4
+ABI_VERSION = 1
+
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+
+EXPORTED = ("dsa_abi_version", "dsa_workspace_bytes", "dsa_index_scores", "dsa_topk",
+            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_status_str", "dsa_last_error")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of dsa_problem_t (all pointers are device addresses)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
+        ("q_pos", ctypes.c_void_p),
+        ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32), ("idx_dtype", ctypes.c_int32),
+        ("iq", ctypes.c_void_p), ("iq_scale", ctypes.c_void_p),
+        ("ik", ctypes.c_void_p), ("ik_scale", ctypes.c_void_p), ("iw", ctypes.c_void_p),
+        ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32), ("kv_latent", ctypes.c_int32), ("attn_dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("top_k", ctypes.c_int32),
+    ]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_str(status)} ({detail})" if detail else status_str(status))
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdsa.so (raises if it is missing: build it with long_context_sparse_relu_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m long_context_sparse_relu_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Problem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.dsa_abi_version.restype = ctypes.c_int
+    lib.dsa_abi_version.argtypes = []
+    lib.dsa_workspace_bytes.restype = sz
+    lib.dsa_workspace_bytes.argtypes = [ctypes.c_int, P]
+    lib.dsa_index_scores.restype = ctypes.c_int
+    lib.dsa_index_scores.argtypes = [P, vp, vp]
+    lib.dsa_topk.restype = ctypes.c_int
+    lib.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.dsa_sparse_attn.restype = ctypes.c_int
+    lib.dsa_sparse_attn.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.dsa_prefill.restype = ctypes.c_int
+    lib.dsa_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.dsa_decode.restype = ctypes.c_int
+    lib.dsa_decode.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.dsa_status_str.restype = ctypes.c_char_p
+    lib.dsa_status_str.argtypes = [ctypes.c_int]
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_last_error.argtypes = []
+    if lib.dsa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libdsa ABI {lib.dsa_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().dsa_status_str(status).decode()
+
+
+def last_error() -> str:
+    return load_library().dsa_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise DSAError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class DSAProblem:
+    """A dsa_problem_t plus the tensors it points into (kept alive here)."""
+
+    def __init__(self, struct: Problem, tensors: dict, device):
+        self.struct = struct
+        self.tensors = tensors
+        self.device = device
+
+    @property
+    def rows(self) -> int:
+        return self.struct.batch * self.struct.n_q
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def _contig(name, t, device, dtypes=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik_scale=None,
+                 q_pos=None, softmax_scale=None, latent_dv=None) -> DSAProblem:
+    """Describe one batch: see include/dsa.h for the layouts.
+
+    iq [B,n_q,H,128], ik [B,n_k,128] (fp32 | bf16 | float8_e4m3fn, same dtype),
+    iq_scale [B,n_q] / ik_scale [B,n_k] fp32 for FP8, iw [B,n_q,H] fp32,
+    q [B,n_q,Hq,dqk], k [B,n_k,Hkv,dqk], v [B,n_k,Hkv,dv] or None with
+    latent_dv (then the value is k[..., :latent_dv] and Hkv must be 1),
+    q_pos [B,n_q] int32 or None.
+    """
+    device = iq.device
+    idt = (torch.float32, torch.bfloat16, torch.float8_e4m3fn)
+    iq = _contig("iq", iq, device, idt)
+    ik = _contig("ik", ik, device, (iq.dtype,))
+    iw = _contig("iw", iw, device, (torch.float32,))
+    iq_scale = _contig("iq_scale", iq_scale, device, (torch.float32,))
+    ik_scale = _contig("ik_scale", ik_scale, device, (torch.float32,))
+    q_pos = _contig("q_pos", q_pos, device, (torch.int32,))
+    if iq.dim() != 4 or ik.dim() != 3 or iw.dim() != 3:
+        raise ValueError("iq must be [B,n_q,H,D], ik [B,n_k,D], iw [B,n_q,H]")
+    B, n_q, H, D = iq.shape
+    n_k = ik.shape[1]
+    if ik.shape != (B, n_k, D) or iw.shape != (B, n_q, H):
+        raise ValueError(f"shape mismatch: iq {tuple(iq.shape)}, ik {tuple(ik.shape)}, iw {tuple(iw.shape)}")
+    if iq.dtype == torch.float8_e4m3fn:
+        if iq_scale is None or ik_scale is None:
+            raise ValueError("FP8 indexer inputs need iq_scale and ik_scale")
+        if iq_scale.shape != (B, n_q) or ik_scale.shape != (B, n_k):
+            raise ValueError("iq_scale must be [B,n_q] and ik_scale [B,n_k]")
+    if q_pos is not None and q_pos.shape != (B, n_q):
+        raise ValueError("q_pos must be [B,n_q]")
+    p = Problem()
+    p.batch, p.n_q, p.n_k = B, n_q, n_k
+    p.q_pos = None if q_pos is None else q_pos.data_ptr()
+    p.idx_heads, p.idx_dim, p.idx_dtype = H, D, _DTYPE_CODE[iq.dtype]
+    p.iq, p.ik, p.iw = iq.data_ptr(), ik.data_ptr(), iw.data_ptr()
+    p.iq_scale = None if iq_scale is None else iq_scale.data_ptr()
+    p.ik_scale = None if ik_scale is None else ik_scale.data_ptr()
+    p.top_k = int(top_k)
+    tensors = dict(iq=iq, ik=ik, iw=iw, iq_scale=iq_scale, ik_scale=ik_scale, q_pos=q_pos)
+    if q is not None:
+        adt = (torch.float32, torch.bfloat16)
+        q = _contig("q", q, device, adt)
+        k = _contig("k", k, device, (q.dtype,))
+        v = _contig("v", v, device, (q.dtype,))
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("q must be [B,n_q,Hq,dqk] and k [B,n_k,Hkv,dqk]")
+        if q.shape[:2] != (B, n_q) or k.shape[:2] != (B, n_k) or k.shape[3] != q.shape[3]:
+            raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}")
+        Hq, dqk, Hkv = q.shape[2], q.shape[3], k.shape[2]
+        if v is None:
+            if latent_dv is None:
+                raise ValueError("v is None: pass latent_dv for latent key/value rows")
+            dv, latent = int(latent_dv), 1
+        else:
+            if v.dim() != 4 or v.shape[:3] != (B, n_k, Hkv):
+                raise ValueError(f"v must be [B,n_k,Hkv,dv], got {tuple(v.shape)}")
+            dv, latent = v.shape[3], 0
+        p.q_heads, p.kv_heads, p.d_qk, p.d_v, p.kv_latent = Hq, Hkv, dqk, dv, latent
+        p.attn_dtype = _DTYPE_CODE[q.dtype]
+        p.q, p.k = q.data_ptr(), k.data_ptr()
+        p.v = None if v is None else v.data_ptr()
+        p.softmax_scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(dqk)
+        tensors.update(q=q, k=k, v=v)
+    return DSAProblem(p, tensors, device)
+
+
+def workspace_bytes(op: int, prob: DSAProblem) -> int:
+    n = load_library().dsa_workspace_bytes(op, prob.ref())
+    if n == ctypes.c_size_t(-1).value:
+        raise DSAError(E_INVALID, last_error())
+    return int(n)
+
+
+def _workspace(op, prob, workspace):
+    need = workspace_bytes(op, prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=prob.device)
+    return workspace
+
+
+def index_scores(prob: DSAProblem, scores=None, stream=None):
+    """scores [B,n_q,n_k] fp32 (I past pos(t) is -inf)."""
+    s = prob.struct
+    if scores is None:
+        scores = torch.empty((s.batch, s.n_q, s.n_k), dtype=torch.float32, device=prob.device)
+    _check(load_library().dsa_index_scores(prob.ref(), _ptr(scores), _stream(stream)))
+    return scores
+
+
+def topk(prob: DSAProblem, scores, idx=None, workspace=None, stream=None):
+    """idx [B,n_q,top_k] int32: kept positions ascending, then -1."""
+    s = prob.struct
+    if idx is None:
+        idx = torch.empty((s.batch, s.n_q, s.top_k), dtype=torch.int32, device=prob.device)
+    ws = _workspace(OP_TOPK, prob, workspace)
+    _check(load_library().dsa_topk(prob.ref(), _ptr(scores), _ptr(idx), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+    return idx
+
+
+def _out_tensors(prob, out, lse):
+    s = prob.struct
+    dt = {F32: torch.float32, BF16: torch.bfloat16}[s.attn_dtype]
+    if out is None:
+        out = torch.empty((s.batch, s.n_q, s.q_heads, s.d_v), dtype=dt, device=prob.device)
+    if lse is None:
+        lse = torch.empty((s.batch, s.n_q, s.q_heads), dtype=torch.float32, device=prob.device)
+    return out, lse
+
+
+def sparse_attn(prob: DSAProblem, idx, out=None, lse=None, stream=None):
+    """(out [B,n_q,Hq,dv], lse [B,n_q,Hq]) of attention over the rows in idx."""
+    out, lse = _out_tensors(prob, out, lse)
+    _check(load_library().dsa_sparse_attn(prob.ref(), _ptr(idx), _ptr(out), _ptr(lse), None, 0,
+                                          _stream(stream)))
+    return out, lse
+
+
+def _fused(fn, op, prob, out, lse, idx_out, workspace, stream):
+    out, lse = _out_tensors(prob, out, lse)
+    ws = _workspace(op, prob, workspace)
+    _check(fn(prob.ref(), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse, idx_out
+
+
+def prefill(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, stream=None):
+    return _fused(load_library().dsa_prefill, OP_PREFILL, prob, out, lse, idx_out, workspace, stream)
+
+
+def decode(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, stream=None):
+    return _fused(load_library().dsa_decode, OP_DECODE, prob, out, lse, idx_out, workspace, stream)

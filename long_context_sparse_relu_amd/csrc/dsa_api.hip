@@ -1,0 +1,271 @@
+// dsa_api.hip -- the C ABI declared in include/dsa.h: host-side validation,
+// workspace layout and launch sequencing on the caller's stream.  Nothing here
+// allocates, frees, copies or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "dsa.h"
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+dsa_status_t device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DSA_OK;
+    return fail(DSA_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxNk = 1 << 24;
+constexpr size_t kAlign = 256;
+// Query rows whose scores the fused prefill keeps at once (bounded scratch).
+constexpr size_t kPrefillScoreBytes = size_t(256) << 20;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+dsa_status_t check_common(const dsa_problem_t* p) {
+    if (!p) return fail(DSA_E_INVALID, "problem pointer is NULL");
+    if (p->batch < 1 || p->n_q < 1 || p->n_k < 1)
+        return fail(DSA_E_INVALID, "batch, n_q and n_k must be >= 1 (got %d, %d, %d)", p->batch, p->n_q, p->n_k);
+    if (p->n_q > p->n_k) return fail(DSA_E_INVALID, "n_q (%d) exceeds n_k (%d)", p->n_q, p->n_k);
+    if (p->n_k > kMaxNk) return fail(DSA_E_UNSUPPORTED, "n_k %d exceeds %d", p->n_k, kMaxNk);
+    if (static_cast<int64_t>(p->batch) * p->n_q > (int64_t(1) << 30))
+        return fail(DSA_E_UNSUPPORTED, "batch*n_q too large");
+    return DSA_OK;
+}
+
+dsa_status_t check_index(const dsa_problem_t* p) {
+    if (p->idx_heads < 1 || p->idx_heads > 64)
+        return fail(DSA_E_UNSUPPORTED, "idx_heads must be in 1..64 (got %d)", p->idx_heads);
+    if (p->idx_dim != 128) return fail(DSA_E_UNSUPPORTED, "idx_dim must be 128 (got %d)", p->idx_dim);
+    if (p->idx_dtype != DSA_F32 && p->idx_dtype != DSA_BF16 && p->idx_dtype != DSA_FP8_E4M3)
+        return fail(DSA_E_INVALID, "idx_dtype %d is not a dsa_dtype_t", p->idx_dtype);
+    if (!p->iq || !p->ik || !p->iw) return fail(DSA_E_INVALID, "iq, ik and iw are required");
+    if (p->idx_dtype == DSA_FP8_E4M3 && (!p->iq_scale || !p->ik_scale))
+        return fail(DSA_E_INVALID, "FP8 indexer inputs need iq_scale and ik_scale");
+    return DSA_OK;
+}
+
+dsa_status_t check_topk(const dsa_problem_t* p) {
+    if (p->top_k < 1 || p->top_k > dsa::kTopkMaxK)
+        return fail(DSA_E_UNSUPPORTED, "top_k must be in 1..%d (got %d)", dsa::kTopkMaxK, p->top_k);
+    return DSA_OK;
+}
+
+dsa_status_t check_attn(const dsa_problem_t* p) {
+    if (p->q_heads < 1 || p->kv_heads < 1 || p->q_heads % p->kv_heads)
+        return fail(DSA_E_INVALID, "q_heads (%d) must be a positive multiple of kv_heads (%d)", p->q_heads, p->kv_heads);
+    if (p->attn_dtype != DSA_F32 && p->attn_dtype != DSA_BF16)
+        return fail(DSA_E_UNSUPPORTED, "attn_dtype must be DSA_F32 or DSA_BF16 (got %d)", p->attn_dtype);
+    if (p->d_qk < 1 || p->d_qk > 576 || p->d_v < 1 || p->d_v > 512)
+        return fail(DSA_E_UNSUPPORTED, "need 1 <= d_qk <= 576 and 1 <= d_v <= 512 (got %d, %d)", p->d_qk, p->d_v);
+    if (p->kv_latent) {
+        if (p->kv_heads != 1) return fail(DSA_E_INVALID, "latent rows need kv_heads == 1");
+        if (p->d_v > p->d_qk) return fail(DSA_E_INVALID, "latent rows need d_v <= d_qk");
+    } else if (!p->v) {
+        return fail(DSA_E_INVALID, "v is required unless kv_latent");
+    }
+    if (!p->q || !p->k) return fail(DSA_E_INVALID, "q and k are required");
+    if (!(p->softmax_scale > 0.0f) || !std::isfinite(p->softmax_scale))
+        return fail(DSA_E_INVALID, "softmax_scale must be finite and > 0");
+    return DSA_OK;
+}
+
+int rows_of(const dsa_problem_t* p) { return p->batch * p->n_q; }
+
+dsa::IndexArgs index_args(const dsa_problem_t* p, int row0, int rows, float* scores) {
+    dsa::IndexArgs a{};
+    a.rows = rows; a.row0 = row0;
+    a.n_q = p->n_q; a.n_k = p->n_k; a.H = p->idx_heads; a.dtype = p->idx_dtype;
+    a.iq = p->iq; a.iq_scale = p->iq_scale;
+    a.ik = p->ik; a.ik_scale = p->ik_scale;
+    a.iw = p->iw;
+    a.q_pos = p->q_pos;
+    a.scores = scores;
+    return a;
+}
+
+dsa::TopkArgs topk_args(const dsa_problem_t* p, int row0, int rows, const float* scores,
+                        int32_t* idx, void* ws) {
+    dsa::TopkArgs a{};
+    a.rows = rows; a.row0 = row0;
+    a.n_q = p->n_q; a.n_k = p->n_k; a.k = p->top_k;
+    a.q_pos = p->q_pos;
+    a.scores = scores;
+    a.idx = idx;
+    dsa::topk_carve(ws, rows, a);
+    a.hist_ready = false;
+    return a;
+}
+
+dsa::AttnArgs attn_args(const dsa_problem_t* p, const int32_t* idx, void* out, float* lse) {
+    dsa::AttnArgs a{};
+    a.rows = rows_of(p); a.n_q = p->n_q; a.n_k = p->n_k; a.kk = p->top_k;
+    a.Hq = p->q_heads; a.Hkv = p->kv_heads; a.dqk = p->d_qk; a.dv = p->d_v;
+    a.latent = p->kv_latent ? 1 : 0; a.dtype = p->attn_dtype;
+    a.q = p->q; a.k = p->k; a.v = p->v; a.idx = idx; a.q_pos = p->q_pos;
+    a.scale = p->softmax_scale; a.out = out; a.lse = lse;
+    return a;
+}
+
+// Rows of scores the fused paths produce per round.
+int fused_block_rows(const dsa_problem_t* p) {
+    size_t per_row = static_cast<size_t>(p->n_k) * sizeof(float);
+    size_t r = kPrefillScoreBytes / per_row;
+    if (r < 1) r = 1;
+    if (r > static_cast<size_t>(rows_of(p))) r = rows_of(p);
+    return static_cast<int>(r);
+}
+
+struct FusedLayout {
+    int block_rows;
+    size_t scores_off, topk_off, idx_off, total;
+};
+
+FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
+    FusedLayout L{};
+    L.block_rows = fused_block_rows(p);
+    L.scores_off = 0;
+    L.topk_off = align_up(static_cast<size_t>(L.block_rows) * p->n_k * sizeof(float));
+    L.idx_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
+    L.total = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t)) : 0);
+    return L;
+}
+
+dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, hipStream_t st) {
+    FusedLayout L = fused_layout(p, idx_out == nullptr);
+    if (!ws || ws_bytes < L.total)
+        return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    float* scores = reinterpret_cast<float*>(base + L.scores_off);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx_off);
+    const int rows = rows_of(p);
+    for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
+        int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
+        dsa::IndexArgs ia = index_args(p, r0, nr, scores);
+        dsa_status_t s = device_status(dsa::launch_index_scores(ia, st), "indexer launch");
+        if (s != DSA_OK) return s;
+        dsa::TopkArgs ta = topk_args(p, r0, nr, scores, idx + static_cast<size_t>(r0) * p->top_k,
+                                     base + L.topk_off);
+        s = device_status(dsa::launch_topk(ta, st), "top-k launch");
+        if (s != DSA_OK) return s;
+    }
+    dsa::AttnArgs aa = attn_args(p, idx, out, lse);
+    return device_status(dsa::launch_sparse_attn(aa, st), "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
+    dsa_status_t s = check_common(p);
+    if (s != DSA_OK) return static_cast<size_t>(-1);
+    switch (op) {
+        case DSA_OP_INDEX_SCORES: return 0;
+        case DSA_OP_SPARSE_ATTN: return 0;
+        case DSA_OP_TOPK:
+            if (check_topk(p) != DSA_OK) return static_cast<size_t>(-1);
+            return dsa::topk_workspace_bytes(rows_of(p), p->n_k);
+        case DSA_OP_PREFILL:
+        case DSA_OP_DECODE:
+            if (check_topk(p) != DSA_OK) return static_cast<size_t>(-1);
+            if (op == DSA_OP_DECODE && p->n_q != 1) {
+                fail(DSA_E_INVALID, "dsa_decode takes n_q == 1 (got %d)", p->n_q);
+                return static_cast<size_t>(-1);
+            }
+            return fused_layout(p, true).total;
+        default:
+            fail(DSA_E_INVALID, "unknown op %d", op);
+            return static_cast<size_t>(-1);
+    }
+}
+
+dsa_status_t dsa_index_scores(const dsa_problem_t* p, float* scores, hipStream_t stream) {
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK || (s = check_index(p)) != DSA_OK) return s;
+    if (!scores) return fail(DSA_E_INVALID, "scores is NULL");
+    dsa::IndexArgs a = index_args(p, 0, rows_of(p), scores);
+    return device_status(dsa::launch_index_scores(a, stream), "indexer launch");
+}
+
+dsa_status_t dsa_topk(const dsa_problem_t* p, const float* scores, int32_t* idx,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK || (s = check_topk(p)) != DSA_OK) return s;
+    if (!scores || !idx) return fail(DSA_E_INVALID, "scores and idx are required");
+    size_t need = dsa::topk_workspace_bytes(rows_of(p), p->n_k);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    dsa::TopkArgs a = topk_args(p, 0, rows_of(p), scores, idx, workspace);
+    return device_status(dsa::launch_topk(a, stream), "top-k launch");
+}
+
+dsa_status_t dsa_sparse_attn(const dsa_problem_t* p, const int32_t* idx, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace; (void)workspace_bytes;
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK || (s = check_topk(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK)
+        return s;
+    if (!idx || !out) return fail(DSA_E_INVALID, "idx and out are required");
+    dsa::AttnArgs a = attn_args(p, idx, out, lse);
+    return device_status(dsa::launch_sparse_attn(a, stream), "attention launch");
+}
+
+dsa_status_t dsa_prefill(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK || (s = check_index(p)) != DSA_OK ||
+        (s = check_topk(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK)
+        return s;
+    if (!out) return fail(DSA_E_INVALID, "out is required");
+    return run_fused(p, out, lse, idx_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status_t dsa_decode(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK) return s;
+    if (p->n_q != 1) return fail(DSA_E_INVALID, "dsa_decode takes n_q == 1 (got %d)", p->n_q);
+    if ((s = check_index(p)) != DSA_OK || (s = check_topk(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK)
+        return s;
+    if (!out) return fail(DSA_E_INVALID, "out is required");
+    return run_fused(p, out, lse, idx_out, workspace, workspace_bytes, stream);
+}
+
+const char* dsa_status_str(dsa_status_t status) {
+    switch (status) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_E_INVALID: return "DSA_E_INVALID: invalid argument";
+        case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: valid problem outside this build";
+        case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing or too small";
+        case DSA_E_DEVICE: return "DSA_E_DEVICE: HIP launch failed";
+        default: return "unknown dsa_status_t";
+    }
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

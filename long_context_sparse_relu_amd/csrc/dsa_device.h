@@ -1,0 +1,79 @@
+// dsa_device.h -- device-side helpers shared by the libdsa kernels (gfx950).
+//
+// Storage formats: fp32, bfloat16 (upper half of a binary32 word) and OCP FP8
+// E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+// infinity, S.1111.111 = NaN; largest finite value 448).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+enum DType { F32 = 0, BF16 = 1, E4M3 = 2 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t rounding = 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>((u + rounding) >> 16);
+}
+
+// E4M3 code -> fp32 by rebuilding the binary32 fields.
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+    uint32_t sign = static_cast<uint32_t>(c & 0x80) << 24;
+    uint32_t e = (c >> 3) & 0xF;
+    uint32_t m = c & 0x7;
+    if (e == 0xF && m == 0x7) return __uint_as_float(0x7FC00000u);
+    if (e == 0) {  // subnormal: m/8 * 2^-6 = m * 2^-9
+        float mag = static_cast<float>(m) * 0.001953125f;
+        return sign ? -mag : mag;
+    }
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+template <int DT>
+__device__ __forceinline__ float load_as_f32(const void* base, size_t i) {
+    if constexpr (DT == F32) return static_cast<const float*>(base)[i];
+    else if constexpr (DT == BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+    else return e4m3_to_f32(static_cast<const uint8_t*>(base)[i]);
+}
+
+// Order-preserving map of fp32 onto uint32: a > b as floats <=> key(a) > key(b)
+// as unsigned integers.  -0.0 is folded onto +0.0 first so equal numbers get
+// equal keys.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int row_pos(const int32_t* q_pos, int row, int n_q, int n_k) {
+    int t = row % n_q;
+    int p = q_pos ? q_pos[row] : (n_k - n_q + t);
+    return p < n_k - 1 ? p : n_k - 1;  // may be negative: nothing visible
+}
+
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max_xor_16_32(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+}  // namespace dsa

@@ -1,0 +1,67 @@
+// dsa_kernels.h -- internal launch interface between the C ABI layer and the
+// kernels.  Host-only structs of device pointers and sizes; not part of the
+// public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexArgs {
+    int rows, row0;      // rows handled, absolute index of the first (b*n_q+t)
+    int n_q, n_k, H;
+    int dtype;           // DType
+    const void* iq;
+    const float* iq_scale;
+    const void* ik;
+    const float* ik_scale;
+    const float* iw;
+    const int32_t* q_pos;
+    float* scores;       // [rows, n_k], row 0 = absolute row row0
+};
+
+// Top-k workspace (device), per row r:
+//   hist  [rows][2048] uint32  counts of the top 11 bits of the order key
+//   count [rows][2]    uint32  {kept-above-threshold, threshold-bucket candidates}
+//   cand  [rows][cap]  uint64  (low 21 key bits << 32 | ~position) candidates
+constexpr int kTopkBins = 2048;
+constexpr int kTopkCandCap = 4096;
+constexpr int kTopkMaxK = 8192;
+
+struct TopkArgs {
+    int rows, row0;        // rows handled, absolute index of the first (for pos)
+    int n_q, n_k, k;
+    const int32_t* q_pos;
+    const float* scores;   // row stride n_k
+    int32_t* idx;          // [rows, k]
+    uint32_t* hist;
+    uint32_t* count;
+    uint64_t* cand;
+    int cand_cap;
+    bool hist_ready;       // the scores producer already filled `hist`
+};
+
+size_t topk_workspace_bytes(int rows, int n_k);
+void topk_carve(void* ws, int rows, TopkArgs& a);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
+
+struct AttnArgs {
+    int rows, n_q, n_k, kk;
+    int Hq, Hkv, dqk, dv, latent, dtype;
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* idx;    // [rows, kk]
+    const int32_t* q_pos;
+    float scale;
+    void* out;             // [rows, Hq, dv]
+    float* lse;            // [rows, Hq] or null
+};
+
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+
+}  // namespace dsa

@@ -51,6 +51,8 @@ def _load():
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     i64, dbl, vp, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+    lib.ora_num_threads.restype = ctypes.c_int
+    lib.ora_num_threads.argtypes = []
     lib.ora_e4m3_value.restype = dbl
     lib.ora_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.ora_bf16_value.restype = dbl
@@ -90,6 +92,11 @@ def _positions(pos, n_q, n_k):
     if pos is None:
         pos = np.arange(n_q, dtype=np.int64) + (n_k - n_q)
     return np.ascontiguousarray(pos, dtype=np.int64)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().ora_num_threads())
 
 
 def e4m3_value(code: int) -> float:

@@ -40,7 +40,21 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_E4M3 = 2 };
+
+/* Threads the parallel loops below use. */
+int ora_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* OCP FP8 E4M3 ("E4M3FN"): 1 sign bit, 4 exponent bits with bias 7, 3
  * mantissa bits.  Exponent field 0 encodes subnormals m/8 * 2^-6.  There is no
@@ -101,14 +115,15 @@ void ora_index_scores(int64_t n_q, int64_t n_k, int64_t H, int64_t D, int dtype,
                       const void *ik, const float *ik_scale,
                       const float *iw, const int64_t *pos, double *out)
 {
-    #pragma omp parallel
-    {
-        double *q = (double *)malloc(sizeof(double) * (size_t)(H * D));
-        double *k = (double *)malloc(sizeof(double) * (size_t)D);
-        #pragma omp for schedule(dynamic, 1)
-        for (int64_t t = 0; t < n_q; ++t) {
-            double sq = iq_scale ? (double)iq_scale[t] : 1.0;
-            load_row(iq, dtype, t * H * D, H * D, sq, q);
+    double *q = (double *)malloc(sizeof(double) * (size_t)(H * D));
+    for (int64_t t = 0; t < n_q; ++t) {
+        double sq = iq_scale ? (double)iq_scale[t] : 1.0;
+        load_row(iq, dtype, t * H * D, H * D, sq, q);
+        /* keys are independent: split them over threads */
+        #pragma omp parallel
+        {
+            double *k = (double *)malloc(sizeof(double) * (size_t)D);
+            #pragma omp for schedule(static)
             for (int64_t s = 0; s < n_k; ++s) {
                 if (s > pos[t]) {
                     out[t * n_k + s] = -INFINITY;
@@ -126,10 +141,10 @@ void ora_index_scores(int64_t n_q, int64_t n_k, int64_t H, int64_t D, int dtype,
                 }
                 out[t * n_k + s] = score;
             }
+            free(k);
         }
-        free(q);
-        free(k);
     }
+    free(q);
 }
 
 typedef struct { double score; int64_t index; } ora_pair;

@@ -1,0 +1,144 @@
+"""CPU checks of the C ABI: the library loads, exports what include/dsa.h
+declares, its struct layout matches the binding, and host-side validation
+rejects bad calls before anything reaches a device (no kernel is launched in
+these tests: every call here fails validation first)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_sparse_relu_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        pytest.fail("libdsa.so is not built (python -m long_context_sparse_relu_amd.build)")
+    return dsa.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = _declared()
+    assert set(names) == set(dsa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libdsa.so"
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (dsa_\w+)", out))
+    assert exported == set(names)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.dsa_abi_version() == dsa.ABI_VERSION
+    for st in (dsa.OK, dsa.E_INVALID, dsa.E_UNSUPPORTED, dsa.E_WORKSPACE, dsa.E_DEVICE):
+        assert dsa.status_str(st).startswith("DSA_")
+    assert "unknown" in dsa.status_str(42)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields = [f[0] for f in dsa.Problem._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'    printf("%s %zu\\n", "{f}", offsetof(dsa_problem_t, {f}));' for f in fields)
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"dsa.h\"\nint main(void){\n"
+                   + body + '\n    printf("sizeof %zu\\n", sizeof(dsa_problem_t));\n    return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(dsa.Problem, f).offset, f
+    assert int(got["sizeof"]) == ctypes.sizeof(dsa.Problem)
+
+
+def _problem(**over):
+    p = dsa.Problem()
+    p.batch, p.n_q, p.n_k = 2, 1, 4096
+    p.idx_heads, p.idx_dim, p.idx_dtype = 16, 128, dsa.FP8_E4M3
+    fake = 0x7F0000000000  # never dereferenced: every call below fails validation first
+    p.iq = p.ik = p.iw = p.iq_scale = p.ik_scale = fake
+    p.q_heads, p.kv_heads, p.d_qk, p.d_v, p.kv_latent = 32, 4, 128, 128, 0
+    p.attn_dtype = dsa.BF16
+    p.q = p.k = p.v = fake
+    p.softmax_scale = 0.088
+    p.top_k = 2048
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+FAKE = ctypes.c_void_p(0x7F0000000000)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(batch=0), dsa.E_INVALID),
+    (dict(n_q=0), dsa.E_INVALID),
+    (dict(n_q=5000), dsa.E_INVALID),
+    (dict(n_k=(1 << 24) + 1, n_q=1), dsa.E_UNSUPPORTED),
+    (dict(idx_dim=64), dsa.E_UNSUPPORTED),
+    (dict(idx_heads=65), dsa.E_UNSUPPORTED),
+    (dict(idx_dtype=7), dsa.E_INVALID),
+    (dict(iq_scale=None), dsa.E_INVALID),
+    (dict(iw=None), dsa.E_INVALID),
+    (dict(top_k=0), dsa.E_UNSUPPORTED),
+    (dict(top_k=8193), dsa.E_UNSUPPORTED),
+    (dict(kv_heads=5), dsa.E_INVALID),
+    (dict(v=None), dsa.E_INVALID),
+    (dict(kv_latent=1), dsa.E_INVALID),             # latent needs kv_heads == 1
+    (dict(d_qk=1024), dsa.E_UNSUPPORTED),
+    (dict(attn_dtype=dsa.FP8_E4M3), dsa.E_UNSUPPORTED),
+    (dict(softmax_scale=0.0), dsa.E_INVALID),
+    (dict(softmax_scale=float("inf")), dsa.E_INVALID),
+    (dict(n_q=2), dsa.E_INVALID),                   # decode takes one query row
+])
+def test_decode_validation(lib, over, status):
+    p = _problem(**over)
+    st = lib.dsa_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == status, dsa.last_error()
+    assert dsa.last_error()
+
+
+def test_null_problem_and_outputs(lib):
+    assert lib.dsa_index_scores(None, FAKE, None) == dsa.E_INVALID
+    p = _problem()
+    assert lib.dsa_index_scores(ctypes.byref(p), None, None) == dsa.E_INVALID
+    assert lib.dsa_topk(ctypes.byref(p), None, FAKE, FAKE, 1 << 40, None) == dsa.E_INVALID
+    assert lib.dsa_sparse_attn(ctypes.byref(p), None, FAKE, None, None, 0, None) == dsa.E_INVALID
+    assert lib.dsa_prefill(ctypes.byref(p), None, None, None, FAKE, 1 << 40, None) == dsa.E_INVALID
+
+
+def test_workspace_sizes_and_shortfall(lib):
+    p = _problem()
+    need_topk = lib.dsa_workspace_bytes(dsa.OP_TOPK, ctypes.byref(p))
+    need_dec = lib.dsa_workspace_bytes(dsa.OP_DECODE, ctypes.byref(p))
+    assert 0 < need_topk < need_dec
+    assert lib.dsa_workspace_bytes(dsa.OP_INDEX_SCORES, ctypes.byref(p)) == 0
+    assert lib.dsa_workspace_bytes(99, ctypes.byref(p)) == ctypes.c_size_t(-1).value
+    assert lib.dsa_topk(ctypes.byref(p), FAKE, FAKE, FAKE, need_topk - 1, None) == dsa.E_WORKSPACE
+    assert lib.dsa_topk(ctypes.byref(p), FAKE, FAKE, None, need_topk, None) == dsa.E_WORKSPACE
+    # idx_out NULL: the workspace must also hold the selection, which is what need_dec counts
+    assert lib.dsa_decode(ctypes.byref(p), FAKE, FAKE, None, FAKE, need_dec - 1, None) == dsa.E_WORKSPACE
+    assert "workspace" in dsa.last_error()
+    bad = _problem(n_q=3)
+    assert lib.dsa_workspace_bytes(dsa.OP_DECODE, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+
+
+def test_binding_rejects_missing_library(tmp_path):
+    saved = dsa._lib
+    dsa._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            dsa.load_library(str(tmp_path / "nope.so"))
+    finally:
+        dsa._lib = saved
