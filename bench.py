@@ -89,7 +89,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_128k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=16, help="sequences the oracle baseline runs")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="sequences the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phase-reps", type=int, default=10)
     args = ap.parse_args(argv)

@@ -321,17 +321,17 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(k_attn_bf16_d128, dim3(a.Hkv, a.rows), dim3(kGqaWaves * 64), 0, st, a);
         return hipGetLastError();
     }
-    static bool lds_raised = false;
-    if (!lds_raised) {   // the latent shape stages ~104 KiB of rows
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_generic<F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_generic<BF16>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        lds_raised = true;
+    const size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +
+                         static_cast<size_t>(kGenTK) * a.dv) * sizeof(float);
+    if (smem > 64 * 1024) {   // the latent shape stages ~104 KiB of rows
+        hipError_t e = a.dtype == F32
+            ? hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_generic<F32>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem))
+            : hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_generic<BF16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (e != hipSuccess) return e;
     }
     dim3 grid((G + kGenHC - 1) / kGenHC, a.Hkv, a.rows);
-    size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +
-                   static_cast<size_t>(kGenTK) * a.dv) * sizeof(float);
     if (a.dtype == F32)
         hipLaunchKernelGGL(k_attn_generic<F32>, grid, dim3(kGenThreads), smem, st, a);
     else

@@ -324,11 +324,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     int kpad = 1;
     while (kpad < a.k) kpad <<= 1;
     const size_t smem = kTopkCandCap * sizeof(uint64_t) + static_cast<size_t>(kpad) * sizeof(int32_t);
-    static bool lds_raised = false;
-    if (!lds_raised) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-        lds_raised = true;
+    if (smem > 64 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_topk_finish, dim3(a.rows), dim3(kFinishThreads), smem, st, a);
     return hipGetLastError();
