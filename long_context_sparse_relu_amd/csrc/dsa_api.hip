@@ -107,7 +107,7 @@ dsa::TopkArgs topk_args(const dsa_problem_t* p, int row0, int rows, const float*
     a.q_pos = p->q_pos;
     a.scores = scores;
     a.idx = idx;
-    dsa::topk_carve(ws, rows, a);
+    dsa::topk_carve(ws, rows, p->n_k, a);
     a.hist_ready = false;
     return a;
 }
@@ -158,10 +158,19 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
     for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
         int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
         dsa::IndexArgs ia = index_args(p, r0, nr, scores);
-        dsa_status_t s = device_status(dsa::launch_index_scores(ia, st), "indexer launch");
-        if (s != DSA_OK) return s;
         dsa::TopkArgs ta = topk_args(p, r0, nr, scores, idx + static_cast<size_t>(r0) * p->top_k,
                                      base + L.topk_off);
+        dsa_status_t s;
+        if (dsa::index_fills_hist(ia)) {
+            // the indexer builds the first-digit histogram as it writes the scores
+            ia.hist = ta.hist;
+            ta.hist_ready = true;
+            size_t n = static_cast<size_t>(nr) * dsa::kTopkBins + static_cast<size_t>(nr) * 2;
+            s = device_status(dsa::launch_zero_u32(ta.hist, n, st), "workspace clear");
+            if (s != DSA_OK) return s;
+        }
+        s = device_status(dsa::launch_index_scores(ia, st), "indexer launch");
+        if (s != DSA_OK) return s;
         s = device_status(dsa::launch_topk(ta, st), "top-k launch");
         if (s != DSA_OK) return s;
     }

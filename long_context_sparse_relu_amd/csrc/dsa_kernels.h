@@ -20,6 +20,7 @@ struct IndexArgs {
     const float* iw;
     const int32_t* q_pos;
     float* scores;       // [rows, n_k], row 0 = absolute row row0
+    uint32_t* hist;      // optional [rows][kTopkBins] top-k histogram to accumulate into
 };
 
 // Top-k workspace (device), per row r:
@@ -27,7 +28,7 @@ struct IndexArgs {
 //   count [rows][2]    uint32  {kept-above-threshold, threshold-bucket candidates}
 //   cand  [rows][cap]  uint64  (low 21 key bits << 32 | ~position) candidates
 constexpr int kTopkBins = 2048;
-constexpr int kTopkCandCap = 4096;
+constexpr int kTopkCandCapMax = 12288;   // candidates per row kept for the LDS select
 constexpr int kTopkMaxK = 8192;
 
 struct TopkArgs {
@@ -40,11 +41,12 @@ struct TopkArgs {
     uint32_t* count;
     uint64_t* cand;
     int cand_cap;
-    bool hist_ready;       // the scores producer already filled `hist`
+    bool hist_ready;       // hist and count were zeroed and the scores producer filled hist
 };
 
 size_t topk_workspace_bytes(int rows, int n_k);
-void topk_carve(void* ws, int rows, TopkArgs& a);
+int topk_cand_cap(int n_k);
+void topk_carve(void* ws, int rows, int n_k, TopkArgs& a);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 
@@ -62,6 +64,9 @@ struct AttnArgs {
 };
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st);
+// True when launch_index_scores accumulates a.hist (the top-k's first-digit
+// histogram) while it writes the scores.
+bool index_fills_hist(const IndexArgs& a);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 
 }  // namespace dsa

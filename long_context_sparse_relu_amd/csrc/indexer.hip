@@ -76,30 +76,47 @@ __global__ __launch_bounds__(256) void k_index_generic(
 // FP8 streaming path (decode and any row count): up to 16 heads, d = 128.
 // One v_mfma_scale_f32_16x16x128_f8f6f4 multiplies the query row's 16 heads
 // (rows of A) by 16 keys (columns of B) over the full 128-wide dot product.
-// Lane l feeds A row l%16 and B column l%16 with the 32 code bytes at offset
-// 32*(l/16); A and B use the same byte->k assignment, so the contraction is
-// correct whatever order the unit sums them in.  The 16x16 result lands as
-// acc[i] = dot(head 4*(l/16)+i, key l%16): ReLU, head weight, then two
-// cross-lane adds finish the head reduction.  Keys stream straight from HBM
-// (every byte read once); each wave keeps U blocks of 16 keys in flight.
+// Lane l feeds A row l%16 and B column l%16 with 32 code bytes: bytes
+// [16g, 16g+16) and [64+16g, 64+16g+16) of the row, g = l/16.  A and B use the
+// same byte->k assignment, so the contraction is exact whatever order the
+// unit sums in, and each 16-byte load instruction of a wave covers 64
+// contiguous bytes of every key row it touches.  The 16x16 result lands as
+// acc[i] = dot(head 4g+i, key l%16): ReLU, head weight, then two cross-lane
+// adds finish the head reduction.  Keys stream from HBM once; each wave keeps
+// U blocks of 16 keys in flight.  When `hist` is given, the workgroup also
+// counts the top 11 bits of each visible score's order key in LDS and adds its
+// non-empty bins to the row's histogram, which saves the top-k a pass.
 // ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8i load_split32(const uint8_t* row, int g) {
+    v4i lo = *reinterpret_cast<const v4i*>(row + 16 * g);
+    v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * g);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int U>
 __global__ __launch_bounds__(256) void k_index_fp8_mfma(
     const uint8_t* __restrict__ iq, const float* __restrict__ iq_scale,
     const uint8_t* __restrict__ ik, const float* __restrict__ ik_scale,
     const float* __restrict__ iw, const int32_t* __restrict__ q_pos,
-    int row0, int n_q, int n_k, int H, int keys_per_block, float* __restrict__ scores)
+    int row0, int n_q, int n_k, int H, int keys_per_block, float* __restrict__ scores,
+    uint32_t* __restrict__ hist)
 {
+    __shared__ uint32_t lh[kTopkBins];
     const int row = row0 + blockIdx.y;
     const int b = row / n_q;
     const int pos = row_pos(q_pos, row, n_q, n_k);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;       // A row (head) and B column (key in block)
-    const int kg = lane >> 4;        // which 32-byte slice of the 128-byte rows
+    const int kg = lane >> 4;        // which byte slices of the 128-byte rows
 
+    if (hist) {
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+    }
     v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col < H) a = *reinterpret_cast<const v8i*>(iq + (static_cast<size_t>(row) * H + col) * 128 + kg * 32);
+    if (col < H) a = load_split32(iq + (static_cast<size_t>(row) * H + col) * 128, kg);
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -110,6 +127,7 @@ __global__ __launch_bounds__(256) void k_index_fp8_mfma(
     const uint8_t* kb = ik + static_cast<size_t>(b) * n_k * 128;
     const float* ksb = ik_scale + static_cast<size_t>(b) * n_k;
     float* out = scores + static_cast<size_t>(blockIdx.y) * n_k;
+    if (hist) __syncthreads();
 
     const int s_begin = blockIdx.x * keys_per_block;
     const int s_end = min(s_begin + keys_per_block, n_k);
@@ -121,7 +139,7 @@ __global__ __launch_bounds__(256) void k_index_fp8_mfma(
         for (int u = 0; u < U; ++u) {
             int s = base + u * 16 + col;
             bool live = s < s_end && s <= pos;
-            bv[u] = live ? *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(s) * 128 + kg * 32)
+            bv[u] = live ? load_split32(kb + static_cast<size_t>(s) * 128, kg)
                          : v8i{0, 0, 0, 0, 0, 0, 0, 0};
             sk[u] = live ? ksb[s] : 0.0f;
         }
@@ -135,8 +153,18 @@ __global__ __launch_bounds__(256) void k_index_fp8_mfma(
             part = fmaf(w[3], fmaxf(acc[3], 0.0f), part);
             part = wave_sum_xor_16_32(part);
             int s = base + u * 16 + col;
-            if (kg == 0 && s < s_end) out[s] = s <= pos ? part * (sq * sk[u]) : -__builtin_inff();
+            if (kg == 0 && s < s_end) {
+                float score = s <= pos ? part * (sq * sk[u]) : -__builtin_inff();
+                out[s] = score;
+                if (hist && s <= pos) atomicAdd(&lh[order_key(score) >> 21], 1u);
+            }
         }
+    }
+    if (hist) {
+        __syncthreads();
+        uint32_t* gh = hist + static_cast<size_t>(blockIdx.y) * kTopkBins;
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
+            if (lh[i]) atomicAdd(&gh[i], lh[i]);
     }
 }
 
@@ -158,6 +186,10 @@ static hipError_t launch_generic_dt(const IndexArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+bool index_fills_hist(const IndexArgs& a) {
+    return a.dtype == E4M3 && a.H <= 16;
+}
+
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st) {
     if (a.dtype == E4M3 && a.H <= 16) {
         constexpr int U = 4;
@@ -166,7 +198,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((k_index_fp8_mfma<U>), grid, dim3(256), 0, st,
                            static_cast<const uint8_t*>(a.iq), a.iq_scale,
                            static_cast<const uint8_t*>(a.ik), a.ik_scale, a.iw, a.q_pos,
-                           a.row0, a.n_q, a.n_k, a.H, kpb, a.scores);
+                           a.row0, a.n_q, a.n_k, a.H, kpb, a.scores, a.hist);
         return hipGetLastError();
     }
     switch (a.dtype) {

@@ -23,8 +23,9 @@
 
 namespace dsa {
 
-constexpr int kChunk = 4096;       // scores per workgroup in hist/filter
+constexpr int kChunk = 2048;       // scores per workgroup in hist/filter
 constexpr int kFilterThreads = 256;
+constexpr int kPerThread = kChunk / kFilterThreads;
 constexpr int kFinishThreads = 512;
 
 __global__ void k_zero_u32(uint32_t* p, size_t n) {
@@ -84,7 +85,8 @@ __device__ __forceinline__ int row_visible(const TopkArgs& a, int row) {
     return row_pos(a.q_pos, row, a.n_q, a.n_k) + 1;   // 0..n_k
 }
 
-// Step 1: histogram of the top 11 bits of every visible key.
+// Step 1: histogram of the top 11 bits of every visible key.  Every thread
+// issues all of its loads before it touches any of them.
 __global__ __launch_bounds__(kFilterThreads) void k_topk_hist(TopkArgs a) {
     __shared__ uint32_t lh[kTopkBins];
     const int lrow = blockIdx.y, row = a.row0 + lrow;
@@ -93,11 +95,20 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_hist(TopkArgs a) {
     const int c0 = blockIdx.x * kChunk;
     if (c0 >= vis) return;
     const int c1 = min(c0 + kChunk, vis);
+    const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+    float x[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        int s = c0 + u * kFilterThreads + threadIdx.x;
+        x[u] = s < c1 ? sc[s] : 0.0f;
+    }
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
     __syncthreads();
-    const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
-    for (int s = c0 + threadIdx.x; s < c1; s += blockDim.x)
-        atomicAdd(&lh[order_key(sc[s]) >> 21], 1u);
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        int s = c0 + u * kFilterThreads + threadIdx.x;
+        if (s < c1) atomicAdd(&lh[order_key(x[u]) >> 21], 1u);
+    }
     __syncthreads();
     uint32_t* gh = a.hist + static_cast<size_t>(lrow) * kTopkBins;
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
@@ -118,6 +129,13 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
     const int c0 = blockIdx.x * kChunk;
     if (c0 >= vis) return;
     const int c1 = min(c0 + kChunk, vis);
+    const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+    float x[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        int s = c0 + u * kFilterThreads + threadIdx.x;
+        x[u] = s < c1 ? sc[s] : 0.0f;
+    }
     const uint32_t* gh = a.hist + static_cast<size_t>(lrow) * kTopkBins;
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh[i];
     if (threadIdx.x == 0) { n_sel = 0; n_cand = 0; }
@@ -125,14 +143,12 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
     int d0; uint32_t gt0;
     find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(a.k), scan, &sh_digit, &sh_gt, &d0, &gt0);
 
-    const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
     const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
-    const int span = c1 - c0;
-    const int iters = (span + blockDim.x - 1) / blockDim.x;
-    for (int it = 0; it < iters; ++it) {
-        int s = c0 + it * blockDim.x + threadIdx.x;
-        uint32_t key = s < c1 ? order_key(sc[s]) : 0u;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        int s = c0 + u * kFilterThreads + threadIdx.x;
+        uint32_t key = s < c1 ? order_key(x[u]) : 0u;
         int dg = static_cast<int>(key >> 21);
         bool is_sel = s < c1 && dg > d0;
         bool is_cand = s < c1 && dg == d0;
@@ -188,6 +204,27 @@ struct CandRow {
     }
 };
 
+// Visit every candidate of `src`, eight loads in flight per thread.
+template <class Src, class F>
+__device__ __forceinline__ void for_each_candidate(const Src& src, F&& f) {
+    const int n = src.size();
+    const int T = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + 7 * T < n; i += 8 * T) {
+        uint64_t c[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ok[u] = src.get(i + u * T, &c[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (ok[u]) f(c[u]);
+    }
+    for (; i < n; i += T) {
+        uint64_t c;
+        if (src.get(i, &c)) f(c);
+    }
+}
+
 // Radix-select the k_rem largest composites of `src` and append their
 // positions to sorted[] at *n_out (an LDS counter).
 template <class Src>
@@ -205,11 +242,9 @@ __device__ void select_candidates(const Src& src, uint32_t k_rem, uint32_t* lh, 
         const int nb = 1 << w;
         for (int i = threadIdx.x; i < nb; i += blockDim.x) lh[i] = 0u;
         __syncthreads();
-        for (int i = threadIdx.x; i < src.size(); i += blockDim.x) {
-            uint64_t c;
-            if (!src.get(i, &c)) continue;
+        for_each_candidate(src, [&](uint64_t c) {
             if ((c >> (sh + w)) == prefix) atomicAdd(&lh[(c >> sh) & (nb - 1)], 1u);
-        }
+        });
         __syncthreads();
         int d; uint32_t gt;
         find_threshold_bin(lh, nb, k_rem, scan, sh_digit, sh_gt, &d, &gt);
@@ -220,14 +255,12 @@ __device__ void select_candidates(const Src& src, uint32_t k_rem, uint32_t* lh, 
         __syncthreads();
         if (done) break;
     }
-    for (int i = threadIdx.x; i < src.size(); i += blockDim.x) {
-        uint64_t c;
-        if (!src.get(i, &c)) continue;
+    for_each_candidate(src, [&](uint64_t c) {
         if ((c >> done_shift) >= prefix) {
             uint32_t slot = atomicAdd(n_out, 1u);
             if (slot < cap) sorted[slot] = static_cast<int32_t>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
         }
-    }
+    });
     __syncthreads();
 }
 
@@ -235,7 +268,7 @@ __device__ void select_candidates(const Src& src, uint32_t k_rem, uint32_t* lh, 
 __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint64_t* cl = reinterpret_cast<uint64_t*>(smem);                       // [cand_cap]
-    int32_t* sorted = reinterpret_cast<int32_t*>(cl + kTopkCandCap);         // [kpad]
+    int32_t* sorted = reinterpret_cast<int32_t*>(cl + a.cand_cap);           // [kpad]
     __shared__ uint32_t lh[kTopkBins];
     __shared__ uint32_t scan[kFinishThreads];
     __shared__ int sh_digit;
@@ -260,7 +293,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     const uint32_t n_cand = a.count[static_cast<size_t>(lrow) * 2 + 1];
     __syncthreads();
     const uint32_t k_rem = static_cast<uint32_t>(a.k) - gt0;
-    if (n_cand <= static_cast<uint32_t>(a.cand_cap) && n_cand <= static_cast<uint32_t>(kTopkCandCap)) {
+    if (n_cand <= static_cast<uint32_t>(a.cand_cap)) {
         const uint64_t* gc = a.cand + static_cast<size_t>(lrow) * a.cand_cap;
         for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
         __syncthreads();
@@ -286,16 +319,19 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = sorted[j];
 }
 
+int topk_cand_cap(int n_k) {
+    return n_k < kTopkCandCapMax ? n_k : kTopkCandCapMax;
+}
+
 size_t topk_workspace_bytes(int rows, int n_k) {
-    (void)n_k;
     size_t r = static_cast<size_t>(rows);
     size_t hist = r * kTopkBins * sizeof(uint32_t);
     size_t cnt = ((r * 2 * sizeof(uint32_t)) + 255) & ~static_cast<size_t>(255);
-    size_t cand = r * kTopkCandCap * sizeof(uint64_t);
+    size_t cand = r * static_cast<size_t>(topk_cand_cap(n_k)) * sizeof(uint64_t);
     return hist + cnt + cand;
 }
 
-void topk_carve(void* ws, int rows, TopkArgs& a) {
+void topk_carve(void* ws, int rows, int n_k, TopkArgs& a) {
     unsigned char* p = static_cast<unsigned char*>(ws);
     size_t r = static_cast<size_t>(rows);
     a.hist = reinterpret_cast<uint32_t*>(p);
@@ -303,7 +339,7 @@ void topk_carve(void* ws, int rows, TopkArgs& a) {
     a.count = reinterpret_cast<uint32_t*>(p);
     p += ((r * 2 * sizeof(uint32_t)) + 255) & ~static_cast<size_t>(255);
     a.cand = reinterpret_cast<uint64_t*>(p);
-    a.cand_cap = kTopkCandCap;
+    a.cand_cap = topk_cand_cap(n_k);
 }
 
 // `a.rows` rows starting at absolute row a.row0; scores, idx and the
@@ -311,9 +347,10 @@ void topk_carve(void* ws, int rows, TopkArgs& a) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipError_t e;
     const size_t r = static_cast<size_t>(a.rows);
-    if (a.hist_ready) e = launch_zero_u32(a.count, r * 2, st);
-    else e = launch_zero_u32(a.hist, r * kTopkBins + r * 2, st);  // hist and count are adjacent
-    if (e != hipSuccess) return e;
+    if (!a.hist_ready) {
+        e = launch_zero_u32(a.hist, r * kTopkBins + r * 2, st);  // hist and count are adjacent
+        if (e != hipSuccess) return e;
+    }
     const dim3 grid((a.n_k + kChunk - 1) / kChunk, a.rows);
     if (!a.hist_ready) {
         hipLaunchKernelGGL(k_topk_hist, grid, dim3(kFilterThreads), 0, st, a);
@@ -323,7 +360,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int kpad = 1;
     while (kpad < a.k) kpad <<= 1;
-    const size_t smem = kTopkCandCap * sizeof(uint64_t) + static_cast<size_t>(kpad) * sizeof(int32_t);
+    const size_t smem = static_cast<size_t>(a.cand_cap) * sizeof(uint64_t) + static_cast<size_t>(kpad) * sizeof(int32_t);
     if (smem > 64 * 1024) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
