@@ -165,8 +165,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
             // the indexer builds the first-digit histogram as it writes the scores
             ia.hist = ta.hist;
             ta.hist_ready = true;
-            size_t n = static_cast<size_t>(nr) * dsa::kTopkBins + static_cast<size_t>(nr) * 2;
-            s = device_status(dsa::launch_zero_u32(ta.hist, n, st), "workspace clear");
+            s = device_status(dsa::launch_zero_u32(ta.hist, ta.zero_words, st), "workspace clear");
             if (s != DSA_OK) return s;
         }
         s = device_status(dsa::launch_index_scores(ia, st), "indexer launch");

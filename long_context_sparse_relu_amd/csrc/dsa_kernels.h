@@ -24,10 +24,13 @@ struct IndexArgs {
 };
 
 // Top-k workspace (device), per row r:
-//   hist  [rows][2048] uint32  counts of the top 11 bits of the order key
-//   count [rows][2]    uint32  {kept-above-threshold, threshold-bucket candidates}
+//   hist  [rows][2048] uint32  counts of digit 0 (key bits 31..21)
+//   hist1 [rows][2048] uint32  counts of digit 1 (key bits 20..10) in the threshold bin
+//   count [rows][4]    uint32  {kept above, candidates, digit-0 bin, count above it}
 //   cand  [rows][cap]  uint64  (low 21 key bits << 32 | ~position) candidates
+// hist, hist1 and count are contiguous (zero_words words) and must start at 0.
 constexpr int kTopkBins = 2048;
+constexpr int kTopkMeta = 4;
 constexpr int kTopkCandCapMax = 12288;   // candidates per row kept for the LDS select
 constexpr int kTopkMaxK = 8192;
 
@@ -38,10 +41,12 @@ struct TopkArgs {
     const float* scores;   // row stride n_k
     int32_t* idx;          // [rows, k]
     uint32_t* hist;
+    uint32_t* hist1;
     uint32_t* count;
+    size_t zero_words;
     uint64_t* cand;
     int cand_cap;
-    bool hist_ready;       // hist and count were zeroed and the scores producer filled hist
+    bool hist_ready;       // hist..count were zeroed and the scores producer filled hist
 };
 
 size_t topk_workspace_bytes(int rows, int n_k);

@@ -7,17 +7,20 @@
 // lower position.
 //
 // Method: radix select on order-preserving uint32 keys, never a full sort.
-//   1. hist   every workgroup histograms the top 11 key bits of its slice of
-//             the row into LDS and adds the non-empty bins to the row's global
-//             histogram (or the score producer already did this).
-//   2. filter every workgroup finds the bin holding the k-th key, writes the
-//             positions above that bin straight into the output row and
-//             appends the bin's own entries to a candidate list.
-//   3. finish one workgroup per row radix-selects the remaining k' entries
-//             among the candidates in LDS on the 53-bit composite
-//             (low 21 key bits, ~position) -- so equal scores resolve to the
-//             lower position -- then bitonic-sorts the row's k positions.
-// The score row is read twice from memory (steps 1 and 2) and never sorted.
+// Digit 0 is key bits 31..21, digit 1 is key bits 20..10.
+//   hist      the top-11-bit histogram of each row (or the indexer built it
+//             while writing the scores);
+//   threshold one workgroup per row finds the digit-0 bin d0 that holds the
+//             k-th key and the count gt0 above it;
+//   filter    every workgroup streams its slice of the row once: keys above
+//             d0 go straight to the output row, keys in d0 are appended to
+//             the row's candidate list and counted in a digit-1 histogram;
+//   finish    one workgroup per row finds the digit-1 bin d1, keeps the
+//             candidates above it, radix-selects the rest inside d1 on the
+//             composite (low 21 key bits, ~position) -- so equal scores
+//             resolve to the lower position -- and bitonic-sorts the row.
+// The score row is read twice (hist, filter) or once when the indexer built
+// the histogram.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -27,6 +30,9 @@ constexpr int kChunk = 2048;       // scores per workgroup in hist/filter
 constexpr int kFilterThreads = 256;
 constexpr int kPerThread = kChunk / kFilterThreads;
 constexpr int kFinishThreads = 512;
+
+// Row metadata words in TopkArgs::count (kTopkMeta per row).
+enum { M_SEL = 0, M_CAND = 1, M_D0 = 2, M_GT0 = 3 };
 
 __global__ void k_zero_u32(uint32_t* p, size_t n) {
     size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -44,40 +50,40 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
 
 // Block-wide search of the threshold bin: the digit d with
 //   count(bins > d) < k_rem <= count(bins >= d).
-// `hist` (nbins entries) and `scan` (blockDim entries) are LDS.  Every thread
-// returns the same d and count(bins > d).  Requires sum(hist) >= k_rem >= 1.
+// `hist` has nbins LDS entries (nbins a multiple of blockDim.x); `wsum` is an
+// LDS array of one slot per wave plus two result slots.  Every thread returns
+// the same d and count(bins > d).  Requires sum(hist) >= k_rem >= 1.
 __device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t k_rem,
-                                   uint32_t* scan, int* sh_digit, uint32_t* sh_gt,
-                                   int* digit, uint32_t* gt)
+                                   uint32_t* wsum, int* digit, uint32_t* gt)
 {
     const int T = blockDim.x, tid = threadIdx.x;
-    const int per = (nbins + T - 1) / T;
+    const int lane = tid & 63, wave = tid >> 6, nwaves = T >> 6;
+    const int per = nbins / T;
+    const int top = nbins - 1 - tid * per;      // this thread's bins: top, top-1, ...
     uint32_t local = 0;
-    for (int j = 0; j < per; ++j) {
-        int bin = nbins - 1 - (tid * per + j);
-        if (bin >= 0) local += hist[bin];
+    for (int j = 0; j < per; ++j) local += hist[top - j];
+    uint32_t x = local;                          // inclusive scan inside the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
     }
-    scan[tid] = local;
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    for (int off = 1; off < T; off <<= 1) {
-        uint32_t v = tid >= off ? scan[tid - off] : 0u;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    uint32_t excl = scan[tid] - local;
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const uint32_t excl = before + x - local;
     if (excl < k_rem && excl + local >= k_rem) {
         uint32_t run = excl;
         for (int j = 0; j < per; ++j) {
-            int bin = nbins - 1 - (tid * per + j);
-            if (bin < 0) break;
-            if (run + hist[bin] >= k_rem) { *sh_digit = bin; *sh_gt = run; break; }
-            run += hist[bin];
+            uint32_t h = hist[top - j];
+            if (run + h >= k_rem) { wsum[nwaves] = static_cast<uint32_t>(top - j); wsum[nwaves + 1] = run; break; }
+            run += h;
         }
     }
     __syncthreads();
-    *digit = *sh_digit;
-    *gt = *sh_gt;
+    *digit = static_cast<int>(wsum[nwaves]);
+    *gt = wsum[nwaves + 1];
     __syncthreads();
 }
 
@@ -85,8 +91,12 @@ __device__ __forceinline__ int row_visible(const TopkArgs& a, int row) {
     return row_pos(a.q_pos, row, a.n_q, a.n_k) + 1;   // 0..n_k
 }
 
-// Step 1: histogram of the top 11 bits of every visible key.  Every thread
-// issues all of its loads before it touches any of them.
+__device__ __forceinline__ uint64_t composite(uint32_t key, int s) {
+    return (static_cast<uint64_t>(key & 0x1FFFFFu) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(s));
+}
+
+// Digit-0 histogram of every visible key.  Each thread issues all of its
+// loads before it touches any of them.
 __global__ __launch_bounds__(kFilterThreads) void k_topk_hist(TopkArgs a) {
     __shared__ uint32_t lh[kTopkBins];
     const int lrow = blockIdx.y, row = a.row0 + lrow;
@@ -115,14 +125,31 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_hist(TopkArgs a) {
         if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
-// Step 2: keep everything above the threshold bin, collect the bin itself.
-__global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
+// One workgroup per row: locate the digit-0 threshold bin once.
+__global__ __launch_bounds__(kFilterThreads) void k_topk_threshold(TopkArgs a) {
     __shared__ uint32_t lh[kTopkBins];
-    __shared__ uint32_t scan[kFilterThreads];
+    __shared__ uint32_t wsum[kFilterThreads / 64 + 2];
+    const int lrow = blockIdx.x, row = a.row0 + lrow;
+    if (row_visible(a, row) <= a.k) return;
+    const uint32_t* gh = a.hist + static_cast<size_t>(lrow) * kTopkBins;
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh[i];
+    __syncthreads();
+    int d0; uint32_t gt0;
+    find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(a.k), wsum, &d0, &gt0);
+    if (threadIdx.x == 0) {
+        uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
+        meta[M_D0] = static_cast<uint32_t>(d0);
+        meta[M_GT0] = gt0;
+    }
+}
+
+// Keys above d0 go to the output row, keys in d0 become candidates and are
+// counted in the digit-1 histogram.
+__global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
+    __shared__ uint32_t lh1[kTopkBins];
     __shared__ int32_t sel_buf[kChunk];
     __shared__ uint64_t cand_buf[kChunk];
-    __shared__ int sh_digit;
-    __shared__ uint32_t sh_gt, n_sel, n_cand, g_sel, g_cand;
+    __shared__ uint32_t n_sel, n_cand, g_sel, g_cand;
     const int lrow = blockIdx.y, row = a.row0 + lrow;
     const int vis = row_visible(a, row);
     if (vis <= a.k) return;
@@ -136,12 +163,11 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
         int s = c0 + u * kFilterThreads + threadIdx.x;
         x[u] = s < c1 ? sc[s] : 0.0f;
     }
-    const uint32_t* gh = a.hist + static_cast<size_t>(lrow) * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh[i];
+    uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
+    const int d0 = static_cast<int>(meta[M_D0]);
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh1[i] = 0u;
     if (threadIdx.x == 0) { n_sel = 0; n_cand = 0; }
     __syncthreads();
-    int d0; uint32_t gt0;
-    find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(a.k), scan, &sh_digit, &sh_gt, &d0, &gt0);
 
     const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
@@ -162,15 +188,15 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
         bs = __shfl(bs, 0);
         bc = __shfl(bc, 0);
         if (is_sel) sel_buf[bs + __popcll(ms & below)] = s;
-        if (is_cand)
-            cand_buf[bc + __popcll(mc & below)] =
-                (static_cast<uint64_t>(key & 0x1FFFFFu) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(s));
+        if (is_cand) {
+            cand_buf[bc + __popcll(mc & below)] = composite(key, s);
+            atomicAdd(&lh1[(key >> 10) & 0x7FFu], 1u);
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t* cnt = a.count + static_cast<size_t>(lrow) * 2;
-        g_sel = n_sel ? atomicAdd(&cnt[0], n_sel) : 0u;
-        g_cand = n_cand ? atomicAdd(&cnt[1], n_cand) : 0u;
+        g_sel = n_sel ? atomicAdd(&meta[M_SEL], n_sel) : 0u;
+        g_cand = n_cand ? atomicAdd(&meta[M_CAND], n_cand) : 0u;
     }
     __syncthreads();
     int32_t* out = a.idx + static_cast<size_t>(lrow) * a.k;
@@ -183,11 +209,16 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
         uint32_t slot = g_cand + i;
         if (slot < static_cast<uint32_t>(a.cand_cap)) cd[slot] = cand_buf[i];
     }
+    if (n_cand) {
+        uint32_t* gh1 = a.hist1 + static_cast<size_t>(lrow) * kTopkBins;
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
+            if (lh1[i]) atomicAdd(&gh1[i], lh1[i]);
+    }
 }
 
-// Candidate source for the finishing select: the compacted list in LDS, or,
-// when the threshold bin overflowed the list, the score row itself filtered
-// to that bin.
+// Candidate sources for the finishing select: a list (LDS or global), or,
+// when the digit-0 bin overflowed the list, the score row itself filtered to
+// that bin.
 struct CandList {
     const uint64_t* c; int n;
     __device__ int size() const { return n; }
@@ -199,7 +230,7 @@ struct CandRow {
     __device__ bool get(int i, uint64_t* out) const {
         uint32_t key = order_key(sc[i]);
         if (static_cast<int>(key >> 21) != d0) return false;
-        *out = (static_cast<uint64_t>(key & 0x1FFFFFu) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(i));
+        *out = composite(key, i);
         return true;
     }
 };
@@ -225,19 +256,24 @@ __device__ __forceinline__ void for_each_candidate(const Src& src, F&& f) {
     }
 }
 
-// Radix-select the k_rem largest composites of `src` and append their
-// positions to sorted[] at *n_out (an LDS counter).
+__device__ __forceinline__ void emit(int32_t* sorted, uint32_t* n_out, uint32_t cap, uint64_t c) {
+    uint32_t slot = atomicAdd(n_out, 1u);
+    if (slot < cap) sorted[slot] = static_cast<int32_t>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
+}
+
+// Candidates whose top composite digit (key bits 20..10) is d1 share the
+// first 22 key bits; radix-select the k_rem largest of them on the remaining
+// digits and append their positions.
 template <class Src>
-__device__ void select_candidates(const Src& src, uint32_t k_rem, uint32_t* lh, uint32_t* scan,
-                                  int* sh_digit, uint32_t* sh_gt, int32_t* sorted, uint32_t* n_out,
-                                  uint32_t cap)
+__device__ void select_in_bin(const Src& src, int d1, uint32_t k_rem, uint32_t* lh, uint32_t* wsum,
+                              int32_t* sorted, uint32_t* n_out, uint32_t cap)
 {
-    // Digits of the 53-bit composite, most significant first.
-    const int shifts[5] = {42, 31, 20, 9, 0};
-    const int widths[5] = {11, 11, 11, 11, 9};
-    uint64_t prefix = 0;
-    int done_shift = 0;
-    for (int p = 0; p < 5; ++p) {
+    // Digits of the 53-bit composite below the top one, most significant first.
+    const int shifts[4] = {31, 20, 9, 0};
+    const int widths[4] = {11, 11, 11, 9};
+    uint64_t prefix = static_cast<uint64_t>(d1);
+    int done_shift = 42;
+    for (int p = 0; p < 4; ++p) {
         const int sh = shifts[p], w = widths[p];
         const int nb = 1 << w;
         for (int i = threadIdx.x; i < nb; i += blockDim.x) lh[i] = 0u;
@@ -247,7 +283,7 @@ __device__ void select_candidates(const Src& src, uint32_t k_rem, uint32_t* lh, 
         });
         __syncthreads();
         int d; uint32_t gt;
-        find_threshold_bin(lh, nb, k_rem, scan, sh_digit, sh_gt, &d, &gt);
+        find_threshold_bin(lh, nb, k_rem, wsum, &d, &gt);
         k_rem -= gt;
         prefix = (prefix << w) | static_cast<uint64_t>(d);
         done_shift = sh;
@@ -256,23 +292,20 @@ __device__ void select_candidates(const Src& src, uint32_t k_rem, uint32_t* lh, 
         if (done) break;
     }
     for_each_candidate(src, [&](uint64_t c) {
-        if ((c >> done_shift) >= prefix) {
-            uint32_t slot = atomicAdd(n_out, 1u);
-            if (slot < cap) sorted[slot] = static_cast<int32_t>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
-        }
+        if ((c >> done_shift) >= prefix) emit(sorted, n_out, cap, c);
     });
     __syncthreads();
 }
 
-// Step 3: exact select inside the threshold bin, then sort the row's picks.
+// One workgroup per row: candidates above d1 are kept, the d1 bin is
+// resolved exactly, then the row's k positions are sorted ascending.
 __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    uint64_t* cl = reinterpret_cast<uint64_t*>(smem);                       // [cand_cap]
-    int32_t* sorted = reinterpret_cast<int32_t*>(cl + a.cand_cap);           // [kpad]
+    uint64_t* grp = reinterpret_cast<uint64_t*>(smem);                      // [cand_cap]
+    int32_t* sorted = reinterpret_cast<int32_t*>(grp + a.cand_cap);          // [kpad]
     __shared__ uint32_t lh[kTopkBins];
-    __shared__ uint32_t scan[kFinishThreads];
-    __shared__ int sh_digit;
-    __shared__ uint32_t sh_gt, n_out;
+    __shared__ uint32_t wsum[kFinishThreads / 64 + 2];
+    __shared__ uint32_t n_out, n_grp;
     const int lrow = blockIdx.x, row = a.row0 + lrow;
     const int vis = row_visible(a, row);
     int32_t* out = a.idx + static_cast<size_t>(lrow) * a.k;
@@ -280,29 +313,50 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
         for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < vis ? j : -1;
         return;
     }
-    const uint32_t* gh = a.hist + static_cast<size_t>(lrow) * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh[i];
-    __syncthreads();
-    int d0; uint32_t gt0;
-    find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(a.k), scan, &sh_digit, &sh_gt, &d0, &gt0);
+    const uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
+    const uint32_t gt0 = meta[M_GT0];
+    const int d0 = static_cast<int>(meta[M_D0]);
+    const uint32_t n_cand = meta[M_CAND];
+    const uint32_t* gh1 = a.hist1 + static_cast<size_t>(lrow) * kTopkBins;
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh1[i];
     int kpad = 1;
     while (kpad < a.k) kpad <<= 1;
     for (int j = threadIdx.x; j < kpad; j += blockDim.x)
         sorted[j] = j < static_cast<int>(gt0) ? out[j] : 0x7FFFFFFF;
-    if (threadIdx.x == 0) n_out = gt0;
-    const uint32_t n_cand = a.count[static_cast<size_t>(lrow) * 2 + 1];
+    if (threadIdx.x == 0) { n_out = gt0; n_grp = 0; }
     __syncthreads();
-    const uint32_t k_rem = static_cast<uint32_t>(a.k) - gt0;
+    const uint32_t k1 = static_cast<uint32_t>(a.k) - gt0;
+    int d1; uint32_t gt1;
+    find_threshold_bin(lh, kTopkBins, k1, wsum, &d1, &gt1);
+    const uint32_t k2 = k1 - gt1;
+    const bool whole_bin = lh[d1] == k2;
+    const uint32_t cap = static_cast<uint32_t>(a.k);
+    __syncthreads();
+
     if (n_cand <= static_cast<uint32_t>(a.cand_cap)) {
-        const uint64_t* gc = a.cand + static_cast<size_t>(lrow) * a.cand_cap;
-        for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
+        // keep what is above d1, gather the d1 bin into LDS
+        CandList gl{a.cand + static_cast<size_t>(lrow) * a.cand_cap, static_cast<int>(n_cand)};
+        for_each_candidate(gl, [&](uint64_t c) {
+            int dg = static_cast<int>(c >> 42);
+            if (dg > d1 || (dg == d1 && whole_bin)) emit(sorted, &n_out, cap, c);
+            else if (dg == d1) grp[atomicAdd(&n_grp, 1u)] = c;
+        });
         __syncthreads();
-        CandList src{cl, static_cast<int>(n_cand)};
-        select_candidates(src, k_rem, lh, scan, &sh_digit, &sh_gt, sorted, &n_out, static_cast<uint32_t>(a.k));
+        if (!whole_bin) {
+            CandList src{grp, static_cast<int>(n_grp)};
+            select_in_bin(src, d1, k2, lh, wsum, sorted, &n_out, cap);
+        }
     } else {
-        CandRow src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, d0};
-        select_candidates(src, k_rem, lh, scan, &sh_digit, &sh_gt, sorted, &n_out, static_cast<uint32_t>(a.k));
+        // the list overflowed: read the row again, filtered to the d0 bin
+        CandRow row_src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, d0};
+        for_each_candidate(row_src, [&](uint64_t c) {
+            int dg = static_cast<int>(c >> 42);
+            if (dg > d1 || (dg == d1 && whole_bin)) emit(sorted, &n_out, cap, c);
+        });
+        __syncthreads();
+        if (!whole_bin) select_in_bin(row_src, d1, k2, lh, wsum, sorted, &n_out, cap);
     }
+    __syncthreads();
     // Bitonic sort of the kpad entries, ascending.
     for (int size = 2; size <= kpad; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -323,39 +377,40 @@ int topk_cand_cap(int n_k) {
     return n_k < kTopkCandCapMax ? n_k : kTopkCandCapMax;
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 size_t topk_workspace_bytes(int rows, int n_k) {
     size_t r = static_cast<size_t>(rows);
-    size_t hist = r * kTopkBins * sizeof(uint32_t);
-    size_t cnt = ((r * 2 * sizeof(uint32_t)) + 255) & ~static_cast<size_t>(255);
+    size_t zeroed = align256(r * (2 * kTopkBins + kTopkMeta) * sizeof(uint32_t));
     size_t cand = r * static_cast<size_t>(topk_cand_cap(n_k)) * sizeof(uint64_t);
-    return hist + cnt + cand;
+    return zeroed + cand;
 }
 
 void topk_carve(void* ws, int rows, int n_k, TopkArgs& a) {
     unsigned char* p = static_cast<unsigned char*>(ws);
     size_t r = static_cast<size_t>(rows);
     a.hist = reinterpret_cast<uint32_t*>(p);
-    p += r * kTopkBins * sizeof(uint32_t);
-    a.count = reinterpret_cast<uint32_t*>(p);
-    p += ((r * 2 * sizeof(uint32_t)) + 255) & ~static_cast<size_t>(255);
+    a.hist1 = a.hist + r * kTopkBins;
+    a.count = a.hist1 + r * kTopkBins;
+    a.zero_words = r * (2 * kTopkBins + kTopkMeta);
+    p += align256(a.zero_words * sizeof(uint32_t));
     a.cand = reinterpret_cast<uint64_t*>(p);
     a.cand_cap = topk_cand_cap(n_k);
 }
 
 // `a.rows` rows starting at absolute row a.row0; scores, idx and the
-// workspace are indexed from the first of them.
+// workspace are indexed from the first of them.  Unless a.hist_ready, the
+// workspace's counters are cleared and the digit-0 histogram built here.
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipError_t e;
-    const size_t r = static_cast<size_t>(a.rows);
-    if (!a.hist_ready) {
-        e = launch_zero_u32(a.hist, r * kTopkBins + r * 2, st);  // hist and count are adjacent
-        if (e != hipSuccess) return e;
-    }
     const dim3 grid((a.n_k + kChunk - 1) / kChunk, a.rows);
     if (!a.hist_ready) {
+        if ((e = launch_zero_u32(a.hist, a.zero_words, st)) != hipSuccess) return e;
         hipLaunchKernelGGL(k_topk_hist, grid, dim3(kFilterThreads), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    hipLaunchKernelGGL(k_topk_threshold, dim3(a.rows), dim3(kFilterThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_topk_filter, grid, dim3(kFilterThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int kpad = 1;
