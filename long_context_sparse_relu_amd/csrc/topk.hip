@@ -18,7 +18,9 @@
 //   finish    one workgroup per row finds the digit-1 bin d1, keeps the
 //             candidates above it, radix-selects the rest inside d1 on the
 //             composite (low 21 key bits, ~position) -- so equal scores
-//             resolve to the lower position -- and bitonic-sorts the row.
+//             resolve to the lower position -- and writes the kept positions
+//             in ascending order (through an LDS bitmap of the row, or a
+//             bitonic sort for rows too long for one).
 // The score row is read twice (hist, filter) or once when the indexer built
 // the histogram.
 #include "dsa_device.h"
@@ -26,10 +28,14 @@
 
 namespace dsa {
 
-constexpr int kChunk = 2048;       // scores per workgroup in hist/filter
+constexpr int kChunk = 2048;       // scores per workgroup in hist
 constexpr int kFilterThreads = 256;
 constexpr int kPerThread = kChunk / kFilterThreads;
+constexpr int kFChunk = 8192;      // scores per workgroup in filter
+constexpr int kFThreads = 512;
+constexpr int kFPer = kFChunk / kFThreads;
 constexpr int kFinishThreads = 512;
+constexpr int kBitmapMaxKeys = 1 << 18;   // rows up to this long are ordered through a bitmap
 
 // Row metadata words in TopkArgs::count (kTopkMeta per row).
 enum { M_SEL = 0, M_CAND = 1, M_D0 = 2, M_GT0 = 3 };
@@ -143,73 +149,91 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_threshold(TopkArgs a) {
     }
 }
 
+// Block-wide exclusive scan of one value per thread (wave scans, then the
+// wave totals); `wsum` holds one LDS slot per wave.  Returns the exclusive
+// prefix; *total gets the block sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        uint32_t t = wsum[w];
+        if (w < wave) before += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + x - v;
+}
+
 // Keys above d0 go to the output row, keys in d0 become candidates and are
-// counted in the digit-1 histogram.
-__global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
+// counted in the digit-1 histogram.  Each thread classifies kFPer scores held
+// in registers; a block scan of the packed (kept, candidate) counts gives
+// every thread its output offsets, so nothing is staged in LDS.
+__global__ __launch_bounds__(kFThreads) void k_topk_filter(TopkArgs a) {
     __shared__ uint32_t lh1[kTopkBins];
-    __shared__ int32_t sel_buf[kChunk];
-    __shared__ uint64_t cand_buf[kChunk];
-    __shared__ uint32_t n_sel, n_cand, g_sel, g_cand;
+    __shared__ uint32_t wsum[kFThreads / 64];
+    __shared__ uint32_t g_base[2];
     const int lrow = blockIdx.y, row = a.row0 + lrow;
     const int vis = row_visible(a, row);
     if (vis <= a.k) return;
-    const int c0 = blockIdx.x * kChunk;
+    const int c0 = blockIdx.x * kFChunk;
     if (c0 >= vis) return;
-    const int c1 = min(c0 + kChunk, vis);
+    const int c1 = min(c0 + kFChunk, vis);
     const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
-    float x[kPerThread];
+    float x[kFPer];
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-        int s = c0 + u * kFilterThreads + threadIdx.x;
+    for (int u = 0; u < kFPer; ++u) {
+        int s = c0 + u * kFThreads + threadIdx.x;
         x[u] = s < c1 ? sc[s] : 0.0f;
     }
     uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
     const int d0 = static_cast<int>(meta[M_D0]);
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh1[i] = 0u;
-    if (threadIdx.x == 0) { n_sel = 0; n_cand = 0; }
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63;
-    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t key[kFPer];
+    uint32_t nsel = 0, ncand = 0;
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-        int s = c0 + u * kFilterThreads + threadIdx.x;
-        uint32_t key = s < c1 ? order_key(x[u]) : 0u;
-        int dg = static_cast<int>(key >> 21);
-        bool is_sel = s < c1 && dg > d0;
-        bool is_cand = s < c1 && dg == d0;
-        uint64_t ms = __ballot(is_sel);
-        uint64_t mc = __ballot(is_cand);
-        uint32_t bs = 0, bc = 0;
-        if (lane == 0) {
-            if (ms) bs = atomicAdd(&n_sel, static_cast<uint32_t>(__popcll(ms)));
-            if (mc) bc = atomicAdd(&n_cand, static_cast<uint32_t>(__popcll(mc)));
-        }
-        bs = __shfl(bs, 0);
-        bc = __shfl(bc, 0);
-        if (is_sel) sel_buf[bs + __popcll(ms & below)] = s;
-        if (is_cand) {
-            cand_buf[bc + __popcll(mc & below)] = composite(key, s);
-            atomicAdd(&lh1[(key >> 10) & 0x7FFu], 1u);
-        }
+    for (int u = 0; u < kFPer; ++u) {
+        int s = c0 + u * kFThreads + threadIdx.x;
+        key[u] = order_key(x[u]);
+        int dg = s < c1 ? static_cast<int>(key[u] >> 21) : -1;
+        nsel += dg > d0;
+        ncand += dg == d0;
     }
-    __syncthreads();
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan((nsel << 16) | ncand, wsum, &total);
     if (threadIdx.x == 0) {
-        g_sel = n_sel ? atomicAdd(&meta[M_SEL], n_sel) : 0u;
-        g_cand = n_cand ? atomicAdd(&meta[M_CAND], n_cand) : 0u;
+        uint32_t ts = total >> 16, tc = total & 0xFFFFu;
+        g_base[0] = ts ? atomicAdd(&meta[M_SEL], ts) : 0u;
+        g_base[1] = tc ? atomicAdd(&meta[M_CAND], tc) : 0u;
     }
     __syncthreads();
+    uint32_t os = g_base[0] + (off >> 16);
+    uint32_t oc = g_base[1] + (off & 0xFFFFu);
     int32_t* out = a.idx + static_cast<size_t>(lrow) * a.k;
-    for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
-        uint32_t slot = g_sel + i;
-        if (slot < static_cast<uint32_t>(a.k)) out[slot] = sel_buf[i];
-    }
     uint64_t* cd = a.cand + static_cast<size_t>(lrow) * a.cand_cap;
-    for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
-        uint32_t slot = g_cand + i;
-        if (slot < static_cast<uint32_t>(a.cand_cap)) cd[slot] = cand_buf[i];
+#pragma unroll
+    for (int u = 0; u < kFPer; ++u) {
+        int s = c0 + u * kFThreads + threadIdx.x;
+        int dg = s < c1 ? static_cast<int>(key[u] >> 21) : -1;
+        if (dg > d0) {
+            if (os < static_cast<uint32_t>(a.k)) out[os] = s;
+            ++os;
+        } else if (dg == d0) {
+            if (oc < static_cast<uint32_t>(a.cand_cap)) cd[oc] = composite(key[u], s);
+            ++oc;
+            atomicAdd(&lh1[(key[u] >> 10) & 0x7FFu], 1u);
+        }
     }
-    if (n_cand) {
+    __syncthreads();
+    if ((total & 0xFFFFu) != 0) {
         uint32_t* gh1 = a.hist1 + static_cast<size_t>(lrow) * kTopkBins;
         for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
             if (lh1[i]) atomicAdd(&gh1[i], lh1[i]);
@@ -256,17 +280,33 @@ __device__ __forceinline__ void for_each_candidate(const Src& src, F&& f) {
     }
 }
 
-__device__ __forceinline__ void emit(int32_t* sorted, uint32_t* n_out, uint32_t cap, uint64_t c) {
-    uint32_t slot = atomicAdd(n_out, 1u);
-    if (slot < cap) sorted[slot] = static_cast<int32_t>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
-}
+// Where the finish puts kept positions: bits of an LDS bitmap over the row
+// (rows up to kBitmapMaxKeys keys; read back in position order), or an LDS
+// list sorted afterwards.
+struct Sink {
+    uint32_t* bitmap;      // null when the list is used
+    int32_t* list;
+    uint32_t* n_list;
+    uint32_t cap;
+    __device__ void put(int s) const {
+        if (bitmap) {
+            atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+        } else {
+            uint32_t slot = atomicAdd(n_list, 1u);
+            if (slot < cap) list[slot] = s;
+        }
+    }
+    __device__ void put_c(uint64_t c) const {
+        put(static_cast<int>(~static_cast<uint32_t>(c & 0xFFFFFFFFull)));
+    }
+};
 
 // Candidates whose top composite digit (key bits 20..10) is d1 share the
 // first 22 key bits; radix-select the k_rem largest of them on the remaining
-// digits and append their positions.
+// digits and keep them.
 template <class Src>
 __device__ void select_in_bin(const Src& src, int d1, uint32_t k_rem, uint32_t* lh, uint32_t* wsum,
-                              int32_t* sorted, uint32_t* n_out, uint32_t cap)
+                              const Sink& sink)
 {
     // Digits of the 53-bit composite below the top one, most significant first.
     const int shifts[4] = {31, 20, 9, 0};
@@ -292,20 +332,21 @@ __device__ void select_in_bin(const Src& src, int d1, uint32_t k_rem, uint32_t* 
         if (done) break;
     }
     for_each_candidate(src, [&](uint64_t c) {
-        if ((c >> done_shift) >= prefix) emit(sorted, n_out, cap, c);
+        if ((c >> done_shift) >= prefix) sink.put_c(c);
     });
     __syncthreads();
 }
 
 // One workgroup per row: candidates above d1 are kept, the d1 bin is
-// resolved exactly, then the row's k positions are sorted ascending.
+// resolved exactly, then the row's k positions are written in ascending
+// order.
 __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint64_t* grp = reinterpret_cast<uint64_t*>(smem);                      // [cand_cap]
-    int32_t* sorted = reinterpret_cast<int32_t*>(grp + a.cand_cap);          // [kpad]
+    uint32_t* tail = reinterpret_cast<uint32_t*>(grp + a.cand_cap);          // bitmap or list
     __shared__ uint32_t lh[kTopkBins];
     __shared__ uint32_t wsum[kFinishThreads / 64 + 2];
-    __shared__ uint32_t n_out, n_grp;
+    __shared__ uint32_t n_list, n_grp;
     const int lrow = blockIdx.x, row = a.row0 + lrow;
     const int vis = row_visible(a, row);
     int32_t* out = a.idx + static_cast<size_t>(lrow) * a.k;
@@ -313,24 +354,31 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
         for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < vis ? j : -1;
         return;
     }
+    const bool use_bitmap = a.n_k <= kBitmapMaxKeys;
+    const int nwords = (vis + 31) >> 5;
+    int kpad = 1;
+    while (kpad < a.k) kpad <<= 1;
+    Sink sink{use_bitmap ? tail : nullptr, reinterpret_cast<int32_t*>(tail), &n_list,
+              static_cast<uint32_t>(a.k)};
+    if (use_bitmap) {
+        for (int i = threadIdx.x; i < nwords; i += blockDim.x) tail[i] = 0u;
+    } else {
+        for (int i = threadIdx.x; i < kpad; i += blockDim.x) tail[i] = 0x7FFFFFFFu;
+    }
     const uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
     const uint32_t gt0 = meta[M_GT0];
     const int d0 = static_cast<int>(meta[M_D0]);
     const uint32_t n_cand = meta[M_CAND];
     const uint32_t* gh1 = a.hist1 + static_cast<size_t>(lrow) * kTopkBins;
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh1[i];
-    int kpad = 1;
-    while (kpad < a.k) kpad <<= 1;
-    for (int j = threadIdx.x; j < kpad; j += blockDim.x)
-        sorted[j] = j < static_cast<int>(gt0) ? out[j] : 0x7FFFFFFF;
-    if (threadIdx.x == 0) { n_out = gt0; n_grp = 0; }
+    if (threadIdx.x == 0) { n_list = 0; n_grp = 0; }
     __syncthreads();
+    for (int j = threadIdx.x; j < static_cast<int>(gt0); j += blockDim.x) sink.put(out[j]);
     const uint32_t k1 = static_cast<uint32_t>(a.k) - gt0;
     int d1; uint32_t gt1;
     find_threshold_bin(lh, kTopkBins, k1, wsum, &d1, &gt1);
     const uint32_t k2 = k1 - gt1;
     const bool whole_bin = lh[d1] == k2;
-    const uint32_t cap = static_cast<uint32_t>(a.k);
     __syncthreads();
 
     if (n_cand <= static_cast<uint32_t>(a.cand_cap)) {
@@ -338,26 +386,46 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
         CandList gl{a.cand + static_cast<size_t>(lrow) * a.cand_cap, static_cast<int>(n_cand)};
         for_each_candidate(gl, [&](uint64_t c) {
             int dg = static_cast<int>(c >> 42);
-            if (dg > d1 || (dg == d1 && whole_bin)) emit(sorted, &n_out, cap, c);
+            if (dg > d1 || (dg == d1 && whole_bin)) sink.put_c(c);
             else if (dg == d1) grp[atomicAdd(&n_grp, 1u)] = c;
         });
         __syncthreads();
         if (!whole_bin) {
             CandList src{grp, static_cast<int>(n_grp)};
-            select_in_bin(src, d1, k2, lh, wsum, sorted, &n_out, cap);
+            select_in_bin(src, d1, k2, lh, wsum, sink);
         }
     } else {
         // the list overflowed: read the row again, filtered to the d0 bin
         CandRow row_src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, d0};
         for_each_candidate(row_src, [&](uint64_t c) {
             int dg = static_cast<int>(c >> 42);
-            if (dg > d1 || (dg == d1 && whole_bin)) emit(sorted, &n_out, cap, c);
+            if (dg > d1 || (dg == d1 && whole_bin)) sink.put_c(c);
         });
         __syncthreads();
-        if (!whole_bin) select_in_bin(row_src, d1, k2, lh, wsum, sorted, &n_out, cap);
+        if (!whole_bin) select_in_bin(row_src, d1, k2, lh, wsum, sink);
     }
     __syncthreads();
-    // Bitonic sort of the kpad entries, ascending.
+    if (use_bitmap) {
+        // positions in order: per-thread runs of words, block scan of their popcounts
+        const int per = (nwords + blockDim.x - 1) / blockDim.x;
+        const int w0 = threadIdx.x * per;
+        uint32_t cnt = 0;
+        for (int w = w0; w < min(w0 + per, nwords); ++w) cnt += __popc(tail[w]);
+        uint32_t total;
+        uint32_t o = block_exclusive_scan(cnt, wsum, &total);
+        for (int w = w0; w < min(w0 + per, nwords); ++w) {
+            uint32_t bits = tail[w];
+            while (bits) {
+                int b = __ffs(bits) - 1;
+                bits &= bits - 1;
+                if (o < static_cast<uint32_t>(a.k)) out[o] = (w << 5) + b;
+                ++o;
+            }
+        }
+        return;
+    }
+    // Bitonic sort of the kpad list entries, ascending.
+    int32_t* sorted = reinterpret_cast<int32_t*>(tail);
     for (int size = 2; size <= kpad; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int i = threadIdx.x; i < (kpad >> 1); i += blockDim.x) {
@@ -371,6 +439,15 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
         }
     }
     for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = sorted[j];
+}
+
+// Dynamic LDS of the finish kernel: the candidate group plus the bitmap or list.
+static size_t finish_lds_bytes(const TopkArgs& a) {
+    int kpad = 1;
+    while (kpad < a.k) kpad <<= 1;
+    size_t tail = a.n_k <= kBitmapMaxKeys ? static_cast<size_t>((a.n_k + 31) >> 5) * 4
+                                          : static_cast<size_t>(kpad) * 4;
+    return static_cast<size_t>(a.cand_cap) * sizeof(uint64_t) + tail;
 }
 
 int topk_cand_cap(int n_k) {
@@ -411,11 +488,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     }
     hipLaunchKernelGGL(k_topk_threshold, dim3(a.rows), dim3(kFilterThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_topk_filter, grid, dim3(kFilterThreads), 0, st, a);
+    const dim3 fgrid((a.n_k + kFChunk - 1) / kFChunk, a.rows);
+    hipLaunchKernelGGL(k_topk_filter, fgrid, dim3(kFThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    int kpad = 1;
-    while (kpad < a.k) kpad <<= 1;
-    const size_t smem = static_cast<size_t>(a.cand_cap) * sizeof(uint64_t) + static_cast<size_t>(kpad) * sizeof(int32_t);
+    const size_t smem = finish_lds_bytes(a);
     if (smem > 64 * 1024) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
