@@ -147,8 +147,9 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 fast path: d_qk = d_v = 128, up to 16 query heads per kv head (GQA and
-// MHA).  One workgroup per (query row, kv head), 8 waves; wave w owns a
-// contiguous 1/8 of the row's selected entries, 16 at a time:
+// MHA).  One workgroup per (query row, kv head), 8 waves; the row's index
+// list is staged in LDS first, then wave w owns a contiguous 1/8 of it, 16
+// entries per block:
 //   S^T[key][head] = K Q^T  with 4 x v_mfma_f32_16x16x32_bf16: A = the 16
 //     gathered key rows (lane l: key l%16, its 64 contiguous bytes at
 //     64*(l/16)), B = Q^T held in registers for the whole loop;
@@ -156,17 +157,24 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 //     online-softmax rescale is per lane and P^T is already the B operand of
 //   O^T[dim][head] += V^T P^T with 8 x v_mfma_f32_16x16x16_bf16, where the
 //     V^T operand is read out of a per-wave LDS copy of the 16 value rows.
-// The next 16 rows are loaded while the current ones are multiplied.  The
-// waves' (max, sum, O) are merged through LDS at the end.
+// Each wave keeps DEPTH further blocks of key/value rows in flight in a
+// register ring while it multiplies the current one.  The waves' (max, sum,
+// O) are merged through LDS at the end.
 // ---------------------------------------------------------------------------
+#ifndef DSA_ATTN_DEPTH
+#define DSA_ATTN_DEPTH 2
+#endif
 constexpr int kGqaWaves = 8;
 constexpr int kGqaVStride = 136;   // bf16 elements per staged value row (128 + pad)
 
+template <int DEPTH>
 __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     __shared__ __align__(16) unsigned char smem[kGqaWaves * 16 * 128 * 4];   // 64 KiB
     __shared__ float m_w[kGqaWaves][16], l_w[kGqaWaves][16];
+    extern __shared__ int32_t idx_s[];                                        // [kk]
     uint16_t* v_all = reinterpret_cast<uint16_t*>(smem);                    // during the loop
     float* o_all = reinterpret_cast<float*>(smem);                           // after the loop
+    constexpr int SLOTS = DEPTH + 1;
 
     const int G = a.Hq / a.Hkv;
     const int g = blockIdx.x;
@@ -179,6 +187,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     const int kg = lane >> 4;
     const float zscale = a.scale * kLog2e;
     uint16_t* v_s = v_all + wave * 16 * kGqaVStride;
+
+    const int32_t* idx_row = a.idx + static_cast<size_t>(row) * a.kk;
+    for (int j = threadIdx.x; j < a.kk; j += blockDim.x) idx_s[j] = idx_row[j];
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     const int per = ((a.kk + kGqaWaves * 16 - 1) / (kGqaWaves * 16)) * 16;
     const int j_begin = wave * per;
     const int j_end = min(j_begin + per, a.kk);
-    const int32_t* idx_row = a.idx + static_cast<size_t>(row) * a.kk;
+    const int nblk = j_end > j_begin ? (j_end - j_begin + 15) / 16 : 0;
     const size_t row_elems = static_cast<size_t>(a.Hkv) * 128;
     const uint16_t* kbase = kp + static_cast<size_t>(b) * a.n_k * row_elems + g * 128 + kg * 32;
     const uint16_t* vbase = vp + static_cast<size_t>(b) * a.n_k * row_elems + g * 128 + kg * 32;
@@ -205,35 +216,29 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     v4f o[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    __syncthreads();                               // idx_s is ready
 
-    // prefetch registers
-    v8bf kc[4], vc[4];
-    bool valid_c = false;
-    auto load_block = [&](int j0, v8bf* kr, v8bf* vr, bool& valid) {
-        int j = j0 + col;
-        int s = j < j_end ? idx_row[j] : -1;
-        valid = s >= 0 && s <= pos;
-        if (valid) {
+    v8bf kr[SLOTS][4], vr[SLOTS][4];
+    bool valid[SLOTS];
+    auto load_block = [&](int blk, v8bf* kd, v8bf* vd, bool& ok) {
+        int j = j_begin + blk * 16 + col;
+        int s = j < j_end ? idx_s[j] : -1;
+        ok = s >= 0 && s <= pos;
+        if (ok) {
             const v8bf* ks = reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(s) * row_elems);
             const v8bf* vs = reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(s) * row_elems);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) { kr[c] = ks[c]; vr[c] = vs[c]; }
+            for (int c = 0; c < 4; ++c) { kd[c] = ks[c]; vd[c] = vs[c]; }
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) { kr[c] = v8bf{}; vr[c] = v8bf{}; }
+            for (int c = 0; c < 4; ++c) { kd[c] = v8bf{}; vd[c] = v8bf{}; }
         }
     };
-    if (j_begin < j_end) load_block(j_begin, kc, vc, valid_c);
-
-    for (int j0 = j_begin; j0 < j_end; j0 += 16) {
-        v8bf kn[4], vn[4];
-        bool valid_n = false;
-        if (j0 + 16 < j_end) load_block(j0 + 16, kn, vn, valid_n);
-
+    auto attend_block = [&](const v8bf* kc, const v8bf* vc, bool ok) {
         v4f sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[c], qb[c], sacc, 0, 0, 0);
-        const uint64_t vm = __ballot(valid_c);
+        const uint64_t vm = __ballot(ok);
         float sv[4];
         float bm = -__builtin_inff();
 #pragma unroll
@@ -277,9 +282,22 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
-        valid_c = valid_n;
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < nblk) load_block(d, kr[d], vr[d], valid[d]);
+    for (int i0 = 0; i0 < nblk; i0 += SLOTS) {
+#pragma unroll
+        for (int r = 0; r < SLOTS; ++r) {
+            const int blk = i0 + r;
+            if (blk < nblk) {
+                const int ahead = blk + DEPTH;
+                if (ahead < nblk) load_block(ahead, kr[(r + DEPTH) % SLOTS], vr[(r + DEPTH) % SLOTS],
+                                             valid[(r + DEPTH) % SLOTS]);
+                attend_block(kr[r], vr[r], valid[r]);
+            }
+        }
     }
 
     const float l_tot = wave_sum_xor_16_32(l_part);
@@ -318,7 +336,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
     if (a.dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128 && G <= 16) {
-        hipLaunchKernelGGL(k_attn_bf16_d128, dim3(a.Hkv, a.rows), dim3(kGqaWaves * 64), 0, st, a);
+        const size_t idx_lds = static_cast<size_t>(a.kk) * sizeof(int32_t);   // kk <= 8192: 32 KiB
+        hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH>), dim3(a.Hkv, a.rows), dim3(kGqaWaves * 64),
+                           idx_lds, st, a);
         return hipGetLastError();
     }
     const size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +

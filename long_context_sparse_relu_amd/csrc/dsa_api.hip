@@ -131,17 +131,33 @@ int fused_block_rows(const dsa_problem_t* p) {
     return static_cast<int>(r);
 }
 
+// The sampled top-k (no score rows in memory) serves long FP8 rows; other
+// problems go through score blocks and the full radix select.
+bool use_sampled(const dsa_problem_t* p) {
+    dsa::IndexArgs probe{};
+    probe.dtype = p->idx_dtype;
+    probe.H = p->idx_heads;
+    return dsa::index_fp8_path(probe) && dsa::topk_sampled_eligible(p->n_k, p->top_k);
+}
+
 struct FusedLayout {
+    bool sampled;
     int block_rows;
     size_t scores_off, topk_off, idx_off, total;
 };
 
 FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
     FusedLayout L{};
+    L.sampled = use_sampled(p);
     L.block_rows = fused_block_rows(p);
     L.scores_off = 0;
-    L.topk_off = align_up(static_cast<size_t>(L.block_rows) * p->n_k * sizeof(float));
-    L.idx_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
+    if (L.sampled) {
+        L.topk_off = 0;
+        L.idx_off = align_up(dsa::topk_sampled_workspace_bytes(L.block_rows, p->n_k));
+    } else {
+        L.topk_off = align_up(static_cast<size_t>(L.block_rows) * p->n_k * sizeof(float));
+        L.idx_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
+    }
     L.total = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t)) : 0);
     return L;
 }
@@ -152,15 +168,29 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
     if (!ws || ws_bytes < L.total)
         return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
     unsigned char* base = static_cast<unsigned char*>(ws);
-    float* scores = reinterpret_cast<float*>(base + L.scores_off);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx_off);
     const int rows = rows_of(p);
     for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
         int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
+        dsa_status_t s;
+        if (L.sampled) {
+            dsa::SampledTopk t{};
+            t.ix = index_args(p, r0, nr, nullptr);
+            t.ix.k = p->top_k;
+            t.idx = idx + static_cast<size_t>(r0) * p->top_k;
+            dsa::topk_sampled_carve(base, nr, p->n_k, t);
+            s = device_status(dsa::launch_topk_sample(t, st), "top-k sample launch");
+            if (s != DSA_OK) return s;
+            s = device_status(dsa::launch_index_candidates(t.ix, st), "indexer launch");
+            if (s != DSA_OK) return s;
+            s = device_status(dsa::launch_topk_finish_sampled(t, st), "top-k launch");
+            if (s != DSA_OK) return s;
+            continue;
+        }
+        float* scores = reinterpret_cast<float*>(base + L.scores_off);
         dsa::IndexArgs ia = index_args(p, r0, nr, scores);
         dsa::TopkArgs ta = topk_args(p, r0, nr, scores, idx + static_cast<size_t>(r0) * p->top_k,
                                      base + L.topk_off);
-        dsa_status_t s;
         if (dsa::index_fills_hist(ia)) {
             // the indexer builds the first-digit histogram as it writes the scores
             ia.hist = ta.hist;

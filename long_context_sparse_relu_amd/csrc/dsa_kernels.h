@@ -12,6 +12,7 @@ namespace dsa {
 struct IndexArgs {
     int rows, row0;      // rows handled, absolute index of the first (b*n_q+t)
     int n_q, n_k, H;
+    int k;               // top_k (candidate mode)
     int dtype;           // DType
     const void* iq;
     const float* iq_scale;
@@ -21,6 +22,10 @@ struct IndexArgs {
     const int32_t* q_pos;
     float* scores;       // [rows, n_k], row 0 = absolute row row0
     uint32_t* hist;      // optional [rows][kTopkBins] top-k histogram to accumulate into
+    // candidate mode (sampled top-k): per-row metadata and candidate lists
+    uint32_t* meta;      // [rows][kTopkMeta]
+    uint64_t* cand;      // [rows][cand_cap]
+    int cand_cap;
 };
 
 // Top-k workspace (device), per row r:
@@ -31,6 +36,9 @@ struct IndexArgs {
 // hist, hist1 and count are contiguous (zero_words words) and must start at 0.
 constexpr int kTopkBins = 2048;
 constexpr int kTopkMeta = 4;
+constexpr int kIdxCandBuf = 1024;        // candidates one indexer workgroup can hold in LDS
+// Row metadata of the sampled top-k (TopkArgs::count / IndexArgs::meta).
+enum { S_NCAND = 0, S_KLOW = 1, S_OVF = 2, S_FALLBACK = 3 };
 constexpr int kTopkCandCapMax = 12288;   // candidates per row kept for the LDS select
 constexpr int kTopkMaxK = 8192;
 
@@ -72,6 +80,29 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st);
 // True when launch_index_scores accumulates a.hist (the top-k's first-digit
 // histogram) while it writes the scores.
 bool index_fills_hist(const IndexArgs& a);
+// True for the FP8 MFMA path (E4M3, <= 16 heads), which also has the
+// candidate mode used by the sampled top-k.
+bool index_fp8_path(const IndexArgs& a);
+// Candidate mode of the FP8 indexer: no scores are written, only the keys at
+// or above the row's sampled bound are appended to a.cand (see topk_sampled).
+hipError_t launch_index_candidates(const IndexArgs& a, hipStream_t st);
+
+// Sampled top-k for long rows (n_k >= 16 k): a sample of each row bounds the
+// k-th score from below, the indexer keeps only keys above the bound, and an
+// exact select runs over those candidates.  A row whose bound proves too high
+// or whose candidates overflow is recomputed and selected in full.
+struct SampledTopk {
+    IndexArgs ix;          // the indexer inputs (ix.meta / ix.cand set from here)
+    int32_t* idx;          // [rows, k]
+    float* scratch;        // [rows, n_k] fp32, used only by a recomputed row
+};
+constexpr int kSampleKeys = 4096;       // keys sampled per row
+constexpr int kSampledCandCap = 12288;  // candidates per row
+bool topk_sampled_eligible(int n_k, int k);
+size_t topk_sampled_workspace_bytes(int rows, int n_k);
+void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t);
+hipError_t launch_topk_sample(const SampledTopk& t, hipStream_t st);
+hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 
 }  // namespace dsa

@@ -1,0 +1,75 @@
+// fp8_index.h -- the FP8 lightning-indexer score of 16 keys at a time, shared
+// by the streaming indexer, the top-k threshold sampler and the top-k
+// recompute path, so that all of them produce bit-identical scores.
+//
+// One v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a query row's heads (rows
+// of A, up to 16) by 16 keys (columns of B) over the full 128-wide dot
+// product.  Lane l feeds A row l%16 and B column l%16 with 32 code bytes:
+// bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the row, g = l/16.  A and B
+// use the same byte->k assignment, so the contraction is exact whatever order
+// the unit sums in, and each 16-byte load of a wave covers 64 contiguous bytes
+// of every key row it touches.  The 16x16 result lands as
+// acc[i] = dot(head 4g+i, key l%16); ReLU, the head weight and two cross-lane
+// adds finish the head reduction; the positive per-token scales multiply last.
+#pragma once
+
+#include "dsa_device.h"
+
+namespace dsa {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8i load_split32(const uint8_t* row, int g) {
+    v4i lo = *reinterpret_cast<const v4i*>(row + 16 * g);
+    v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * g);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A query row's operands as one lane holds them.
+struct Fp8Query {
+    v8i a;        // head (lane % 16) code bytes, zero for heads >= H
+    float w[4];   // weights of heads 4*(lane/16) + i
+    float sq;     // the row's scale
+};
+
+__device__ __forceinline__ Fp8Query load_fp8_query(const uint8_t* iq, const float* iq_scale, const float* iw,
+                                                   int row, int H, int lane) {
+    Fp8Query q;
+    const int col = lane & 15, kg = lane >> 4;
+    q.a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (col < H) q.a = load_split32(iq + (static_cast<size_t>(row) * H + col) * 128, kg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int h = 4 * kg + i;
+        q.w[i] = h < H ? iw[static_cast<size_t>(row) * H + h] : 0.0f;
+    }
+    q.sq = iq_scale[row];
+    return q;
+}
+
+// Operands of key s for this lane (zeros when !live).
+__device__ __forceinline__ void load_fp8_key(const uint8_t* kb, const float* ksb, int s, bool live, int lane,
+                                             v8i& bv, float& sk) {
+    bv = live ? load_split32(kb + static_cast<size_t>(s) * 128, lane >> 4) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    sk = live ? ksb[s] : 0.0f;
+}
+
+// Score of key (lane % 16) of the block whose operands are bv/sk; every lane
+// of the wave must call it (the MFMA and the lane exchanges are wave-wide).
+__device__ __forceinline__ float fp8_block_score(const Fp8Query& q, const v8i& bv, float sk) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a, bv, acc, 0, 0, 0, 127, 0, 127);
+    float part = q.w[0] * fmaxf(acc[0], 0.0f);
+    part = fmaf(q.w[1], fmaxf(acc[1], 0.0f), part);
+    part = fmaf(q.w[2], fmaxf(acc[2], 0.0f), part);
+    part = fmaf(q.w[3], fmaxf(acc[3], 0.0f), part);
+    part = wave_sum_xor_16_32(part);
+    return part * (q.sq * sk);
+}
+
+// (order key << 32 | ~position): larger means higher score, then lower position.
+__device__ __forceinline__ uint64_t composite64(uint32_t key, int s) {
+    return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(s));
+}
+
+}  // namespace dsa

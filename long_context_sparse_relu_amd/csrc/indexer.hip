@@ -6,8 +6,8 @@
 // sheratonhq.com, section 1).  With E4M3 inputs the per-token scales are
 // positive, so they factor out of the ReLU: I = sq[t]*sk[s]*sum_h w*ReLU(c_q.c_k)
 // where c are the decoded codes; the code products are exact in fp32.
-#include "dsa_device.h"
 #include "dsa_kernels.h"
+#include "fp8_index.h"
 
 namespace dsa {
 
@@ -73,94 +73,132 @@ __global__ __launch_bounds__(256) void k_index_generic(
 }
 
 // ---------------------------------------------------------------------------
-// FP8 streaming path (decode and any row count): up to 16 heads, d = 128.
-// One v_mfma_scale_f32_16x16x128_f8f6f4 multiplies the query row's 16 heads
-// (rows of A) by 16 keys (columns of B) over the full 128-wide dot product.
-// Lane l feeds A row l%16 and B column l%16 with 32 code bytes: bytes
-// [16g, 16g+16) and [64+16g, 64+16g+16) of the row, g = l/16.  A and B use the
-// same byte->k assignment, so the contraction is exact whatever order the
-// unit sums in, and each 16-byte load instruction of a wave covers 64
-// contiguous bytes of every key row it touches.  The 16x16 result lands as
-// acc[i] = dot(head 4g+i, key l%16): ReLU, head weight, then two cross-lane
-// adds finish the head reduction.  Keys stream from HBM once; each wave keeps
-// U blocks of 16 keys in flight.  When `hist` is given, the workgroup also
-// counts the top 11 bits of each visible score's order key in LDS and adds its
-// non-empty bins to the row's histogram, which saves the top-k a pass.
+// FP8 streaming path (decode and any row count): up to 16 heads, d = 128,
+// 16 keys per MFMA (fp8_index.h).  Keys stream from HBM once; each wave keeps
+// U blocks of 16 keys in flight.  Two output modes:
+//   scores      every score is written; when `hist` is given the workgroup
+//               also counts the top 11 bits of each visible score's order key
+//               in LDS and adds its non-empty bins to the row's histogram,
+//               which saves the top-k a pass;
+//   candidates  nothing is written except the scores whose order key reaches
+//               the row's sampled lower bound (meta[S_KLOW]); they are
+//               gathered per workgroup in LDS and appended to the row's
+//               candidate list as (key << 32 | ~position).
 // ---------------------------------------------------------------------------
-typedef int v4i __attribute__((ext_vector_type(4)));
+#ifndef DSA_IDX_U
+#define DSA_IDX_U 4          // blocks of 16 keys each wave loads per step
+#endif
+#ifndef DSA_IDX_KPB
+#define DSA_IDX_KPB 4096     // keys per workgroup
+#endif
+#ifndef DSA_IDX_PREFETCH
+#define DSA_IDX_PREFETCH 0   // 1: load the next step's keys before multiplying the current ones
+#endif
+#ifndef DSA_IDX_WAVES
+#define DSA_IDX_WAVES 4      // waves per workgroup
+#endif
 
-__device__ __forceinline__ v8i load_split32(const uint8_t* row, int g) {
-    v4i lo = *reinterpret_cast<const v4i*>(row + 16 * g);
-    v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * g);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-template <int U>
-__global__ __launch_bounds__(256) void k_index_fp8_mfma(
-    const uint8_t* __restrict__ iq, const float* __restrict__ iq_scale,
-    const uint8_t* __restrict__ ik, const float* __restrict__ ik_scale,
-    const float* __restrict__ iw, const int32_t* __restrict__ q_pos,
-    int row0, int n_q, int n_k, int H, int keys_per_block, float* __restrict__ scores,
-    uint32_t* __restrict__ hist)
-{
-    __shared__ uint32_t lh[kTopkBins];
-    const int row = row0 + blockIdx.y;
+template <int U, bool PREFETCH, bool CAND>
+__global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
+    __shared__ uint32_t lh[CAND ? 1 : kTopkBins];
+    __shared__ uint64_t cbuf[CAND ? kIdxCandBuf : 1];
+    __shared__ uint32_t n_c, g_c;
+    const int row = x.row0 + blockIdx.y;
+    const int n_q = x.n_q, n_k = x.n_k, H = x.H;
     const int b = row / n_q;
-    const int pos = row_pos(q_pos, row, n_q, n_k);
+    const int pos = row_pos(x.q_pos, row, n_q, n_k);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int col = lane & 15;       // A row (head) and B column (key in block)
-    const int kg = lane >> 4;        // which byte slices of the 128-byte rows
-
-    if (hist) {
+    const int col = lane & 15;
+    const int kg = lane >> 4;
+    uint32_t* hist = CAND ? nullptr : x.hist;
+    uint32_t* meta = CAND ? x.meta + static_cast<size_t>(blockIdx.y) * kTopkMeta : nullptr;
+    uint32_t k_low = 0;
+    bool collect = false;
+    if constexpr (CAND) {
+        if (threadIdx.x == 0) n_c = 0;
+        k_low = meta[S_KLOW];
+        collect = pos + 1 > x.k;          // rows that keep every visible key need no candidates
+    } else if (hist) {
         for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
     }
-    v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col < H) a = load_split32(iq + (static_cast<size_t>(row) * H + col) * 128, kg);
-    float w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int h = 4 * kg + i;
-        w[i] = h < H ? iw[static_cast<size_t>(row) * H + h] : 0.0f;
-    }
-    const float sq = iq_scale[row];
-    const uint8_t* kb = ik + static_cast<size_t>(b) * n_k * 128;
-    const float* ksb = ik_scale + static_cast<size_t>(b) * n_k;
-    float* out = scores + static_cast<size_t>(blockIdx.y) * n_k;
-    if (hist) __syncthreads();
+    const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, H, lane);
+    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * n_k * 128;
+    const float* ksb = x.ik_scale + static_cast<size_t>(b) * n_k;
+    float* out = x.scores + static_cast<size_t>(blockIdx.y) * n_k;
+    if (CAND || hist) __syncthreads();
 
     const int s_begin = blockIdx.x * keys_per_block;
     const int s_end = min(s_begin + keys_per_block, n_k);
     const int nwaves = blockDim.x >> 6;
-    for (int base = s_begin + wave * 16 * U; base < s_end; base += nwaves * 16 * U) {
-        v8i bv[U];
-        float sk[U];
+    const int step = nwaves * 16 * U;
+    const uint64_t below = (1ull << lane) - 1ull;
+
+    auto load_batch = [&](int base, v8i* bv, float* sk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int s = base + u * 16 + col;
-            bool live = s < s_end && s <= pos;
-            bv[u] = live ? load_split32(kb + static_cast<size_t>(s) * 128, kg)
-                         : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            sk[u] = live ? ksb[s] : 0.0f;
+            load_fp8_key(kb, ksb, s, s < s_end && s <= pos, lane, bv[u], sk[u]);
         }
+    };
+    auto score_batch = [&](int base, const v8i* bv, const float* sk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bv[u], acc, 0, 0, 0, 127, 0, 127);
-            float part = w[0] * fmaxf(acc[0], 0.0f);
-            part = fmaf(w[1], fmaxf(acc[1], 0.0f), part);
-            part = fmaf(w[2], fmaxf(acc[2], 0.0f), part);
-            part = fmaf(w[3], fmaxf(acc[3], 0.0f), part);
-            part = wave_sum_xor_16_32(part);
-            int s = base + u * 16 + col;
-            if (kg == 0 && s < s_end) {
-                float score = s <= pos ? part * (sq * sk[u]) : -__builtin_inff();
+            const float part = fp8_block_score(q, bv[u], sk[u]);
+            const int s = base + u * 16 + col;
+            const bool mine = kg == 0 && s < s_end;
+            if constexpr (CAND) {
+                const uint32_t key = order_key(part);
+                const bool take = mine && collect && s <= pos && key >= k_low;
+                const uint64_t m = __ballot(take);
+                if (m) {
+                    uint32_t base_slot = 0;
+                    if (lane == 0) base_slot = atomicAdd(&n_c, static_cast<uint32_t>(__popcll(m)));
+                    base_slot = __shfl(base_slot, 0);
+                    const uint32_t slot = base_slot + static_cast<uint32_t>(__popcll(m & below));
+                    if (take && slot < static_cast<uint32_t>(kIdxCandBuf)) cbuf[slot] = composite64(key, s);
+                }
+            } else if (mine) {
+                const float score = s <= pos ? part : -__builtin_inff();
                 out[s] = score;
                 if (hist && s <= pos) atomicAdd(&lh[order_key(score) >> 21], 1u);
             }
         }
+    };
+
+    int base = s_begin + wave * 16 * U;
+    if constexpr (PREFETCH) {
+        v8i bv[U];
+        float sk[U];
+        if (base < s_end) load_batch(base, bv, sk);
+        for (; base < s_end; base += step) {
+            v8i bn[U];
+            float skn[U];
+            if (base + step < s_end) load_batch(base + step, bn, skn);
+            score_batch(base, bv, sk);
+#pragma unroll
+            for (int u = 0; u < U; ++u) { bv[u] = bn[u]; sk[u] = skn[u]; }
+        }
+    } else {
+        for (; base < s_end; base += step) {
+            v8i bv[U];
+            float sk[U];
+            load_batch(base, bv, sk);
+            score_batch(base, bv, sk);
+        }
     }
-    if (hist) {
+    if constexpr (CAND) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            g_c = n_c ? atomicAdd(&meta[S_NCAND], n_c) : 0u;
+            if (n_c > static_cast<uint32_t>(kIdxCandBuf)) atomicOr(&meta[S_OVF], 1u);
+        }
+        __syncthreads();
+        const uint32_t nkeep = min(n_c, static_cast<uint32_t>(kIdxCandBuf));
+        uint64_t* cd = x.cand + static_cast<size_t>(blockIdx.y) * x.cand_cap;
+        for (uint32_t i = threadIdx.x; i < nkeep; i += blockDim.x)
+            if (g_c + i < static_cast<uint32_t>(x.cand_cap)) cd[g_c + i] = cbuf[i];
+    } else if (hist) {
         __syncthreads();
         uint32_t* gh = hist + static_cast<size_t>(blockIdx.y) * kTopkBins;
         for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
@@ -186,19 +224,18 @@ static hipError_t launch_generic_dt(const IndexArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-bool index_fills_hist(const IndexArgs& a) {
+bool index_fp8_path(const IndexArgs& a) {
     return a.dtype == E4M3 && a.H <= 16;
 }
 
+bool index_fills_hist(const IndexArgs& a) { return index_fp8_path(a); }
+
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st) {
-    if (a.dtype == E4M3 && a.H <= 16) {
-        constexpr int U = 4;
-        const int kpb = 4096;
+    if (index_fp8_path(a)) {
+        const int kpb = DSA_IDX_KPB;
         dim3 grid((a.n_k + kpb - 1) / kpb, a.rows);
-        hipLaunchKernelGGL((k_index_fp8_mfma<U>), grid, dim3(256), 0, st,
-                           static_cast<const uint8_t*>(a.iq), a.iq_scale,
-                           static_cast<const uint8_t*>(a.ik), a.ik_scale, a.iw, a.q_pos,
-                           a.row0, a.n_q, a.n_k, a.H, kpb, a.scores, a.hist);
+        hipLaunchKernelGGL((k_index_fp8_mfma<DSA_IDX_U, DSA_IDX_PREFETCH != 0, false>), grid,
+                           dim3(DSA_IDX_WAVES * 64), 0, st, a, kpb);
         return hipGetLastError();
     }
     switch (a.dtype) {
@@ -206,6 +243,14 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st) {
         case BF16: return launch_generic_dt<BF16>(a, st);
         default: return launch_generic_dt<E4M3>(a, st);
     }
+}
+
+hipError_t launch_index_candidates(const IndexArgs& a, hipStream_t st) {
+    const int kpb = DSA_IDX_KPB;
+    dim3 grid((a.n_k + kpb - 1) / kpb, a.rows);
+    hipLaunchKernelGGL((k_index_fp8_mfma<DSA_IDX_U, DSA_IDX_PREFETCH != 0, true>), grid,
+                       dim3(DSA_IDX_WAVES * 64), 0, st, a, kpb);
+    return hipGetLastError();
 }
 
 }  // namespace dsa

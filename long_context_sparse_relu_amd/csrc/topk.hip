@@ -23,8 +23,7 @@
 //             bitonic sort for rows too long for one).
 // The score row is read twice (hist, filter) or once when the indexer built
 // the histogram.
-#include "dsa_device.h"
-#include "dsa_kernels.h"
+#include "topk_common.h"
 
 namespace dsa {
 
@@ -35,7 +34,6 @@ constexpr int kFChunk = 8192;      // scores per workgroup in filter
 constexpr int kFThreads = 512;
 constexpr int kFPer = kFChunk / kFThreads;
 constexpr int kFinishThreads = 512;
-constexpr int kBitmapMaxKeys = 1 << 18;   // rows up to this long are ordered through a bitmap
 
 // Row metadata words in TopkArgs::count (kTopkMeta per row).
 enum { M_SEL = 0, M_CAND = 1, M_D0 = 2, M_GT0 = 3 };
@@ -52,45 +50,6 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(k_zero_u32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, n);
     return hipGetLastError();
-}
-
-// Block-wide search of the threshold bin: the digit d with
-//   count(bins > d) < k_rem <= count(bins >= d).
-// `hist` has nbins LDS entries (nbins a multiple of blockDim.x); `wsum` is an
-// LDS array of one slot per wave plus two result slots.  Every thread returns
-// the same d and count(bins > d).  Requires sum(hist) >= k_rem >= 1.
-__device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t k_rem,
-                                   uint32_t* wsum, int* digit, uint32_t* gt)
-{
-    const int T = blockDim.x, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, nwaves = T >> 6;
-    const int per = nbins / T;
-    const int top = nbins - 1 - tid * per;      // this thread's bins: top, top-1, ...
-    uint32_t local = 0;
-    for (int j = 0; j < per; ++j) local += hist[top - j];
-    uint32_t x = local;                          // inclusive scan inside the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const uint32_t excl = before + x - local;
-    if (excl < k_rem && excl + local >= k_rem) {
-        uint32_t run = excl;
-        for (int j = 0; j < per; ++j) {
-            uint32_t h = hist[top - j];
-            if (run + h >= k_rem) { wsum[nwaves] = static_cast<uint32_t>(top - j); wsum[nwaves + 1] = run; break; }
-            run += h;
-        }
-    }
-    __syncthreads();
-    *digit = static_cast<int>(wsum[nwaves]);
-    *gt = wsum[nwaves + 1];
-    __syncthreads();
 }
 
 __device__ __forceinline__ int row_visible(const TopkArgs& a, int row) {
@@ -147,30 +106,6 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_threshold(TopkArgs a) {
         meta[M_D0] = static_cast<uint32_t>(d0);
         meta[M_GT0] = gt0;
     }
-}
-
-// Block-wide exclusive scan of one value per thread (wave scans, then the
-// wave totals); `wsum` holds one LDS slot per wave.  Returns the exclusive
-// prefix; *total gets the block sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-    for (int w = 0; w < nwaves; ++w) {
-        uint32_t t = wsum[w];
-        if (w < wave) before += t;
-        all += t;
-    }
-    __syncthreads();
-    *total = all;
-    return before + x - v;
 }
 
 // Keys above d0 go to the output row, keys in d0 become candidates and are
@@ -259,48 +194,6 @@ struct CandRow {
     }
 };
 
-// Visit every candidate of `src`, eight loads in flight per thread.
-template <class Src, class F>
-__device__ __forceinline__ void for_each_candidate(const Src& src, F&& f) {
-    const int n = src.size();
-    const int T = blockDim.x;
-    int i = threadIdx.x;
-    for (; i + 7 * T < n; i += 8 * T) {
-        uint64_t c[8];
-        bool ok[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ok[u] = src.get(i + u * T, &c[u]);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (ok[u]) f(c[u]);
-    }
-    for (; i < n; i += T) {
-        uint64_t c;
-        if (src.get(i, &c)) f(c);
-    }
-}
-
-// Where the finish puts kept positions: bits of an LDS bitmap over the row
-// (rows up to kBitmapMaxKeys keys; read back in position order), or an LDS
-// list sorted afterwards.
-struct Sink {
-    uint32_t* bitmap;      // null when the list is used
-    int32_t* list;
-    uint32_t* n_list;
-    uint32_t cap;
-    __device__ void put(int s) const {
-        if (bitmap) {
-            atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-        } else {
-            uint32_t slot = atomicAdd(n_list, 1u);
-            if (slot < cap) list[slot] = s;
-        }
-    }
-    __device__ void put_c(uint64_t c) const {
-        put(static_cast<int>(~static_cast<uint32_t>(c & 0xFFFFFFFFull)));
-    }
-};
-
 // Candidates whose top composite digit (key bits 20..10) is d1 share the
 // first 22 key bits; radix-select the k_rem largest of them on the remaining
 // digits and keep them.
@@ -308,33 +201,9 @@ template <class Src>
 __device__ void select_in_bin(const Src& src, int d1, uint32_t k_rem, uint32_t* lh, uint32_t* wsum,
                               const Sink& sink)
 {
-    // Digits of the 53-bit composite below the top one, most significant first.
     const int shifts[4] = {31, 20, 9, 0};
     const int widths[4] = {11, 11, 11, 9};
-    uint64_t prefix = static_cast<uint64_t>(d1);
-    int done_shift = 42;
-    for (int p = 0; p < 4; ++p) {
-        const int sh = shifts[p], w = widths[p];
-        const int nb = 1 << w;
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) lh[i] = 0u;
-        __syncthreads();
-        for_each_candidate(src, [&](uint64_t c) {
-            if ((c >> (sh + w)) == prefix) atomicAdd(&lh[(c >> sh) & (nb - 1)], 1u);
-        });
-        __syncthreads();
-        int d; uint32_t gt;
-        find_threshold_bin(lh, nb, k_rem, wsum, &d, &gt);
-        k_rem -= gt;
-        prefix = (prefix << w) | static_cast<uint64_t>(d);
-        done_shift = sh;
-        bool done = lh[d] == k_rem;
-        __syncthreads();
-        if (done) break;
-    }
-    for_each_candidate(src, [&](uint64_t c) {
-        if ((c >> done_shift) >= prefix) sink.put_c(c);
-    });
-    __syncthreads();
+    radix_select(src, k_rem, shifts, widths, 4, static_cast<uint64_t>(d1), lh, wsum, sink);
 }
 
 // One workgroup per row: candidates above d1 are kept, the d1 bin is
@@ -405,40 +274,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
         if (!whole_bin) select_in_bin(row_src, d1, k2, lh, wsum, sink);
     }
     __syncthreads();
-    if (use_bitmap) {
-        // positions in order: per-thread runs of words, block scan of their popcounts
-        const int per = (nwords + blockDim.x - 1) / blockDim.x;
-        const int w0 = threadIdx.x * per;
-        uint32_t cnt = 0;
-        for (int w = w0; w < min(w0 + per, nwords); ++w) cnt += __popc(tail[w]);
-        uint32_t total;
-        uint32_t o = block_exclusive_scan(cnt, wsum, &total);
-        for (int w = w0; w < min(w0 + per, nwords); ++w) {
-            uint32_t bits = tail[w];
-            while (bits) {
-                int b = __ffs(bits) - 1;
-                bits &= bits - 1;
-                if (o < static_cast<uint32_t>(a.k)) out[o] = (w << 5) + b;
-                ++o;
-            }
-        }
-        return;
-    }
-    // Bitonic sort of the kpad list entries, ascending.
-    int32_t* sorted = reinterpret_cast<int32_t*>(tail);
-    for (int size = 2; size <= kpad; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (kpad >> 1); i += blockDim.x) {
-                int lo = 2 * i - (i & (stride - 1));
-                int hi = lo + stride;
-                bool asc = (lo & size) == 0;
-                int32_t x = sorted[lo], y = sorted[hi];
-                if ((x > y) == asc) { sorted[lo] = y; sorted[hi] = x; }
-            }
-            __syncthreads();
-        }
-    }
-    for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = sorted[j];
+    write_ordered(sink, nwords, kpad, a.k, out, wsum);
 }
 
 // Dynamic LDS of the finish kernel: the candidate group plus the bitmap or list.

@@ -1,0 +1,212 @@
+// topk_sampled.hip -- top-k for long rows without materialising the scores.
+//
+// The selector keeps the k highest-scoring keys of each query
+// ("DeepSeek-V3.2-Exp 稀疏注意力机制(DSA)技术深度解析", sheratonhq.com,
+// section 1; "DeepSeek-V4 百万 token 上下文的工程实现", blog.hotdry.top, section
+// "从 O(N²) 到 O(N・k)", which recommends k = 256..512 over 1M tokens).  When a
+// row holds many more keys than k, writing every score to memory and reading
+// it back costs more than finding the k largest, so:
+//   sample  one workgroup per row scores kSampleKeys evenly spaced keys (the
+//           same MFMA code as the indexer) and takes a lower bound of the
+//           r-th largest sample, r ~ 1.5 k * samples / visible keys + 24: the
+//           indexer then keeps about 1.5 k + 24 * visible / samples keys;
+//   index   the FP8 indexer appends only scores at or above that bound to the
+//           row's candidate list (indexer.hip, candidate mode);
+//   finish  one workgroup per row radix-selects the exact k largest of the
+//           candidates on (order key, ~position) -- ties go to the lower
+//           position -- and writes the positions in ascending order.
+// If a row ends with fewer than k candidates or more than the list holds, the
+// finish workgroup recomputes that row's scores in full and selects from all
+// of them, so the result never depends on how good the sample was.
+#include "fp8_index.h"
+#include "topk_common.h"
+
+namespace dsa {
+
+constexpr int kSampleThreads = 512;
+constexpr int kSFinishThreads = 512;
+
+bool topk_sampled_eligible(int n_k, int k) {
+    return static_cast<int64_t>(n_k) >= 16 * static_cast<int64_t>(k) && n_k >= kSampleKeys;
+}
+
+
+struct Cand64List {
+    const uint64_t* c; int n;
+    __device__ int size() const { return n; }
+    __device__ bool get(int i, uint64_t* out) const { *out = c[i]; return true; }
+};
+struct ScoreRow64 {
+    const float* sc; int n;
+    __device__ int size() const { return n; }
+    __device__ bool get(int i, uint64_t* out) const { *out = composite64(order_key(sc[i]), i); return true; }
+};
+
+// Lower bound of each row's r-th largest sampled score; clears the row's
+// candidate counters.
+__global__ __launch_bounds__(kSampleThreads) void k_topk_sample(SampledTopk t) {
+    __shared__ uint32_t skey[kSampleKeys];
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t wsum[kSampleThreads / 64 + 2];
+    const IndexArgs& x = t.ix;
+    const int lrow = blockIdx.x, row = x.row0 + lrow;
+    const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
+    const int vis = pos + 1;
+    uint32_t* meta = x.meta + static_cast<size_t>(lrow) * kTopkMeta;
+    if (threadIdx.x == 0) { meta[S_NCAND] = 0u; meta[S_OVF] = 0u; meta[S_FALLBACK] = 0u; }
+    if (vis <= x.k) {                      // every visible key is kept: nothing to bound
+        if (threadIdx.x == 0) meta[S_KLOW] = 0xFFFFFFFFu;
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int m = vis < kSampleKeys ? vis : kSampleKeys;
+    const int stride = vis / m;            // >= 1; sample j is key j * stride < vis
+    const int b = row / x.n_q;
+    const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
+    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
+    const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
+    for (int blk = wave; blk * 16 < m; blk += nwaves) {       // uniform per wave
+        const int j = blk * 16 + col;
+        const bool live = j < m;
+        v8i bv;
+        float sk;
+        load_fp8_key(kb, ksb, j * stride, live, lane, bv, sk);
+        const float score = fp8_block_score(q, bv, sk);
+        if (kg == 0 && live) skey[j] = order_key(score);
+    }
+    __syncthreads();
+    const int64_t want = (3 * static_cast<int64_t>(m) * x.k + 2 * static_cast<int64_t>(vis) - 1) /
+                         (2 * static_cast<int64_t>(vis)) + 24;
+    uint32_t k_low = 0u;                   // every visible key a candidate
+    if (want < m) {
+        const uint32_t r = static_cast<uint32_t>(want);
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+        __syncthreads();
+        for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[skey[j] >> 21], 1u);
+        __syncthreads();
+        int d0; uint32_t gt0;
+        find_threshold_bin(lh, kTopkBins, r, wsum, &d0, &gt0);
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+        __syncthreads();
+        for (int j = threadIdx.x; j < m; j += blockDim.x)
+            if (static_cast<int>(skey[j] >> 21) == d0) atomicAdd(&lh[(skey[j] >> 10) & 0x7FFu], 1u);
+        __syncthreads();
+        int d1; uint32_t gt1;
+        find_threshold_bin(lh, kTopkBins, r - gt0, wsum, &d1, &gt1);
+        k_low = (static_cast<uint32_t>(d0) << 21) | (static_cast<uint32_t>(d1) << 10);
+    }
+    if (threadIdx.x == 0) meta[S_KLOW] = k_low;
+}
+
+// Exact top-k over the candidate list (or the recomputed row), then the
+// positions in ascending order.
+__global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(SampledTopk t) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t wsum[kSFinishThreads / 64 + 2];
+    __shared__ uint32_t n_list;
+    const IndexArgs& x = t.ix;
+    const int lrow = blockIdx.x, row = x.row0 + lrow;
+    const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
+    const int vis = pos + 1;
+    const int k = x.k;
+    int32_t* out = t.idx + static_cast<size_t>(lrow) * k;
+    if (vis <= k) {
+        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < vis ? j : -1;
+        return;
+    }
+    uint64_t* cl = reinterpret_cast<uint64_t*>(smem);                       // [cand_cap]
+    uint32_t* tail = reinterpret_cast<uint32_t*>(cl + x.cand_cap);          // bitmap or list
+    const bool use_bitmap = x.n_k <= kBitmapMaxKeys;
+    const int nwords = (vis + 31) >> 5;
+    int kpad = 1;
+    while (kpad < k) kpad <<= 1;
+    Sink sink{use_bitmap ? tail : nullptr, reinterpret_cast<int32_t*>(tail), &n_list, static_cast<uint32_t>(k)};
+    if (use_bitmap) {
+        for (int i = threadIdx.x; i < nwords; i += blockDim.x) tail[i] = 0u;
+    } else {
+        for (int i = threadIdx.x; i < kpad; i += blockDim.x) tail[i] = 0x7FFFFFFFu;
+    }
+    if (threadIdx.x == 0) n_list = 0;
+    // digits of the 64-bit (order key << 32 | ~position) composite
+    const int shifts64[6] = {53, 42, 32, 21, 10, 0};
+    const int widths64[6] = {11, 11, 10, 11, 11, 10};
+    uint32_t* meta = x.meta + static_cast<size_t>(lrow) * kTopkMeta;
+    const uint32_t n = meta[S_NCAND];
+    const bool ok = meta[S_OVF] == 0u && n >= static_cast<uint32_t>(k) && n <= static_cast<uint32_t>(x.cand_cap);
+    if (ok) {
+        const uint64_t* gc = x.cand + static_cast<size_t>(lrow) * x.cand_cap;
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) cl[i] = gc[i];
+        __syncthreads();
+        Cand64List src{cl, static_cast<int>(n)};
+        radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
+    } else {
+        // recompute this row's scores in full, then select from all of them
+        if (threadIdx.x == 0) meta[S_FALLBACK] = 1u;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+        const int col = lane & 15, kg = lane >> 4;
+        const int b = row / x.n_q;
+        const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
+        const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
+        const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
+        float* sc = t.scratch + static_cast<size_t>(lrow) * x.n_k;
+        for (int base = wave * 16; base < vis; base += nwaves * 16) {      // uniform per wave
+            const int s = base + col;
+            v8i bv;
+            float sk;
+            load_fp8_key(kb, ksb, s, s < vis, lane, bv, sk);
+            const float score = fp8_block_score(q, bv, sk);
+            if (kg == 0 && s < vis) sc[s] = score;
+        }
+        __threadfence_block();
+        __syncthreads();
+        ScoreRow64 src{sc, vis};
+        radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
+    }
+    __syncthreads();
+    write_ordered(sink, nwords, kpad, k, out, wsum);
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+size_t topk_sampled_workspace_bytes(int rows, int n_k) {
+    const size_t r = static_cast<size_t>(rows);
+    return align256(r * kTopkMeta * sizeof(uint32_t)) +
+           align256(r * kSampledCandCap * sizeof(uint64_t)) +
+           align256(r * static_cast<size_t>(n_k) * sizeof(float));
+}
+
+void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t) {
+    unsigned char* p = static_cast<unsigned char*>(ws);
+    const size_t r = static_cast<size_t>(rows);
+    t.ix.meta = reinterpret_cast<uint32_t*>(p);
+    p += align256(r * kTopkMeta * sizeof(uint32_t));
+    t.ix.cand = reinterpret_cast<uint64_t*>(p);
+    t.ix.cand_cap = kSampledCandCap;
+    p += align256(r * kSampledCandCap * sizeof(uint64_t));
+    t.scratch = reinterpret_cast<float*>(p);
+    (void)n_k;
+}
+
+hipError_t launch_topk_sample(const SampledTopk& t, hipStream_t st) {
+    hipLaunchKernelGGL(k_topk_sample, dim3(t.ix.rows), dim3(kSampleThreads), 0, st, t);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st) {
+    int kpad = 1;
+    while (kpad < t.ix.k) kpad <<= 1;
+    const size_t tail = t.ix.n_k <= kBitmapMaxKeys ? static_cast<size_t>((t.ix.n_k + 31) >> 5) * 4
+                                                   : static_cast<size_t>(kpad) * 4;
+    const size_t smem = static_cast<size_t>(t.ix.cand_cap) * sizeof(uint64_t) + tail;
+    if (smem > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish_sampled),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_topk_finish_sampled, dim3(t.ix.rows), dim3(kSFinishThreads), smem, st, t);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -125,6 +125,9 @@ EDGE_CASES = {
                                   q_heads=32, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16"),
     "latent_small": dict(B=2, n_q=1, n_k=4000, idx_heads=16, idx_dtype="e4m3", top_k=512, q_heads=20,
                          kv_heads=1, d_qk=576, d_v=512, latent=True, attn_dtype="bf16"),
+    # long ragged rows: the fused decode takes the sampled top-k (n_k >= 16 k)
+    "fp8_sampled_ragged": dict(B=3, n_q=1, n_k=50001, idx_heads=16, idx_dtype="e4m3", top_k=1000,
+                               q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16"),
     "bf16_generic_d64": dict(n_q=50, n_k=2000, idx_heads=8, top_k=128, q_heads=8, kv_heads=2,
                              d_qk=64, d_v=64, attn_dtype="bf16", idx_dtype="bf16"),
 }
@@ -182,6 +185,37 @@ def test_explicit_positions_and_empty_rows():
                 continue
             check_scores(scores[b, t].cpu().numpy(), sc[t], pos[t])
             check_topk_row(g[t], o_idx[t], sc[t], kth[t], pos[t], 700)
+
+
+def test_sampled_topk_positions_and_ties():
+    """Fused decode in the sampled regime: per-row positions (empty, short and
+    long rows) and an all-zero-weight row, whose ties force the recompute path."""
+    sp = custom_spec(name="sampled_qpos", B=6, n_q=1, n_k=20000, idx_heads=16, idx_dtype="e4m3",
+                     top_k=256, q_heads=8, kv_heads=1, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=17)
+    q_pos = torch.tensor([[-1], [0], [255], [256], [5000], [19999]], dtype=torch.int32, device=DEV)
+    inp["iw"][5].zero_()                  # every score of row 5 ties at zero
+    inp["pos"] = q_pos
+    prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=256, q=inp["q"], k=inp["k"],
+                            v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"], q_pos=q_pos)
+    idx = dsa.topk(prob, dsa.index_scores(prob))
+    idx_f = torch.empty_like(idx)
+    out_f, lse_f, _ = dsa.decode(prob, idx_out=idx_f)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_f), "sampled and full top-k differ"
+    got = idx_f.cpu().numpy()
+    assert np.all(got[0, 0] == -1)
+    assert got[1, 0].tolist() == [0] + [-1] * 255
+    assert got[2, 0].tolist() == list(range(256))
+    assert got[5, 0].tolist() == list(range(256))        # ties resolve to the lowest positions
+    ov = oracle_view(inp)
+    for b in (3, 4):
+        pos = ov["pos"][b].astype(np.int64)
+        sc = oracle.index_scores(ov["iq"][b], ov["ik"][b], ov["iw"][b], "e4m3",
+                                 ov["iq_scale"][b], ov["ik_scale"][b], pos)
+        o_idx, kth = oracle.topk(sc, 256, pos)
+        check_topk_row(got[b, 0], o_idx[0], sc[0], kth[0], pos[0], 256)
+    assert torch.all(out_f[0, 0] == 0) and torch.all(torch.isneginf(lse_f[0, 0]))
 
 
 def test_decode_is_deterministic():
