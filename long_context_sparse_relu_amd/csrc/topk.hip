@@ -96,8 +96,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_threshold(TopkArgs a) {
     __shared__ uint32_t wsum[kFilterThreads / 64 + 2];
     const int lrow = blockIdx.x, row = a.row0 + lrow;
     if (row_visible(a, row) <= a.k) return;
-    const uint32_t* gh = a.hist + static_cast<size_t>(lrow) * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh[i];
+    copy_to_lds(lh, a.hist + static_cast<size_t>(lrow) * kTopkBins, kTopkBins);
     __syncthreads();
     int d0; uint32_t gt0;
     find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(a.k), wsum, &d0, &gt0);
@@ -238,8 +237,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     const uint32_t gt0 = meta[M_GT0];
     const int d0 = static_cast<int>(meta[M_D0]);
     const uint32_t n_cand = meta[M_CAND];
-    const uint32_t* gh1 = a.hist1 + static_cast<size_t>(lrow) * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = gh1[i];
+    copy_to_lds(lh, a.hist1 + static_cast<size_t>(lrow) * kTopkBins, kTopkBins);
     if (threadIdx.x == 0) { n_list = 0; n_grp = 0; }
     __syncthreads();
     for (int j = threadIdx.x; j < static_cast<int>(gt0); j += blockDim.x) sink.put(out[j]);

@@ -73,6 +73,21 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
     return before + x - v;
 }
 
+// dst[i] = src[i] for i < n (global -> LDS), eight loads in flight per thread.
+template <class T>
+__device__ __forceinline__ void copy_to_lds(T* dst, const T* src, int n) {
+    const int T_ = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + 7 * T_ < n; i += 8 * T_) {
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[i + u * T_];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dst[i + u * T_] = v[u];
+    }
+    for (; i < n; i += T_) dst[i] = src[i];
+}
+
 // Visit every candidate of `src`, eight loads in flight per thread.
 template <class Src, class F>
 __device__ __forceinline__ void for_each_candidate(const Src& src, F&& f) {

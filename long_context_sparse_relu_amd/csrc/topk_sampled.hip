@@ -66,14 +66,21 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample(SampledTopk t) {
     const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
     const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
     const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
-    for (int blk = wave; blk * 16 < m; blk += nwaves) {       // uniform per wave
-        const int j = blk * 16 + col;
-        const bool live = j < m;
-        v8i bv;
-        float sk;
-        load_fp8_key(kb, ksb, j * stride, live, lane, bv, sk);
-        const float score = fp8_block_score(q, bv, sk);
-        if (kg == 0 && live) skey[j] = order_key(score);
+    constexpr int U = 8;                   // blocks of 16 samples in flight per wave
+    for (int blk0 = wave * U; blk0 * 16 < m; blk0 += nwaves * U) {   // uniform per wave
+        v8i bv[U];
+        float sk[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = (blk0 + u) * 16 + col;
+            load_fp8_key(kb, ksb, j * stride, j < m, lane, bv[u], sk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = (blk0 + u) * 16 + col;
+            const float score = fp8_block_score(q, bv[u], sk[u]);
+            if (kg == 0 && j < m) skey[j] = order_key(score);
+        }
     }
     __syncthreads();
     const int64_t want = (3 * static_cast<int64_t>(m) * x.k + 2 * static_cast<int64_t>(vis) - 1) /
@@ -136,8 +143,7 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
     const uint32_t n = meta[S_NCAND];
     const bool ok = meta[S_OVF] == 0u && n >= static_cast<uint32_t>(k) && n <= static_cast<uint32_t>(x.cand_cap);
     if (ok) {
-        const uint64_t* gc = x.cand + static_cast<size_t>(lrow) * x.cand_cap;
-        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) cl[i] = gc[i];
+        copy_to_lds(cl, x.cand + static_cast<size_t>(lrow) * x.cand_cap, static_cast<int>(n));
         __syncthreads();
         Cand64List src{cl, static_cast<int>(n)};
         radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
@@ -151,13 +157,21 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
         const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
         const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
         float* sc = t.scratch + static_cast<size_t>(lrow) * x.n_k;
-        for (int base = wave * 16; base < vis; base += nwaves * 16) {      // uniform per wave
-            const int s = base + col;
-            v8i bv;
-            float sk;
-            load_fp8_key(kb, ksb, s, s < vis, lane, bv, sk);
-            const float score = fp8_block_score(q, bv, sk);
-            if (kg == 0 && s < vis) sc[s] = score;
+        constexpr int U = 4;
+        for (int base = wave * 16 * U; base < vis; base += nwaves * 16 * U) {   // uniform per wave
+            v8i bv[U];
+            float sk[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = base + u * 16 + col;
+                load_fp8_key(kb, ksb, s, s < vis, lane, bv[u], sk[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = base + u * 16 + col;
+                const float score = fp8_block_score(q, bv[u], sk[u]);
+                if (kg == 0 && s < vis) sc[s] = score;
+            }
         }
         __threadfence_block();
         __syncthreads();
