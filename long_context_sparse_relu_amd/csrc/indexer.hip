@@ -97,6 +97,9 @@ __global__ __launch_bounds__(256) void k_index_generic(
 #ifndef DSA_IDX_WAVES
 #define DSA_IDX_WAVES 4      // waves per workgroup
 #endif
+#ifndef DSA_IDX_INTERLEAVE
+#define DSA_IDX_INTERLEAVE 0 // 1: the workgroups of a row take interleaved chunks of it
+#endif
 
 template <int U, bool PREFETCH, bool CAND>
 __global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
@@ -128,10 +131,19 @@ __global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs
     float* out = x.scores + static_cast<size_t>(blockIdx.y) * n_k;
     if (CAND || hist) __syncthreads();
 
+    const int nwaves = blockDim.x >> 6;
+#if DSA_IDX_INTERLEAVE
+    // chunk c of 16*U keys goes to wave c % (nwaves*gridDim.x): at any time
+    // the row's workgroups stream neighbouring chunks
+    const int s_begin = (blockIdx.x * nwaves) * 16 * U;
+    const int s_end = n_k;
+    const int step = nwaves * gridDim.x * 16 * U;
+    (void)keys_per_block;
+#else
     const int s_begin = blockIdx.x * keys_per_block;
     const int s_end = min(s_begin + keys_per_block, n_k);
-    const int nwaves = blockDim.x >> 6;
     const int step = nwaves * 16 * U;
+#endif
     const uint64_t below = (1ull << lane) - 1ull;
 
     auto load_batch = [&](int base, v8i* bv, float* sk) {

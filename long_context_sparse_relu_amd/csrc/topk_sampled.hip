@@ -6,10 +6,12 @@
 // "从 O(N²) 到 O(N・k)", which recommends k = 256..512 over 1M tokens).  When a
 // row holds many more keys than k, writing every score to memory and reading
 // it back costs more than finding the k largest, so:
-//   sample  one workgroup per row scores kSampleKeys evenly spaced keys (the
-//           same MFMA code as the indexer) and takes a lower bound of the
-//           r-th largest sample, r ~ 1.5 k * samples / visible keys + 24: the
-//           indexer then keeps about 1.5 k + 24 * visible / samples keys;
+//   sample  one workgroup per row scores kSampleKeys keys -- runs of 16
+//           consecutive keys spread evenly over the row, so every load is a
+//           contiguous 2 KiB block -- with the same MFMA code as the indexer,
+//           and takes a lower bound of the r-th largest sample,
+//           r ~ 1.5 k * samples / visible keys + 24: the indexer then keeps
+//           about 1.5 k + 24 * visible / samples keys;
 //   index   the FP8 indexer appends only scores at or above that bound to the
 //           row's candidate list (indexer.hip, candidate mode);
 //   finish  one workgroup per row radix-selects the exact k largest of the
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample(SampledTopk t) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
     const int m = vis < kSampleKeys ? vis : kSampleKeys;
-    const int stride = vis / m;            // >= 1; sample j is key j * stride < vis
+    const int nrun = (m + 15) / 16;        // runs of 16 consecutive keys
+    const int gap = vis / nrun;            // >= 16 unless m == vis; run g starts at key g * gap
     const int b = row / x.n_q;
     const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
     const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
@@ -73,7 +76,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample(SampledTopk t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = (blk0 + u) * 16 + col;
-            load_fp8_key(kb, ksb, j * stride, j < m, lane, bv[u], sk[u]);
+            const int key = m == vis ? j : (blk0 + u) * gap + col;
+            load_fp8_key(kb, ksb, key, j < m, lane, bv[u], sk[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
