@@ -1,11 +1,13 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-One step = one fused decode call (lightning indexer over every cached key,
-top-k selection, attention over the selected rows) for the whole batch of the
-workload: by default 64 single-token queries over 131072 cached tokens each,
-16 FP8 indexer heads of dim 128, k = 2048, bf16 KV cache with 32 query heads
-over 4 KV heads of dim 128.  Inputs are seeded synthetic Gaussians already
-resident in HBM when the timed region starts.
+One step = one fused call (lightning indexer over every visible key, top-k
+selection, attention over the selected rows) for the whole batch of the
+workload: by default decode_128k, 64 single-token queries over 131072 cached
+tokens each, 16 FP8 indexer heads of dim 128, k = 2048, bf16 KV cache with 32
+query heads over 4 KV heads of dim 128 (dsa_decode).  The prefill workloads
+(--workload prefill_*) time dsa_prefill over the whole sequence.  Inputs are
+seeded synthetic Gaussians already resident in HBM when the timed region
+starts.
 
 Prints ONE JSON line (rank 0):
   value         query tokens per second over the K timed steps
@@ -67,19 +69,29 @@ def _events_mean_us(fn, reps, stream):
     return 1000.0 * sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
 
 
-def _cpu_baseline(inp, n_seq):
+def _cpu_baseline(inp, n_seq, n_rows):
+    """The oracle on n_seq sequences (decode) or n_rows evenly spread query rows (prefill)."""
     import oracle
     from dsa_inputs import oracle_view
-    seqs = list(range(min(n_seq, inp["B"])))
-    ov = oracle_view(inp, seqs)
     threads = oracle.num_threads()
+    if inp["n_q"] == 1:
+        seqs = list(range(min(n_seq, inp["B"])))
+        ov = oracle_view(inp, seqs)
+        rows = None
+        what = f"{len(seqs)} of {inp['B']} sequences (1 query x {inp['n_k']} keys each)"
+        count = len(seqs)
+    else:
+        ov = oracle_view(inp, [0])
+        n_q = inp["n_q"]
+        ts = sorted({int(round(i * (n_q - 1) / max(1, n_rows - 1))) for i in range(n_rows)})
+        rows = [(0, t) for t in ts]
+        what = f"{len(ts)} of {n_q} query rows of sequence 0, evenly spread (their prefixes average {sum(ts) / len(ts) + 1:.0f} keys)"
+        count = len(ts)
     t0 = time.perf_counter()
-    oracle.dsa_forward(ov)
+    oracle.dsa_forward(ov, rows)
     dt = time.perf_counter() - t0
-    return {"value": len(seqs) * inp["n_q"] / dt, "unit": "query-tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": (f"{len(seqs)} of {inp['B']} sequences ({inp['n_q']} query x {inp['n_k']} keys each), "
-                       f"whole path in fp64: indexer, top-k, attention; {dt:.2f} s")}
+    return {"value": count / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, whole path in fp64: indexer, top-k, attention; {dt:.2f} s"}
 
 
 def main(argv=None):
@@ -89,7 +101,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_128k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=64, help="sequences the oracle baseline runs")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="sequences the oracle baseline runs (decode)")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows the oracle baseline runs (prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phase-reps", type=int, default=10)
     args = ap.parse_args(argv)
@@ -105,22 +118,22 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     s = spec(args.workload)
-    if s["n_q"] != 1:
-        print("bench.py times the decode workloads (n_q == 1)", file=sys.stderr)
-        return 2
+    decode = s["n_q"] == 1
     print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
     inp = make_inputs(s, device=dev, seed=args.seed)
-    B, N, k = s["B"], s["n_k"], s["top_k"]
+    B, N, k, n_q = s["B"], s["n_k"], s["top_k"], s["n_q"]
     prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
                             v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
                             softmax_scale=inp["scale"], latent_dv=inp["latent_dv"])
     out, lse = dsa._out_tensors(prob, None, None)
-    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
-    ws = torch.empty(dsa.workspace_bytes(dsa.OP_DECODE, prob), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
+    op = dsa.OP_DECODE if decode else dsa.OP_PREFILL
+    ws = torch.empty(dsa.workspace_bytes(op, prob), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    fused = dsa.decode if decode else dsa.prefill
 
     def step():
-        dsa.decode(prob, out=out, lse=lse, idx_out=idx, workspace=ws, stream=stream)
+        fused(prob, out=out, lse=lse, idx_out=idx, workspace=ws, stream=stream)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -138,25 +151,49 @@ def main(argv=None):
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
     # unfused phases, each its own launch sequence on the same stream
-    scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, n_q, N), dtype=torch.float32, device=dev)
     tws = torch.empty(dsa.workspace_bytes(dsa.OP_TOPK, prob), dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_SPARSE_ATTN, prob)), dtype=torch.uint8, device=dev)
     reps = args.phase_reps
     idx_us = _events_mean_us(lambda: dsa.index_scores(prob, scores, stream), reps, stream)
     topk_us = _events_mean_us(lambda: dsa.topk(prob, scores, idx, tws, stream), reps, stream)
-    attn_us = _events_mean_us(lambda: dsa.sparse_attn(prob, idx, out, lse, stream), reps, stream)
+    attn_us = _events_mean_us(lambda: dsa.sparse_attn(prob, idx, out, lse, aws, stream), reps, stream)
 
-    # algorithmic bytes of the indexer launch: every FP8 key row + its scale,
-    # plus the queries, scales and head weights
     H, D = s["idx_heads"], s["idx_dim"]
-    idx_bytes = B * N * (D + 4) + B * (H * D + 4 + 4 * H)
-    row = s["kv_heads"] * (s["d_qk"] + (0 if s["latent"] else s["d_v"])) * 2
-    gather_bytes = B * k * row
-    achieved = idx_bytes / (idx_us * 1e-6) / 1e9
-    traffic = _traffic(f"k_index_fp8_mfma@{args.workload}")
-    total_bytes = idx_bytes + gather_bytes
+    kbytes = {"f32": 4, "bf16": 2, "e4m3": 1}[s["idx_dtype"]]
+    abytes = {"f32": 4, "bf16": 2}[s["attn_dtype"]]
+    row = s["kv_heads"] * (s["d_qk"] + (0 if s["latent"] else s["d_v"])) * abytes
+    # visible keys and kept keys summed over every query row
+    pairs = sum(N - n_q + t + 1 for t in range(n_q)) * B
+    kept = sum(min(k, N - n_q + t + 1) for t in range(n_q)) * B
+    gather_bytes = kept * row
+    attn_flops = 2 * kept * s["q_heads"] * (s["d_qk"] + s["d_v"])
+    if decode:
+        # HBM bound: every key row (+ its scale) streams once, plus queries and head weights
+        idx_bytes = B * N * (D * kbytes + (4 if s["idx_dtype"] == "e4m3" else 0)) + B * (H * D * kbytes + 4 + 4 * H)
+        achieved = idx_bytes / (idx_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_index_fp8_mfma", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": _traffic(f"k_index_fp8_mfma@{args.workload}"),
+                "algorithmic_bytes": idx_bytes, "mean_us": idx_us}
+        total_bytes = idx_bytes + gather_bytes
+        step_roof = {"algorithmic_bytes": total_bytes,
+                     "achieved_GBs": total_bytes / (ms_per_step * 1e-3) / 1e9,
+                     "frac": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    else:
+        # a dense contraction: 2*H*D flops per visible (query, key) pair
+        idx_flops = 2 * pairs * H * D
+        peak = {"e4m3": 5000.0, "bf16": 2500.0, "f32": 157.3}[s["idx_dtype"]]
+        achieved = idx_flops / (idx_us * 1e-6) / 1e12
+        kern = "k_index_fp8_mfma" if s["idx_dtype"] == "e4m3" else "k_index_generic"
+        roof = {"bound": "mfma" if s["idx_dtype"] != "f32" else "alu", "kernel": kern, "achieved": achieved,
+                "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "algorithmic_flops": idx_flops, "mean_us": idx_us}
+        step_roof = {"indexer_flops": idx_flops, "attention_flops": attn_flops,
+                     "ideal_us_at_peaks": idx_flops / (peak * 1e6) + attn_flops / (2500.0 * 1e6)}
     res = {
         "metric": METRIC,
-        "value": B / (ms_per_step * 1e-3),
+        "value": B * n_q / (ms_per_step * 1e-3),
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -165,24 +202,21 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-indexer/bf16-attn",
+        "dtype": f"{s['idx_dtype']}-indexer/{s['attn_dtype']}-attn",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "context": N, "top_k": k,
+        "config": {"workload": args.workload, "batch": B, "n_q": n_q, "context": N, "top_k": k,
                    "idx_heads": H, "idx_dim": D, "idx_dtype": s["idx_dtype"],
                    "q_heads": s["q_heads"], "kv_heads": s["kv_heads"], "d_qk": s["d_qk"],
                    "d_v": s["d_v"], "latent": s["latent"], "attn_dtype": s["attn_dtype"]},
-        "roofline": {"bound": "hbm", "kernel": "k_index_fp8_mfma", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": idx_bytes, "mean_us": idx_us},
-        "step_roofline": {"algorithmic_bytes": total_bytes,
-                          "achieved_GBs": total_bytes / (ms_per_step * 1e-3) / 1e9,
-                          "frac": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": roof,
+        "step_roofline": step_roof,
         "phases_us": {"index_scores": idx_us, "topk": topk_us, "sparse_attn": attn_us,
-                      "gather_GBs": gather_bytes / (attn_us * 1e-6) / 1e9},
+                      "gather_GBs": gather_bytes / (attn_us * 1e-6) / 1e9,
+                      "attn_TFLOPs": attn_flops / (attn_us * 1e-6) / 1e12},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = _cpu_baseline(inp, args.cpu_sample)
+        res["cpu_baseline"] = _cpu_baseline(inp, args.cpu_sample, args.cpu_rows)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

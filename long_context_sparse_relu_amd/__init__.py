@@ -255,10 +255,11 @@ def _out_tensors(prob, out, lse):
     return out, lse
 
 
-def sparse_attn(prob: DSAProblem, idx, out=None, lse=None, stream=None):
+def sparse_attn(prob: DSAProblem, idx, out=None, lse=None, workspace=None, stream=None):
     """(out [B,n_q,Hq,dv], lse [B,n_q,Hq]) of attention over the rows in idx."""
     out, lse = _out_tensors(prob, out, lse)
-    _check(load_library().dsa_sparse_attn(prob.ref(), _ptr(idx), _ptr(out), _ptr(lse), None, 0,
+    ws = _workspace(OP_SPARSE_ATTN, prob, workspace)
+    _check(load_library().dsa_sparse_attn(prob.ref(), _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                           _stream(stream)))
     return out, lse
 

@@ -333,14 +333,24 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     }
 }
 
-hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
+static bool gqa_d128_eligible(const AttnArgs& a) {
+    return a.dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128 && a.Hq / a.Hkv <= 16;
+}
+
+size_t attn_workspace_bytes(const AttnArgs& a) {
+    if (gqa_d128_eligible(a) || !attn_wide_eligible(a)) return 0;
+    return attn_wide_workspace_bytes(a);
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
-    if (a.dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128 && G <= 16) {
+    if (gqa_d128_eligible(a)) {
         const size_t idx_lds = static_cast<size_t>(a.kk) * sizeof(int32_t);   // kk <= 8192: 32 KiB
         hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH>), dim3(a.Hkv, a.rows), dim3(kGqaWaves * 64),
                            idx_lds, st, a);
         return hipGetLastError();
     }
+    if (attn_wide_eligible(a)) return launch_attn_wide(a, static_cast<float*>(ws), st);
     const size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +
                          static_cast<size_t>(kGenTK) * a.dv) * sizeof(float);
     if (smem > 64 * 1024) {   // the latent shape stages ~104 KiB of rows

@@ -143,7 +143,7 @@ bool use_sampled(const dsa_problem_t* p) {
 struct FusedLayout {
     bool sampled;
     int block_rows;
-    size_t scores_off, topk_off, idx_off, total;
+    size_t scores_off, topk_off, idx_off, attn_off, total;
 };
 
 FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
@@ -158,7 +158,9 @@ FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
         L.topk_off = align_up(static_cast<size_t>(L.block_rows) * p->n_k * sizeof(float));
         L.idx_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
     }
-    L.total = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t)) : 0);
+    L.attn_off = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t)) : 0);
+    dsa::AttnArgs aa = attn_args(p, nullptr, nullptr, nullptr);
+    L.total = L.attn_off + align_up(dsa::attn_workspace_bytes(aa));
     return L;
 }
 
@@ -204,7 +206,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         if (s != DSA_OK) return s;
     }
     dsa::AttnArgs aa = attn_args(p, idx, out, lse);
-    return device_status(dsa::launch_sparse_attn(aa, st), "attention launch");
+    return device_status(dsa::launch_sparse_attn(aa, base + L.attn_off, st), "attention launch");
 }
 
 }  // namespace
@@ -218,7 +220,9 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
     if (s != DSA_OK) return static_cast<size_t>(-1);
     switch (op) {
         case DSA_OP_INDEX_SCORES: return 0;
-        case DSA_OP_SPARSE_ATTN: return 0;
+        case DSA_OP_SPARSE_ATTN:
+            if (check_topk(p) != DSA_OK || check_attn(p) != DSA_OK) return static_cast<size_t>(-1);
+            return dsa::attn_workspace_bytes(attn_args(p, nullptr, nullptr, nullptr));
         case DSA_OP_TOPK:
             if (check_topk(p) != DSA_OK) return static_cast<size_t>(-1);
             return dsa::topk_workspace_bytes(rows_of(p), p->n_k);
@@ -260,14 +264,16 @@ dsa_status_t dsa_topk(const dsa_problem_t* p, const float* scores, int32_t* idx,
 
 dsa_status_t dsa_sparse_attn(const dsa_problem_t* p, const int32_t* idx, void* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace; (void)workspace_bytes;
     g_last_error.clear();
     dsa_status_t s;
     if ((s = check_common(p)) != DSA_OK || (s = check_topk(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK)
         return s;
     if (!idx || !out) return fail(DSA_E_INVALID, "idx and out are required");
     dsa::AttnArgs a = attn_args(p, idx, out, lse);
-    return device_status(dsa::launch_sparse_attn(a, stream), "attention launch");
+    const size_t need = dsa::attn_workspace_bytes(a);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    return device_status(dsa::launch_sparse_attn(a, workspace, stream), "attention launch");
 }
 
 dsa_status_t dsa_prefill(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,

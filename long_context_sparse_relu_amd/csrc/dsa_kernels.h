@@ -103,6 +103,13 @@ size_t topk_sampled_workspace_bytes(int rows, int n_k);
 void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t);
 hipError_t launch_topk_sample(const SampledTopk& t, hipStream_t st);
 hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st);
-hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+// Attention over index sets; `ws` holds attn_workspace_bytes(a) bytes (the
+// per-slice partials of the split kernel), possibly 0.
+size_t attn_workspace_bytes(const AttnArgs& a);
+hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st);
+// MFMA kernel for wide rows / many heads per kv head (attn_wide.hip).
+bool attn_wide_eligible(const AttnArgs& a);
+size_t attn_wide_workspace_bytes(const AttnArgs& a);
+hipError_t launch_attn_wide(const AttnArgs& a, float* part, hipStream_t st);
 
 }  // namespace dsa
