@@ -338,12 +338,14 @@ static bool gqa_d128_eligible(const AttnArgs& a) {
 }
 
 size_t attn_workspace_bytes(const AttnArgs& a) {
+    if (attn_masked_eligible(a)) return attn_masked_workspace_bytes(a);
     if (gqa_d128_eligible(a) || !attn_wide_eligible(a)) return 0;
     return attn_wide_workspace_bytes(a);
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
+    if (attn_masked_eligible(a)) return launch_attn_masked(a, static_cast<uint32_t*>(ws), st);
     if (gqa_d128_eligible(a)) {
         const size_t idx_lds = static_cast<size_t>(a.kk) * sizeof(int32_t);   // kk <= 8192: 32 KiB
         hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH>), dim3(a.Hkv, a.rows), dim3(kGqaWaves * 64),

@@ -128,6 +128,11 @@ EDGE_CASES = {
     # long ragged rows: the fused decode takes the sampled top-k (n_k >= 16 k)
     "fp8_sampled_ragged": dict(B=3, n_q=1, n_k=50001, idx_heads=16, idx_dtype="e4m3", top_k=1000,
                                q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16"),
+    # prefill long enough for the masked dense tiles (GQA, ragged last query block)
+    "masked_prefill_gqa": dict(n_q=300, n_k=300, idx_heads=8, idx_dtype="bf16", top_k=64, q_heads=4,
+                               kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16"),
+    "masked_prefill_prefix": dict(B=2, n_q=130, n_k=1000, idx_heads=4, idx_dtype="bf16", top_k=200,
+                                  q_heads=2, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16"),
     "bf16_generic_d64": dict(n_q=50, n_k=2000, idx_heads=8, top_k=128, q_heads=8, kv_heads=2,
                              d_qk=64, d_v=64, attn_dtype="bf16", idx_dtype="bf16"),
 }
