@@ -131,13 +131,14 @@ int fused_block_rows(const dsa_problem_t* p) {
     return static_cast<int>(r);
 }
 
-// The sampled top-k (no score rows in memory) serves long FP8 rows; other
-// problems go through score blocks and the full radix select.
+// The sampled top-k (no score rows in memory) serves decode-shaped problems
+// with long FP8 rows; prefill (the tiled indexer) and other problems go
+// through score blocks and the full radix select.
 bool use_sampled(const dsa_problem_t* p) {
     dsa::IndexArgs probe{};
     probe.dtype = p->idx_dtype;
     probe.H = p->idx_heads;
-    return dsa::index_fp8_path(probe) && dsa::topk_sampled_eligible(p->n_k, p->top_k);
+    return p->n_q < 16 && dsa::index_fp8_path(probe) && dsa::topk_sampled_eligible(p->n_k, p->top_k);
 }
 
 struct FusedLayout {
@@ -191,6 +192,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         }
         float* scores = reinterpret_cast<float*>(base + L.scores_off);
         dsa::IndexArgs ia = index_args(p, r0, nr, scores);
+        ia.visible_only = true;
         dsa::TopkArgs ta = topk_args(p, r0, nr, scores, idx + static_cast<size_t>(r0) * p->top_k,
                                      base + L.topk_off);
         if (dsa::index_fills_hist(ia)) {

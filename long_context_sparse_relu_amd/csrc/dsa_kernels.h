@@ -22,6 +22,7 @@ struct IndexArgs {
     const int32_t* q_pos;
     float* scores;       // [rows, n_k], row 0 = absolute row row0
     uint32_t* hist;      // optional [rows][kTopkBins] top-k histogram to accumulate into
+    bool visible_only;   // scores past pos(t) may be left unwritten (the top-k never reads them)
     // candidate mode (sampled top-k): per-row metadata and candidate lists
     uint32_t* meta;      // [rows][kTopkMeta]
     uint64_t* cand;      // [rows][cand_cap]
