@@ -15,9 +15,9 @@
 //           last visible key.  Per tile: S^T = K Q^T on
 //           v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T in registers), the
 //           query's bits mask S, online softmax per lane (query l%16) in fp32,
-//           then O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 with V^T read
-//           from LDS.  Tiles where none of a wave's queries keep a key are
-//           skipped by that wave.
+//           then O^T += V^T P^T, also on v_mfma_f32_16x16x32_bf16, with V^T
+//           read from LDS.  Tiles where none of a wave's queries keep a key
+//           are skipped by that wave.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -51,9 +51,17 @@ __global__ __launch_bounds__(256) void k_sel_bitmap(AttnArgs a, uint32_t* bm, in
     for (int i = threadIdx.x; i < words; i += blockDim.x) out[i] = lb[i];
 }
 
+// V is staged transposed (V^T[dim][key]) so that the P.V operand is two
+// 8-byte LDS reads; P.V runs on v_mfma_f32_16x16x32_bf16 over 32 keys: lane l
+// supplies keys {32m + 4(l/16) + i, 32m + 16 + 4(l/16) + i : i < 4} -- the
+// four S^T values it already holds from each of the two 16-key tiles -- and
+// the V^T operand takes the same eight keys.  Tiles are double-buffered: the
+// next tile's rows are in flight while the current one is multiplied.
+constexpr int kVtStr = kKB + 8;   // V^T row stride (bf16)
+
 __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
-    __shared__ __align__(16) uint16_t k_s[kKB * kStr];
-    __shared__ __align__(16) uint16_t v_s[kKB * kStr];
+    __shared__ __align__(16) uint16_t k_s[2][kKB * kStr];
+    __shared__ __align__(16) uint16_t vt_s[2][128 * kVtStr];
     __shared__ int last_s[4];
 
     const int nqb = (a.n_q + kQB - 1) / kQB;
@@ -100,39 +108,58 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // tile loader: 256 threads x 4 x 16 B per matrix; key rows past n_k read as zero
+    // loader: 256 threads x 4 rows x 16 B of K and of V per tile
     const int lrow = threadIdx.x >> 4;          // 0..15, plus 16 per step
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
-    for (int tile = 0; tile < ntiles; ++tile) {
+    v8bf pk[4], pv[4];
+    uint32_t pw0 = 0u, pw1 = 0u;
+    auto fetch = [&](int tile) {
         const int key0 = tile * kKB;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int kr = lrow + 16 * r;
-            const int key = key0 + kr;
-            v8bf kv = v8bf{}, vv = v8bf{};
+            const int key = key0 + lrow + 16 * r;
             if (key < a.n_k) {
-                kv = *reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(key) * rstride + lcol);
-                vv = *reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(key) * rstride + lcol);
+                pk[r] = *reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(key) * rstride + lcol);
+                pv[r] = *reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(key) * rstride + lcol);
+            } else {
+                pk[r] = v8bf{};
+                pv[r] = v8bf{};
             }
-            *reinterpret_cast<v8bf*>(k_s + kr * kStr + lcol) = kv;
-            *reinterpret_cast<v8bf*>(v_s + kr * kStr + lcol) = vv;
         }
-        // this query's 64 mask bits for the tile
-        uint32_t w0 = 0u, w1 = 0u;
-        if (live_q) {
-            w0 = brow[2 * tile];
-            w1 = brow[2 * tile + 1];
+        pw0 = live_q ? brow[2 * tile] : 0u;
+        pw1 = live_q ? brow[2 * tile + 1] : 0u;
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int kr = lrow + 16 * r;
+            *reinterpret_cast<v8bf*>(&k_s[buf][kr * kStr + lcol]) = pk[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<__bf16*>(&vt_s[buf][(lcol + e) * kVtStr + kr]) = pv[r][e];
         }
-        __syncthreads();
+    };
+
+    if (ntiles > 0) {
+        fetch(0);
+        stage(0);
+    }
+    uint32_t w0 = pw0, w1 = pw1;
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int buf = tile & 1;
+        if (tile + 1 < ntiles) fetch(tile + 1);  // in flight during the multiply
         const bool any = __ballot((w0 | w1) != 0u) != 0ull;
         if (any) {                               // uniform per wave
+            const uint16_t* kt_s = k_s[buf];
+            const uint16_t* vt = vt_s[buf];
             v4f acc[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 acc[kt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const v8bf ka = *reinterpret_cast<const v8bf*>(k_s + (kt * 16 + col) * kStr + kg * 32 + c * 8);
+                    const v8bf ka = *reinterpret_cast<const v8bf*>(kt_s + (kt * 16 + col) * kStr + kg * 32 + c * 8);
                     acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb4[c], acc[kt], 0, 0, 0);
                 }
             }
@@ -151,32 +178,38 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
             bmax = wave_max_xor_16_32(bmax);
             const float m_new = fmaxf(m_run, bmax);
             float corr = 1.0f, psum = 0.0f;
-            v4bf pb[4];
+            v8bf pb[2];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float p = m_new != -__builtin_inff() ? exp2f(z[kt][i] - m_new) : 0.0f;
                     psum += p;
-                    pb[kt][i] = static_cast<__bf16>(p);
+                    pb[kt >> 1][(kt & 1) * 4 + i] = static_cast<__bf16>(p);
                 }
             if (m_new != -__builtin_inff()) corr = exp2f(m_run - m_new);
             l_part = l_part * corr + psum;
             m_run = m_new;
 #pragma unroll
-            for (int d = 0; d < 8; ++d) o[d] *= corr;
+            for (int d = 0; d < 8; ++d) {
+                o[d] *= corr;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    v4bf va;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        va[i] = *reinterpret_cast<const __bf16*>(v_s + (kt * 16 + 4 * kg + i) * kStr + 16 * d + col);
-                    o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kt], o[d], 0, 0, 0);
+                for (int m = 0; m < 2; ++m) {
+                    // keys 32m + 4kg + (0..3) and 32m + 16 + 4kg + (0..3) of dim 16d + col
+                    const uint16_t* vrow = vt + (16 * d + col) * kVtStr + 32 * m + 4 * kg;
+                    const v4bf lo = *reinterpret_cast<const v4bf*>(vrow);
+                    const v4bf hi = *reinterpret_cast<const v4bf*>(vrow + 16);
+                    const v8bf va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[m], o[d], 0, 0, 0);
                 }
+            }
         }
-        __syncthreads();                         // the tile buffers are reused
+        if (tile + 1 < ntiles) {
+            stage(buf ^ 1);                      // the other buffer was last read a tile ago
+            w0 = pw0;
+            w1 = pw1;
+        }
+        __syncthreads();
     }
 
     const float l_tot = wave_sum_xor_16_32(l_part);
