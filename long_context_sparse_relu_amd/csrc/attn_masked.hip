@@ -16,8 +16,9 @@
 //           v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T in registers), the
 //           query's bits mask S, online softmax per lane (query l%16) in fp32,
 //           then O^T += V^T P^T, also on v_mfma_f32_16x16x32_bf16, with V^T
-//           read from LDS.  Tiles where none of a wave's queries keep a key
-//           are skipped by that wave.
+//           read from the row-major V tile by transposing LDS reads.  Tiles
+//           where none of a wave's queries keep a key are skipped by that
+//           wave.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -51,17 +52,31 @@ __global__ __launch_bounds__(256) void k_sel_bitmap(AttnArgs a, uint32_t* bm, in
     for (int i = threadIdx.x; i < words; i += blockDim.x) out[i] = lb[i];
 }
 
-// V is staged transposed (V^T[dim][key]) so that the P.V operand is two
-// 8-byte LDS reads; P.V runs on v_mfma_f32_16x16x32_bf16 over 32 keys: lane l
-// supplies keys {32m + 4(l/16) + i, 32m + 16 + 4(l/16) + i : i < 4} -- the
-// four S^T values it already holds from each of the two 16-key tiles -- and
-// the V^T operand takes the same eight keys.  Tiles are double-buffered: the
-// next tile's rows are in flight while the current one is multiplied.
-constexpr int kVtStr = kKB + 8;   // V^T row stride (bf16)
+// P.V runs on v_mfma_f32_16x16x32_bf16 over 32 keys.  Lane l supplies the
+// eight keys {32m + 4(l/16) + i, 32m + 16 + 4(l/16) + i : i < 4} -- the four
+// S^T values it already holds from each of the two 16-key tiles -- and the V^T
+// operand takes the same eight keys from the row-major V tile with two
+// ds_read_b64_tr_b16: within each 16-lane group, lane i of that instruction
+// receives element i%4 of the 8-byte chunks addressed by lanes i/4, 4+i/4,
+// 8+i/4 and 12+i/4, so lane j addresses key (j/4) of the quadruple and dims
+// 4(j%4)..4(j%4)+3 of the 16-dim slice.  The next tile's rows are fetched into
+// registers while the current one is multiplied.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short lds_s4_t;
+typedef __attribute__((address_space(3))) lds_s4_t* lds_s4_ptr;
+typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr;
+
+__device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
+    lds_s4_ptr lp = (lds_s4_ptr)((lds_u16_ptr)(const_cast<uint16_t*>(p)));
+    lds_s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp);
+    v4bf r;
+    __builtin_memcpy(&r, &v, sizeof r);
+    return r;
+}
 
 __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
-    __shared__ __align__(16) uint16_t k_s[2][kKB * kStr];
-    __shared__ __align__(16) uint16_t vt_s[2][128 * kVtStr];
+    __shared__ __align__(16) uint16_t k_s[kKB * kStr];
+    __shared__ __align__(16) uint16_t v_s[kKB * kStr];
     __shared__ int last_s[4];
 
     const int nqb = (a.n_q + kQB - 1) / kQB;
@@ -129,37 +144,35 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
         pw0 = live_q ? brow[2 * tile] : 0u;
         pw1 = live_q ? brow[2 * tile + 1] : 0u;
     };
-    auto stage = [&](int buf) {
+    auto stage = [&]() {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int kr = lrow + 16 * r;
-            *reinterpret_cast<v8bf*>(&k_s[buf][kr * kStr + lcol]) = pk[r];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<__bf16*>(&vt_s[buf][(lcol + e) * kVtStr + kr]) = pv[r][e];
+            *reinterpret_cast<v8bf*>(&k_s[kr * kStr + lcol]) = pk[r];
+            *reinterpret_cast<v8bf*>(&v_s[kr * kStr + lcol]) = pv[r];
         }
     };
+    // this lane's address pattern for the transposing V reads (see above)
+    const int tr_key = (col >> 2);              // key within a quadruple
+    const int tr_dim = 4 * (col & 3);           // dims within a 16-dim slice
 
     if (ntiles > 0) {
         fetch(0);
-        stage(0);
+        stage();
     }
     uint32_t w0 = pw0, w1 = pw1;
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
         if (tile + 1 < ntiles) fetch(tile + 1);  // in flight during the multiply
         const bool any = __ballot((w0 | w1) != 0u) != 0ull;
         if (any) {                               // uniform per wave
-            const uint16_t* kt_s = k_s[buf];
-            const uint16_t* vt = vt_s[buf];
             v4f acc[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 acc[kt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const v8bf ka = *reinterpret_cast<const v8bf*>(kt_s + (kt * 16 + col) * kStr + kg * 32 + c * 8);
+                    const v8bf ka = *reinterpret_cast<const v8bf*>(k_s + (kt * 16 + col) * kStr + kg * 32 + c * 8);
                     acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb4[c], acc[kt], 0, 0, 0);
                 }
             }
@@ -195,17 +208,17 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
                 o[d] *= corr;
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    // keys 32m + 4kg + (0..3) and 32m + 16 + 4kg + (0..3) of dim 16d + col
-                    const uint16_t* vrow = vt + (16 * d + col) * kVtStr + 32 * m + 4 * kg;
-                    const v4bf lo = *reinterpret_cast<const v4bf*>(vrow);
-                    const v4bf hi = *reinterpret_cast<const v4bf*>(vrow + 16);
+                    const uint16_t* v0 = v_s + (32 * m + 4 * kg + tr_key) * kStr + 16 * d + tr_dim;
+                    const v4bf lo = lds_read_tr16(v0);
+                    const v4bf hi = lds_read_tr16(v0 + 16 * kStr);
                     const v8bf va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[m], o[d], 0, 0, 0);
                 }
             }
         }
         if (tile + 1 < ntiles) {
-            stage(buf ^ 1);                      // the other buffer was last read a tile ago
+            __syncthreads();                     // every wave is done with this tile
+            stage();
             w0 = pw0;
             w1 = pw1;
         }
