@@ -34,7 +34,7 @@ METRIC = "query-tokens/s for indexer+top-k+sparse attn at 128K ctx, k=2048; % of
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 INDEXER_SOURCES = [os.path.join(ROOT, "long_context_sparse_relu_amd", "csrc", f)
-                   for f in ("indexer.hip", "dsa_device.h")]
+                   for f in ("indexer.hip", "fp8_index.h", "dsa_device.h", "dsa_kernels.h")]
 
 
 def _source_hash(paths):
