@@ -164,7 +164,10 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 #ifndef DSA_ATTN_DEPTH
 #define DSA_ATTN_DEPTH 2
 #endif
-constexpr int kGqaWaves = 8;
+#ifndef DSA_ATTN_WAVES
+#define DSA_ATTN_WAVES 8
+#endif
+constexpr int kGqaWaves = DSA_ATTN_WAVES;
 constexpr int kGqaVStride = 136;   // bf16 elements per staged value row (128 + pad)
 
 template <int DEPTH>

@@ -95,9 +95,11 @@ hipError_t launch_index_candidates(const IndexArgs& a, hipStream_t st);
 struct SampledTopk {
     IndexArgs ix;          // the indexer inputs (ix.meta / ix.cand set from here)
     int32_t* idx;          // [rows, k]
+    uint32_t* samples;     // [rows, kSampleKeys] order keys of the sampled scores
     float* scratch;        // [rows, n_k] fp32, used only by a recomputed row
 };
 constexpr int kSampleKeys = 4096;       // keys sampled per row
+constexpr int kSampleSplit = 16;        // workgroups scoring one row's sample
 constexpr int kSampledCandCap = 12288;  // candidates per row
 bool topk_sampled_eligible(int n_k, int k);
 size_t topk_sampled_workspace_bytes(int rows, int n_k);

@@ -6,12 +6,12 @@
 // "从 O(N²) 到 O(N・k)", which recommends k = 256..512 over 1M tokens).  When a
 // row holds many more keys than k, writing every score to memory and reading
 // it back costs more than finding the k largest, so:
-//   sample  one workgroup per row scores kSampleKeys keys -- runs of 16
-//           consecutive keys spread evenly over the row, so every load is a
-//           contiguous 2 KiB block -- with the same MFMA code as the indexer,
-//           and takes a lower bound of the r-th largest sample,
-//           r ~ 1.5 k * samples / visible keys + 24: the indexer then keeps
-//           about 1.5 k + 24 * visible / samples keys;
+//   sample  kSampleSplit workgroups per row score kSampleKeys keys -- runs
+//           of 16 consecutive keys spread evenly over the row, so every load
+//           is a contiguous 2 KiB block -- with the same MFMA code as the
+//           indexer; then one workgroup per row takes a lower bound of the
+//           r-th largest sample, r ~ 1.5 k * samples / visible keys + 24: the
+//           indexer then keeps about 1.5 k + 24 * visible / samples keys;
 //   index   the FP8 indexer appends only scores at or above that bound to the
 //           row's candidate list (indexer.hip, candidate mode);
 //   finish  one workgroup per row radix-selects the exact k largest of the
@@ -44,9 +44,52 @@ struct ScoreRow64 {
     __device__ bool get(int i, uint64_t* out) const { *out = composite64(order_key(sc[i]), i); return true; }
 };
 
-// Lower bound of each row's r-th largest sampled score; clears the row's
+// The sample: kSampleKeys keys per row as runs of 16 consecutive keys spread
+// evenly over the visible prefix (all of it when it is shorter); sample j is
+// key j when m == vis, else run j/16 starts at (j/16) * gap.
+__device__ __forceinline__ int sample_key(int j, int m, int vis, int gap) {
+    return m == vis ? j : (j >> 4) * gap + (j & 15);
+}
+
+// Score the row's samples: grid (kSampleSplit, rows), each workgroup scores
+// kSampleKeys / kSampleSplit of them and stores their order keys.
+__global__ __launch_bounds__(256) void k_topk_sample_score(SampledTopk t) {
+    const IndexArgs& x = t.ix;
+    const int lrow = blockIdx.y, row = x.row0 + lrow;
+    const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
+    const int vis = pos + 1;
+    if (vis <= x.k) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int m = vis < kSampleKeys ? vis : kSampleKeys;
+    const int gap = vis / ((m + 15) / 16);   // >= 16 unless m == vis
+    const int per = kSampleKeys / kSampleSplit;                 // samples per workgroup
+    const int j0 = blockIdx.x * per;
+    if (j0 >= m) return;
+    const int b = row / x.n_q;
+    const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
+    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
+    const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
+    uint32_t* skey = t.samples + static_cast<size_t>(lrow) * kSampleKeys;
+    constexpr int U = kSampleKeys / kSampleSplit / 64;            // blocks of 16 per wave
+    v8i bv[U];
+    float sk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = j0 + (wave * U + u) * 16 + col;
+        load_fp8_key(kb, ksb, j < m ? sample_key(j, m, vis, gap) : 0, j < m, lane, bv[u], sk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = j0 + (wave * U + u) * 16 + col;
+        const float score = fp8_block_score(q, bv[u], sk[u]);
+        if (kg == 0 && j < m) skey[j] = order_key(score);
+    }
+}
+
+// Lower bound of each row's r-th largest sample score; clears the row's
 // candidate counters.
-__global__ __launch_bounds__(kSampleThreads) void k_topk_sample(SampledTopk t) {
+__global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTopk t) {
     __shared__ uint32_t skey[kSampleKeys];
     __shared__ uint32_t lh[kTopkBins];
     __shared__ uint32_t wsum[kSampleThreads / 64 + 2];
@@ -60,40 +103,15 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample(SampledTopk t) {
         if (threadIdx.x == 0) meta[S_KLOW] = 0xFFFFFFFFu;
         return;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    const int col = lane & 15, kg = lane >> 4;
     const int m = vis < kSampleKeys ? vis : kSampleKeys;
-    const int nrun = (m + 15) / 16;        // runs of 16 consecutive keys
-    const int gap = vis / nrun;            // >= 16 unless m == vis; run g starts at key g * gap
-    const int b = row / x.n_q;
-    const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
-    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
-    const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
-    constexpr int U = 8;                   // blocks of 16 samples in flight per wave
-    for (int blk0 = wave * U; blk0 * 16 < m; blk0 += nwaves * U) {   // uniform per wave
-        v8i bv[U];
-        float sk[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = (blk0 + u) * 16 + col;
-            const int key = m == vis ? j : (blk0 + u) * gap + col;
-            load_fp8_key(kb, ksb, key, j < m, lane, bv[u], sk[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = (blk0 + u) * 16 + col;
-            const float score = fp8_block_score(q, bv[u], sk[u]);
-            if (kg == 0 && j < m) skey[j] = order_key(score);
-        }
-    }
+    copy_to_lds(skey, t.samples + static_cast<size_t>(lrow) * kSampleKeys, m);
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
     __syncthreads();
     const int64_t want = (3 * static_cast<int64_t>(m) * x.k + 2 * static_cast<int64_t>(vis) - 1) /
                          (2 * static_cast<int64_t>(vis)) + 24;
     uint32_t k_low = 0u;                   // every visible key a candidate
     if (want < m) {
         const uint32_t r = static_cast<uint32_t>(want);
-        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-        __syncthreads();
         for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[skey[j] >> 21], 1u);
         __syncthreads();
         int d0; uint32_t gt0;
@@ -192,6 +210,7 @@ size_t topk_sampled_workspace_bytes(int rows, int n_k) {
     const size_t r = static_cast<size_t>(rows);
     return align256(r * kTopkMeta * sizeof(uint32_t)) +
            align256(r * kSampledCandCap * sizeof(uint64_t)) +
+           align256(r * kSampleKeys * sizeof(uint32_t)) +
            align256(r * static_cast<size_t>(n_k) * sizeof(float));
 }
 
@@ -203,12 +222,17 @@ void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t) {
     t.ix.cand = reinterpret_cast<uint64_t*>(p);
     t.ix.cand_cap = kSampledCandCap;
     p += align256(r * kSampledCandCap * sizeof(uint64_t));
+    t.samples = reinterpret_cast<uint32_t*>(p);
+    p += align256(r * kSampleKeys * sizeof(uint32_t));
     t.scratch = reinterpret_cast<float*>(p);
     (void)n_k;
 }
 
 hipError_t launch_topk_sample(const SampledTopk& t, hipStream_t st) {
-    hipLaunchKernelGGL(k_topk_sample, dim3(t.ix.rows), dim3(kSampleThreads), 0, st, t);
+    hipLaunchKernelGGL(k_topk_sample_score, dim3(kSampleSplit, t.ix.rows), dim3(256), 0, st, t);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_topk_sample_bound, dim3(t.ix.rows), dim3(kSampleThreads), 0, st, t);
     return hipGetLastError();
 }
 
