@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 // O) are merged through LDS at the end.
 // ---------------------------------------------------------------------------
 #ifndef DSA_ATTN_DEPTH
-#define DSA_ATTN_DEPTH 2
+#define DSA_ATTN_DEPTH 1
 #endif
 #ifndef DSA_ATTN_WAVES
 #define DSA_ATTN_WAVES 8
