@@ -64,16 +64,32 @@ __device__ __forceinline__ int row_pos(const int32_t* q_pos, int row, int n_q, i
     return p < n_k - 1 ? p : n_k - 1;  // may be negative: nothing visible
 }
 
-__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+// Exchanges between the four 16-lane rows of a wave, on the VALU: with both
+// operands equal, v_permlane16_swap leaves row r's lanes holding rows 2(r/2)
+// and 2(r/2)+1 in its two results, and v_permlane32_swap does the same for
+// the two halves, so one op plus one add combines lanes l and l^16 (l^32).
+// The combined values are the same in every lane of a group and do not
+// depend on the order of the two operands (IEEE add and max commute).
+__device__ __forceinline__ float pair16_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
-}
+// Sum (max) over the lanes l, l^16, l^32, l^48: the four lanes holding the
+// same column of a 16x16 MFMA result.
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) { return pair32_sum(pair16_sum(x)); }
+__device__ __forceinline__ float wave_max_xor_16_32(float x) { return pair32_max(pair16_max(x)); }
 
 }  // namespace dsa
