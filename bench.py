@@ -185,7 +185,7 @@ def main(argv=None):
         idx_flops = 2 * pairs * H * D
         peak = {"e4m3": 5000.0, "bf16": 2500.0, "f32": 157.3}[s["idx_dtype"]]
         achieved = idx_flops / (idx_us * 1e-6) / 1e12
-        kern = "k_index_fp8_mfma" if s["idx_dtype"] == "e4m3" else "k_index_generic"
+        kern = "k_index_tiled" if (s["idx_dtype"] != "f32" and n_q >= 16 and H <= 16) else "k_index_generic"
         roof = {"bound": "mfma" if s["idx_dtype"] != "f32" else "alu", "kernel": kern, "achieved": achieved,
                 "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                 "algorithmic_flops": idx_flops, "mean_us": idx_us}

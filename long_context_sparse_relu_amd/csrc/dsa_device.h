@@ -87,6 +87,24 @@ __device__ __forceinline__ float pair32_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Column sums of four 16x16 MFMA partials at once.  p[j] holds, in lane l,
+// one partial of column l%16 of block j (the four 16-lane rows hold different
+// partials of the same column).  v_permlane32_swap(X, Y) swaps X's upper half
+// with Y's lower half, so the sum of its two results holds X's half-sums in
+// the lower half and Y's in the upper; v_permlane16_swap(X, Y) swaps X's odd
+// rows with Y's even rows, so the sum holds X's row-pair sums in the even rows
+// and Y's in the odd ones.  Applied to (p0,p2), (p1,p3) and then to the two
+// sums, lane 16j + c ends with the full sum over the four rows of column c of
+// block j: one value per lane and 64 distinct columns in lane order.
+__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+    const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Sum (max) over the lanes l, l^16, l^32, l^48: the four lanes holding the
 // same column of a 16x16 MFMA result.
 __device__ __forceinline__ float wave_sum_xor_16_32(float x) { return pair32_sum(pair16_sum(x)); }

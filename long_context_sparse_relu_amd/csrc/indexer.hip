@@ -220,45 +220,57 @@ __global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs
 
 // ---------------------------------------------------------------------------
 // Tiled path for prefill rows (FP8 E4M3 or bf16, up to 16 heads, d = 128).
-// Each workgroup takes 16 consecutive query rows of one sequence and one
-// chunk of kIdxChunk keys; the chunk's keys are staged 64 at a time in LDS
-// and shared by the 16 queries (4 per wave), so every key row is fetched once
-// per 16 queries instead of once per query.  Per (query, 16 keys) the scores
-// come from one v_mfma_scale_f32_16x16x128_f8f6f4 (FP8) or four
-// v_mfma_f32_16x16x32_bf16 (bf16) with the heads as M, then the ReLU-weighted
-// head reduction of fp8_index.h.  Keys past a query's last visible key are
-// written as -inf only when `write_future` (the unfused entry point).
+// Each workgroup takes kTQ consecutive query rows of one sequence (kQPW per
+// wave) and one chunk of kIdxChunk keys; the chunk's keys are staged 64 at a
+// time in LDS and shared by all kTQ queries, so every key row is fetched once
+// per kTQ queries, and each key operand read from LDS feeds kQPW MFMAs.  The
+// next tile is fetched into registers while the current one is scored.  Per
+// (query, 16 keys) the scores come from one v_mfma_scale_f32_16x16x128_f8f6f4
+// (FP8) or four v_mfma_f32_16x16x32_bf16 (bf16) with the heads as M; each lane
+// folds its four heads with ReLU and the head weights, and one reduce-scatter
+// over the four 16-key blocks of a tile finishes the head sums, leaving lane l
+// with the score of key l of the tile (one coalesced 256-byte store per query
+// and tile).  Keys past a query's last visible key are written as -inf only
+// when `write_future` (the unfused entry point).
 // ---------------------------------------------------------------------------
 constexpr int kIdxChunk = 2048;   // keys per workgroup
 constexpr int kTileKeys = 64;     // keys per LDS tile
+// query rows per wave and waves per workgroup (measured best: FP8 4 x 8, bf16 2 x 4)
+template <int DT> struct TiledShape { static constexpr int QPW = DT == E4M3 ? 4 : 2, TW = DT == E4M3 ? 8 : 4; };
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_index_tiled(IndexArgs x, int t_first, int nrows, int write_future) {
+__global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexArgs x, int t_first, int nrows,
+                                                                        int write_future) {
+    constexpr int kQPW = TiledShape<DT>::QPW, kTW = TiledShape<DT>::TW, kTQ = kQPW * kTW;
     constexpr int KROW = DT == E4M3 ? 128 : 256;           // bytes per key row
     constexpr int KSTR = KROW + 16;                         // padded LDS stride (conflict-free 16 B reads)
     constexpr int NC = DT == E4M3 ? 1 : 4;                  // MFMAs per 16 keys
+    constexpr int LPT = kTileKeys * KROW / 16 / (kTW * 64); // 16-byte loads per thread per tile
+    static_assert(LPT * kTW * 64 * 16 == kTileKeys * KROW, "a tile must split evenly over the threads");
     __shared__ __align__(16) uint8_t k_s[kTileKeys * KSTR];
     __shared__ float ks_s[kTileKeys];
-    __shared__ int last_s[4];
+    __shared__ int last_s[kTW];
 
-    const int nqb = (nrows + 15) / 16;
+    const int nqb = (nrows + kTQ - 1) / kTQ;
     const int qb = nqb - 1 - static_cast<int>(blockIdx.y);  // longest query blocks first
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
     const int n_k = x.n_k, H = x.H;
 
-    // this wave's 4 query rows (absolute row index t_first + qb*16 + 4*wave + q)
-    int rows[4], pos[4];
-    float w[4][4], sq[4];
-    v8i a8[4];
-    v8bf a16[4][4];
+    // this wave's query rows (absolute row index t_first + qb*kTQ + kQPW*wave + q)
+    int rows[kQPW], pos[kQPW];
+    float w[kQPW][4], sq[kQPW];
+    v8i a8[DT == E4M3 ? kQPW : 1];
+    v8bf a16[DT == E4M3 ? 1 : kQPW][4];
+    unsigned livem = 0;                                      // bit q: row q exists
     int mp = -1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int lr = qb * 16 + wave * 4 + q;              // row within the launch
+    for (int q = 0; q < kQPW; ++q) {
+        const int lr = qb * kTQ + wave * kQPW + q;          // row within the launch
         const bool live = lr < nrows;
+        livem |= live ? 1u << q : 0u;
         rows[q] = t_first + (live ? lr : 0);
-        pos[q] = live ? row_pos(x.q_pos, rows[q], x.n_q, n_k) : -1;
+        pos[q] = live ? row_pos(x.q_pos, rows[q], x.n_q, n_k) : -1;  // may be negative for a live row
         mp = max(mp, pos[q]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -278,11 +290,13 @@ __global__ __launch_bounds__(256) void k_index_tiled(IndexArgs x, int t_first, i
                 a16[q][c] = (live && col < H) ? *reinterpret_cast<const v8bf*>(qrow + c * 8) : v8bf{};
         }
     }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) mp = max(mp, __shfl_xor(mp, o));
+    mp = max(mp, __shfl_xor(mp, 16));
+    mp = max(mp, __shfl_xor(mp, 32));
     if (lane == 0) last_s[wave] = mp;
     __syncthreads();
-    const int last = max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3]));
+    int last = last_s[0];
+#pragma unroll
+    for (int i = 1; i < kTW; ++i) last = max(last, last_s[i]);
     const int b = t_first / x.n_q;                           // every row of the launch is in sequence b
     const int c0 = blockIdx.x * kIdxChunk;
     const int c1 = min(c0 + kIdxChunk, n_k);
@@ -290,64 +304,90 @@ __global__ __launch_bounds__(256) void k_index_tiled(IndexArgs x, int t_first, i
     const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * n_k * KROW;
     const float* ksb = DT == E4M3 ? x.ik_scale + static_cast<size_t>(b) * n_k : nullptr;
 
-    for (int k0 = c0; k0 < cvis; k0 += kTileKeys) {
-        // stage 64 key rows (and their scales)
-        for (int i = threadIdx.x; i < kTileKeys * KROW / 16; i += blockDim.x) {
+    v4i pre[LPT];
+    float pre_s = 0.0f;
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int i = threadIdx.x + u * kTW * 64;
             const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
             const int key = k0 + kr;
-            v4i val = {0, 0, 0, 0};
-            if (key < n_k) val = *reinterpret_cast<const v4i*>(kb + static_cast<size_t>(key) * KROW + off);
-            *reinterpret_cast<v4i*>(k_s + kr * KSTR + off) = val;
+            pre[u] = key < n_k ? *reinterpret_cast<const v4i*>(kb + static_cast<size_t>(key) * KROW + off)
+                               : v4i{0, 0, 0, 0};
         }
         if constexpr (DT == E4M3) {
-            if (threadIdx.x < kTileKeys) {
-                const int key = k0 + threadIdx.x;
-                ks_s[threadIdx.x] = key < n_k ? ksb[key] : 0.0f;
-            }
+            const int key = k0 + threadIdx.x;
+            pre_s = (threadIdx.x < kTileKeys && key < n_k) ? ksb[key] : 0.0f;
         }
-        __syncthreads();
+    };
+    auto stage = [&]() {
 #pragma unroll
-        for (int g16 = 0; g16 < kTileKeys / 16; ++g16) {
-            const int kr = g16 * 16 + col;
-            const int s = k0 + kr;
-            v8i b8;
-            v8bf b16[4];
+        for (int u = 0; u < LPT; ++u) {
+            const int i = threadIdx.x + u * kTW * 64;
+            const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
+            *reinterpret_cast<v4i*>(k_s + kr * KSTR + off) = pre[u];
+        }
+        if (DT == E4M3 && threadIdx.x < kTileKeys) ks_s[threadIdx.x] = pre_s;
+    };
+
+    if (c0 < cvis) {
+        fetch(c0);
+        stage();
+    }
+    __syncthreads();
+    for (int k0 = c0; k0 < cvis; k0 += kTileKeys) {
+        const bool more = k0 + kTileKeys < cvis;
+        if (more) fetch(k0 + kTileKeys);                     // in flight while this tile is scored
+        // key k0 + g16*16 + col sits in LDS row g16*16 + col; lane l scores key k0 + l
+        v8i b8[4];
+        v8bf b16[4][4];
+#pragma unroll
+        for (int g16 = 0; g16 < 4; ++g16) {
+            const uint8_t* kr = k_s + (g16 * 16 + col) * KSTR;
             if constexpr (DT == E4M3) {
-                b8 = load_split32(k_s + kr * KSTR, kg);
+                b8[g16] = load_split32(kr, kg);
             } else {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    b16[c] = *reinterpret_cast<const v8bf*>(k_s + kr * KSTR + kg * 64 + c * 16);
+                for (int c = 0; c < 4; ++c) b16[g16][c] = *reinterpret_cast<const v8bf*>(kr + kg * 64 + c * 16);
             }
-            const float sk = DT == E4M3 ? ks_s[kr] : 1.0f;
+        }
+        const int s = k0 + lane;
+        const float sk = DT == E4M3 ? ks_s[lane] : 1.0f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kQPW; ++q) {
+            float p[4];
+#pragma unroll
+            for (int g16 = 0; g16 < 4; ++g16) {
                 v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
                 if constexpr (DT == E4M3) {
-                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8[q], b8, acc, 0, 0, 0, 127, 0, 127);
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8[q], b8[g16], acc, 0, 0, 0, 127, 0, 127);
                 } else {
 #pragma unroll
-                    for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a16[q][c], b16[c], acc, 0, 0, 0);
+                    for (int c = 0; c < NC; ++c)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a16[q][c], b16[g16][c], acc, 0, 0, 0);
                 }
                 float part = w[q][0] * fmaxf(acc[0], 0.0f);
                 part = fmaf(w[q][1], fmaxf(acc[1], 0.0f), part);
                 part = fmaf(w[q][2], fmaxf(acc[2], 0.0f), part);
-                part = fmaf(w[q][3], fmaxf(acc[3], 0.0f), part);
-                part = wave_sum_xor_16_32(part);
-                if (kg == 0 && s < c1 && pos[q] >= 0) {
-                    float* out = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
-                    if (s <= pos[q]) out[s] = DT == E4M3 ? part * (sq[q] * sk) : part;
-                    else if (write_future) out[s] = -__builtin_inff();
-                }
+                p[g16] = fmaf(w[q][3], fmaxf(acc[3], 0.0f), part);
             }
+            const float part = reduce_scatter4(p[0], p[1], p[2], p[3]);
+            if (s < c1 && (livem >> q & 1u)) {
+                float* out = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
+                if (s <= pos[q]) out[s] = DT == E4M3 ? part * (sq[q] * sk) : part;
+                else if (write_future) out[s] = -__builtin_inff();
+            }
+        }
+        if (more) {
+            __syncthreads();                                 // every wave is done with this tile
+            stage();
         }
         __syncthreads();
     }
     if (write_future) {
         // keys of this chunk no query of the block sees
-        for (int q = 0; q < 4; ++q) {
-            const int lr = qb * 16 + wave * 4 + q;
-            if (lr >= nrows) continue;
+        for (int q = 0; q < kQPW; ++q) {
+            if (!(livem >> q & 1u)) continue;
             float* out = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
             for (int s = max(c0, cvis) + lane; s < c1; s += 64) out[s] = -__builtin_inff();
         }
@@ -358,23 +398,27 @@ bool index_tiled_path(const IndexArgs& a) {
     return (a.dtype == E4M3 || a.dtype == BF16) && a.H <= 16 && a.n_q >= 16;
 }
 
-hipError_t launch_index_tiled(const IndexArgs& a, bool write_future, hipStream_t st) {
+template <int DT>
+static hipError_t launch_index_tiled_dt(const IndexArgs& a, bool write_future, hipStream_t st) {
+    constexpr int kTW = TiledShape<DT>::TW, kTQ = TiledShape<DT>::QPW * kTW;
     // one launch per sequence the rows touch, so a query block never spans two
     int r = a.row0;
     const int r_end = a.row0 + a.rows;
     while (r < r_end) {
         const int seq_end = (r / a.n_q + 1) * a.n_q;
         const int n = min(r_end, seq_end) - r;
-        const dim3 grid((a.n_k + kIdxChunk - 1) / kIdxChunk, (n + 15) / 16);
-        if (a.dtype == E4M3)
-            hipLaunchKernelGGL(k_index_tiled<E4M3>, grid, dim3(256), 0, st, a, r, n, write_future ? 1 : 0);
-        else
-            hipLaunchKernelGGL(k_index_tiled<BF16>, grid, dim3(256), 0, st, a, r, n, write_future ? 1 : 0);
+        const dim3 grid((a.n_k + kIdxChunk - 1) / kIdxChunk, (n + kTQ - 1) / kTQ);
+        hipLaunchKernelGGL(k_index_tiled<DT>, grid, dim3(kTW * 64), 0, st, a, r, n, write_future ? 1 : 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         r += n;
     }
     return hipSuccess;
+}
+
+hipError_t launch_index_tiled(const IndexArgs& a, bool write_future, hipStream_t st) {
+    return a.dtype == E4M3 ? launch_index_tiled_dt<E4M3>(a, write_future, st)
+                           : launch_index_tiled_dt<BF16>(a, write_future, st);
 }
 
 // ---------------------------------------------------------------------------

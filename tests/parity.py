@@ -25,7 +25,7 @@ LSE_TOL = {"f32": 1e-4, "bf16": 2e-3}
 
 def check_scores(gpu_row, ora_row, pos):
     gpu_row = np.asarray(gpu_row, dtype=np.float64)
-    vis = min(pos + 1, len(ora_row))
+    vis = max(0, min(pos + 1, len(ora_row)))
     assert np.all(np.isneginf(gpu_row[vis:])), "future keys must score -inf"
     a, b = gpu_row[:vis], ora_row[:vis]
     err = np.abs(a - b)

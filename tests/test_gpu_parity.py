@@ -192,6 +192,43 @@ def test_explicit_positions_and_empty_rows():
             check_topk_row(g[t], o_idx[t], sc[t], kth[t], pos[t], 700)
 
 
+@pytest.mark.parametrize("idt", ["e4m3", "bf16"])
+def test_prefill_indexer_explicit_positions(idt):
+    """Query blocks of the tiled prefill indexer with a ragged last block and
+    per-row positions: empty rows (negative positions) next to long ones, so
+    one block mixes rows that see nothing with rows that see every chunk."""
+    n_q, n_k = 45, 5000
+    sp = custom_spec(name="qpos_tiled", B=2, n_q=n_q, n_k=n_k, idx_heads=16 if idt == "e4m3" else 8,
+                     idx_dtype=idt, top_k=300, q_heads=4, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=23)
+    rng = np.random.default_rng(23)
+    qp = rng.integers(0, n_k, size=(2, n_q))
+    qp[0, [0, 7, 33, 44]] = [-1, -9, -1, n_k - 1]
+    qp[1, [1, 32, 40]] = [-3, 0, n_k - 1]
+    q_pos = torch.tensor(qp, dtype=torch.int32, device=DEV)
+    prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=300, q=inp["q"],
+                            k=inp["k"], v=inp["v"], iq_scale=inp.get("iq_scale"),
+                            ik_scale=inp.get("ik_scale"), q_pos=q_pos)
+    scores = dsa.index_scores(prob)
+    idx = dsa.topk(prob, scores)
+    idx_f = torch.empty((2, n_q, 300), dtype=torch.int32, device=DEV)
+    dsa.prefill(prob, idx_out=idx_f)
+    torch.cuda.synchronize()
+    inp["pos"] = q_pos
+    ov = oracle_view(inp)
+    for b in range(2):
+        pos = ov["pos"][b].astype(np.int64)
+        sc = oracle.index_scores(ov["iq"][b], ov["ik"][b], ov["iw"][b], idt,
+                                 ov["iq_scale"][b] if idt == "e4m3" else None,
+                                 ov["ik_scale"][b] if idt == "e4m3" else None, pos)
+        o_idx, kth = oracle.topk(sc, 300, pos)
+        g, gf = idx[b].cpu().numpy(), idx_f[b].cpu().numpy()
+        for t in range(n_q):
+            check_scores(scores[b, t].cpu().numpy(), sc[t], pos[t])
+            check_topk_row(g[t], o_idx[t], sc[t], kth[t], pos[t], 300)
+            check_topk_row(gf[t], o_idx[t], sc[t], kth[t], pos[t], 300)
+
+
 def test_sampled_topk_positions_and_ties():
     """Fused decode in the sampled regime: per-row positions (empty, short and
     long rows) and an all-zero-weight row, whose ties force the recompute path."""
