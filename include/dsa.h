@@ -152,6 +152,26 @@ dsa_status_t dsa_prefill(const dsa_problem_t *p, void *out, float *lse, int32_t 
 dsa_status_t dsa_decode(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Phase timing of the fused entry points, for profiling.
+ * dsa_phase_timing(1) makes every later dsa_prefill / dsa_decode call record
+ * HIP events on its own stream: one before its first kernel and one after
+ * each phase; dsa_phase_timing(0) stops it (the default).  While it is on, the
+ * fused calls create HIP events the first time they need them (kept by the
+ * library until the process ends), and the timer keeps only the latest call:
+ * time one caller at a time.  dsa_phase_times() waits for that call's last
+ * event and writes DSA_PHASE_COUNT floats to `us`, the GPU microseconds of
+ * each phase summed over the call's row blocks (0 for a phase it did not
+ * run).  Returns DSA_E_INVALID if us is NULL or no timed call was made. */
+typedef enum {
+    DSA_PHASE_PREP = 0,      /* threshold sample (decode) or histogram clear */
+    DSA_PHASE_INDEX = 1,     /* indexer kernel */
+    DSA_PHASE_TOPK = 2,      /* top-k selection */
+    DSA_PHASE_ATTN = 3,      /* sparse attention */
+    DSA_PHASE_COUNT = 4
+} dsa_phase_t;
+dsa_status_t dsa_phase_timing(int enable);
+dsa_status_t dsa_phase_times(float *us);
+
 /* Static text for a status code. */
 const char *dsa_status_str(dsa_status_t status);
 

@@ -29,7 +29,10 @@ ABI_VERSION = 1
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
 EXPORTED = ("dsa_abi_version", "dsa_workspace_bytes", "dsa_index_scores", "dsa_topk",
-            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_status_str", "dsa_last_error")
+            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_phase_timing", "dsa_phase_times",
+            "dsa_status_str", "dsa_last_error")
+# dsa_phase_t, in order
+PHASES = ("prep", "index", "topk", "attn")
 
 
 class Problem(ctypes.Structure):
@@ -81,6 +84,10 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp]
     lib.dsa_decode.restype = ctypes.c_int
     lib.dsa_decode.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.dsa_phase_timing.restype = ctypes.c_int
+    lib.dsa_phase_timing.argtypes = [ctypes.c_int]
+    lib.dsa_phase_times.restype = ctypes.c_int
+    lib.dsa_phase_times.argtypes = [ctypes.POINTER(ctypes.c_float)]
     lib.dsa_status_str.restype = ctypes.c_char_p
     lib.dsa_status_str.argtypes = [ctypes.c_int]
     lib.dsa_last_error.restype = ctypes.c_char_p
@@ -277,3 +284,15 @@ def prefill(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, 
 
 def decode(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, stream=None):
     return _fused(load_library().dsa_decode, OP_DECODE, prob, out, lse, idx_out, workspace, stream)
+
+
+def phase_timing(enable: bool):
+    """Turn the fused entry points' phase timer on or off (see dsa_phase_timing)."""
+    _check(load_library().dsa_phase_timing(1 if enable else 0))
+
+
+def phase_times() -> dict:
+    """GPU microseconds per phase of the latest timed fused call (waits for it)."""
+    buf = (ctypes.c_float * len(PHASES))()
+    _check(load_library().dsa_phase_times(buf))
+    return {name: float(buf[i]) for i, name in enumerate(PHASES)}

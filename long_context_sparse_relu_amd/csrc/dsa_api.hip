@@ -1,11 +1,14 @@
 // dsa_api.hip -- the C ABI declared in include/dsa.h: host-side validation,
 // workspace layout and launch sequencing on the caller's stream.  Nothing here
-// allocates, frees, copies or synchronises.
+// allocates device memory, copies or synchronises; only the opt-in phase timer
+// creates HIP events and waits on them.
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "dsa.h"
 #include "dsa_kernels.h"
@@ -28,6 +31,44 @@ dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
 dsa_status_t device_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return DSA_OK;
     return fail(DSA_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Opt-in phase timer: events recorded on the caller's stream between the
+// phases of one fused call, reused by the next timed call.
+struct PhaseTimer {
+    std::mutex mu;
+    bool on = false;
+    int device = -1;
+    std::vector<hipEvent_t> ev;   // ev[0] before the first kernel, ev[i] after a phase
+    std::vector<int> phase;       // phase[i]: the phase ending at ev[i]
+    int used = 0;
+};
+PhaseTimer g_timer;
+
+hipError_t timer_mark(int ph, hipStream_t st) {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (!g_timer.on) return hipSuccess;
+    if (ph < 0) {                              // a new call
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev != g_timer.device) {           // events belong to the device current at creation
+            for (hipEvent_t x : g_timer.ev) (void)hipEventDestroy(x);
+            g_timer.ev.clear();
+            g_timer.phase.clear();
+            g_timer.device = dev;
+        }
+        g_timer.used = 0;
+    }
+    if (g_timer.used == static_cast<int>(g_timer.ev.size())) {
+        hipEvent_t x;
+        hipError_t e = hipEventCreate(&x);
+        if (e != hipSuccess) return e;
+        g_timer.ev.push_back(x);
+        g_timer.phase.push_back(-1);
+    }
+    g_timer.phase[g_timer.used] = ph;
+    return hipEventRecord(g_timer.ev[g_timer.used++], st);
 }
 
 constexpr int kMaxNk = 1 << 24;
@@ -173,9 +214,11 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
     unsigned char* base = static_cast<unsigned char*>(ws);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx_off);
     const int rows = rows_of(p);
+    dsa_status_t s = device_status(timer_mark(-1, st), "phase timer");
+    if (s != DSA_OK) return s;
+    auto mark = [&](int ph) { return device_status(timer_mark(ph, st), "phase timer"); };
     for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
         int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
-        dsa_status_t s;
         if (L.sampled) {
             dsa::SampledTopk t{};
             t.ix = index_args(p, r0, nr, nullptr);
@@ -183,11 +226,11 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
             t.idx = idx + static_cast<size_t>(r0) * p->top_k;
             dsa::topk_sampled_carve(base, nr, p->n_k, t);
             s = device_status(dsa::launch_topk_sample(t, st), "top-k sample launch");
-            if (s != DSA_OK) return s;
+            if (s != DSA_OK || (s = mark(DSA_PHASE_PREP)) != DSA_OK) return s;
             s = device_status(dsa::launch_index_candidates(t.ix, st), "indexer launch");
-            if (s != DSA_OK) return s;
+            if (s != DSA_OK || (s = mark(DSA_PHASE_INDEX)) != DSA_OK) return s;
             s = device_status(dsa::launch_topk_finish_sampled(t, st), "top-k launch");
-            if (s != DSA_OK) return s;
+            if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
             continue;
         }
         float* scores = reinterpret_cast<float*>(base + L.scores_off);
@@ -200,15 +243,17 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
             ia.hist = ta.hist;
             ta.hist_ready = true;
             s = device_status(dsa::launch_zero_u32(ta.hist, ta.zero_words, st), "workspace clear");
-            if (s != DSA_OK) return s;
+            if (s != DSA_OK || (s = mark(DSA_PHASE_PREP)) != DSA_OK) return s;
         }
         s = device_status(dsa::launch_index_scores(ia, st), "indexer launch");
-        if (s != DSA_OK) return s;
+        if (s != DSA_OK || (s = mark(DSA_PHASE_INDEX)) != DSA_OK) return s;
         s = device_status(dsa::launch_topk(ta, st), "top-k launch");
-        if (s != DSA_OK) return s;
+        if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
     }
     dsa::AttnArgs aa = attn_args(p, idx, out, lse);
-    return device_status(dsa::launch_sparse_attn(aa, base + L.attn_off, st), "attention launch");
+    s = device_status(dsa::launch_sparse_attn(aa, base + L.attn_off, st), "attention launch");
+    if (s != DSA_OK) return s;
+    return mark(DSA_PHASE_ATTN);
 }
 
 }  // namespace
@@ -299,6 +344,31 @@ dsa_status_t dsa_decode(const dsa_problem_t* p, void* out, float* lse, int32_t* 
         return s;
     if (!out) return fail(DSA_E_INVALID, "out is required");
     return run_fused(p, out, lse, idx_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status_t dsa_phase_timing(int enable) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    g_timer.on = enable != 0;
+    g_timer.used = 0;
+    return DSA_OK;
+}
+
+dsa_status_t dsa_phase_times(float* us) {
+    g_last_error.clear();
+    if (!us) return fail(DSA_E_INVALID, "us is NULL");
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (g_timer.used < 2) return fail(DSA_E_INVALID, "no timed fused call");
+    for (int i = 0; i < DSA_PHASE_COUNT; ++i) us[i] = 0.0f;
+    dsa_status_t s = device_status(hipEventSynchronize(g_timer.ev[g_timer.used - 1]), "phase timer");
+    if (s != DSA_OK) return s;
+    for (int i = 1; i < g_timer.used; ++i) {
+        float ms = 0.0f;
+        s = device_status(hipEventElapsedTime(&ms, g_timer.ev[i - 1], g_timer.ev[i]), "phase timer");
+        if (s != DSA_OK) return s;
+        us[g_timer.phase[i]] += ms * 1000.0f;
+    }
+    return DSA_OK;
 }
 
 const char* dsa_status_str(dsa_status_t status) {

@@ -9,8 +9,10 @@
 // use the same byte->k assignment, so the contraction is exact whatever order
 // the unit sums in, and each 16-byte load of a wave covers 64 contiguous bytes
 // of every key row it touches.  The 16x16 result lands as
-// acc[i] = dot(head 4g+i, key l%16); ReLU, the head weight and two cross-lane
-// adds finish the head reduction; the positive per-token scales multiply last.
+// acc[i] = dot(head 4g+i, key l%16); ReLU and the head weights fold each
+// lane's four heads, one reduce-scatter over four blocks finishes the head
+// sums (lane l ends with key l%16 of block l/16), and the positive per-token
+// scales multiply last.
 #pragma once
 
 #include "dsa_device.h"
@@ -47,24 +49,27 @@ __device__ __forceinline__ Fp8Query load_fp8_query(const uint8_t* iq, const floa
     return q;
 }
 
-// Operands of key s for this lane (zeros when !live).
-__device__ __forceinline__ void load_fp8_key(const uint8_t* kb, const float* ksb, int s, bool live, int lane,
-                                             v8i& bv, float& sk) {
-    bv = live ? load_split32(kb + static_cast<size_t>(s) * 128, lane >> 4) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    sk = live ? ksb[s] : 0.0f;
+// This lane's operand bytes of key s (zeros when !live).
+__device__ __forceinline__ v8i load_fp8_key(const uint8_t* kb, int s, bool live, int lane) {
+    return live ? load_split32(kb + static_cast<size_t>(s) * 128, lane >> 4) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 }
 
-// Score of key (lane % 16) of the block whose operands are bv/sk; every lane
-// of the wave must call it (the MFMA and the lane exchanges are wave-wide).
-__device__ __forceinline__ float fp8_block_score(const Fp8Query& q, const v8i& bv, float sk) {
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a, bv, acc, 0, 0, 0, 127, 0, 127);
-    float part = q.w[0] * fmaxf(acc[0], 0.0f);
-    part = fmaf(q.w[1], fmaxf(acc[1], 0.0f), part);
-    part = fmaf(q.w[2], fmaxf(acc[2], 0.0f), part);
-    part = fmaf(q.w[3], fmaxf(acc[3], 0.0f), part);
-    part = wave_sum_xor_16_32(part);
-    return part * (q.sq * sk);
+// Scores of four blocks of 16 keys.  bv[u] holds this lane's operand of key
+// (lane % 16) of block u; the result in lane l is the score of key (l % 16) of
+// block l / 16, and sk must be that key's scale.  Every lane of the wave must
+// call it (the MFMAs and lane exchanges are wave-wide).
+__device__ __forceinline__ float fp8_score4(const Fp8Query& q, const v8i* bv, float sk) {
+    float p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a, bv[u], acc, 0, 0, 0, 127, 0, 127);
+        float part = q.w[0] * fmaxf(acc[0], 0.0f);
+        part = fmaf(q.w[1], fmaxf(acc[1], 0.0f), part);
+        part = fmaf(q.w[2], fmaxf(acc[2], 0.0f), part);
+        p[u] = fmaf(q.w[3], fmaxf(acc[3], 0.0f), part);
+    }
+    return reduce_scatter4(p[0], p[1], p[2], p[3]) * (q.sq * sk);
 }
 
 // (order key << 32 | ~position): larger means higher score, then lower position.

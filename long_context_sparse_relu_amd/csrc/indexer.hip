@@ -101,8 +101,14 @@ __global__ __launch_bounds__(256) void k_index_generic(
 #define DSA_IDX_INTERLEAVE 0 // 1: the workgroups of a row take interleaved chunks of it
 #endif
 
+#ifndef DSA_IDX_OCC
+#define DSA_IDX_OCC 8        // waves per SIMD the register budget must allow
+#endif
+
 template <int U, bool PREFETCH, bool CAND>
-__global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
+__global__ __launch_bounds__(DSA_IDX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(DSA_IDX_OCC)))
+void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
+    static_assert(U % 4 == 0, "keys are scored 64 at a time");
     __shared__ uint32_t lh[CAND ? 1 : kTopkBins];
     __shared__ uint64_t cbuf[CAND ? kIdxCandBuf : 1];
     __shared__ uint32_t n_c, g_c;
@@ -146,19 +152,25 @@ __global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs
 #endif
     const uint64_t below = (1ull << lane) - 1ull;
 
+    // a batch is U/4 groups of 64 keys; lane l scores key base + 64g + l of group g
     auto load_batch = [&](int base, v8i* bv, float* sk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int s = base + u * 16 + col;
-            load_fp8_key(kb, ksb, s, s < s_end && s <= pos, lane, bv[u], sk[u]);
+            const int s = base + u * 16 + col;
+            bv[u] = load_fp8_key(kb, s, s < s_end && s <= pos, lane);
+        }
+#pragma unroll
+        for (int g = 0; g < U / 4; ++g) {
+            const int s = base + g * 64 + lane;
+            sk[g] = s < s_end && s <= pos ? ksb[s] : 0.0f;
         }
     };
     auto score_batch = [&](int base, const v8i* bv, const float* sk) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float part = fp8_block_score(q, bv[u], sk[u]);
-            const int s = base + u * 16 + col;
-            const bool mine = kg == 0 && s < s_end;
+        for (int g = 0; g < U / 4; ++g) {
+            const float part = fp8_score4(q, bv + 4 * g, sk[g]);
+            const int s = base + g * 64 + lane;
+            const bool mine = s < s_end;
             if constexpr (CAND) {
                 const uint32_t key = order_key(part);
                 const bool take = mine && collect && s <= pos && key >= k_low;
@@ -181,20 +193,22 @@ __global__ __launch_bounds__(DSA_IDX_WAVES * 64) void k_index_fp8_mfma(IndexArgs
     int base = s_begin + wave * 16 * U;
     if constexpr (PREFETCH) {
         v8i bv[U];
-        float sk[U];
+        float sk[U / 4];
         if (base < s_end) load_batch(base, bv, sk);
         for (; base < s_end; base += step) {
             v8i bn[U];
-            float skn[U];
+            float skn[U / 4];
             if (base + step < s_end) load_batch(base + step, bn, skn);
             score_batch(base, bv, sk);
 #pragma unroll
-            for (int u = 0; u < U; ++u) { bv[u] = bn[u]; sk[u] = skn[u]; }
+            for (int u = 0; u < U; ++u) bv[u] = bn[u];
+#pragma unroll
+            for (int g = 0; g < U / 4; ++g) sk[g] = skn[g];
         }
     } else {
         for (; base < s_end; base += step) {
             v8i bv[U];
-            float sk[U];
+            float sk[U / 4];
             load_batch(base, bv, sk);
             score_batch(base, bv, sk);
         }

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_topk_sample_score(SampledTopk t) {
     const int vis = pos + 1;
     if (vis <= x.k) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, kg = lane >> 4;
+    const int col = lane & 15;
     const int m = vis < kSampleKeys ? vis : kSampleKeys;
     const int gap = vis / ((m + 15) / 16);   // >= 16 unless m == vis
     const int per = kSampleKeys / kSampleSplit;                 // samples per workgroup
@@ -71,20 +71,18 @@ __global__ __launch_bounds__(256) void k_topk_sample_score(SampledTopk t) {
     const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
     const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
     uint32_t* skey = t.samples + static_cast<size_t>(lrow) * kSampleKeys;
-    constexpr int U = kSampleKeys / kSampleSplit / 64;            // blocks of 16 per wave
-    v8i bv[U];
-    float sk[U];
+    static_assert(kSampleKeys / kSampleSplit == 4 * 64, "one group of 64 samples per wave");
+    // block u of this wave holds samples j0 + 64*wave + 16u + (0..15); lane l scores sample j0 + 64*wave + l
+    v8i bv[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int j = j0 + (wave * U + u) * 16 + col;
-        load_fp8_key(kb, ksb, j < m ? sample_key(j, m, vis, gap) : 0, j < m, lane, bv[u], sk[u]);
+    for (int u = 0; u < 4; ++u) {
+        const int j = j0 + wave * 64 + u * 16 + col;
+        bv[u] = load_fp8_key(kb, j < m ? sample_key(j, m, vis, gap) : 0, j < m, lane);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int j = j0 + (wave * U + u) * 16 + col;
-        const float score = fp8_block_score(q, bv[u], sk[u]);
-        if (kg == 0 && j < m) skey[j] = order_key(score);
-    }
+    const int j = j0 + wave * 64 + lane;
+    const float sk = j < m ? ksb[sample_key(j, m, vis, gap)] : 0.0f;
+    const float score = fp8_score4(q, bv, sk);
+    if (j < m) skey[j] = order_key(score);
 }
 
 // Lower bound of each row's r-th largest sample score; clears the row's
@@ -173,27 +171,22 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
         // recompute this row's scores in full, then select from all of them
         if (threadIdx.x == 0) meta[S_FALLBACK] = 1u;
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-        const int col = lane & 15, kg = lane >> 4;
+        const int col = lane & 15;
         const int b = row / x.n_q;
         const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
         const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
         const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
         float* sc = t.scratch + static_cast<size_t>(lrow) * x.n_k;
-        constexpr int U = 4;
-        for (int base = wave * 16 * U; base < vis; base += nwaves * 16 * U) {   // uniform per wave
-            v8i bv[U];
-            float sk[U];
+        for (int base = wave * 64; base < vis; base += nwaves * 64) {   // uniform per wave
+            v8i bv[4];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 const int s = base + u * 16 + col;
-                load_fp8_key(kb, ksb, s, s < vis, lane, bv[u], sk[u]);
+                bv[u] = load_fp8_key(kb, s, s < vis, lane);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int s = base + u * 16 + col;
-                const float score = fp8_block_score(q, bv[u], sk[u]);
-                if (kg == 0 && s < vis) sc[s] = score;
-            }
+            const int s = base + lane;
+            const float score = fp8_score4(q, bv, s < vis ? ksb[s] : 0.0f);
+            if (s < vis) sc[s] = score;
         }
         __threadfence_block();
         __syncthreads();

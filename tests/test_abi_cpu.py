@@ -142,3 +142,16 @@ def test_binding_rejects_missing_library(tmp_path):
             dsa.load_library(str(tmp_path / "nope.so"))
     finally:
         dsa._lib = saved
+
+
+def test_phase_timer_without_a_timed_call(lib):
+    """The timer's host side: nothing timed yet (or timing switched off) is an
+    error, as is a NULL output; switching it on and off always succeeds."""
+    assert lib.dsa_phase_timing(0) == dsa.OK
+    assert lib.dsa_phase_times(None) == dsa.E_INVALID
+    buf = (ctypes.c_float * len(dsa.PHASES))()
+    assert lib.dsa_phase_times(buf) == dsa.E_INVALID
+    assert "no timed" in dsa.last_error()
+    assert lib.dsa_phase_timing(1) == dsa.OK
+    assert lib.dsa_phase_times(buf) == dsa.E_INVALID
+    assert lib.dsa_phase_timing(0) == dsa.OK

@@ -283,6 +283,30 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == dsa.E_WORKSPACE
 
 
+def test_phase_timer_records_each_phase():
+    """The opt-in phase timer: a sampled decode runs all four phases, the
+    timed call's results equal an untimed call's, and switching it off stops
+    the recording."""
+    sp = custom_spec(name="timer", B=4, n_q=1, n_k=40000, idx_heads=16, idx_dtype="e4m3", top_k=512,
+                     q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=3)
+    prob = _problem(inp)
+    i0 = torch.empty((4, 1, 512), dtype=torch.int32, device=DEV)
+    i1 = torch.empty_like(i0)
+    o0, l0, _ = dsa.decode(prob, idx_out=i0)
+    dsa.phase_timing(True)
+    try:
+        o1, l1, _ = dsa.decode(prob, idx_out=i1)
+        t = dsa.phase_times()
+    finally:
+        dsa.phase_timing(False)
+    assert set(t) == set(dsa.PHASES)
+    assert all(v > 0 for v in t.values()), t
+    assert torch.equal(i0, i1) and torch.equal(o0, o1) and torch.equal(l0, l1)
+    with pytest.raises(dsa.DSAError):
+        dsa.phase_times()
+
+
 def test_tiny_prefill_f32_full():
     inp = make_inputs(spec("tiny_prefill_f32"), device=DEV, seed=0)
     stats, idx, _ = run_case(inp, [0], list(range(512)))
