@@ -171,7 +171,7 @@ constexpr int kGqaWaves = DSA_ATTN_WAVES;
 constexpr int kGqaVStride = 136;   // bf16 elements per staged value row (128 + pad)
 
 template <int DEPTH>
-__global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
+__global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, int slice_len, float* part) {
     __shared__ __align__(16) unsigned char smem[kGqaWaves * 16 * 128 * 4];   // 64 KiB
     __shared__ float m_w[kGqaWaves][16], l_w[kGqaWaves][16];
     extern __shared__ int32_t idx_s[];                                        // [kk]
@@ -182,6 +182,10 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     const int G = a.Hq / a.Hkv;
     const int g = blockIdx.x;
     const int row = blockIdx.y;
+    const int nsplit = gridDim.z;
+    const int sl = blockIdx.z;                     // this workgroup's slice of the index list
+    const int jb = sl * slice_len;
+    const int nj = max(0, min(slice_len, a.kk - jb));
     const int b = row / a.n_q;
     const int pos = row_pos(a.q_pos, row, a.n_q, a.n_k);
     const int lane = threadIdx.x & 63;
@@ -191,8 +195,8 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
     const float zscale = a.scale * kLog2e;
     uint16_t* v_s = v_all + wave * 16 * kGqaVStride;
 
-    const int32_t* idx_row = a.idx + static_cast<size_t>(row) * a.kk;
-    for (int j = threadIdx.x; j < a.kk; j += blockDim.x) idx_s[j] = idx_row[j];
+    const int32_t* idx_row = a.idx + static_cast<size_t>(row) * a.kk + jb;
+    for (int j = threadIdx.x; j < nj; j += blockDim.x) idx_s[j] = idx_row[j];
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
@@ -206,9 +210,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
             qb[c] = v8bf{};
     }
 
-    const int per = ((a.kk + kGqaWaves * 16 - 1) / (kGqaWaves * 16)) * 16;
+    const int per = ((nj + kGqaWaves * 16 - 1) / (kGqaWaves * 16)) * 16;
     const int j_begin = wave * per;
-    const int j_end = min(j_begin + per, a.kk);
+    const int j_end = min(j_begin + per, nj);
     const int nblk = j_end > j_begin ? (j_end - j_begin + 15) / 16 : 0;
     const size_t row_elems = static_cast<size_t>(a.Hkv) * 128;
     const uint16_t* kbase = kp + static_cast<size_t>(b) * a.n_k * row_elems + g * 128 + kg * 32;
@@ -328,11 +332,17 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a) {
                 O += o_all[(w * 16 + h) * 128 + d] * f;
             }
         }
+        const size_t rh = static_cast<size_t>(row) * a.Hq + g * G + h;
+        if (nsplit > 1) {
+            // this slice's (max, sum, unnormalised O) record for k_attn_merge
+            float* rec = part + (rh * nsplit + sl) * (128 + 2);
+            rec[2 + d] = O;
+            if (d == 0) { rec[0] = M; rec[1] = L; }
+            continue;
+        }
         float val = L > 0.0f ? O / L : 0.0f;
-        size_t oi = (static_cast<size_t>(row) * a.Hq + g * G + h) * 128 + d;
-        outp[oi] = f32_to_bf16_bits(val);
-        if (d == 0 && a.lse)
-            a.lse[static_cast<size_t>(row) * a.Hq + g * G + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
+        outp[rh * 128 + d] = f32_to_bf16_bits(val);
+        if (d == 0 && a.lse) a.lse[rh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
     }
 }
 
@@ -340,9 +350,30 @@ static bool gqa_d128_eligible(const AttnArgs& a) {
     return a.dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128 && a.Hq / a.Hkv <= 16;
 }
 
+#ifndef DSA_ATTN_TARGET_WGS
+#define DSA_ATTN_TARGET_WGS 256
+#endif
+// Slices of each row's index list.  A workgroup's gather rate is bounded by
+// its compute unit, so with fewer (row, kv head) pairs than compute units the
+// list is split (at least 256 entries per slice) to reach them all, and the
+// slices' (max, sum, O) records are merged afterwards.  With one workgroup
+// per compute unit already, splitting measured slower.
+static int gqa_splits(const AttnArgs& a) {
+    const int64_t wgs = static_cast<int64_t>(a.rows) * a.Hkv;
+    int s = static_cast<int>((DSA_ATTN_TARGET_WGS + wgs - 1) / wgs);
+    const int max_s = a.kk / 256;
+    if (s > max_s) s = max_s;
+    return s < 1 ? 1 : s;
+}
+static int gqa_slice_len(const AttnArgs& a, int s) { return ((a.kk + s - 1) / s + 15) / 16 * 16; }
+
 size_t attn_workspace_bytes(const AttnArgs& a) {
     if (attn_masked_eligible(a)) return attn_masked_workspace_bytes(a);
-    if (gqa_d128_eligible(a) || !attn_wide_eligible(a)) return 0;
+    if (gqa_d128_eligible(a)) {
+        const int s = gqa_splits(a);
+        return s > 1 ? static_cast<size_t>(a.rows) * a.Hq * s * (128 + 2) * sizeof(float) : 0;
+    }
+    if (!attn_wide_eligible(a)) return 0;
     return attn_wide_workspace_bytes(a);
 }
 
@@ -350,10 +381,15 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
     if (attn_masked_eligible(a)) return launch_attn_masked(a, static_cast<uint32_t*>(ws), st);
     if (gqa_d128_eligible(a)) {
-        const size_t idx_lds = static_cast<size_t>(a.kk) * sizeof(int32_t);   // kk <= 8192: 32 KiB
-        hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH>), dim3(a.Hkv, a.rows), dim3(kGqaWaves * 64),
-                           idx_lds, st, a);
-        return hipGetLastError();
+        const int s = gqa_splits(a);
+        const int len = gqa_slice_len(a, s);
+        float* part = static_cast<float*>(ws);
+        const size_t idx_lds = static_cast<size_t>(len) * sizeof(int32_t);   // <= 8192 entries: 32 KiB
+        hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH>), dim3(a.Hkv, a.rows, s), dim3(kGqaWaves * 64),
+                           idx_lds, st, a, len, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || s == 1) return e;
+        return launch_attn_merge(a, s, part, st);
     }
     if (attn_wide_eligible(a)) return launch_attn_wide(a, static_cast<float*>(ws), st);
     const size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +

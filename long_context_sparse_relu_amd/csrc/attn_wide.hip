@@ -207,6 +207,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int nsplit, cons
     if (threadIdx.x == 0 && a.lse) a.lse[rh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
 }
 
+hipError_t launch_attn_merge(const AttnArgs& a, int nsplit, const float* part, hipStream_t st) {
+    hipLaunchKernelGGL(k_attn_merge, dim3(a.rows * a.Hq), dim3(256), 0, st, a, nsplit, part);
+    return hipGetLastError();
+}
+
 // Shapes with an instantiated kernel.
 static bool wide_shape(int dqk, int dv) {
     return (dqk == 576 && dv == 512) || (dqk == 128 && dv == 128) || (dqk == 64 && dv == 64);

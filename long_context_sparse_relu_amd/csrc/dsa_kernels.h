@@ -118,5 +118,8 @@ hipError_t launch_attn_masked(const AttnArgs& a, uint32_t* bitmap, hipStream_t s
 bool attn_wide_eligible(const AttnArgs& a);
 size_t attn_wide_workspace_bytes(const AttnArgs& a);
 hipError_t launch_attn_wide(const AttnArgs& a, float* part, hipStream_t st);
+// Combine per-slice records part[(row*Hq + head)*nsplit + slice] = (max (base 2),
+// sum, unnormalised O[dv]) into out and lse (bf16 out).
+hipError_t launch_attn_merge(const AttnArgs& a, int nsplit, const float* part, hipStream_t st);
 
 }  // namespace dsa

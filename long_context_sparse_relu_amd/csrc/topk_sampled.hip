@@ -33,10 +33,14 @@ bool topk_sampled_eligible(int n_k, int k) {
 }
 
 
-struct Cand64List {
-    const uint64_t* c; int n;
+// Candidates relative to the row's bound: every candidate has key >= k_low,
+// so subtracting (k_low << 32) keeps the order and leaves small keys whose
+// top digit spreads the candidates over the histogram instead of piling them
+// into the one or two bins just above the bound.
+struct Cand64Rel {
+    const uint64_t* c; int n; uint64_t base;
     __device__ int size() const { return n; }
-    __device__ bool get(int i, uint64_t* out) const { *out = c[i]; return true; }
+    __device__ bool get(int i, uint64_t* out) const { *out = c[i] - base; return true; }
 };
 struct ScoreRow64 {
     const float* sc; int n;
@@ -160,13 +164,53 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
     const int shifts64[6] = {53, 42, 32, 21, 10, 0};
     const int widths64[6] = {11, 11, 10, 11, 11, 10};
     uint32_t* meta = x.meta + static_cast<size_t>(lrow) * kTopkMeta;
+    // the first kSpecLoads*blockDim.x list entries are fetched together with the
+    // counters, before the list's length is known (entries past it are ignored;
+    // they lie inside the row's list, whose capacity is larger)
+    constexpr int kSpecLoads = 8;
+    static_assert(kSpecLoads * kSFinishThreads <= kSampledCandCap, "speculative reads stay inside the list");
+    const uint64_t* cg = x.cand + static_cast<size_t>(lrow) * x.cand_cap;
+    uint64_t spec[kSpecLoads];
+#pragma unroll
+    for (int u = 0; u < kSpecLoads; ++u) spec[u] = cg[threadIdx.x + u * kSFinishThreads];
     const uint32_t n = meta[S_NCAND];
+    const uint32_t k_low = meta[S_KLOW];
     const bool ok = meta[S_OVF] == 0u && n >= static_cast<uint32_t>(k) && n <= static_cast<uint32_t>(x.cand_cap);
     if (ok) {
-        copy_to_lds(cl, x.cand + static_cast<size_t>(lrow) * x.cand_cap, static_cast<int>(n));
+        uint32_t kmax = 0u;
+#pragma unroll
+        for (int u = 0; u < kSpecLoads; ++u) {
+            const uint32_t i = threadIdx.x + u * kSFinishThreads;
+            if (i < n) { cl[i] = spec[u]; kmax = max(kmax, static_cast<uint32_t>(spec[u] >> 32)); }
+        }
+        for (uint32_t i = threadIdx.x + kSpecLoads * kSFinishThreads; i < n; i += kSFinishThreads) {
+            const uint64_t c = cg[i];
+            cl[i] = c;
+            kmax = max(kmax, static_cast<uint32_t>(c >> 32));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+        if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = kmax;
         __syncthreads();
-        Cand64List src{cl, static_cast<int>(n)};
-        radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
+        for (int w = 0; w < kSFinishThreads / 64; ++w) kmax = max(kmax, wsum[w]);
+        __syncthreads();                       // wsum is reused by the select
+        // digits of the relative composite ((key - k_low) << 32 | ~position):
+        // the first covers the top 11 bits of the candidates' key range, the
+        // rest the remaining bits 11 at a time
+        const uint32_t range = kmax - k_low;
+        const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
+        const int sh = bits > 11 ? bits - 11 : 0;
+        int shifts[6], widths[6], np = 1;
+        shifts[0] = 32 + sh;
+        widths[0] = 11;
+        for (int below = 32 + sh; below > 0 && np < 6; ++np) {
+            const int w = below < 11 ? below : 11;
+            below -= w;
+            shifts[np] = below;
+            widths[np] = w;
+        }
+        Cand64Rel src{cl, static_cast<int>(n), static_cast<uint64_t>(k_low) << 32};
+        radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
     } else {
         // recompute this row's scores in full, then select from all of them
         if (threadIdx.x == 0) meta[S_FALLBACK] = 1u;
