@@ -17,6 +17,9 @@ Prints ONE JSON line (rank 0):
                 per launch / its mean duration inside the fused step, from the
                 library's phase timer (HIP events on the step's stream)
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+  attn_roofline the attention phase of the step: gathered K/V bytes against HBM
+                bandwidth (decode), or the sparse flops against the bf16 peak
+                (prefill)
   fused_phases_us  mean time of each phase of the fused step
   phases_us     mean time of each unfused entry point (indexer, top-k, attention)
 """
@@ -192,6 +195,11 @@ def main(argv=None):
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                 "traffic": _traffic(f"k_index_fp8_mfma@{args.workload}"),
                 "algorithmic_bytes": idx_bytes, "mean_us": idx_us_fused}
+        # the gather attention against HBM bandwidth: selected K/V bytes / its fused-phase time
+        attn_roof = {"bound": "hbm", "kernel": "sparse gather attention", "achieved":
+                     gather_bytes / (fused_us["attn"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "algorithmic_bytes": gather_bytes, "mean_us": fused_us["attn"]}
+        attn_roof["frac"] = attn_roof["achieved"] / HBM_PEAK_GBS
         total_bytes = idx_bytes + gather_bytes
         step_roof = {"algorithmic_bytes": total_bytes,
                      "achieved_GBs": total_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -205,6 +213,10 @@ def main(argv=None):
         roof = {"bound": "mfma" if s["idx_dtype"] != "f32" else "alu", "kernel": kern, "achieved": achieved,
                 "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                 "algorithmic_flops": idx_flops, "mean_us": idx_us_fused}
+        attn_roof = {"bound": "mfma", "kernel": "sparse attention", "achieved":
+                     attn_flops / (fused_us["attn"] * 1e-6) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
+                     "algorithmic_flops": attn_flops, "mean_us": fused_us["attn"]}
+        attn_roof["frac"] = attn_roof["achieved"] / 2500.0
         step_roof = {"indexer_flops": idx_flops, "attention_flops": attn_flops,
                      "ideal_us_at_peaks": idx_flops / (peak * 1e6) + attn_flops / (2500.0 * 1e6)}
     res = {
@@ -225,6 +237,7 @@ def main(argv=None):
                    "q_heads": s["q_heads"], "kv_heads": s["kv_heads"], "d_qk": s["d_qk"],
                    "d_v": s["d_v"], "latent": s["latent"], "attn_dtype": s["attn_dtype"]},
         "roofline": roof,
+        "attn_roofline": attn_roof,
         "step_roofline": step_roof,
         "fused_phases_us": fused_us,
         "phases_us": {"index_scores": idx_us, "topk": topk_us, "sparse_attn": attn_us,

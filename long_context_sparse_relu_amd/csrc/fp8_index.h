@@ -34,18 +34,24 @@ struct Fp8Query {
     float sq;     // the row's scale
 };
 
+// Every load is issued unconditionally (heads past H read head H-1 and are
+// zeroed afterwards), so no branch separates the loads and one wait covers
+// them together with whatever the caller loads next to them.
 __device__ __forceinline__ Fp8Query load_fp8_query(const uint8_t* iq, const float* iq_scale, const float* iw,
                                                    int row, int H, int lane) {
     Fp8Query q;
     const int col = lane & 15, kg = lane >> 4;
-    q.a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    if (col < H) q.a = load_split32(iq + (static_cast<size_t>(row) * H + col) * 128, kg);
+    const v8i a = load_split32(iq + (static_cast<size_t>(row) * H + (col < H ? col : H - 1)) * 128, kg);
+    float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int h = 4 * kg + i;
-        q.w[i] = h < H ? iw[static_cast<size_t>(row) * H + h] : 0.0f;
+        const int h = 4 * kg + i;
+        w[i] = iw[static_cast<size_t>(row) * H + (h < H ? h : H - 1)];
     }
     q.sq = iq_scale[row];
+    q.a = col < H ? a : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q.w[i] = 4 * kg + i < H ? w[i] : 0.0f;
     return q;
 }
 

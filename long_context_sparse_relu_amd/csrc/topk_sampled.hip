@@ -64,27 +64,30 @@ __global__ __launch_bounds__(256) void k_topk_sample_score(SampledTopk t) {
     const int vis = pos + 1;
     if (vis <= x.k) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15;
+    const int col = lane & 15, kg = lane >> 4;
     const int m = vis < kSampleKeys ? vis : kSampleKeys;
     const int gap = vis / ((m + 15) / 16);   // >= 16 unless m == vis
     const int per = kSampleKeys / kSampleSplit;                 // samples per workgroup
     const int j0 = blockIdx.x * per;
     if (j0 >= m) return;
     const int b = row / x.n_q;
-    const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
     const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
     const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
     uint32_t* skey = t.samples + static_cast<size_t>(lrow) * kSampleKeys;
     static_assert(kSampleKeys / kSampleSplit == 4 * 64, "one group of 64 samples per wave");
-    // block u of this wave holds samples j0 + 64*wave + 16u + (0..15); lane l scores sample j0 + 64*wave + l
+    // block u of this wave holds samples j0 + 64*wave + 16u + (0..15); lane l
+    // scores sample j0 + 64*wave + l.  All loads go out before any wait:
+    // samples past m read sample m-1 and are not stored.
     v8i bv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int j = j0 + wave * 64 + u * 16 + col;
-        bv[u] = load_fp8_key(kb, j < m ? sample_key(j, m, vis, gap) : 0, j < m, lane);
+        const int j = min(j0 + wave * 64 + u * 16 + col, m - 1);
+        bv[u] = load_split32(kb + static_cast<size_t>(sample_key(j, m, vis, gap)) * 128, kg);
     }
     const int j = j0 + wave * 64 + lane;
-    const float sk = j < m ? ksb[sample_key(j, m, vis, gap)] : 0.0f;
+    const float sk = ksb[sample_key(min(j, m - 1), m, vis, gap)];
+    const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
+    __builtin_amdgcn_sched_barrier(0);    // keep every load above the first wait
     const float score = fp8_score4(q, bv, sk);
     if (j < m) skey[j] = order_key(score);
 }
@@ -106,26 +109,59 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
         return;
     }
     const int m = vis < kSampleKeys ? vis : kSampleKeys;
-    copy_to_lds(skey, t.samples + static_cast<size_t>(lrow) * kSampleKeys, m);
+    const uint32_t* src = t.samples + static_cast<size_t>(lrow) * kSampleKeys;
+    // the whole sample buffer is read at once (entries past m are ignored)
+    static_assert(kSampleKeys % kSampleThreads == 0, "sample buffer splits evenly");
+    constexpr int kPer = kSampleKeys / kSampleThreads;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) v[u] = src[threadIdx.x + u * kSampleThreads];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int j = threadIdx.x + u * kSampleThreads;
+        if (j < m) { skey[j] = v[u]; kmin = min(kmin, v[u]); kmax = max(kmax, v[u]); }
+    }
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    }
+    __shared__ uint32_t wmin[kSampleThreads / 64], wmax[kSampleThreads / 64];
+    if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
     __syncthreads();
+    for (int w = 0; w < kSampleThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
     const int64_t want = (3 * static_cast<int64_t>(m) * x.k + 2 * static_cast<int64_t>(vis) - 1) /
                          (2 * static_cast<int64_t>(vis)) + 24;
     uint32_t k_low = 0u;                   // every visible key a candidate
     if (want < m) {
+        // two 11-bit digits of (key - kmin), the first over the top of the
+        // samples' range: the bound is the floor of the r-th largest sample
+        // at that resolution
         const uint32_t r = static_cast<uint32_t>(want);
-        for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[skey[j] >> 21], 1u);
+        const uint32_t range = kmax - kmin;
+        const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
+        const int sh1 = bits > 11 ? bits - 11 : 0;
+        for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[(skey[j] - kmin) >> sh1], 1u);
         __syncthreads();
         int d0; uint32_t gt0;
         find_threshold_bin(lh, kTopkBins, r, wsum, &d0, &gt0);
-        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-        __syncthreads();
-        for (int j = threadIdx.x; j < m; j += blockDim.x)
-            if (static_cast<int>(skey[j] >> 21) == d0) atomicAdd(&lh[(skey[j] >> 10) & 0x7FFu], 1u);
-        __syncthreads();
-        int d1; uint32_t gt1;
-        find_threshold_bin(lh, kTopkBins, r - gt0, wsum, &d1, &gt1);
-        k_low = (static_cast<uint32_t>(d0) << 21) | (static_cast<uint32_t>(d1) << 10);
+        k_low = kmin + (static_cast<uint32_t>(d0) << sh1);
+        if (sh1 > 0) {
+            const int sh2 = sh1 > 11 ? sh1 - 11 : 0;
+            const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
+            for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+            __syncthreads();
+            for (int j = threadIdx.x; j < m; j += blockDim.x) {
+                const uint32_t rel = skey[j] - kmin;
+                if (static_cast<int>(rel >> sh1) == d0) atomicAdd(&lh[(rel >> sh2) & mask2], 1u);
+            }
+            __syncthreads();
+            int d1; uint32_t gt1;
+            find_threshold_bin(lh, kTopkBins, r - gt0, wsum, &d1, &gt1);
+            k_low += static_cast<uint32_t>(d1) << sh2;
+        }
     }
     if (threadIdx.x == 0) meta[S_KLOW] = k_low;
 }
