@@ -58,6 +58,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ReLU as the signed-integer max of the bit pattern with 0: a negative float
+// (or -0.0) has the sign bit set and becomes +0.0, a positive one is kept.
+// One VALU op, where fmaxf on an MFMA result also pays a NaN-quieting max.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ int row_pos(const int32_t* q_pos, int row, int n_q, int n_k) {
     int t = row % n_q;
     int p = q_pos ? q_pos[row] : (n_k - n_q + t);

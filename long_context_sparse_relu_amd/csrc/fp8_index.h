@@ -70,10 +70,10 @@ __device__ __forceinline__ float fp8_score4(const Fp8Query& q, const v8i* bv, fl
     for (int u = 0; u < 4; ++u) {
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a, bv[u], acc, 0, 0, 0, 127, 0, 127);
-        float part = q.w[0] * fmaxf(acc[0], 0.0f);
-        part = fmaf(q.w[1], fmaxf(acc[1], 0.0f), part);
-        part = fmaf(q.w[2], fmaxf(acc[2], 0.0f), part);
-        p[u] = fmaf(q.w[3], fmaxf(acc[3], 0.0f), part);
+        float part = q.w[0] * relu(acc[0]);
+        part = fmaf(q.w[1], relu(acc[1]), part);
+        part = fmaf(q.w[2], relu(acc[2]), part);
+        p[u] = fmaf(q.w[3], relu(acc[3]), part);
     }
     return reduce_scatter4(p[0], p[1], p[2], p[3]) * (q.sq * sk);
 }

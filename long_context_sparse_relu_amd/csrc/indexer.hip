@@ -348,6 +348,10 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         fetch(c0);
         stage();
     }
+    // every prologue load (queries, weights, positions) has landed: otherwise
+    // the loop's first MFMA waits on all outstanding memory operations,
+    // including the previous tile's score stores, in every iteration
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int k0 = c0; k0 < cvis; k0 += kTileKeys) {
         const bool more = k0 + kTileKeys < cvis;
@@ -380,10 +384,10 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
                     for (int c = 0; c < NC; ++c)
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a16[q][c], b16[g16][c], acc, 0, 0, 0);
                 }
-                float part = w[q][0] * fmaxf(acc[0], 0.0f);
-                part = fmaf(w[q][1], fmaxf(acc[1], 0.0f), part);
-                part = fmaf(w[q][2], fmaxf(acc[2], 0.0f), part);
-                p[g16] = fmaf(w[q][3], fmaxf(acc[3], 0.0f), part);
+                float part = w[q][0] * relu(acc[0]);
+                part = fmaf(w[q][1], relu(acc[1]), part);
+                part = fmaf(w[q][2], relu(acc[2]), part);
+                p[g16] = fmaf(w[q][3], relu(acc[3]), part);
             }
             const float part = reduce_scatter4(p[0], p[1], p[2], p[3]);
             if (s < c1 && (livem >> q & 1u)) {
