@@ -247,10 +247,25 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
 // and tile).  Keys past a query's last visible key are written as -inf only
 // when `write_future` (the unfused entry point).
 // ---------------------------------------------------------------------------
-constexpr int kIdxChunk = 2048;   // keys per workgroup
-constexpr int kTileKeys = 64;     // keys per LDS tile
+#ifndef DSA_TILED_CHUNK
+#define DSA_TILED_CHUNK 4096
+#endif
+constexpr int kIdxChunk = DSA_TILED_CHUNK;   // keys per workgroup
+#ifndef DSA_TILED_TILE
+#define DSA_TILED_TILE 64
+#endif
+constexpr int kTileKeys = DSA_TILED_TILE;   // keys per LDS tile (a multiple of 64)
+static_assert(kTileKeys % 64 == 0, "tiles are scored 64 keys at a time");
 // query rows per wave and waves per workgroup (measured best: FP8 4 x 8, bf16 2 x 4)
-template <int DT> struct TiledShape { static constexpr int QPW = DT == E4M3 ? 4 : 2, TW = DT == E4M3 ? 8 : 4; };
+#ifndef DSA_TILED_F8_QPW
+#define DSA_TILED_F8_QPW 4
+#endif
+#ifndef DSA_TILED_F8_TW
+#define DSA_TILED_F8_TW 8
+#endif
+template <int DT> struct TiledShape {
+    static constexpr int QPW = DT == E4M3 ? DSA_TILED_F8_QPW : 2, TW = DT == E4M3 ? DSA_TILED_F8_TW : 4;
+};
 
 template <int DT>
 __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexArgs x, int t_first, int nrows,
@@ -356,12 +371,15 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
     for (int k0 = c0; k0 < cvis; k0 += kTileKeys) {
         const bool more = k0 + kTileKeys < cvis;
         if (more) fetch(k0 + kTileKeys);                     // in flight while this tile is scored
-        // key k0 + g16*16 + col sits in LDS row g16*16 + col; lane l scores key k0 + l
+#pragma unroll
+        for (int sub = 0; sub < kTileKeys / 64; ++sub) {
+        // key k0 + 64*sub + g16*16 + col sits in LDS row 64*sub + g16*16 + col;
+        // lane l scores key k0 + 64*sub + l
         v8i b8[4];
         v8bf b16[4][4];
 #pragma unroll
         for (int g16 = 0; g16 < 4; ++g16) {
-            const uint8_t* kr = k_s + (g16 * 16 + col) * KSTR;
+            const uint8_t* kr = k_s + (sub * 64 + g16 * 16 + col) * KSTR;
             if constexpr (DT == E4M3) {
                 b8[g16] = load_split32(kr, kg);
             } else {
@@ -369,8 +387,8 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
                 for (int c = 0; c < 4; ++c) b16[g16][c] = *reinterpret_cast<const v8bf*>(kr + kg * 64 + c * 16);
             }
         }
-        const int s = k0 + lane;
-        const float sk = DT == E4M3 ? ks_s[lane] : 1.0f;
+        const int s = k0 + sub * 64 + lane;
+        const float sk = DT == E4M3 ? ks_s[sub * 64 + lane] : 1.0f;
 #pragma unroll
         for (int q = 0; q < kQPW; ++q) {
             float p[4];
@@ -395,6 +413,7 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
                 if (s <= pos[q]) out[s] = DT == E4M3 ? part * (sq[q] * sk) : part;
                 else if (write_future) out[s] = -__builtin_inff();
             }
+        }
         }
         if (more) {
             __syncthreads();                                 // every wave is done with this tile
