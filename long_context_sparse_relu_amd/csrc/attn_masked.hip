@@ -10,15 +10,15 @@
 // cheaper as a tile), so prefill rows take this path:
 //   bitmap  one workgroup per query row turns its index list into a bit row
 //           over the keys (bit s set <=> s kept);
-//   attend  one workgroup per (block of 64 queries, query head), 4 waves of
-//           16 queries each, walks the key tiles of 64 up to the block's
-//           last visible key.  Per tile: S^T = K Q^T on
-//           v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T in registers), the
-//           query's bits mask S, online softmax per lane (query l%16) in fp32,
-//           then O^T += V^T P^T, also on v_mfma_f32_16x16x32_bf16, with V^T
-//           read from the row-major V tile by transposing LDS reads.  Tiles
-//           where none of a wave's queries keep a key are skipped by that
-//           wave.
+//   attend  one workgroup per (block of 128 queries, query head), 4 waves of
+//           32 queries each, walks the key tiles of 64 up to the block's
+//           last visible key.  Per tile and wave: S^T = K Q^T on
+//           v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T in registers), the
+//           query's bits mask S, online softmax per lane (query l%32, half
+//           of the tile's keys; the other half sits in lane l^32) in fp32,
+//           then O^T += V^T P^T, also on v_mfma_f32_32x32x16_bf16, with V^T
+//           read from the row-major V tile by transposing LDS reads.  A wave
+//           skips a tile none of its queries keeps a key of.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -27,9 +27,10 @@ namespace dsa {
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kQB = 64;            // queries per workgroup
+constexpr int kQB = 128;           // queries per workgroup (32 per wave)
 constexpr int kKB = 64;            // keys per tile
 constexpr int kStr = 136;          // LDS row stride (bf16) of the K and V tiles
+constexpr int kMinQ = 64;          // fewest query rows this path takes
 constexpr int kMaskedMaxKeys = 1 << 18;
 }
 
@@ -52,19 +53,26 @@ __global__ __launch_bounds__(256) void k_sel_bitmap(AttnArgs a, uint32_t* bm, in
     for (int i = threadIdx.x; i < words; i += blockDim.x) out[i] = lb[i];
 }
 
-// P.V runs on v_mfma_f32_16x16x32_bf16 over 32 keys.  Lane l supplies the
-// eight keys {32m + 4(l/16) + i, 32m + 16 + 4(l/16) + i : i < 4} -- the four
-// S^T values it already holds from each of the two 16-key tiles -- and the V^T
-// operand takes the same eight keys from the row-major V tile with two
-// ds_read_b64_tr_b16: within each 16-lane group, lane i of that instruction
-// receives element i%4 of the 8-byte chunks addressed by lanes i/4, 4+i/4,
-// 8+i/4 and 12+i/4, so lane j addresses key (j/4) of the quadruple and dims
-// 4(j%4)..4(j%4)+3 of the 16-dim slice.  The next tile's rows are fetched into
-// registers while the current one is multiplied.
-typedef short v4s_t __attribute__((ext_vector_type(4)));
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, D 32x32):
+// lane l holds A[l%32][8(l/32)+j] and B[8(l/32)+j][l%32] for j < 8, and
+// D[8(r/4) + 4(l/32) + r%4][l%32] in result register r < 16.
+//
+// S^T (keys x queries) leaves lane l with query l%32 and, of each 32-key
+// half of the tile, keys 8(r/4) + 4(l/32) + r%4.  In P.V the 16 keys of a
+// chunk are taken in the order kappa = 8h + j <-> key 4h + j (j < 4) and
+// 8 + 4h + (j - 4) (j >= 4), h = l/32, so the eight P values a lane already
+// holds for a chunk are its B operand as they are.  The V^T operand (rows =
+// 32 dims, columns = the same 16 kappa) comes from the row-major V tile with
+// two ds_read_b64_tr_b16: within each 16-lane group, lane i of that
+// instruction receives element i%4 of the 8-byte chunks addressed by lanes
+// i/4, 4+i/4, 8+i/4 and 12+i/4, so lane a of the group addresses key
+// (a/4) of the four and dims 4(a%4)..4(a%4)+3 of the group's 16 dims, and
+// every lane ends with its own dim over the four keys.  The next tile's rows
+// are fetched into registers while the current one is multiplied.
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short lds_s4_t;
 typedef __attribute__((address_space(3))) lds_s4_t* lds_s4_ptr;
 typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr;
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
     lds_s4_ptr lp = (lds_s4_ptr)((lds_u16_ptr)(const_cast<uint16_t*>(p)));
@@ -74,7 +82,7 @@ __device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
     return r;
 }
 
-__global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
     __shared__ __align__(16) uint16_t k_s[kKB * kStr];
     __shared__ __align__(16) uint16_t v_s[kKB * kStr];
     __shared__ int last_s[4];
@@ -86,10 +94,11 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
     const int G = a.Hq / a.Hkv;
     const int g = h / G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, kg = lane >> 4;
+    const int qc = lane & 31;                   // this lane's query (S^T column)
+    const int hh = lane >> 5;                   // which half of each 32-key block it holds
     const float zscale = a.scale * kLog2e;
 
-    const int t = qb * kQB + wave * 16 + col;   // this lane's query (S^T column)
+    const int t = qb * kQB + wave * 32 + qc;
     const bool live_q = t < a.n_q;
     const int row = b * a.n_q + (live_q ? t : 0);
     const int pos = live_q ? row_pos(a.q_pos, row, a.n_q, a.n_k) : -1;
@@ -100,12 +109,14 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
     for (int o = 1; o < 64; o <<= 1) mp = max(mp, __shfl_xor(mp, o));
     if (lane == 0) last_s[wave] = mp;
 
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-    v8bf qb4[4];
+    // Q^T operand of every 16-dim chunk: query qc, dims 16c + 8hh .. +7
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(row) * a.Hq + h) * 128 + 8 * hh;
+    v8bf qv[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-        qb4[c] = live_q ? *reinterpret_cast<const v8bf*>(qp + (static_cast<size_t>(row) * a.Hq + h) * 128 + kg * 32 + c * 8)
-                        : v8bf{};
+    for (int c = 0; c < 8; ++c) {
+        const v8bf x = *reinterpret_cast<const v8bf*>(qp + 16 * c);
+        qv[c] = live_q ? x : v8bf{};
+    }
     __syncthreads();
     const int last = max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3]));
     const int ntiles = last < 0 ? 0 : last / kKB + 1;
@@ -117,102 +128,110 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
     const uint16_t* vbase = vp + static_cast<size_t>(b) * a.n_k * rstride + g * 128;
     const uint32_t* brow = bm + static_cast<size_t>(row) * words;
 
-    float m_run = -__builtin_inff();
-    float l_part = 0.0f;
-    v4f o[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // loader: 256 threads x 4 rows x 16 B of K and of V per tile
+    // loader: 256 threads x 4 rows x 16 B of K and of V per tile; rows past
+    // n_k read row n_k-1 and are zeroed when staged
     const int lrow = threadIdx.x >> 4;          // 0..15, plus 16 per step
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
     v8bf pk[4], pv[4];
     uint32_t pw0 = 0u, pw1 = 0u;
+    int pkey0 = 0;
     auto fetch = [&](int tile) {
-        const int key0 = tile * kKB;
+        pkey0 = tile * kKB;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int key = key0 + lrow + 16 * r;
-            if (key < a.n_k) {
-                pk[r] = *reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(key) * rstride + lcol);
-                pv[r] = *reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(key) * rstride + lcol);
-            } else {
-                pk[r] = v8bf{};
-                pv[r] = v8bf{};
-            }
+            const size_t key = static_cast<size_t>(min(pkey0 + lrow + 16 * r, a.n_k - 1));
+            pk[r] = *reinterpret_cast<const v8bf*>(kbase + key * rstride + lcol);
+            pv[r] = *reinterpret_cast<const v8bf*>(vbase + key * rstride + lcol);
         }
-        pw0 = live_q ? brow[2 * tile] : 0u;
-        pw1 = live_q ? brow[2 * tile + 1] : 0u;
+        const uint32_t x0 = brow[2 * tile], x1 = brow[2 * tile + 1];
+        pw0 = live_q ? x0 : 0u;
+        pw1 = live_q ? x1 : 0u;
     };
     auto stage = [&]() {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int kr = lrow + 16 * r;
-            *reinterpret_cast<v8bf*>(&k_s[kr * kStr + lcol]) = pk[r];
-            *reinterpret_cast<v8bf*>(&v_s[kr * kStr + lcol]) = pv[r];
+            const bool in = pkey0 + kr < a.n_k;
+            *reinterpret_cast<v8bf*>(&k_s[kr * kStr + lcol]) = in ? pk[r] : v8bf{};
+            *reinterpret_cast<v8bf*>(&v_s[kr * kStr + lcol]) = in ? pv[r] : v8bf{};
         }
     };
-    // this lane's address pattern for the transposing V reads (see above)
-    const int tr_key = (col >> 2);              // key within a quadruple
-    const int tr_dim = 4 * (col & 3);           // dims within a 16-dim slice
+    // this lane's addresses for the transposing V reads: group dims 16*(lane/16 % 2),
+    // key (a/4) of the quadruple, dims 4(a%4)..+3
+    const int ga = lane & 15;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (ga & 3);
+    const int tr_key = 4 * hh + (ga >> 2);
+
+    float m_run = -__builtin_inff();            // running max of the raw scores
+    float l_part = 0.0f;
+    v16f o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = v16f{};
 
     if (ntiles > 0) {
         fetch(0);
         stage();
     }
     uint32_t w0 = pw0, w1 = pw1;
+    __builtin_amdgcn_s_waitcnt(0);              // prologue loads landed (see the indexer's tile loop)
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
-        if (tile + 1 < ntiles) fetch(tile + 1);  // in flight during the multiply
+        fetch(tile + 1 < ntiles ? tile + 1 : tile);   // in flight during the multiply
         const bool any = __ballot((w0 | w1) != 0u) != 0ull;
         if (any) {                               // uniform per wave
-            v4f acc[4];
+            v16f sa = v16f{}, sb = v16f{};       // S^T of keys 0..31 and 32..63
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                acc[kt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const v8bf ka = *reinterpret_cast<const v8bf*>(k_s + (kt * 16 + col) * kStr + kg * 32 + c * 8);
-                    acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb4[c], acc[kt], 0, 0, 0);
-                }
+            for (int c = 0; c < 8; ++c) {
+                const v8bf ka = *reinterpret_cast<const v8bf*>(k_s + qc * kStr + 16 * c + 8 * hh);
+                const v8bf kb = *reinterpret_cast<const v8bf*>(k_s + (32 + qc) * kStr + 16 * c + 8 * hh);
+                sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[c], sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qv[c], sb, 0, 0, 0);
             }
-            // acc[kt][i] = S^T[key kt*16 + 4*kg + i][query col]
-            float z[4][4];
+            // the query's bits: key 8(r/4) + 4hh + r%4 of each half
+            const uint32_t ma = w0 >> (4 * hh), mb = w1 >> (4 * hh);
             float bmax = -__builtin_inff();
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int off = kt * 16 + 4 * kg + i;
-                    const uint32_t bit = off < 32 ? (w0 >> off) & 1u : (w1 >> (off - 32)) & 1u;
-                    z[kt][i] = bit ? acc[kt][i] * zscale : -__builtin_inff();
-                    bmax = fmaxf(bmax, z[kt][i]);
-                }
-            bmax = wave_max_xor_16_32(bmax);
+            for (int r = 0; r < 16; ++r) {
+                const int bit = 8 * (r >> 2) + (r & 3);
+                sa[r] = (ma >> bit) & 1u ? sa[r] : -__builtin_inff();
+                sb[r] = (mb >> bit) & 1u ? sb[r] : -__builtin_inff();
+                bmax = fmaxf(bmax, fmaxf(sa[r], sb[r]));
+            }
+            bmax = pair32_max(bmax);
+            // everything below runs on every lane (the MFMAs and transposing
+            // reads take their operands from all of them): a query with no
+            // kept key yet gets p = 0 and corr = 1 through selects
             const float m_new = fmaxf(m_run, bmax);
-            float corr = 1.0f, psum = 0.0f;
-            v8bf pb[2];
+            const bool none = m_new == -__builtin_inff();
+            const float mz = none ? 0.0f : m_new * zscale;
+            const float corr = none ? 1.0f : exp2f(fmaf(m_run, zscale, -mz));   // 0 on the first kept key
+            {
+                float psum = 0.0f;
+                v8bf pb[4];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = m_new != -__builtin_inff() ? exp2f(z[kt][i] - m_new) : 0.0f;
-                    psum += p;
-                    pb[kt >> 1][(kt & 1) * 4 + i] = static_cast<__bf16>(p);
+                for (int r = 0; r < 16; ++r) {
+                    const float pa = exp2f(fmaf(sa[r], zscale, -mz));
+                    const float pc = exp2f(fmaf(sb[r], zscale, -mz));
+                    psum += pa + pc;
+                    pb[r >> 3][r & 7] = static_cast<__bf16>(pa);       // keys 0..31: chunks 0, 1
+                    pb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(pc); // keys 32..63: chunks 2, 3
                 }
-            if (m_new != -__builtin_inff()) corr = exp2f(m_run - m_new);
-            l_part = l_part * corr + psum;
-            m_run = m_new;
+                l_part = l_part * corr + psum;
+                if (__ballot(m_new != m_run) != 0ull) {
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                o[d] *= corr;
+                    for (int d = 0; d < 4; ++d) o[d] *= corr;
+                }
+                m_run = m_new;
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const uint16_t* v0 = v_s + (32 * m + 4 * kg + tr_key) * kStr + 16 * d + tr_dim;
-                    const v4bf lo = lds_read_tr16(v0);
-                    const v4bf hi = lds_read_tr16(v0 + 16 * kStr);
-                    const v8bf va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[m], o[d], 0, 0, 0);
+                for (int c16 = 0; c16 < 4; ++c16) {
+                    const uint16_t* vr = v_s + (16 * c16 + tr_key) * kStr + tr_dim;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const v4bf lo = lds_read_tr16(vr + 32 * d);
+                        const v4bf hi = lds_read_tr16(vr + 8 * kStr + 32 * d);
+                        const v8bf va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c16], o[d], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -225,26 +244,34 @@ __global__ __launch_bounds__(256) void k_attn_masked_d128(AttnArgs a, const uint
         __syncthreads();
     }
 
-    const float l_tot = wave_sum_xor_16_32(l_part);
+    const float l_tot = pair32_sum(l_part);
     if (!live_q) return;
-    // o[d][i] = O^T[dim 16d + 4kg + i][query col]
-    uint16_t* outp = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(row) * a.Hq + h) * 128;
+    // o[d][r] = O^T[dim 32d + 8(r/4) + 4hh + r%4][query qc]
+    uint16_t* outp = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(row) * a.Hq + h) * 128 + 4 * hh;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) outp[16 * d + 4 * kg + i] = f32_to_bf16_bits(o[d][i] * inv);
-    if (kg == 0 && a.lse)
-        a.lse[static_cast<size_t>(row) * a.Hq + h] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -__builtin_inff();
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint16_t v4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v4[i] = f32_to_bf16_bits(o[d][4 * q4 + i] * inv);
+            uint2 pk2;
+            pk2.x = static_cast<uint32_t>(v4[0]) | (static_cast<uint32_t>(v4[1]) << 16);
+            pk2.y = static_cast<uint32_t>(v4[2]) | (static_cast<uint32_t>(v4[3]) << 16);
+            *reinterpret_cast<uint2*>(outp + 32 * d + 8 * q4) = pk2;
+        }
+    if (hh == 0 && a.lse)
+        a.lse[static_cast<size_t>(row) * a.Hq + h] = l_tot > 0.0f ? (m_run * zscale + log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
 bool attn_masked_eligible(const AttnArgs& a) {
     if (!(a.dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128)) return false;
-    if (a.n_q < kQB || a.n_k > kMaskedMaxKeys) return false;
+    if (a.n_q < kMinQ || a.n_k > kMaskedMaxKeys) return false;
     // a key tile is shared by the block's 64 queries: worth it once a row keeps
     // more than 1/64 of what it sees (the average prefix of this problem)
     const double avg_vis = static_cast<double>(a.n_k) - 0.5 * a.n_q;
-    return static_cast<double>(a.kk) * kQB >= avg_vis;
+    return static_cast<double>(a.kk) * kMinQ >= avg_vis;
 }
 
 size_t attn_masked_workspace_bytes(const AttnArgs& a) {
