@@ -73,6 +73,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short lds_s4_t;
 typedef __attribute__((address_space(3))) lds_s4_t* lds_s4_ptr;
 typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr;
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
     lds_s4_ptr lp = (lds_s4_ptr)((lds_u16_ptr)(const_cast<uint16_t*>(p)));
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (ga & 3);
     const int tr_key = 4 * hh + (ga >> 2);
 
-    float m_run = -__builtin_inff();            // running max of the raw scores
+    float m_ref = -__builtin_inff();            // reference max of the raw scores
     float l_part = 0.0f;
     v16f o[4];
 #pragma unroll
@@ -187,41 +189,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[c], sa, 0, 0, 0);
                 sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qv[c], sb, 0, 0, 0);
             }
-            // the query's bits: key 8(r/4) + 4hh + r%4 of each half
-            const uint32_t ma = w0 >> (4 * hh), mb = w1 >> (4 * hh);
+            // the query's bits: key 8(r/4) + 4hh + r%4 of each half; a
+            // sign-extended one-bit field selects the score or -inf
+            const int ma = static_cast<int>(w0 >> (4 * hh)), mb = static_cast<int>(w1 >> (4 * hh));
+            const uint32_t ninf = __float_as_uint(-__builtin_inff());
             float bmax = -__builtin_inff();
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int bit = 8 * (r >> 2) + (r & 3);
-                sa[r] = (ma >> bit) & 1u ? sa[r] : -__builtin_inff();
-                sb[r] = (mb >> bit) & 1u ? sb[r] : -__builtin_inff();
+                const uint32_t ka = static_cast<uint32_t>(__builtin_amdgcn_sbfe(ma, bit, 1));
+                const uint32_t kb = static_cast<uint32_t>(__builtin_amdgcn_sbfe(mb, bit, 1));
+                sa[r] = __uint_as_float((__float_as_uint(sa[r]) & ka) | (ninf & ~ka));
+                sb[r] = __uint_as_float((__float_as_uint(sb[r]) & kb) | (ninf & ~kb));
                 bmax = fmaxf(bmax, fmaxf(sa[r], sb[r]));
             }
             bmax = pair32_max(bmax);
-            // everything below runs on every lane (the MFMAs and transposing
-            // reads take their operands from all of them): a query with no
-            // kept key yet gets p = 0 and corr = 1 through selects
-            const float m_new = fmaxf(m_run, bmax);
-            const bool none = m_new == -__builtin_inff();
-            const float mz = none ? 0.0f : m_new * zscale;
-            const float corr = none ? 1.0f : exp2f(fmaf(m_run, zscale, -mz));   // 0 on the first kept key
+            // Everything below runs on every lane (the MFMAs and transposing
+            // reads take their operands from all of them).  The exponents use
+            // a reference max m_ref that moves only when a query's max rises
+            // more than 2^8 above it (any reference gives the same softmax;
+            // p <= 256 stays exact enough in bf16 and far from overflow), so O
+            // is rarely rescaled; a query with no kept key yet gets p = 0.
+            const float m_new = fmaxf(m_ref, bmax);
+            const bool move = m_new != -__builtin_inff() && (m_ref == -__builtin_inff() ||
+                                                             (m_new - m_ref) * zscale > 8.0f);
+            float corr = 1.0f;
+            if (__ballot(move) != 0ull) {         // uniform per wave
+                const float m_to = move ? m_new : m_ref;
+                corr = m_ref == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_to) * zscale);
+                m_ref = m_to;
+                l_part *= corr;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] *= corr;
+            }
+            const float mz = m_ref == -__builtin_inff() ? 0.0f : m_ref * zscale;
             {
                 float psum = 0.0f;
                 v8bf pb[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pa = exp2f(fmaf(sa[r], zscale, -mz));
-                    const float pc = exp2f(fmaf(sb[r], zscale, -mz));
-                    psum += pa + pc;
-                    pb[r >> 3][r & 7] = static_cast<__bf16>(pa);       // keys 0..31: chunks 0, 1
-                    pb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(pc); // keys 32..63: chunks 2, 3
+                for (int r = 0; r < 16; r += 2) {
+                    const float pa0 = __builtin_amdgcn_exp2f(fmaf(sa[r], zscale, -mz));
+                    const float pa1 = __builtin_amdgcn_exp2f(fmaf(sa[r + 1], zscale, -mz));
+                    const float pc0 = __builtin_amdgcn_exp2f(fmaf(sb[r], zscale, -mz));
+                    const float pc1 = __builtin_amdgcn_exp2f(fmaf(sb[r + 1], zscale, -mz));
+                    psum += (pa0 + pa1) + (pc0 + pc1);
+                    // pairs convert with one v_cvt_pk_bf16_f32 (round to nearest even)
+                    const v2bf qa = __builtin_convertvector((v2f){pa0, pa1}, v2bf);
+                    const v2bf qc = __builtin_convertvector((v2f){pc0, pc1}, v2bf);
+                    pb[r >> 3][r & 7] = qa[0];               // keys 0..31: chunks 0, 1
+                    pb[r >> 3][(r & 7) + 1] = qa[1];
+                    pb[2 + (r >> 3)][r & 7] = qc[0];         // keys 32..63: chunks 2, 3
+                    pb[2 + (r >> 3)][(r & 7) + 1] = qc[1];
                 }
-                l_part = l_part * corr + psum;
-                if (__ballot(m_new != m_run) != 0ull) {
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) o[d] *= corr;
-                }
-                m_run = m_new;
+                l_part += psum;
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
                     const uint16_t* vr = v_s + (16 * c16 + tr_key) * kStr + tr_dim;
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             *reinterpret_cast<uint2*>(outp + 32 * d + 8 * q4) = pk2;
         }
     if (hh == 0 && a.lse)
-        a.lse[static_cast<size_t>(row) * a.Hq + h] = l_tot > 0.0f ? (m_run * zscale + log2f(l_tot)) * kLn2 : -__builtin_inff();
+        a.lse[static_cast<size_t>(row) * a.Hq + h] = l_tot > 0.0f ? (m_ref * zscale + log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
 bool attn_masked_eligible(const AttnArgs& a) {
