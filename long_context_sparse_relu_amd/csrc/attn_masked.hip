@@ -29,7 +29,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQB = 128;           // queries per workgroup (32 per wave)
 constexpr int kKB = 64;            // keys per tile
-constexpr int kStr = 136;          // LDS row stride (bf16) of the K and V tiles
+// LDS row strides (bf16), one bank pattern per access: the K tile is read a
+// row per lane (16-byte reads; 68 words per row spread 16 rows over all 64
+// banks), the V tile by the transposing reads (4 keys x 32 dims per 32 lanes;
+// 80 words per row puts the 4 keys 16 banks apart)
+constexpr int kStr = 136;          // K tile
+constexpr int kStrV = 160;         // V tile
 constexpr int kMinQ = 64;          // fewest query rows this path takes
 constexpr int kMaskedMaxKeys = 1 << 18;
 }
@@ -85,8 +90,13 @@ __device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
-    __shared__ __align__(16) uint16_t k_s[kKB * kStr];
-    __shared__ __align__(16) uint16_t v_s[kKB * kStr];
+#ifndef DSA_MASKED_BUFS
+#define DSA_MASKED_BUFS 2
+#endif
+    // DSA_MASKED_BUFS = 2: the next tile is staged into the other buffer while
+    // the current one is read (one barrier per tile); 1: single buffer, two
+    __shared__ __align__(16) uint16_t k_all[DSA_MASKED_BUFS * kKB * kStr];
+    __shared__ __align__(16) uint16_t v_all[DSA_MASKED_BUFS * kKB * kStrV];
     __shared__ int last_s[4];
 
     const int nqb = (a.n_q + kQB - 1) / kQB;
@@ -149,13 +159,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         pw0 = live_q ? x0 : 0u;
         pw1 = live_q ? x1 : 0u;
     };
-    auto stage = [&]() {
+    auto stage = [&](int buf) {
+        uint16_t* ks = k_all + buf * kKB * kStr;
+        uint16_t* vs = v_all + buf * kKB * kStrV;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int kr = lrow + 16 * r;
             const bool in = pkey0 + kr < a.n_k;
-            *reinterpret_cast<v8bf*>(&k_s[kr * kStr + lcol]) = in ? pk[r] : v8bf{};
-            *reinterpret_cast<v8bf*>(&v_s[kr * kStr + lcol]) = in ? pv[r] : v8bf{};
+            *reinterpret_cast<v8bf*>(&ks[kr * kStr + lcol]) = in ? pk[r] : v8bf{};
+            *reinterpret_cast<v8bf*>(&vs[kr * kStrV + lcol]) = in ? pv[r] : v8bf{};
         }
     };
     // this lane's addresses for the transposing V reads: group dims 16*(lane/16 % 2),
@@ -172,13 +184,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     if (ntiles > 0) {
         fetch(0);
-        stage();
+        stage(0);
     }
     uint32_t w0 = pw0, w1 = pw1;
     __builtin_amdgcn_s_waitcnt(0);              // prologue loads landed (see the indexer's tile loop)
     __syncthreads();
+    int buf = 0;
     for (int tile = 0; tile < ntiles; ++tile) {
         fetch(tile + 1 < ntiles ? tile + 1 : tile);   // in flight during the multiply
+        const uint16_t* k_s = k_all + buf * kKB * kStr;
+        const uint16_t* v_s = v_all + buf * kKB * kStrV;
         const bool any = __ballot((w0 | w1) != 0u) != 0ull;
         if (any) {                               // uniform per wave
             v16f sa = v16f{}, sb = v16f{};       // S^T of keys 0..31 and 32..63
@@ -244,24 +259,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 l_part += psum;
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
-                    const uint16_t* vr = v_s + (16 * c16 + tr_key) * kStr + tr_dim;
+                    const uint16_t* vr = v_s + (16 * c16 + tr_key) * kStrV + tr_dim;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const v4bf lo = lds_read_tr16(vr + 32 * d);
-                        const v4bf hi = lds_read_tr16(vr + 8 * kStr + 32 * d);
+                        const v4bf hi = lds_read_tr16(vr + 8 * kStrV + 32 * d);
                         const v8bf va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c16], o[d], 0, 0, 0);
                     }
                 }
             }
         }
+#if DSA_MASKED_BUFS == 2
+        // the other buffer was last read before the previous barrier
+        if (tile + 1 < ntiles) {
+            stage(buf ^ 1);
+            w0 = pw0;
+            w1 = pw1;
+            buf ^= 1;
+        }
+        __syncthreads();
+#else
         if (tile + 1 < ntiles) {
             __syncthreads();                     // every wave is done with this tile
-            stage();
+            stage(0);
             w0 = pw0;
             w1 = pw1;
         }
         __syncthreads();
+#endif
     }
 
     const float l_tot = pair32_sum(l_part);
