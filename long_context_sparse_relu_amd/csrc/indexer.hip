@@ -153,17 +153,16 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
     const uint64_t below = (1ull << lane) - 1ull;
 
     // a batch is U/4 groups of 64 keys; lane l scores key base + 64g + l of group g
+    // Loads are issued unconditionally: a key past the chunk or past pos
+    // reads the chunk's last visible key (key 0 when it has none) and its
+    // score is discarded, so no branch separates a load from its use.
+    const int lim = max(0, min(s_end, pos + 1) - 1);
     auto load_batch = [&](int base, v8i* bv, float* sk) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = base + u * 16 + col;
-            bv[u] = load_fp8_key(kb, s, s < s_end && s <= pos, lane);
-        }
+        for (int u = 0; u < U; ++u)
+            bv[u] = load_split32(kb + static_cast<size_t>(min(base + u * 16 + col, lim)) * 128, kg);
 #pragma unroll
-        for (int g = 0; g < U / 4; ++g) {
-            const int s = base + g * 64 + lane;
-            sk[g] = s < s_end && s <= pos ? ksb[s] : 0.0f;
-        }
+        for (int g = 0; g < U / 4; ++g) sk[g] = ksb[min(base + g * 64 + lane, lim)];
     };
     auto score_batch = [&](int base, const v8i* bv, const float* sk) {
 #pragma unroll
@@ -198,7 +197,7 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
         for (; base < s_end; base += step) {
             v8i bn[U];
             float skn[U / 4];
-            if (base + step < s_end) load_batch(base + step, bn, skn);
+            load_batch(base + step, bn, skn);      // past the end: clamped copies, never scored
             score_batch(base, bv, sk);
 #pragma unroll
             for (int u = 0; u < U; ++u) bv[u] = bn[u];
