@@ -238,7 +238,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         ia.visible_only = true;
         dsa::TopkArgs ta = topk_args(p, r0, nr, scores, idx + static_cast<size_t>(r0) * p->top_k,
                                      base + L.topk_off);
-        if (dsa::index_fills_hist(ia)) {
+        if (dsa::index_fills_hist(ia) && !dsa::topk_row_lds(p->n_k)) {
             // the indexer builds the first-digit histogram as it writes the scores
             ia.hist = ta.hist;
             ta.hist_ready = true;

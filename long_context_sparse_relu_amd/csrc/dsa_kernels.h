@@ -62,6 +62,9 @@ size_t topk_workspace_bytes(int rows, int n_k);
 int topk_cand_cap(int n_k);
 void topk_carve(void* ws, int rows, int n_k, TopkArgs& a);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// Rows of at most this many keys are selected by one workgroup from LDS (no
+// histogram from the indexer needed).
+bool topk_row_lds(int n_k);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 
 struct AttnArgs {

@@ -290,6 +290,91 @@ int topk_cand_cap(int n_k) {
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// ---------------------------------------------------------------------------
+// Rows short enough for LDS (every prefill row up to 32K keys): one workgroup
+// per row reads the row's visible scores once, as order keys, into LDS and
+// radix-selects there on the composite ((key - row minimum) << 32 | ~position),
+// whose first digit covers the top 11 bits of the row's key range, so the
+// histogram passes spread over the bins and never re-read memory; the kept
+// positions come out in ascending order through an LDS bitmap.
+// ---------------------------------------------------------------------------
+constexpr int kRowLdsMax = 32768;       // scores a row may hold in LDS (128 KiB)
+constexpr int kRowThreads = 1024;
+
+bool topk_row_lds(int n_k) { return n_k <= kRowLdsMax; }
+
+struct LdsRel {
+    const uint32_t* key; int n; uint32_t base;
+    __device__ int size() const { return n; }
+    __device__ bool get(int i, uint64_t* out) const {
+        *out = (static_cast<uint64_t>(key[i] - base) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(i));
+        return true;
+    }
+};
+
+__global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
+    extern __shared__ uint32_t keys[];                        // [min(n_k, kRowLdsMax)]
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t bm[kRowLdsMax / 32];
+    __shared__ uint32_t wsum[kRowThreads / 64 + 2];
+    __shared__ uint32_t n_list;
+    const int lrow = blockIdx.x, row = a.row0 + lrow;
+    const int vis = row_visible(a, row);
+    const int k = a.k;
+    int32_t* out = a.idx + static_cast<size_t>(lrow) * k;
+    if (vis <= k) {
+        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < vis ? j : -1;
+        return;
+    }
+    const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+    // the row's keys, eight loads in flight per thread (indices past vis
+    // re-read the last score and are not stored)
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * kRowThreads) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = sc[min(i0 + u * kRowThreads, vis - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kRowThreads;
+            if (i < vis) {
+                const uint32_t kk = order_key(v[u]);
+                keys[i] = kk;
+                kmin = min(kmin, kk);
+                kmax = max(kmax, kk);
+            }
+        }
+    }
+    const int nwords = (vis + 31) >> 5;
+    for (int i = threadIdx.x; i < nwords; i += kRowThreads) bm[i] = 0u;
+    if (threadIdx.x == 0) n_list = 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    }
+    __shared__ uint32_t wmin[kRowThreads / 64], wmax[kRowThreads / 64];
+    if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
+    __syncthreads();
+    for (int w = 0; w < kRowThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
+    const uint32_t range = kmax - kmin;
+    const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
+    const int sh = bits > 11 ? bits - 11 : 0;
+    int shifts[6], widths[6], np = 1;
+    shifts[0] = 32 + sh;
+    widths[0] = 11;
+    for (int below = 32 + sh; below > 0 && np < 6; ++np) {
+        const int w = below < 11 ? below : 11;
+        below -= w;
+        shifts[np] = below;
+        widths[np] = w;
+    }
+    Sink sink{bm, nullptr, &n_list, static_cast<uint32_t>(k)};
+    LdsRel src{keys, vis, kmin};
+    radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
+    write_ordered(sink, nwords, 1, k, out, wsum);
+}
+
 size_t topk_workspace_bytes(int rows, int n_k) {
     size_t r = static_cast<size_t>(rows);
     size_t zeroed = align256(r * (2 * kTopkBins + kTopkMeta) * sizeof(uint32_t));
@@ -314,6 +399,25 @@ void topk_carve(void* ws, int rows, int n_k, TopkArgs& a) {
 // workspace's counters are cleared and the digit-0 histogram built here.
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipError_t e;
+    if (topk_row_lds(a.n_k)) {
+        // LDS for the longest visible prefix among the rows: known on the
+        // host when positions are implicit (pos = n_k - n_q + t), else n_k
+        int vis_max = a.n_k;
+        if (!a.q_pos && a.rows > 0) {
+            const int last = a.row0 + a.rows - 1;
+            const int t_max = a.row0 / a.n_q == last / a.n_q ? last % a.n_q : a.n_q - 1;
+            vis_max = min(a.n_k, a.n_k - a.n_q + t_max + 1);
+            if (vis_max < 1) vis_max = 1;
+        }
+        const size_t smem = static_cast<size_t>(vis_max) * sizeof(uint32_t);
+        if (smem > 64 * 1024) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_row_lds),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(k_topk_row_lds, dim3(a.rows), dim3(kRowThreads), smem, st, a);
+        return hipGetLastError();
+    }
     const dim3 grid((a.n_k + kChunk - 1) / kChunk, a.rows);
     if (!a.hist_ready) {
         if ((e = launch_zero_u32(a.hist, a.zero_words, st)) != hipSuccess) return e;

@@ -12,15 +12,16 @@ constexpr int kBitmapMaxKeys = 1 << 18;   // rows up to this long are ordered th
 
 // Block-wide search of the threshold bin: the digit d with
 //   count(bins > d) < k_rem <= count(bins >= d).
-// `hist` has nbins LDS entries (nbins a multiple of blockDim.x); `wsum` is an
-// LDS array of one slot per wave plus two result slots.  Every thread returns
-// the same d and count(bins > d).  Requires sum(hist) >= k_rem >= 1.
+// `hist` has nbins LDS entries (nbins and blockDim.x powers of two; with
+// fewer bins than threads, the first nbins threads own one bin each); `wsum`
+// is an LDS array of one slot per wave plus two result slots.  Every thread
+// returns the same d and count(bins > d).  Requires sum(hist) >= k_rem >= 1.
 __device__ inline void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t k_rem,
                                    uint32_t* wsum, int* digit, uint32_t* gt)
 {
     const int T = blockDim.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = T >> 6;
-    const int per = nbins / T;
+    const int per = nbins >= T ? nbins / T : (tid < nbins ? 1 : 0);
     const int top = nbins - 1 - tid * per;      // this thread's bins: top, top-1, ...
     uint32_t local = 0;
     for (int j = 0; j < per; ++j) local += hist[top - j];

@@ -283,6 +283,37 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == dsa.E_WORKSPACE
 
 
+@pytest.mark.parametrize("n_k,fused", [(40000, "decode"), (9000, "unfused")])
+def test_massive_exact_ties_resolve_to_lowest_positions(n_k, fused):
+    """5000 key rows are byte copies of the query's strongest indexer head, so
+    their scores are bit-identical and lead the row: the k kept positions
+    must be exactly 0..k-1 of the copies.  Selecting them takes every radix
+    digit down to the last position bits (the long decode rows go through
+    the sampled candidate path, the 9000-key rows through the LDS row path)."""
+    k = 512
+    sp = custom_spec(name="ties", B=2, n_q=1, n_k=n_k, idx_heads=16, idx_dtype="e4m3", top_k=k,
+                     q_heads=8, kv_heads=1, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=29)
+    for b in range(2):
+        h = int(torch.argmax(inp["iw"][b, 0]).item())
+        inp["ik"][b, :5000] = inp["iq"][b, 0, h].unsqueeze(0)
+        inp["ik_scale"][b, :5000] = inp["iq_scale"][b, 0]
+    prob = _problem(inp)
+    if fused == "decode":
+        idx = torch.empty((2, 1, k), dtype=torch.int32, device=DEV)
+        dsa.decode(prob, idx_out=idx)
+    else:
+        idx = dsa.topk(prob, dsa.index_scores(prob))
+    torch.cuda.synchronize()
+    ov = oracle_view(inp)
+    for b in range(2):
+        sc = oracle.index_scores(ov["iq"][b], ov["ik"][b], ov["iw"][b], "e4m3", ov["iq_scale"][b],
+                                 ov["ik_scale"][b], None)
+        o_idx, _ = oracle.topk(sc, k, None)
+        assert o_idx[0].tolist() == list(range(k)), "the copies must lead the row"
+        assert idx[b, 0].cpu().tolist() == list(range(k))
+
+
 def test_phase_timer_records_each_phase():
     """The opt-in phase timer: a sampled decode runs all four phases, the
     timed call's results equal an untimed call's, and switching it off stops
