@@ -90,13 +90,10 @@ __device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
-#ifndef DSA_MASKED_BUFS
-#define DSA_MASKED_BUFS 2
-#endif
-    // DSA_MASKED_BUFS = 2: the next tile is staged into the other buffer while
-    // the current one is read (one barrier per tile); 1: single buffer, two
-    __shared__ __align__(16) uint16_t k_all[DSA_MASKED_BUFS * kKB * kStr];
-    __shared__ __align__(16) uint16_t v_all[DSA_MASKED_BUFS * kKB * kStrV];
+    // two buffers: the next tile is staged into one while the other is read
+    // (one barrier per tile)
+    __shared__ __align__(16) uint16_t k_all[2 * kKB * kStr];
+    __shared__ __align__(16) uint16_t v_all[2 * kKB * kStrV];
     __shared__ int last_s[4];
 
     const int nqb = (a.n_q + kQB - 1) / kQB;
@@ -270,7 +267,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 }
             }
         }
-#if DSA_MASKED_BUFS == 2
         // the other buffer was last read before the previous barrier
         if (tile + 1 < ntiles) {
             stage(buf ^ 1);
@@ -279,15 +275,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             buf ^= 1;
         }
         __syncthreads();
-#else
-        if (tile + 1 < ntiles) {
-            __syncthreads();                     // every wave is done with this tile
-            stage(0);
-            w0 = pw0;
-            w1 = pw1;
-        }
-        __syncthreads();
-#endif
     }
 
     const float l_tot = pair32_sum(l_part);

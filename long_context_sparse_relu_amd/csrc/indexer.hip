@@ -85,27 +85,23 @@ __global__ __launch_bounds__(256) void k_index_generic(
 //               gathered per workgroup in LDS and appended to the row's
 //               candidate list as (key << 32 | ~position).
 // ---------------------------------------------------------------------------
+// Launch shape (measured on decode_128k: register prefetch of the next step,
+// other chunk sizes, wave counts and interleaved chunks were all slower or
+// equal).
 #ifndef DSA_IDX_U
 #define DSA_IDX_U 4          // blocks of 16 keys each wave loads per step
 #endif
 #ifndef DSA_IDX_KPB
 #define DSA_IDX_KPB 4096     // keys per workgroup
 #endif
-#ifndef DSA_IDX_PREFETCH
-#define DSA_IDX_PREFETCH 0   // 1: load the next step's keys before multiplying the current ones
-#endif
 #ifndef DSA_IDX_WAVES
 #define DSA_IDX_WAVES 4      // waves per workgroup
 #endif
-#ifndef DSA_IDX_INTERLEAVE
-#define DSA_IDX_INTERLEAVE 0 // 1: the workgroups of a row take interleaved chunks of it
-#endif
-
 #ifndef DSA_IDX_OCC
 #define DSA_IDX_OCC 8        // waves per SIMD the register budget must allow
 #endif
 
-template <int U, bool PREFETCH, bool CAND>
+template <int U, bool CAND>
 __global__ __launch_bounds__(DSA_IDX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(DSA_IDX_OCC)))
 void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
     static_assert(U % 4 == 0, "keys are scored 64 at a time");
@@ -138,18 +134,9 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
     if (CAND || hist) __syncthreads();
 
     const int nwaves = blockDim.x >> 6;
-#if DSA_IDX_INTERLEAVE
-    // chunk c of 16*U keys goes to wave c % (nwaves*gridDim.x): at any time
-    // the row's workgroups stream neighbouring chunks
-    const int s_begin = (blockIdx.x * nwaves) * 16 * U;
-    const int s_end = n_k;
-    const int step = nwaves * gridDim.x * 16 * U;
-    (void)keys_per_block;
-#else
     const int s_begin = blockIdx.x * keys_per_block;
     const int s_end = min(s_begin + keys_per_block, n_k);
     const int step = nwaves * 16 * U;
-#endif
     const uint64_t below = (1ull << lane) - 1ull;
 
     // a batch is U/4 groups of 64 keys; lane l scores key base + 64g + l of group g
@@ -189,28 +176,11 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
         }
     };
 
-    int base = s_begin + wave * 16 * U;
-    if constexpr (PREFETCH) {
+    for (int base = s_begin + wave * 16 * U; base < s_end; base += step) {
         v8i bv[U];
         float sk[U / 4];
-        if (base < s_end) load_batch(base, bv, sk);
-        for (; base < s_end; base += step) {
-            v8i bn[U];
-            float skn[U / 4];
-            load_batch(base + step, bn, skn);      // past the end: clamped copies, never scored
-            score_batch(base, bv, sk);
-#pragma unroll
-            for (int u = 0; u < U; ++u) bv[u] = bn[u];
-#pragma unroll
-            for (int g = 0; g < U / 4; ++g) sk[g] = skn[g];
-        }
-    } else {
-        for (; base < s_end; base += step) {
-            v8i bv[U];
-            float sk[U / 4];
-            load_batch(base, bv, sk);
-            score_batch(base, bv, sk);
-        }
+        load_batch(base, bv, sk);
+        score_batch(base, bv, sk);
     }
     if constexpr (CAND) {
         __syncthreads();
@@ -486,7 +456,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st) {
     if (index_fp8_path(a)) {
         const int kpb = DSA_IDX_KPB;
         dim3 grid((a.n_k + kpb - 1) / kpb, a.rows);
-        hipLaunchKernelGGL((k_index_fp8_mfma<DSA_IDX_U, DSA_IDX_PREFETCH != 0, false>), grid,
+        hipLaunchKernelGGL((k_index_fp8_mfma<DSA_IDX_U, false>), grid,
                            dim3(DSA_IDX_WAVES * 64), 0, st, a, kpb);
         return hipGetLastError();
     }
@@ -500,7 +470,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st) {
 hipError_t launch_index_candidates(const IndexArgs& a, hipStream_t st) {
     const int kpb = DSA_IDX_KPB;
     dim3 grid((a.n_k + kpb - 1) / kpb, a.rows);
-    hipLaunchKernelGGL((k_index_fp8_mfma<DSA_IDX_U, DSA_IDX_PREFETCH != 0, true>), grid,
+    hipLaunchKernelGGL((k_index_fp8_mfma<DSA_IDX_U, true>), grid,
                        dim3(DSA_IDX_WAVES * 64), 0, st, a, kpb);
     return hipGetLastError();
 }
