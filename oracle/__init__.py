@@ -62,11 +62,11 @@ def _load():
     lib.ora_topk.restype = None
     lib.ora_topk.argtypes = [i64, i64, vp, vp, i64, vp, vp]
     lib.ora_sparse_attn.restype = None
-    lib.ora_sparse_attn.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32,
-                                    vp, vp, vp, dbl, vp, i64, vp, vp, vp]
+    lib.ora_sparse_attn.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32,
+                                    vp, vp, vp, vp, vp, dbl, vp, i64, vp, vp, vp]
     lib.ora_dense_causal_attn.restype = None
-    lib.ora_dense_causal_attn.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32,
-                                          vp, vp, vp, dbl, vp, vp, vp]
+    lib.ora_dense_causal_attn.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32,
+                                          vp, vp, vp, vp, vp, dbl, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -144,15 +144,27 @@ def topk(scores, k: int, pos=None):
     return idx, kth
 
 
-def sparse_attn(q, k, v, idx, dtype: str, scale: float, pos=None, latent_dv: int | None = None):
+def _kv_scales(kv_dtype, k_scale, v_scale, n_k, Hkv, latent):
+    if kv_dtype != "e4m3":
+        return None, None
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32).reshape(n_k, Hkv)
+    vs = None if latent else np.ascontiguousarray(v_scale, dtype=np.float32).reshape(n_k, Hkv)
+    return ks, vs
+
+
+def sparse_attn(q, k, v, idx, dtype: str, scale: float, pos=None, latent_dv: int | None = None,
+                kv_dtype: str | None = None, k_scale=None, v_scale=None):
     """Softmax attention of each query over its selected key rows only.
 
-    q [n_q,Hq,dqk], k [n_k,Hkv,dqk], v [n_k,Hkv,dv] (or None with latent_dv: the
-    value is then the first latent_dv entries of the key row), idx [n_q,kk].
+    q [n_q,Hq,dqk] (dtype), k [n_k,Hkv,dqk], v [n_k,Hkv,dv] (kv_dtype, default
+    dtype; or v None with latent_dv: the value is then the first latent_dv
+    entries of the key row), idx [n_q,kk].  An "e4m3" cache carries one fp32
+    scale per (token, kv head) row: k_scale, v_scale [n_k,Hkv].
     Returns (out [n_q,Hq,dv] fp64, lse [n_q,Hq] fp64).
     """
+    kv_dtype = kv_dtype or dtype
     q = _stored(q, dtype)
-    k = _stored(k, dtype)
+    k = _stored(k, kv_dtype)
     n_q, Hq, dqk = q.shape
     n_k, Hkv, _ = k.shape
     latent = v is None
@@ -160,37 +172,41 @@ def sparse_attn(q, k, v, idx, dtype: str, scale: float, pos=None, latent_dv: int
         dv = int(latent_dv)
         assert Hkv == 1 and dv <= dqk
     else:
-        v = _stored(v, dtype)
+        v = _stored(v, kv_dtype)
         dv = v.shape[2]
+    ks, vs = _kv_scales(kv_dtype, k_scale, v_scale, n_k, Hkv, latent)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     kk = idx.shape[1]
     pos = _positions(pos, n_q, n_k)
     out = np.empty((n_q, Hq, dv), dtype=np.float64)
     lse = np.empty((n_q, Hq), dtype=np.float64)
     _load().ora_sparse_attn(n_q, n_k, Hq, Hkv, dqk, dv, int(latent), _DTYPE_CODES[dtype],
-                            _ptr(q), _ptr(k), _ptr(v), float(scale), _ptr(idx), kk,
-                            _ptr(pos), _ptr(out), _ptr(lse))
+                            _DTYPE_CODES[kv_dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
+                            float(scale), _ptr(idx), kk, _ptr(pos), _ptr(out), _ptr(lse))
     return out, lse
 
 
-def dense_causal_attn(q, k, v, dtype: str, scale: float, pos=None, latent_dv: int | None = None):
+def dense_causal_attn(q, k, v, dtype: str, scale: float, pos=None, latent_dv: int | None = None,
+                      kv_dtype: str | None = None, k_scale=None, v_scale=None):
     """Textbook dense causal attention over keys s <= pos[t] (a pin for sparse_attn)."""
+    kv_dtype = kv_dtype or dtype
     q = _stored(q, dtype)
-    k = _stored(k, dtype)
+    k = _stored(k, kv_dtype)
     n_q, Hq, dqk = q.shape
     n_k, Hkv, _ = k.shape
     latent = v is None
     if latent:
         dv = int(latent_dv)
     else:
-        v = _stored(v, dtype)
+        v = _stored(v, kv_dtype)
         dv = v.shape[2]
+    ks, vs = _kv_scales(kv_dtype, k_scale, v_scale, n_k, Hkv, latent)
     pos = _positions(pos, n_q, n_k)
     out = np.empty((n_q, Hq, dv), dtype=np.float64)
     lse = np.empty((n_q, Hq), dtype=np.float64)
     _load().ora_dense_causal_attn(n_q, n_k, Hq, Hkv, dqk, dv, int(latent), _DTYPE_CODES[dtype],
-                                  _ptr(q), _ptr(k), _ptr(v), float(scale), _ptr(pos),
-                                  _ptr(out), _ptr(lse))
+                                  _DTYPE_CODES[kv_dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
+                                  float(scale), _ptr(pos), _ptr(out), _ptr(lse))
     return out, lse
 
 
@@ -200,7 +216,8 @@ def dsa_forward(inp: dict, rows=None):
     `inp` holds numpy arrays in stored form for every sequence b:
       iq [B,n_q,H,D], iq_scale [B,n_q]|None, ik [B,n_k,D], ik_scale [B,n_k]|None,
       iw [B,n_q,H], q [B,n_q,Hq,dqk], k [B,n_k,Hkv,dqk], v [B,n_k,Hkv,dv]|None,
-    plus scalars idx_dtype, attn_dtype, top_k, scale, latent_dv, pos [B,n_q].
+      for an FP8 cache (kv_dtype "e4m3") k_scale / v_scale [B,n_k,Hkv],
+    plus scalars idx_dtype, attn_dtype, kv_dtype, top_k, scale, latent_dv, pos [B,n_q].
     `rows` is a list of (b, t) pairs (default: all).  Returns a dict of per-row
     results keyed by (b, t): scores, idx, kth, out, lse.
     """
@@ -221,8 +238,12 @@ def dsa_forward(inp: dict, rows=None):
                           iqs, iks, pos)
         idx, kth = topk(sc, inp["top_k"], pos)
         v = None if inp.get("v") is None else inp["v"][b]
+        kvs = {}
+        if inp.get("kv_dtype", inp["attn_dtype"]) == "e4m3":
+            kvs = dict(kv_dtype="e4m3", k_scale=inp["k_scale"][b],
+                       v_scale=None if inp.get("v_scale") is None else inp["v_scale"][b])
         out, lse = sparse_attn(inp["q"][b][ts], inp["k"][b], v, idx, inp["attn_dtype"],
-                               inp["scale"], pos, inp.get("latent_dv"))
+                               inp["scale"], pos, inp.get("latent_dv"), **kvs)
         for j, t in enumerate(ts.tolist()):
             res[(b, t)] = dict(scores=sc[j], idx=idx[j], kth=kth[j], out=out[j], lse=lse[j])
     return res

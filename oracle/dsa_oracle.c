@@ -102,6 +102,13 @@ static void load_row(const void *base, int dtype, int64_t off, int64_t n,
         dst[i] = load_elem(base, dtype, off + i) * scale;
 }
 
+/* Scale of K/V row r (token * Hkv + kv head): the row's fp32 scale for FP8
+ * caches, 1 for unscaled formats (scales == NULL). */
+static double kv_row_scale(const float *scales, int64_t r)
+{
+    return scales ? (double)scales[r] : 1.0;
+}
+
 /*
  * Lightning-indexer scores of one sequence [DD §1].
  *   iq  [n_q, H, D]  (dtype), iq_scale [n_q] fp32 or NULL (treated as 1)
@@ -209,17 +216,21 @@ void ora_topk(int64_t n_q, int64_t n_k, const double *scores, const int64_t *pos
  * Main attention over the selected rows only [DD §1: the main attention looks
  * at the selected subset; O(n*k)].  One sequence:
  *   q   [n_q, Hq, dqk]                      (dtype)
- *   k   [n_k, Hkv, dqk]                     (dtype)
- *   v   [n_k, Hkv, dv]  or NULL when latent (dtype): the value is then the
+ *   k   [n_k, Hkv, dqk]                     (kv_dtype)
+ *   v   [n_k, Hkv, dv]  or NULL when latent (kv_dtype): the value is then the
  *                       first dv entries of the key row (Hkv must be 1)
+ *   k_scale, v_scale [n_k, Hkv] fp32 or NULL: an FP8 cache stores each
+ *                       (token, kv head) row as codes times one scale; the
+ *                       latent value uses its key row's scale
  *   idx [n_q, kk] int32; entries < 0 or > pos[t] or >= n_k are skipped
  *   out [n_q, Hq, dv] fp64, lse [n_q, Hq] fp64 (natural log; -inf and out = 0
  *   for a row with no valid entry)
  * Heads are grouped: query head h reads kv head h / (Hq / Hkv).
  */
 void ora_sparse_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
-                     int64_t dqk, int64_t dv, int latent, int dtype,
-                     const void *q, const void *k, const void *v, double scale,
+                     int64_t dqk, int64_t dv, int latent, int dtype, int kv_dtype,
+                     const void *q, const void *k, const void *v,
+                     const float *k_scale, const float *v_scale, double scale,
                      const int32_t *idx, int64_t kk, const int64_t *pos,
                      double *out, double *lse)
 {
@@ -251,7 +262,8 @@ void ora_sparse_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
                 load_row(q, dtype, (t * Hq + h) * dqk, dqk, 1.0, qh);
                 double zmax = -INFINITY;
                 for (int64_t j = 0; j < n_sel; ++j) {
-                    load_row(k, dtype, (sel[j] * Hkv + g) * dqk, dqk, 1.0, kr);
+                    load_row(k, kv_dtype, (sel[j] * Hkv + g) * dqk, dqk,
+                             kv_row_scale(k_scale, sel[j] * Hkv + g), kr);
                     double dot = 0.0;
                     for (int64_t d = 0; d < dqk; ++d)
                         dot += qh[d] * kr[d];
@@ -264,9 +276,11 @@ void ora_sparse_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
                 for (int64_t d = 0; d < dv; ++d) o[d] = 0.0;
                 for (int64_t j = 0; j < n_sel; ++j) {
                     if (latent)
-                        load_row(k, dtype, (sel[j] * Hkv + g) * dqk, dv, 1.0, vr);
+                        load_row(k, kv_dtype, (sel[j] * Hkv + g) * dqk, dv,
+                                 kv_row_scale(k_scale, sel[j] * Hkv + g), vr);
                     else
-                        load_row(v, dtype, (sel[j] * Hkv + g) * dv, dv, 1.0, vr);
+                        load_row(v, kv_dtype, (sel[j] * Hkv + g) * dv, dv,
+                                 kv_row_scale(v_scale, sel[j] * Hkv + g), vr);
                     double p = exp(z[j] - zmax) / denom;
                     for (int64_t d = 0; d < dv; ++d)
                         o[d] += p * vr[d];
@@ -284,8 +298,9 @@ void ora_sparse_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
  * Written separately on purpose: full score row, then max, then normalise.
  */
 void ora_dense_causal_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
-                           int64_t dqk, int64_t dv, int latent, int dtype,
-                           const void *q, const void *k, const void *v, double scale,
+                           int64_t dqk, int64_t dv, int latent, int dtype, int kv_dtype,
+                           const void *q, const void *k, const void *v,
+                           const float *k_scale, const float *v_scale, double scale,
                            const int64_t *pos, double *out, double *lse)
 {
     int64_t group = Hq / Hkv;
@@ -302,8 +317,8 @@ void ora_dense_causal_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
                 double dot = 0.0;
                 for (int64_t d = 0; d < dqk; ++d)
                     dot += load_elem(q, dtype, (t * Hq + h) * dqk + d) *
-                           load_elem(k, dtype, (s * Hkv + g) * dqk + d);
-                row[s] = scale * dot;
+                           load_elem(k, kv_dtype, (s * Hkv + g) * dqk + d);
+                row[s] = scale * dot * kv_row_scale(k_scale, s * Hkv + g);
                 if (row[s] > mx) mx = row[s];
             }
             double sum = 0.0;
@@ -313,8 +328,9 @@ void ora_dense_causal_attn(int64_t n_q, int64_t n_k, int64_t Hq, int64_t Hkv,
             }
             for (int64_t s = 0; s <= last; ++s) {
                 for (int64_t d = 0; d < dv; ++d) {
-                    double val = latent ? load_elem(k, dtype, (s * Hkv + g) * dqk + d)
-                                        : load_elem(v, dtype, (s * Hkv + g) * dv + d);
+                    double val = latent
+                        ? load_elem(k, kv_dtype, (s * Hkv + g) * dqk + d) * kv_row_scale(k_scale, s * Hkv + g)
+                        : load_elem(v, kv_dtype, (s * Hkv + g) * dv + d) * kv_row_scale(v_scale, s * Hkv + g);
                     o[d] += row[s] / sum * val;
                 }
             }

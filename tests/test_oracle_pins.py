@@ -338,3 +338,85 @@ def test_pipeline_matches_brute_force_subset_attention():
         ref = _sdpa64(q[t:t + 1].astype(np.float64), np.repeat(k, 2, 1).astype(np.float64),
                       np.repeat(v, 2, 1).astype(np.float64), mask, ov["scale"])
         np.testing.assert_allclose(res[(0, t)]["out"], ref[0], rtol=1e-10, atol=1e-12)
+
+
+# --- FP8 (E4M3) main KV cache: codes times one fp32 scale per (token, kv head) row ---
+
+def _e4m3_codes(rng, shape):
+    """Random finite E4M3 codes (NaN codes 0x7F / 0xFF excluded)."""
+    c = rng.integers(0, 256, size=shape, dtype=np.uint16)
+    return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)
+
+
+def _e4m3_dequant_torch(codes, scales):
+    """torch's own float8_e4m3fn decoder, times the row scales, in float64."""
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+    return (vals * torch.from_numpy(scales.astype(np.float64))[..., None]).numpy()
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+def test_fp8_cache_attention_matches_torch_sdpa(hq, hkv):
+    """The FP8 cache path against torch's float8 decoder and float64 SDPA over
+    the selected rows (a boolean mask per query)."""
+    rng = np.random.default_rng(41 + hq)
+    n_q, n_k, d = 4, 30, 16
+    q = rng.standard_normal((n_q, hq, d)).astype(np.float32)
+    kc, vc = _e4m3_codes(rng, (n_k, hkv, d)), _e4m3_codes(rng, (n_k, hkv, d))
+    ks = rng.uniform(0.001, 0.01, (n_k, hkv)).astype(np.float32)
+    vs = rng.uniform(0.5, 2.0, (n_k, hkv)).astype(np.float32)
+    idx = np.stack([rng.choice(n_k, 9, replace=False) for _ in range(n_q)]).astype(np.int32)
+    pos = np.full(n_q, n_k - 1)
+    out, lse = oracle.sparse_attn(q, kc, vc, idx, "f32", 0.3, pos, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    kd, vd = _e4m3_dequant_torch(kc, ks), _e4m3_dequant_torch(vc, vs)
+    grp = hq // hkv
+    mask = np.zeros((n_q, n_k), dtype=bool)
+    for t in range(n_q):
+        mask[t, idx[t]] = True
+    ref = _sdpa64(q.astype(np.float64), np.repeat(kd, grp, 1), np.repeat(vd, grp, 1), mask, 0.3)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    z = 0.3 * np.einsum("thd,shd->ths", q.astype(np.float64), np.repeat(kd, grp, 1))
+    z[np.broadcast_to(~mask[:, None, :], z.shape)] = -np.inf
+    np.testing.assert_allclose(lse, np.log(np.sum(np.exp(z - z.max(2, keepdims=True)), 2)) + z.max(2),
+                               rtol=1e-12)
+
+
+def test_fp8_cache_scale_invariants():
+    """Scaling every V scale by c scales the output by c; scaling every K
+    scale by c equals scaling the softmax scale by c; the dense routine
+    agrees with the sparse one on the FP8 cache with every key kept."""
+    rng = np.random.default_rng(47)
+    n_k, hq, hkv, d = 24, 6, 3, 32
+    q = rng.standard_normal((n_k, hq, d)).astype(np.float32)
+    kc, vc = _e4m3_codes(rng, (n_k, hkv, d)), _e4m3_codes(rng, (n_k, hkv, d))
+    ks = rng.uniform(0.002, 0.02, (n_k, hkv)).astype(np.float32)
+    vs = rng.uniform(0.25, 4.0, (n_k, hkv)).astype(np.float32)
+    idx = np.tile(np.arange(n_k, dtype=np.int32), (n_k, 1))
+    kw = dict(kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    o, l = oracle.sparse_attn(q, kc, vc, idx, "f32", 0.2, None, **kw)
+    o2, _ = oracle.sparse_attn(q, kc, vc, idx, "f32", 0.2, None, kv_dtype="e4m3", k_scale=ks, v_scale=vs * 2)
+    np.testing.assert_allclose(o2, 2 * o, rtol=1e-12, atol=1e-14)
+    o3, l3 = oracle.sparse_attn(q, kc, vc, idx, "f32", 0.1, None, kv_dtype="e4m3", k_scale=ks * 2, v_scale=vs)
+    np.testing.assert_allclose(o3, o, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(l3, l, rtol=1e-12)
+    od, ld = oracle.dense_causal_attn(q, kc, vc, "f32", 0.2, None, **kw)
+    np.testing.assert_allclose(o, od, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l, ld, rtol=1e-13)
+
+
+def test_fp8_latent_value_uses_key_scale():
+    """A latent FP8 row: the value is the first dv dequantised entries of the
+    key row, with the key row's scale."""
+    rng = np.random.default_rng(53)
+    n_k, hq, dqk, dv = 16, 4, 48, 32
+    q = rng.standard_normal((3, hq, dqk)).astype(np.float32)
+    kc = _e4m3_codes(rng, (n_k, 1, dqk))
+    ks = rng.uniform(0.01, 0.1, (n_k, 1)).astype(np.float32)
+    idx = np.array([[1, 4, 9], [0, 2, -1], [15, 7, 3]], dtype=np.int32)
+    out, _ = oracle.sparse_attn(q, kc, None, idx, "f32", 0.25, np.full(3, n_k - 1), latent_dv=dv,
+                                kv_dtype="e4m3", k_scale=ks)
+    kd = _e4m3_dequant_torch(kc, ks)
+    for t, sel in enumerate([[1, 4, 9], [0, 2], [15, 7, 3]]):
+        for h in range(hq):
+            z = 0.25 * kd[sel, 0, :] @ q[t, h].astype(np.float64)
+            p = np.exp(z - z.max()); p /= p.sum()
+            np.testing.assert_allclose(out[t, h], p @ kd[sel, 0, :dv], rtol=1e-11, atol=1e-13)
