@@ -4,8 +4,9 @@ One step = one fused call (lightning indexer over every visible key, top-k
 selection, attention over the selected rows) for the whole batch of the
 workload: by default decode_128k, 64 single-token queries over 131072 cached
 tokens each, 16 FP8 indexer heads of dim 128, k = 2048, bf16 KV cache with 32
-query heads over 4 KV heads of dim 128 (dsa_decode).  The prefill workloads
-(--workload prefill_*) time dsa_prefill over the whole sequence.  Inputs are
+query heads over 4 KV heads of dim 128 (dsa_decode).  decode_128k_fp8kv is
+the same over an E4M3 main KV cache.  The prefill workloads (--workload
+prefill_*) time dsa_prefill over the whole sequence.  Inputs are
 seeded synthetic Gaussians already resident in HBM when the timed region
 starts.
 
@@ -134,7 +135,8 @@ def main(argv=None):
     B, N, k, n_q = s["B"], s["n_k"], s["top_k"], s["n_q"]
     prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
                             v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-                            softmax_scale=inp["scale"], latent_dv=inp["latent_dv"])
+                            softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
+                            k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     out, lse = dsa._out_tensors(prob, None, None)
     idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
     op = dsa.OP_DECODE if decode else dsa.OP_PREFILL
@@ -184,8 +186,12 @@ def main(argv=None):
 
     H, D = s["idx_heads"], s["idx_dim"]
     kbytes = {"f32": 4, "bf16": 2, "e4m3": 1}[s["idx_dtype"]]
-    abytes = {"f32": 4, "bf16": 2}[s["attn_dtype"]]
-    row = s["kv_heads"] * (s["d_qk"] + (0 if s["latent"] else s["d_v"])) * abytes
+    kvt = inp["kv_dtype"]
+    abytes = {"f32": 4, "bf16": 2, "e4m3": 1}[kvt]
+    # bytes of one kept token's K/V rows over all kv heads (an FP8 cache adds a 4-byte scale per row)
+    n_rows_kv = 1 if s["latent"] else 2
+    row = s["kv_heads"] * ((s["d_qk"] + (0 if s["latent"] else s["d_v"])) * abytes
+                           + (4 * n_rows_kv if kvt == "e4m3" else 0))
     # visible keys and kept keys summed over every query row
     pairs = sum(N - n_q + t + 1 for t in range(n_q)) * B
     kept = sum(min(k, N - n_q + t + 1) for t in range(n_q)) * B
@@ -234,12 +240,14 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{s['idx_dtype']}-indexer/{s['attn_dtype']}-attn",
+        "dtype": f"{s['idx_dtype']}-indexer/{s['attn_dtype']}-attn"
+                 + (f"/{kvt}-kv" if kvt != s["attn_dtype"] else ""),
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "n_q": n_q, "context": N, "top_k": k,
                    "idx_heads": H, "idx_dim": D, "idx_dtype": s["idx_dtype"],
                    "q_heads": s["q_heads"], "kv_heads": s["kv_heads"], "d_qk": s["d_qk"],
-                   "d_v": s["d_v"], "latent": s["latent"], "attn_dtype": s["attn_dtype"]},
+                   "d_v": s["d_v"], "latent": s["latent"], "attn_dtype": s["attn_dtype"],
+                   "kv_dtype": kvt},
         "roofline": roof,
         "attn_roofline": attn_roof,
         "step_roofline": step_roof,

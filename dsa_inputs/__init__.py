@@ -23,6 +23,13 @@ w ~ N(0,1)/2, main q/k/v ~ N(0,1), softmax scale 1/sqrt(d_qk)):
                     E4M3, k=512, one shared latent bf16 row of width 576 per
                     token (value = first 512 entries), 128 query heads,
                     256 planted needles per sequence
+  decode_128k_fp8kv decode_128k with the main KV cache stored as E4M3 codes
+                    and one fp32 scale per (token, kv head) row
+
+Any spec may set kv_dtype="e4m3" (with attn_dtype "bf16"): the main k and v
+are drawn as above and stored as E4M3 codes with one fp32 scale (amax/448) per
+(token, kv head) row, in k_scale / v_scale [B,n_k,Hkv] (latent rows: k_scale
+only).
 
 A needle is an indexer key made a noisy copy of one query's strongest head:
 for a random key position s and a query t >= s, h = argmax_h w[t,h] (the query
@@ -55,6 +62,7 @@ CONFIGS: dict[str, dict] = {
                       top_k=512, q_heads=128, kv_heads=1, d_qk=576, d_v=512, latent=True,
                       attn_dtype="bf16", needles=256, outlier_frac=0.0, w_bf16=False),
 }
+CONFIGS["decode_128k_fp8kv"] = dict(CONFIGS["decode_128k"], kv_dtype="e4m3")
 
 _TORCH_STORE = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
 _TENSOR_IDS = {"iq": 1, "ik": 2, "iw": 3, "q": 4, "k": 5, "v": 6, "needle": 7, "outlier": 8}
@@ -105,23 +113,28 @@ def make_inputs(s: dict, device="cpu", seed: int = 0) -> dict:
     Returns a dict of tensors in stored form:
       iq [B,n_q,H,D], iq_scale [B,n_q] (E4M3 only), ik [B,n_k,D], ik_scale [B,n_k],
       iw [B,n_q,H] fp32, q [B,n_q,Hq,dqk], k [B,n_k,Hkv,dqk], v [B,n_k,Hkv,dv] or
-      None (latent), pos [B,n_q] int32 (last visible key: n_k-n_q+t),
+      None (latent), k_scale / v_scale [B,n_k,Hkv] (E4M3 cache only, else None),
+      pos [B,n_q] int32 (last visible key: n_k-n_q+t),
     and the scalars of the spec plus `scale` = 1/sqrt(d_qk).
     """
     B, n_q, n_k = s["B"], s["n_q"], s["n_k"]
     H, D = s["idx_heads"], s["idx_dim"]
     Hq, Hkv, dqk, dv = s["q_heads"], s["kv_heads"], s["d_qk"], s["d_v"]
     idt, adt = s["idx_dtype"], s["attn_dtype"]
+    kvt = s.get("kv_dtype") or adt
+    if kvt != adt:
+        assert kvt == "e4m3" and adt == "bf16", "an FP8 cache goes with bf16 queries"
     latent = bool(s["latent"])
     if latent:
         assert Hkv == 1 and dv <= dqk
     out = {k: v for k, v in s.items()}
+    out["kv_dtype"] = kvt
     out["scale"] = 1.0 / math.sqrt(dqk)
     out["latent_dv"] = dv if latent else None
     pos = (torch.arange(n_q, dtype=torch.int32) + (n_k - n_q)).expand(B, n_q).contiguous()
     out["pos"] = pos.to(device)
 
-    iq_l, iqs_l, ik_l, iks_l, iw_l, q_l, k_l, v_l = ([] for _ in range(8))
+    iq_l, iqs_l, ik_l, iks_l, iw_l, q_l, k_l, v_l, ks_l, vs_l = ([] for _ in range(10))
     needle_pairs = []
     for b in range(B):
         iq = _randn((n_q, H, D), _gen(device, seed, "iq", b), device) / math.sqrt(D)
@@ -145,9 +158,18 @@ def make_inputs(s: dict, device="cpu", seed: int = 0) -> dict:
             iq_l.append(iq.to(_TORCH_STORE[idt])); ik_l.append(ik.to(_TORCH_STORE[idt]))
         iw_l.append(iw)
         q_l.append(_randn((n_q, Hq, dqk), _gen(device, seed, "q", b), device).to(_TORCH_STORE[adt]))
-        k_l.append(_randn((n_k, Hkv, dqk), _gen(device, seed, "k", b), device).to(_TORCH_STORE[adt]))
-        if not latent:
-            v_l.append(_randn((n_k, Hkv, dv), _gen(device, seed, "v", b), device).to(_TORCH_STORE[adt]))
+        kb = _randn((n_k, Hkv, dqk), _gen(device, seed, "k", b), device)
+        vb = None if latent else _randn((n_k, Hkv, dv), _gen(device, seed, "v", b), device)
+        if kvt == "e4m3":
+            c, sc = quantize_e4m3_per_row(kb)
+            k_l.append(c); ks_l.append(sc)
+            if vb is not None:
+                c, sc = quantize_e4m3_per_row(vb)
+                v_l.append(c); vs_l.append(sc)
+        else:
+            k_l.append(kb.to(_TORCH_STORE[kvt]))
+            if vb is not None:
+                v_l.append(vb.to(_TORCH_STORE[kvt]))
     out["iq"] = torch.stack(iq_l)
     out["ik"] = torch.stack(ik_l)
     out["iq_scale"] = torch.stack(iqs_l) if idt == "e4m3" else None
@@ -156,6 +178,8 @@ def make_inputs(s: dict, device="cpu", seed: int = 0) -> dict:
     out["q"] = torch.stack(q_l)
     out["k"] = torch.stack(k_l)
     out["v"] = torch.stack(v_l) if not latent else None
+    out["k_scale"] = torch.stack(ks_l) if ks_l else None
+    out["v_scale"] = torch.stack(vs_l) if vs_l else None
     out["needle_pairs"] = needle_pairs
     return out
 
@@ -229,7 +253,7 @@ def oracle_view(inp: dict, seqs=None) -> dict:
     res["needle_pairs"] = [(seqs.index(b), s, t) for (b, s, t) in inp.get("needle_pairs", [])
                            if b in seqs]
     res["latent_dv"] = inp.get("latent_dv")
-    for name in ("iq", "iq_scale", "ik", "ik_scale", "iw", "q", "k", "v", "pos"):
+    for name in ("iq", "iq_scale", "ik", "ik_scale", "iw", "q", "k", "v", "k_scale", "v_scale", "pos"):
         t = inp.get(name)
         if t is None:
             res[name] = None

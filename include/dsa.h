@@ -27,6 +27,14 @@
  *            out = sum_j softmax(z)_j * v[s_j,g], lse = log sum_j exp(z_j).
  *            In latent mode (kv_latent = 1, kv_heads = 1) the value is the
  *            first d_v entries of the key row.
+ *   cache    the main k and v may be stored in FP8 (kv_dtype = DSA_FP8_E4M3),
+ *            the cache format "DeepSeek-V4 百万 token 上下文的工程实现" names
+ *            in its section on the sliding-window KV cache and mixed strategy
+ *            (FP8 instead of FP16, half the memory).  Each (token, kv head) row
+ *            is its E4M3 codes times one fp32 scale: k[s,g] = k_scale[s,g] *
+ *            code, v[s,g] = v_scale[s,g] * code; a latent value row is part of
+ *            its key row and takes k_scale.  The attention above runs on those
+ *            decoded values.
  *
  * Memory and ownership.  Every pointer inside dsa_problem_t and every output
  * pointer is DEVICE memory owned by the caller, contiguous and row-major in
@@ -59,7 +67,7 @@ extern "C" {
 /* Same typedef as HIP's own header, so both may be included together. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
     DSA_OK = 0,
@@ -106,10 +114,13 @@ typedef struct {
     int32_t d_qk;             /* 64, 128, or 576 (latent) */
     int32_t d_v;              /* 64, 128, or 512 (latent) */
     int32_t kv_latent;        /* 1: v is NULL, value = first d_v entries of the k row */
-    int32_t attn_dtype;       /* DSA_F32 or DSA_BF16, for q, k, v and out */
+    int32_t attn_dtype;       /* DSA_F32 or DSA_BF16, for q and out */
+    int32_t kv_dtype;         /* dtype of k and v: attn_dtype, or DSA_FP8_E4M3 when attn_dtype is DSA_BF16 */
     const void *q;            /* [B, n_q, Hq, d_qk] */
     const void *k;            /* [B, n_k, Hkv, d_qk] */
     const void *v;            /* [B, n_k, Hkv, d_v], NULL when kv_latent */
+    const float *k_scale;     /* [B, n_k, Hkv] fp32 scale of each k row (FP8 cache only, else NULL) */
+    const float *v_scale;     /* [B, n_k, Hkv] fp32 scale of each v row (FP8 cache without kv_latent, else NULL) */
     float softmax_scale;      /* > 0, e.g. 1/sqrt(d_qk) */
 
     int32_t top_k;            /* k, 1..8192 */

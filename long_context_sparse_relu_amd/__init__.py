@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE = 0, -1, -2, -3, -4
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE = 0, 1, 2, 3, 4
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
@@ -45,7 +45,9 @@ class Problem(ctypes.Structure):
         ("ik", ctypes.c_void_p), ("ik_scale", ctypes.c_void_p), ("iw", ctypes.c_void_p),
         ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
         ("d_v", ctypes.c_int32), ("kv_latent", ctypes.c_int32), ("attn_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("softmax_scale", ctypes.c_float),
         ("top_k", ctypes.c_int32),
     ]
@@ -152,14 +154,16 @@ def _contig(name, t, device, dtypes=None):
 
 
 def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik_scale=None,
-                 q_pos=None, softmax_scale=None, latent_dv=None) -> DSAProblem:
+                 q_pos=None, softmax_scale=None, latent_dv=None, k_scale=None, v_scale=None) -> DSAProblem:
     """Describe one batch: see include/dsa.h for the layouts.
 
     iq [B,n_q,H,128], ik [B,n_k,128] (fp32 | bf16 | float8_e4m3fn, same dtype),
     iq_scale [B,n_q] / ik_scale [B,n_k] fp32 for FP8, iw [B,n_q,H] fp32,
     q [B,n_q,Hq,dqk], k [B,n_k,Hkv,dqk], v [B,n_k,Hkv,dv] or None with
     latent_dv (then the value is k[..., :latent_dv] and Hkv must be 1),
-    q_pos [B,n_q] int32 or None.
+    q_pos [B,n_q] int32 or None.  k and v have q's dtype, or float8_e4m3fn
+    (an FP8 cache, q bf16) with k_scale [B,n_k,Hkv] and, unless latent,
+    v_scale [B,n_k,Hkv] fp32.
     """
     device = iq.device
     idt = (torch.float32, torch.bfloat16, torch.float8_e4m3fn)
@@ -194,8 +198,11 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     if q is not None:
         adt = (torch.float32, torch.bfloat16)
         q = _contig("q", q, device, adt)
-        k = _contig("k", k, device, (q.dtype,))
-        v = _contig("v", v, device, (q.dtype,))
+        kvt = (q.dtype, torch.float8_e4m3fn) if q.dtype == torch.bfloat16 else (q.dtype,)
+        k = _contig("k", k, device, kvt)
+        v = _contig("v", v, device, (k.dtype,))
+        k_scale = _contig("k_scale", k_scale, device, (torch.float32,))
+        v_scale = _contig("v_scale", v_scale, device, (torch.float32,))
         if q.dim() != 4 or k.dim() != 4:
             raise ValueError("q must be [B,n_q,Hq,dqk] and k [B,n_k,Hkv,dqk]")
         if q.shape[:2] != (B, n_q) or k.shape[:2] != (B, n_k) or k.shape[3] != q.shape[3]:
@@ -209,12 +216,22 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
             if v.dim() != 4 or v.shape[:3] != (B, n_k, Hkv):
                 raise ValueError(f"v must be [B,n_k,Hkv,dv], got {tuple(v.shape)}")
             dv, latent = v.shape[3], 0
+        if k.dtype == torch.float8_e4m3fn:
+            if k_scale is None or (not latent and v_scale is None):
+                raise ValueError("an FP8 KV cache needs k_scale (and v_scale unless latent)")
+            if k_scale.shape != (B, n_k, Hkv) or (v_scale is not None and v_scale.shape != (B, n_k, Hkv)):
+                raise ValueError("k_scale and v_scale must be [B,n_k,Hkv]")
+        elif k_scale is not None or v_scale is not None:
+            raise ValueError("k_scale / v_scale are for an FP8 (float8_e4m3fn) KV cache only")
         p.q_heads, p.kv_heads, p.d_qk, p.d_v, p.kv_latent = Hq, Hkv, dqk, dv, latent
         p.attn_dtype = _DTYPE_CODE[q.dtype]
+        p.kv_dtype = _DTYPE_CODE[k.dtype]
         p.q, p.k = q.data_ptr(), k.data_ptr()
         p.v = None if v is None else v.data_ptr()
+        p.k_scale = None if k_scale is None else k_scale.data_ptr()
+        p.v_scale = None if v_scale is None else v_scale.data_ptr()
         p.softmax_scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(dqk)
-        tensors.update(q=q, k=k, v=v)
+        tensors.update(q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale)
     return DSAProblem(p, tensors, device)
 
 

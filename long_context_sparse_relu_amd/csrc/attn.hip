@@ -17,16 +17,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
-// Generic path: fp32 or bf16, any head grouping, d_qk <= 576, d_v <= 512,
-// latent rows.  One workgroup per (query row, kv head, chunk of <= 16 query
-// heads); selected rows are staged 16 at a time in LDS as fp32.
+// Generic path: fp32 or bf16 (KV also E4M3 with per-row scales), any head
+// grouping, d_qk <= 576, d_v <= 512, latent rows.  One workgroup per (query
+// row, kv head, chunk of <= 16 query heads); selected rows are staged 16 at a
+// time in LDS as fp32, decoded (code * row scale) on the way in.
 // ---------------------------------------------------------------------------
 constexpr int kGenHC = 16;   // query heads per workgroup
 constexpr int kGenTK = 16;   // selected rows per tile
 constexpr int kGenThreads = 256;
 constexpr int kGenMaxOut = 32;  // (kGenHC * 512) / kGenThreads
 
-template <int DT>
+template <int DT, int KDT>
 __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
     extern __shared__ __align__(16) float sm[];
     float* q_s = sm;                                   // [HC][dqk]
@@ -68,15 +69,27 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
         for (int i = tid; i < kGenTK * dqk; i += blockDim.x) {
             int j = i / dqk, d = i % dqk;
             int s = sidx[j];
-            k_s[i] = s >= 0 ? load_as_f32<DT>(a.k, (static_cast<size_t>(b) * a.n_k + s) * kv_row_stride + g * dqk + d) : 0.0f;
+            float val = 0.0f;
+            if (s >= 0) {
+                const size_t r = static_cast<size_t>(b) * a.n_k + s;
+                val = load_as_f32<KDT>(a.k, r * kv_row_stride + g * dqk + d);
+                if constexpr (KDT == E4M3) val *= a.k_scale[r * a.Hkv + g];
+            }
+            k_s[i] = val;
         }
         for (int i = tid; i < kGenTK * dv; i += blockDim.x) {
             int j = i / dv, d = i % dv;
             int s = sidx[j];
             float val = 0.0f;
             if (s >= 0) {
-                val = a.latent ? load_as_f32<DT>(a.k, (static_cast<size_t>(b) * a.n_k + s) * kv_row_stride + d)
-                               : load_as_f32<DT>(a.v, (static_cast<size_t>(b) * a.n_k + s) * v_row_stride + g * dv + d);
+                const size_t r = static_cast<size_t>(b) * a.n_k + s;
+                if (a.latent) {
+                    val = load_as_f32<KDT>(a.k, r * kv_row_stride + d);
+                    if constexpr (KDT == E4M3) val *= a.k_scale[r];
+                } else {
+                    val = load_as_f32<KDT>(a.v, r * v_row_stride + g * dv + d);
+                    if constexpr (KDT == E4M3) val *= a.v_scale[r * a.Hkv + g];
+                }
             }
             v_s[i] = val;
         }
@@ -170,10 +183,38 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 constexpr int kGqaWaves = DSA_ATTN_WAVES;
 constexpr int kGqaVStride = 136;   // bf16 elements per staged value row (128 + pad)
 
-template <int DEPTH>
+// Ring slot of one 16-key block: a lane's 32 dims of its key's k and v row,
+// as bf16 or, from an E4M3 cache, as the 32 code bytes plus the row scales.
+template <bool KV8> struct GqaBlock;
+template <> struct GqaBlock<false> { v8bf k[4], v[4]; bool ok; };
+template <> struct GqaBlock<true> { v4i k[2], v[2]; float ks, vs; bool ok; };
+
+// 32 E4M3 codes -> 32 bf16 (exact: every E4M3 value is a bf16 value).  Byte i
+// of the input becomes element i of the output.
+__device__ __forceinline__ void e4m3x32_to_bf16(const v4i* w, v8bf* out) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t w0 = static_cast<uint32_t>(w[c >> 1][(c & 1) * 2]);
+        const uint32_t w1 = static_cast<uint32_t>(w[c >> 1][(c & 1) * 2 + 1]);
+        const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+        out[c] = v8bf{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+    }
+}
+
+// KV8: the cache holds E4M3 codes with one fp32 scale per (token, kv head)
+// row.  The codes are widened to bf16 exactly; the key scale multiplies the
+// scores (z = scale * ks * q.code) and the value scale multiplies the softmax
+// weights before their bf16 rounding (p * vs * code), so the running sum stays
+// the plain softmax denominator.
+template <int DEPTH, bool KV8>
 __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, int slice_len, float* part) {
     __shared__ __align__(16) unsigned char smem[kGqaWaves * 16 * 128 * 4];   // 64 KiB
     __shared__ float m_w[kGqaWaves][16], l_w[kGqaWaves][16];
+    __shared__ __align__(16) float sc_w[kGqaWaves][2][16];                   // KV8: block's k / v scales
     extern __shared__ int32_t idx_s[];                                        // [kk]
     uint16_t* v_all = reinterpret_cast<uint16_t*>(smem);                    // during the loop
     float* o_all = reinterpret_cast<float*>(smem);                           // after the loop
@@ -199,8 +240,6 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     for (int j = threadIdx.x; j < nj; j += blockDim.x) idx_s[j] = idx_row[j];
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k);
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v);
     v8bf qb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -214,9 +253,14 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     const int j_begin = wave * per;
     const int j_end = min(j_begin + per, nj);
     const int nblk = j_end > j_begin ? (j_end - j_begin + 15) / 16 : 0;
-    const size_t row_elems = static_cast<size_t>(a.Hkv) * 128;
-    const uint16_t* kbase = kp + static_cast<size_t>(b) * a.n_k * row_elems + g * 128 + kg * 32;
-    const uint16_t* vbase = vp + static_cast<size_t>(b) * a.n_k * row_elems + g * 128 + kg * 32;
+    // this lane's 32 dims of kv head g: bytes [32*kg, 32*kg + 32) (E4M3) or
+    // elements of it (bf16) within each 128-dim row
+    constexpr int ESZ = KV8 ? 1 : 2;
+    const size_t row_bytes = static_cast<size_t>(a.Hkv) * 128 * ESZ;
+    const size_t base_off = static_cast<size_t>(b) * a.n_k * row_bytes + (g * 128 + kg * 32) * ESZ;
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + base_off;
+    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + base_off;
+    const size_t sc_base = static_cast<size_t>(b) * a.n_k * a.Hkv + g;
 
     float m_run = -__builtin_inff();
     float l_part = 0.0f;
@@ -225,33 +269,73 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     for (int t = 0; t < 8; ++t) o[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     __syncthreads();                               // idx_s is ready
 
-    v8bf kr[SLOTS][4], vr[SLOTS][4];
-    bool valid[SLOTS];
-    auto load_block = [&](int blk, v8bf* kd, v8bf* vd, bool& ok) {
+    GqaBlock<KV8> ring[SLOTS];
+    auto load_block = [&](int blk, GqaBlock<KV8>& d) {
         int j = j_begin + blk * 16 + col;
         int s = j < j_end ? idx_s[j] : -1;
-        ok = s >= 0 && s <= pos;
-        if (ok) {
-            const v8bf* ks = reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(s) * row_elems);
-            const v8bf* vs = reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(s) * row_elems);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) { kd[c] = ks[c]; vd[c] = vs[c]; }
+        d.ok = s >= 0 && s <= pos;
+        if constexpr (KV8) {
+            if (d.ok) {
+                const v4i* ks = reinterpret_cast<const v4i*>(kbase + static_cast<size_t>(s) * row_bytes);
+                const v4i* vs = reinterpret_cast<const v4i*>(vbase + static_cast<size_t>(s) * row_bytes);
+                d.k[0] = ks[0]; d.k[1] = ks[1]; d.v[0] = vs[0]; d.v[1] = vs[1];
+                d.ks = a.k_scale[sc_base + static_cast<size_t>(s) * a.Hkv];
+                d.vs = a.v_scale[sc_base + static_cast<size_t>(s) * a.Hkv];
+            } else {
+                d.k[0] = d.k[1] = d.v[0] = d.v[1] = v4i{0, 0, 0, 0};
+                d.ks = 0.0f; d.vs = 0.0f;
+            }
         } else {
+            if (d.ok) {
+                const v8bf* ks = reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(s) * row_bytes);
+                const v8bf* vs = reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(s) * row_bytes);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) { kd[c] = v8bf{}; vd[c] = v8bf{}; }
+                for (int c = 0; c < 4; ++c) { d.k[c] = ks[c]; d.v[c] = vs[c]; }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) { d.k[c] = v8bf{}; d.v[c] = v8bf{}; }
+            }
         }
     };
-    auto attend_block = [&](const v8bf* kc, const v8bf* vc, bool ok) {
+    auto stage_values = [&](const v8bf* vc) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<v8bf*>(v_s + col * kGqaVStride + kg * 32 + c * 8) = vc[c];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto attend_block = [&](const GqaBlock<KV8>& blkd) {
+        v8bf kc[4];
+        float ksc[4], vsc[4];
+        if constexpr (KV8) {
+            v8bf vc[4];
+            e4m3x32_to_bf16(blkd.v, vc);
+            // key c's scales go to slot c; lane (kg, col) reads keys 4kg..4kg+3
+            sc_w[wave][0][col] = blkd.ks;
+            sc_w[wave][1][col] = blkd.vs;
+            stage_values(vc);
+            e4m3x32_to_bf16(blkd.k, kc);
+            const v4f k4 = *reinterpret_cast<const v4f*>(&sc_w[wave][0][4 * kg]);
+            const v4f v4 = *reinterpret_cast<const v4f*>(&sc_w[wave][1][4 * kg]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) { ksc[v] = zscale * k4[v]; vsc[v] = v4[v]; }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kc[c] = blkd.k[c];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) { ksc[v] = zscale; vsc[v] = 1.0f; }
+        }
         v4f sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[c], qb[c], sacc, 0, 0, 0);
-        const uint64_t vm = __ballot(ok);
+        const uint64_t vm = __ballot(blkd.ok);
         float sv[4];
         float bm = -__builtin_inff();
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             int slot = 4 * kg + v;
-            sv[v] = ((vm >> slot) & 1ull) ? sacc[v] * zscale : -__builtin_inff();
+            sv[v] = ((vm >> slot) & 1ull) ? sacc[v] * ksc[v] : -__builtin_inff();
             bm = fmaxf(bm, sv[v]);
         }
         bm = wave_max_xor_16_32(bm);
@@ -268,16 +352,11 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
 #pragma unroll
         for (int t = 0; t < 8; ++t) o[t] *= corr;
 
-        // stage the 16 value rows of this wave, then read them transposed
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<v8bf*>(v_s + col * kGqaVStride + kg * 32 + c * 8) = vc[c];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // the 16 value rows of this wave, read transposed
+        if constexpr (!KV8) stage_values(blkd.v);
         v4bf pb;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) pb[v] = static_cast<__bf16>(p[v]);
+        for (int v = 0; v < 4; ++v) pb[v] = static_cast<__bf16>(KV8 ? p[v] * vsc[v] : p[v]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             v4bf va;
@@ -293,16 +372,15 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
 
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-        if (d < nblk) load_block(d, kr[d], vr[d], valid[d]);
+        if (d < nblk) load_block(d, ring[d]);
     for (int i0 = 0; i0 < nblk; i0 += SLOTS) {
 #pragma unroll
         for (int r = 0; r < SLOTS; ++r) {
             const int blk = i0 + r;
             if (blk < nblk) {
                 const int ahead = blk + DEPTH;
-                if (ahead < nblk) load_block(ahead, kr[(r + DEPTH) % SLOTS], vr[(r + DEPTH) % SLOTS],
-                                             valid[(r + DEPTH) % SLOTS]);
-                attend_block(kr[r], vr[r], valid[r]);
+                if (ahead < nblk) load_block(ahead, ring[(r + DEPTH) % SLOTS]);
+                attend_block(ring[r]);
             }
         }
     }
@@ -385,8 +463,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
         const int len = gqa_slice_len(a, s);
         float* part = static_cast<float*>(ws);
         const size_t idx_lds = static_cast<size_t>(len) * sizeof(int32_t);   // <= 8192 entries: 32 KiB
-        hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH>), dim3(a.Hkv, a.rows, s), dim3(kGqaWaves * 64),
-                           idx_lds, st, a, len, part);
+        if (a.kv_dtype == E4M3)
+            hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, true>), dim3(a.Hkv, a.rows, s),
+                               dim3(kGqaWaves * 64), idx_lds, st, a, len, part);
+        else
+            hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, false>), dim3(a.Hkv, a.rows, s),
+                               dim3(kGqaWaves * 64), idx_lds, st, a, len, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || s == 1) return e;
         return launch_attn_merge(a, s, part, st);
@@ -394,19 +476,20 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     if (attn_wide_eligible(a)) return launch_attn_wide(a, static_cast<float*>(ws), st);
     const size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +
                          static_cast<size_t>(kGenTK) * a.dv) * sizeof(float);
+    const void* fn = a.dtype == F32        ? reinterpret_cast<const void*>(k_attn_generic<F32, F32>)
+                     : a.kv_dtype == E4M3  ? reinterpret_cast<const void*>(k_attn_generic<BF16, E4M3>)
+                                           : reinterpret_cast<const void*>(k_attn_generic<BF16, BF16>);
     if (smem > 64 * 1024) {   // the latent shape stages ~104 KiB of rows
-        hipError_t e = a.dtype == F32
-            ? hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_generic<F32>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem))
-            : hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_generic<BF16>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
         if (e != hipSuccess) return e;
     }
     dim3 grid((G + kGenHC - 1) / kGenHC, a.Hkv, a.rows);
     if (a.dtype == F32)
-        hipLaunchKernelGGL(k_attn_generic<F32>, grid, dim3(kGenThreads), smem, st, a);
+        hipLaunchKernelGGL((k_attn_generic<F32, F32>), grid, dim3(kGenThreads), smem, st, a);
+    else if (a.kv_dtype == E4M3)
+        hipLaunchKernelGGL((k_attn_generic<BF16, E4M3>), grid, dim3(kGenThreads), smem, st, a);
     else
-        hipLaunchKernelGGL(k_attn_generic<BF16>, grid, dim3(kGenThreads), smem, st, a);
+        hipLaunchKernelGGL((k_attn_generic<BF16, BF16>), grid, dim3(kGenThreads), smem, st, a);
     return hipGetLastError();
 }
 

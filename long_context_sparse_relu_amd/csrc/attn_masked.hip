@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 bool attn_masked_eligible(const AttnArgs& a) {
-    if (!(a.dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128)) return false;
+    if (!(a.dtype == BF16 && a.kv_dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128)) return false;
     if (a.n_q < kMinQ || a.n_k > kMaskedMaxKeys) return false;
     // a key tile is shared by the block's 64 queries: worth it once a row keeps
     // more than 1/64 of what it sees (the average prefix of this problem)

@@ -218,7 +218,7 @@ static bool wide_shape(int dqk, int dv) {
 }
 
 bool attn_wide_eligible(const AttnArgs& a) {
-    return a.dtype == BF16 && wide_shape(a.dqk, a.dv) && (!a.latent || a.Hkv == 1);
+    return a.dtype == BF16 && a.kv_dtype == BF16 && wide_shape(a.dqk, a.dv) && (!a.latent || a.Hkv == 1);
 }
 
 // Slices per row: enough waves to cover the chip, at least two blocks each.

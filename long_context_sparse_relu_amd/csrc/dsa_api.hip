@@ -112,6 +112,15 @@ dsa_status_t check_attn(const dsa_problem_t* p) {
         return fail(DSA_E_INVALID, "q_heads (%d) must be a positive multiple of kv_heads (%d)", p->q_heads, p->kv_heads);
     if (p->attn_dtype != DSA_F32 && p->attn_dtype != DSA_BF16)
         return fail(DSA_E_UNSUPPORTED, "attn_dtype must be DSA_F32 or DSA_BF16 (got %d)", p->attn_dtype);
+    if (p->kv_dtype == DSA_FP8_E4M3) {
+        if (p->attn_dtype != DSA_BF16)
+            return fail(DSA_E_UNSUPPORTED, "an FP8 KV cache needs attn_dtype DSA_BF16");
+        if (!p->k_scale || (!p->kv_latent && !p->v_scale))
+            return fail(DSA_E_INVALID, "an FP8 KV cache needs k_scale (and v_scale unless kv_latent)");
+    } else if (p->kv_dtype != p->attn_dtype) {
+        return fail(DSA_E_INVALID, "kv_dtype (%d) must equal attn_dtype (%d) or be DSA_FP8_E4M3",
+                    p->kv_dtype, p->attn_dtype);
+    }
     if (p->d_qk < 1 || p->d_qk > 576 || p->d_v < 1 || p->d_v > 512)
         return fail(DSA_E_UNSUPPORTED, "need 1 <= d_qk <= 576 and 1 <= d_v <= 512 (got %d, %d)", p->d_qk, p->d_v);
     if (p->kv_latent) {
@@ -157,8 +166,10 @@ dsa::AttnArgs attn_args(const dsa_problem_t* p, const int32_t* idx, void* out, f
     dsa::AttnArgs a{};
     a.rows = rows_of(p); a.n_q = p->n_q; a.n_k = p->n_k; a.kk = p->top_k;
     a.Hq = p->q_heads; a.Hkv = p->kv_heads; a.dqk = p->d_qk; a.dv = p->d_v;
-    a.latent = p->kv_latent ? 1 : 0; a.dtype = p->attn_dtype;
+    a.latent = p->kv_latent ? 1 : 0; a.dtype = p->attn_dtype; a.kv_dtype = p->kv_dtype;
     a.q = p->q; a.k = p->k; a.v = p->v; a.idx = idx; a.q_pos = p->q_pos;
+    a.k_scale = p->kv_dtype == DSA_FP8_E4M3 ? p->k_scale : nullptr;
+    a.v_scale = p->kv_dtype == DSA_FP8_E4M3 && !p->kv_latent ? p->v_scale : nullptr;
     a.scale = p->softmax_scale; a.out = out; a.lse = lse;
     return a;
 }

@@ -70,9 +70,12 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 struct AttnArgs {
     int rows, n_q, n_k, kk;
     int Hq, Hkv, dqk, dv, latent, dtype;
+    int kv_dtype;          // dtype of k and v: dtype, or E4M3 (then dtype is BF16)
     const void* q;
     const void* k;
     const void* v;
+    const float* k_scale;  // [rows of k, Hkv] per-row scales of an E4M3 cache, else null
+    const float* v_scale;  // the same for v (null for latent rows, which use k_scale)
     const int32_t* idx;    // [rows, kk]
     const int32_t* q_pos;
     float scale;

@@ -19,8 +19,6 @@
 
 namespace dsa {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ v8i load_split32(const uint8_t* row, int g) {
     v4i lo = *reinterpret_cast<const v4i*>(row + 16 * g);
     v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * g);

@@ -69,7 +69,7 @@ def _problem(**over):
     fake = 0x7F0000000000  # never dereferenced: every call below fails validation first
     p.iq = p.ik = p.iw = p.iq_scale = p.ik_scale = fake
     p.q_heads, p.kv_heads, p.d_qk, p.d_v, p.kv_latent = 32, 4, 128, 128, 0
-    p.attn_dtype = dsa.BF16
+    p.attn_dtype = p.kv_dtype = dsa.BF16
     p.q = p.k = p.v = fake
     p.softmax_scale = 0.088
     p.top_k = 2048
@@ -98,6 +98,11 @@ FAKE = ctypes.c_void_p(0x7F0000000000)
     (dict(kv_latent=1), dsa.E_INVALID),             # latent needs kv_heads == 1
     (dict(d_qk=1024), dsa.E_UNSUPPORTED),
     (dict(attn_dtype=dsa.FP8_E4M3), dsa.E_UNSUPPORTED),
+    (dict(kv_dtype=dsa.F32), dsa.E_INVALID),         # neither attn_dtype nor FP8
+    (dict(kv_dtype=dsa.FP8_E4M3), dsa.E_INVALID),    # FP8 cache without scales
+    (dict(kv_dtype=dsa.FP8_E4M3, k_scale=0x7F0000000000), dsa.E_INVALID),   # no v_scale
+    (dict(kv_dtype=dsa.FP8_E4M3, attn_dtype=dsa.F32, k_scale=0x7F0000000000,
+          v_scale=0x7F0000000000), dsa.E_UNSUPPORTED),                        # FP8 cache needs bf16 q
     (dict(softmax_scale=0.0), dsa.E_INVALID),
     (dict(softmax_scale=float("inf")), dsa.E_INVALID),
     (dict(n_q=2), dsa.E_INVALID),                   # decode takes one query row

@@ -25,7 +25,8 @@ def _problem(inp, row_sel=None):
     """dsa problem for the whole batch, or for query rows `row_sel` (via q_pos)."""
     kw = dict(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=inp["top_k"], q=inp["q"],
               k=inp["k"], v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-              softmax_scale=inp["scale"], latent_dv=inp["latent_dv"])
+              softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
+              k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
     if row_sel is not None:
         sel = torch.as_tensor(row_sel, dtype=torch.long, device=DEV)
         for name in ("iq", "iw", "q", "iq_scale"):
@@ -85,15 +86,19 @@ def run_case(inp, seqs, rows, fused="prefill", check_e2e=True):
         sub = _problem({**inp, **{n: inp[n][b:b + 1] for n in
                                   ("iq", "iw", "q", "k", "ik", "pos")},
                         "v": None if inp["v"] is None else inp["v"][b:b + 1],
-                        "iq_scale": None if inp["iq_scale"] is None else inp["iq_scale"][b:b + 1],
-                        "ik_scale": None if inp["ik_scale"] is None else inp["ik_scale"][b:b + 1]},
+                        **{n: None if inp.get(n) is None else inp[n][b:b + 1]
+                           for n in ("iq_scale", "ik_scale", "k_scale", "v_scale")}},
                        row_sel=rows)
         o_idx_dev = torch.from_numpy(ora_idx).to(DEV).reshape(1, len(rows), k).contiguous()
         g_out, g_lse = dsa.sparse_attn(sub, o_idx_dev)
         torch.cuda.synchronize()
         v = None if ov["v"] is None else ov["v"][j]
+        kv = {}
+        if inp["kv_dtype"] == "e4m3":
+            kv = dict(kv_dtype="e4m3", k_scale=ov["k_scale"][j],
+                      v_scale=None if ov["v_scale"] is None else ov["v_scale"][j])
         ora_out, ora_lse = oracle.sparse_attn(ov["q"][j][rows], ov["k"][j], v, ora_idx, adt,
-                                              inp["scale"], pos, inp["latent_dv"])
+                                              inp["scale"], pos, inp["latent_dv"], **kv)
         stats["attn_err"] = max(stats["attn_err"],
                                 check_attn(_host(g_out[0]), _host(g_lse[0]), ora_out, ora_lse, adt))
         if check_e2e:
@@ -135,6 +140,16 @@ EDGE_CASES = {
                                   q_heads=2, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16"),
     "bf16_generic_d64": dict(n_q=50, n_k=2000, idx_heads=8, top_k=128, q_heads=8, kv_heads=2,
                              d_qk=64, d_v=64, attn_dtype="bf16", idx_dtype="bf16"),
+    # FP8 (E4M3) main KV cache with per-(token, kv head) scales
+    "fp8kv_gqa_decode_ragged": dict(B=5, n_q=1, n_k=12345, idx_heads=16, idx_dtype="e4m3", top_k=2048,
+                                    q_heads=32, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16",
+                                    kv_dtype="e4m3"),
+    "fp8kv_prefill_mha": dict(n_q=70, n_k=900, idx_heads=8, idx_dtype="bf16", top_k=100, q_heads=4,
+                              kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16", kv_dtype="e4m3"),
+    "fp8kv_latent": dict(B=2, n_q=1, n_k=4000, idx_heads=16, idx_dtype="e4m3", top_k=512, q_heads=20,
+                         kv_heads=1, d_qk=576, d_v=512, latent=True, attn_dtype="bf16", kv_dtype="e4m3"),
+    "fp8kv_generic_d64": dict(n_q=20, n_k=1500, idx_heads=4, top_k=77, q_heads=8, kv_heads=2,
+                              d_qk=64, d_v=64, attn_dtype="bf16", idx_dtype="bf16", kv_dtype="e4m3"),
 }
 
 
@@ -361,6 +376,38 @@ def test_decode_128k_sampled():
     """The benchmarked workload, in the launch configuration the benchmark times."""
     inp = make_inputs(spec("decode_128k"), device=DEV, seed=0)
     run_case(inp, [0, 17, 63], [0], fused="decode")
+
+
+def test_decode_128k_fp8kv_sampled():
+    """The 128K decode workload over an E4M3 main KV cache."""
+    inp = make_inputs(spec("decode_128k_fp8kv"), device=DEV, seed=0)
+    run_case(inp, [0, 31, 63], [0], fused="decode")
+
+
+def test_fp8kv_scales_act_per_row():
+    """Scaling one kept row's value scale changes out (as the oracle says) and never lse."""
+    sp = custom_spec(name="fp8kv_scale", B=1, n_q=1, n_k=3000, idx_heads=16, idx_dtype="e4m3",
+                     top_k=256, q_heads=16, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16",
+                     kv_dtype="e4m3")
+    inp = make_inputs(sp, device=DEV, seed=3)
+    prob = _problem(inp)
+    idx = dsa.topk(prob, dsa.index_scores(prob))
+    out0, lse0 = dsa.sparse_attn(prob, idx)
+    torch.cuda.synchronize()
+    s = int(idx[0, 0, 5])
+    inp2 = dict(inp)
+    inp2["v_scale"] = inp["v_scale"].clone()
+    inp2["v_scale"][0, s] *= 64.0
+    out1, lse1 = dsa.sparse_attn(_problem(inp2), idx)
+    torch.cuda.synchronize()
+    assert torch.equal(lse0, lse1), "the value scale must not touch the softmax"
+    ov = oracle_view(inp2, [0])
+    pos = ov["pos"][0].astype(np.int64)
+    ora_out, ora_lse = oracle.sparse_attn(ov["q"][0], ov["k"][0], ov["v"][0], idx[0].cpu().numpy(), "bf16",
+                                          inp["scale"], pos, None, kv_dtype="e4m3",
+                                          k_scale=ov["k_scale"][0], v_scale=ov["v_scale"][0])
+    check_attn(_host(out1[0]), _host(lse1[0]), ora_out, ora_lse, "bf16")
+    assert (out1.float() - out0.float()).abs().max().item() > 1e-3
 
 
 def test_decode_1m_sampled():
