@@ -211,7 +211,8 @@ __device__ __forceinline__ void e4m3x32_to_bf16(const v4i* w, v8bf* out) {
 // weights before their bf16 rounding (p * vs * code), so the running sum stays
 // the plain softmax denominator.
 template <int DEPTH, bool KV8>
-__global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, int slice_len, float* part) {
+__global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, int row0, int nrows, int nsplit, int slice_len,
+                                                                           float* part) {
     __shared__ __align__(16) unsigned char smem[kGqaWaves * 16 * 128 * 4];   // 64 KiB
     __shared__ float m_w[kGqaWaves][16], l_w[kGqaWaves][16];
     __shared__ __align__(16) float sc_w[kGqaWaves][2][16];                   // KV8: block's k / v scales
@@ -221,10 +222,27 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     constexpr int SLOTS = DEPTH + 1;
 
     const int G = a.Hq / a.Hkv;
-    const int g = blockIdx.x;
-    const int row = blockIdx.y;
-    const int nsplit = gridDim.z;
-    const int sl = blockIdx.z;                     // this workgroup's slice of the index list
+    // One workgroup per (kv head, row, slice).  Consecutive workgroup ids go to
+    // the 8 XCDs in turn; when the (row, slice) units divide by 8, the ids are
+    // mapped so that the kv heads of one unit land on the same XCD, back to
+    // back: they gather the same tokens, and the row scales of an E4M3 cache
+    // (one 16-byte group per token for 4 kv heads) are then read into that
+    // XCD's L2 once instead of once per kv head.
+    int g, unit;
+    {
+        const int id = blockIdx.x;
+        const int units = nrows * nsplit;
+        if ((units & 7) == 0) {
+            const int k = id >> 3;
+            g = k % a.Hkv;
+            unit = (k / a.Hkv) * 8 + (id & 7);
+        } else {
+            g = id % a.Hkv;
+            unit = id / a.Hkv;
+        }
+    }
+    const int row = row0 + unit / nsplit;          // rows [row0, row0 + nrows) in this launch
+    const int sl = unit % nsplit;                  // this workgroup's slice of the index list
     const int jb = sl * slice_len;
     const int nj = max(0, min(slice_len, a.kk - jb));
     const int b = row / a.n_q;
@@ -237,7 +255,6 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     uint16_t* v_s = v_all + wave * 16 * kGqaVStride;
 
     const int32_t* idx_row = a.idx + static_cast<size_t>(row) * a.kk + jb;
-    for (int j = threadIdx.x; j < nj; j += blockDim.x) idx_s[j] = idx_row[j];
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     v8bf qb[4];
@@ -267,35 +284,49 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     v4f o[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    __syncthreads();                               // idx_s is ready
+
+    // each wave stages its own entries [j_begin, j_end) of the index list,
+    // all loads of a round before any store, so no workgroup barrier is needed
+    for (int j0 = j_begin; j0 < j_end; j0 += 256) {
+        int e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = idx_row[min(j0 + lane + 64 * u, j_end - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (j0 + lane + 64 * u < j_end) idx_s[j0 + lane + 64 * u] = e[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     GqaBlock<KV8> ring[SLOTS];
+    // Every lane loads, whatever its entry: an invalid one (past the list, < 0
+    // or > pos) reads token 0 of the sequence instead, and attend_block drops
+    // it (zeroed operands, masked score).  With no branch around the loads the
+    // compiler's wait counts stay exact, so a block's wait does not also wait
+    // for the blocks loaded after it.
     auto load_block = [&](int blk, GqaBlock<KV8>& d) {
-        int j = j_begin + blk * 16 + col;
-        int s = j < j_end ? idx_s[j] : -1;
-        d.ok = s >= 0 && s <= pos;
+        const int j = j_begin + blk * 16 + col;
+        const int s = idx_s[min(j, j_end - 1)];
+        d.ok = j < j_end && s >= 0 && s <= pos;
+        const size_t sr = d.ok ? static_cast<size_t>(s) : 0;
+        // the loads go out in one fixed order wherever a block is loaded, so
+        // that the wait counts agree on every path into the loop
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (KV8) {
-            if (d.ok) {
-                const v4i* ks = reinterpret_cast<const v4i*>(kbase + static_cast<size_t>(s) * row_bytes);
-                const v4i* vs = reinterpret_cast<const v4i*>(vbase + static_cast<size_t>(s) * row_bytes);
-                d.k[0] = ks[0]; d.k[1] = ks[1]; d.v[0] = vs[0]; d.v[1] = vs[1];
-                d.ks = a.k_scale[sc_base + static_cast<size_t>(s) * a.Hkv];
-                d.vs = a.v_scale[sc_base + static_cast<size_t>(s) * a.Hkv];
-            } else {
-                d.k[0] = d.k[1] = d.v[0] = d.v[1] = v4i{0, 0, 0, 0};
-                d.ks = 0.0f; d.vs = 0.0f;
-            }
+            const v4i* ks = reinterpret_cast<const v4i*>(kbase + sr * row_bytes);
+            const v4i* vs = reinterpret_cast<const v4i*>(vbase + sr * row_bytes);
+            const float* kq = a.k_scale + sc_base + sr * a.Hkv;
+            const float* vq = a.v_scale + sc_base + sr * a.Hkv;
+            d.k[0] = ks[0]; d.k[1] = ks[1]; d.v[0] = vs[0]; d.v[1] = vs[1];
+            d.ks = *kq; d.vs = *vq;
         } else {
-            if (d.ok) {
-                const v8bf* ks = reinterpret_cast<const v8bf*>(kbase + static_cast<size_t>(s) * row_bytes);
-                const v8bf* vs = reinterpret_cast<const v8bf*>(vbase + static_cast<size_t>(s) * row_bytes);
+            const v8bf* ks = reinterpret_cast<const v8bf*>(kbase + sr * row_bytes);
+            const v8bf* vs = reinterpret_cast<const v8bf*>(vbase + sr * row_bytes);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) { d.k[c] = ks[c]; d.v[c] = vs[c]; }
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) { d.k[c] = v8bf{}; d.v[c] = v8bf{}; }
-            }
+            for (int c = 0; c < 4; ++c) { d.k[c] = ks[c]; d.v[c] = vs[c]; }
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto stage_values = [&](const v8bf* vc) {
 #pragma unroll
@@ -305,10 +336,19 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
-    auto attend_block = [&](const GqaBlock<KV8>& blkd) {
+    auto attend_block = [&](GqaBlock<KV8>& blkd) {
         v8bf kc[4];
         float ksc[4], vsc[4];
+        // an invalid entry's operands are zeroed, so that whatever token 0
+        // holds cannot reach the sums
         if constexpr (KV8) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                blkd.k[c] = blkd.ok ? blkd.k[c] : v4i{0, 0, 0, 0};
+                blkd.v[c] = blkd.ok ? blkd.v[c] : v4i{0, 0, 0, 0};
+            }
+            blkd.ks = blkd.ok ? blkd.ks : 0.0f;
+            blkd.vs = blkd.ok ? blkd.vs : 0.0f;
             v8bf vc[4];
             e4m3x32_to_bf16(blkd.v, vc);
             // key c's scales go to slot c; lane (kg, col) reads keys 4kg..4kg+3
@@ -322,7 +362,11 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
             for (int v = 0; v < 4; ++v) { ksc[v] = zscale * k4[v]; vsc[v] = v4[v]; }
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kc[c] = blkd.k[c];
+            for (int c = 0; c < 4; ++c) {
+                blkd.k[c] = blkd.ok ? blkd.k[c] : v8bf{};
+                blkd.v[c] = blkd.ok ? blkd.v[c] : v8bf{};
+                kc[c] = blkd.k[c];
+            }
 #pragma unroll
             for (int v = 0; v < 4; ++v) { ksc[v] = zscale; vsc[v] = 1.0f; }
         }
@@ -357,12 +401,13 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
         v4bf pb;
 #pragma unroll
         for (int v = 0; v < 4; ++v) pb[v] = static_cast<__bf16>(KV8 ? p[v] * vsc[v] : p[v]);
+        // va = V[4kg + v][16t + col], v < 4: lane (kg, col) addresses row
+        // 4kg + col/4 at dims 16t + 4(col%4)..+3 and the transposing read
+        // hands every lane its own dim of the group's four rows
+        const uint16_t* trp = v_s + (4 * kg + (col >> 2)) * kGqaVStride + 4 * (col & 3);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            v4bf va;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                va[v] = *reinterpret_cast<const __bf16*>(v_s + (4 * kg + v) * kGqaVStride + 16 * t + col);
+            const v4bf va = lds_read_tr16(trp + 16 * t);
             o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[t], 0, 0, 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -370,16 +415,18 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
+    if (nblk > 0) {
+        // whole turns of the ring: blocks past nblk have no valid entry and
+        // change nothing
+        const int nblk_pad = (nblk + SLOTS - 1) / SLOTS * SLOTS;
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (d < nblk) load_block(d, ring[d]);
-    for (int i0 = 0; i0 < nblk; i0 += SLOTS) {
+        for (int d = 0; d < DEPTH; ++d) load_block(d, ring[d]);
+        for (int i0 = 0; i0 < nblk_pad; i0 += SLOTS) {
 #pragma unroll
-        for (int r = 0; r < SLOTS; ++r) {
-            const int blk = i0 + r;
-            if (blk < nblk) {
-                const int ahead = blk + DEPTH;
-                if (ahead < nblk) load_block(ahead, ring[(r + DEPTH) % SLOTS]);
+            for (int r = 0; r < SLOTS; ++r) {
+                load_block(i0 + r + DEPTH, ring[(r + DEPTH) % SLOTS]);
+                // keep the block's use (and its wait) after the loads ahead
+                __builtin_amdgcn_sched_barrier(0);
                 attend_block(ring[r]);
             }
         }
@@ -463,13 +510,22 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
         const int len = gqa_slice_len(a, s);
         float* part = static_cast<float*>(ws);
         const size_t idx_lds = static_cast<size_t>(len) * sizeof(int32_t);   // <= 8192 entries: 32 KiB
-        if (a.kv_dtype == E4M3)
-            hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, true>), dim3(a.Hkv, a.rows, s),
-                               dim3(kGqaWaves * 64), idx_lds, st, a, len, part);
-        else
-            hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, false>), dim3(a.Hkv, a.rows, s),
-                               dim3(kGqaWaves * 64), idx_lds, st, a, len, part);
-        hipError_t e = hipGetLastError();
+        // a 1-D grid, in launches of at most 2^22 workgroups (2^31 work-items)
+        const int64_t per_row = static_cast<int64_t>(a.Hkv) * s;
+        int chunk = static_cast<int>(((int64_t{1} << 22) / per_row) & ~int64_t{7});
+        if (chunk < 8) chunk = 8;
+        hipError_t e = hipSuccess;
+        for (int r0 = 0; r0 < a.rows && e == hipSuccess; r0 += chunk) {
+            const int nr = a.rows - r0 < chunk ? a.rows - r0 : chunk;
+            const dim3 grid(static_cast<unsigned>(per_row * nr));
+            if (a.kv_dtype == E4M3)
+                hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, true>), grid, dim3(kGqaWaves * 64), idx_lds,
+                                   st, a, r0, nr, s, len, part);
+            else
+                hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, false>), grid, dim3(kGqaWaves * 64), idx_lds,
+                                   st, a, r0, nr, s, len, part);
+            e = hipGetLastError();
+        }
         if (e != hipSuccess || s == 1) return e;
         return launch_attn_merge(a, s, part, st);
     }

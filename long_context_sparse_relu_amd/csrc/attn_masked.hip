@@ -74,20 +74,9 @@ __global__ __launch_bounds__(256) void k_sel_bitmap(AttnArgs a, uint32_t* bm, in
 // (a/4) of the four and dims 4(a%4)..4(a%4)+3 of the group's 16 dims, and
 // every lane ends with its own dim over the four keys.  The next tile's rows
 // are fetched into registers while the current one is multiplied.
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short lds_s4_t;
-typedef __attribute__((address_space(3))) lds_s4_t* lds_s4_ptr;
-typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr;
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
-    lds_s4_ptr lp = (lds_s4_ptr)((lds_u16_ptr)(const_cast<uint16_t*>(p)));
-    lds_s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp);
-    v4bf r;
-    __builtin_memcpy(&r, &v, sizeof r);
-    return r;
-}
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
     // two buffers: the next tile is staged into one while the other is read

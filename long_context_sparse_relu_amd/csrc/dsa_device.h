@@ -70,6 +70,23 @@ __device__ __forceinline__ int row_pos(const int32_t* q_pos, int row, int n_q, i
     return p < n_k - 1 ? p : n_k - 1;  // may be negative: nothing visible
 }
 
+// ds_read_b64_tr_b16: each lane addresses an 8-byte chunk (4 bf16) of LDS;
+// within each 16-lane group, lane i receives element i%4 of the chunks
+// addressed by lanes i/4, 4+i/4, 8+i/4 and 12+i/4 of the group, in that order.
+// With lane a of a group addressing row a/4 of four rows at column 4(a%4),
+// every lane ends with its own column of the four rows.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short lds_s4_t;
+typedef __attribute__((address_space(3))) lds_s4_t* lds_s4_ptr;
+typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr;
+
+__device__ __forceinline__ v4bf lds_read_tr16(const uint16_t* p) {
+    lds_s4_ptr lp = (lds_s4_ptr)((lds_u16_ptr)(const_cast<uint16_t*>(p)));
+    lds_s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp);
+    v4bf r;
+    __builtin_memcpy(&r, &v, sizeof r);
+    return r;
+}
+
 // Exchanges between the four 16-lane rows of a wave, on the VALU: with both
 // operands equal, v_permlane16_swap leaves row r's lanes holding rows 2(r/2)
 // and 2(r/2)+1 in its two results, and v_permlane32_swap does the same for
