@@ -88,8 +88,22 @@ typedef enum {
     DSA_OP_TOPK = 1,
     DSA_OP_SPARSE_ATTN = 2,
     DSA_OP_PREFILL = 3,
-    DSA_OP_DECODE = 4
+    DSA_OP_DECODE = 4,
+    DSA_OP_DENSE_ATTN = 5
 } dsa_op_t;
+
+/* How the attention over the kept rows is computed; every mode gives the same
+ * result up to fp32 rounding order.  "DeepSeek-V3.2-Exp 稀疏注意力机制(DSA)技术深度
+ * 解析" (sheratonhq.com), section 1, says short sequences run DSA as masked MHA:
+ * dense attention whose mask admits each query's selected keys. */
+typedef enum {
+    DSA_ATTN_AUTO = 0,       /* the library picks (the masked form for long prefill blocks
+                                whose selections cover enough of each key tile) */
+    DSA_ATTN_GATHER = 1,     /* gather each query's kept rows */
+    DSA_ATTN_MASKED = 2      /* masked MHA: every key tile up to the block's last visible
+                                key, the selection as a mask (bf16, d_qk = d_v = 128,
+                                not latent, bf16 KV; else DSA_E_UNSUPPORTED) */
+} dsa_attn_mode_t;
 
 /* One problem: B sequences, each with n_q query rows and n_k key rows. */
 typedef struct {
@@ -124,6 +138,7 @@ typedef struct {
     float softmax_scale;      /* > 0, e.g. 1/sqrt(d_qk) */
 
     int32_t top_k;            /* k, 1..8192 */
+    int32_t attn_mode;        /* dsa_attn_mode_t */
 } dsa_problem_t;
 
 /* DSA_ABI_VERSION of the loaded library. */
@@ -154,7 +169,11 @@ dsa_status_t dsa_sparse_attn(const dsa_problem_t *p, const int32_t *idx, void *o
 /* Fused prefill: indexer, top-k and sparse attention for every query row.  The
  * full [n_q, n_k] score matrix is never held in memory: scores are produced
  * and consumed one bounded block of query rows at a time inside the
- * workspace.  idx_out: [B, n_q, top_k] or NULL (then kept in the workspace). */
+ * workspace.  idx_out: [B, n_q, top_k] or NULL (then kept in the workspace).
+ * A row with pos(t) + 1 <= top_k keeps every visible key whatever the scores,
+ * so when q_pos is NULL, blocks of such rows skip the indexer and the top-k
+ * (their selection is written as 0..pos(t) directly) and a problem made only
+ * of such rows is dense causal attention. */
 dsa_status_t dsa_prefill(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -162,6 +181,14 @@ dsa_status_t dsa_prefill(const dsa_problem_t *p, void *out, float *lse, int32_t 
  * own key row is already the last cached row, unless q_pos says otherwise). */
 dsa_status_t dsa_decode(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense causal attention: every query row over all its visible keys, the
+ * attention DSA reduces to when top_k >= pos(t) + 1 and the baseline the
+ * pages measure DSA against.  Uses the main-attention fields only (q, k, v,
+ * heads, dims, softmax_scale, q_pos); bf16, d_qk = d_v = 128, not latent,
+ * bf16 KV (else DSA_E_UNSUPPORTED).  out: [B, n_q, Hq, d_v] bf16; lse:
+ * [B, n_q, Hq] fp32 or NULL.  Needs no workspace (dsa_workspace_bytes = 0). */
+dsa_status_t dsa_dense_attn(const dsa_problem_t *p, void *out, float *lse, hipStream_t stream);
 
 /* Phase timing of the fused entry points, for profiling.
  * dsa_phase_timing(1) makes every later dsa_prefill / dsa_decode call record

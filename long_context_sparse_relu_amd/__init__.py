@@ -23,13 +23,14 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE = 0, -1, -2, -3, -4
 F32, BF16, FP8_E4M3 = 0, 1, 2
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE = 0, 1, 2, 3, 4
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE_ATTN = 0, 1, 2, 3, 4, 5
+ATTN_AUTO, ATTN_GATHER, ATTN_MASKED = 0, 1, 2
 ABI_VERSION = 2
 
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
 EXPORTED = ("dsa_abi_version", "dsa_workspace_bytes", "dsa_index_scores", "dsa_topk",
-            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_phase_timing", "dsa_phase_times",
+            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_dense_attn", "dsa_phase_timing", "dsa_phase_times",
             "dsa_status_str", "dsa_last_error")
 # dsa_phase_t, in order
 PHASES = ("prep", "index", "topk", "attn")
@@ -50,6 +51,7 @@ class Problem(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("softmax_scale", ctypes.c_float),
         ("top_k", ctypes.c_int32),
+        ("attn_mode", ctypes.c_int32),
     ]
 
 
@@ -86,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp]
     lib.dsa_decode.restype = ctypes.c_int
     lib.dsa_decode.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.dsa_dense_attn.restype = ctypes.c_int
+    lib.dsa_dense_attn.argtypes = [P, vp, vp, vp]
     lib.dsa_phase_timing.restype = ctypes.c_int
     lib.dsa_phase_timing.argtypes = [ctypes.c_int]
     lib.dsa_phase_times.restype = ctypes.c_int
@@ -154,7 +158,8 @@ def _contig(name, t, device, dtypes=None):
 
 
 def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik_scale=None,
-                 q_pos=None, softmax_scale=None, latent_dv=None, k_scale=None, v_scale=None) -> DSAProblem:
+                 q_pos=None, softmax_scale=None, latent_dv=None, k_scale=None, v_scale=None,
+                 attn_mode: int = ATTN_AUTO) -> DSAProblem:
     """Describe one batch: see include/dsa.h for the layouts.
 
     iq [B,n_q,H,128], ik [B,n_k,128] (fp32 | bf16 | float8_e4m3fn, same dtype),
@@ -163,7 +168,7 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     latent_dv (then the value is k[..., :latent_dv] and Hkv must be 1),
     q_pos [B,n_q] int32 or None.  k and v have q's dtype, or float8_e4m3fn
     (an FP8 cache, q bf16) with k_scale [B,n_k,Hkv] and, unless latent,
-    v_scale [B,n_k,Hkv] fp32.
+    v_scale [B,n_k,Hkv] fp32.  attn_mode: ATTN_AUTO, ATTN_GATHER or ATTN_MASKED.
     """
     device = iq.device
     idt = (torch.float32, torch.bfloat16, torch.float8_e4m3fn)
@@ -194,6 +199,7 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     p.iq_scale = None if iq_scale is None else iq_scale.data_ptr()
     p.ik_scale = None if ik_scale is None else ik_scale.data_ptr()
     p.top_k = int(top_k)
+    p.attn_mode = int(attn_mode)
     tensors = dict(iq=iq, ik=ik, iw=iw, iq_scale=iq_scale, ik_scale=ik_scale, q_pos=q_pos)
     if q is not None:
         adt = (torch.float32, torch.bfloat16)
@@ -301,6 +307,13 @@ def prefill(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, 
 
 def decode(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, stream=None):
     return _fused(load_library().dsa_decode, OP_DECODE, prob, out, lse, idx_out, workspace, stream)
+
+
+def dense_attn(prob: DSAProblem, out=None, lse=None, stream=None):
+    """(out, lse) of dense causal attention: every query over all its visible keys."""
+    out, lse = _out_tensors(prob, out, lse)
+    _check(load_library().dsa_dense_attn(prob.ref(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def phase_timing(enable: bool):

@@ -19,6 +19,9 @@
 //           then O^T += V^T P^T, also on v_mfma_f32_32x32x16_bf16, with V^T
 //           read from the row-major V tile by transposing LDS reads.  A wave
 //           skips a tile none of its queries keeps a key of.
+// When every row keeps all its visible keys (top_k >= pos(t) + 1, or the
+// dense causal attention entry) the mask is causal only: no bit rows are built
+// or read, and the same kernel is plain causal flash attention.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -36,7 +39,6 @@ constexpr int kKB = 64;            // keys per tile
 constexpr int kStr = 136;          // K tile
 constexpr int kStrV = 160;         // V tile
 constexpr int kMinQ = 64;          // fewest query rows this path takes
-constexpr int kMaskedMaxKeys = 1 << 18;
 }
 
 // Words (uint32) per bit row: keys rounded up to 64.
@@ -78,6 +80,16 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+// The 32 bits of keys key0..key0+31 that a causal mask admits for a query
+// whose last visible key is pos.
+__device__ __forceinline__ uint32_t causal_word(int pos, int key0) {
+    const int n = pos - key0 + 1;
+    return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u));
+}
+
+// DENSE: every query keeps all its visible keys; the mask is causal and no
+// bit rows are read (bm may be null).
+template <bool DENSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
     // two buffers: the next tile is staged into one while the other is read
     // (one barrier per tile)
@@ -124,7 +136,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const size_t rstride = static_cast<size_t>(a.Hkv) * 128;
     const uint16_t* kbase = kp + static_cast<size_t>(b) * a.n_k * rstride + g * 128;
     const uint16_t* vbase = vp + static_cast<size_t>(b) * a.n_k * rstride + g * 128;
-    const uint32_t* brow = bm + static_cast<size_t>(row) * words;
+    const uint32_t* brow = DENSE ? nullptr : bm + static_cast<size_t>(row) * words;
 
     // loader: 256 threads x 4 rows x 16 B of K and of V per tile; rows past
     // n_k read row n_k-1 and are zeroed when staged
@@ -141,7 +153,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             pk[r] = *reinterpret_cast<const v8bf*>(kbase + key * rstride + lcol);
             pv[r] = *reinterpret_cast<const v8bf*>(vbase + key * rstride + lcol);
         }
-        const uint32_t x0 = brow[2 * tile], x1 = brow[2 * tile + 1];
+        uint32_t x0, x1;
+        if constexpr (DENSE) {
+            x0 = causal_word(pos, pkey0);
+            x1 = causal_word(pos, pkey0 + 32);
+        } else {
+            x0 = brow[2 * tile];
+            x1 = brow[2 * tile + 1];
+        }
         pw0 = live_q ? x0 : 0u;
         pw1 = live_q ? x1 : 0u;
     };
@@ -289,7 +308,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 bool attn_masked_eligible(const AttnArgs& a) {
     if (!(a.dtype == BF16 && a.kv_dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128)) return false;
-    if (a.n_q < kMinQ || a.n_k > kMaskedMaxKeys) return false;
+    if (a.mode == ATTN_GATHER) return false;
+    if (a.all_visible) return a.mode == ATTN_MASKED || a.n_q >= kMinQ;   // causal mask, no bit rows
+    if (a.n_k > kMaskedMaxKeys) return false;
+    if (a.mode == ATTN_MASKED) return true;
+    if (a.n_q < kMinQ) return false;
     // a key tile is shared by the block's 64 queries: worth it once a row keeps
     // more than 1/64 of what it sees (the average prefix of this problem)
     const double avg_vis = static_cast<double>(a.n_k) - 0.5 * a.n_q;
@@ -297,18 +320,23 @@ bool attn_masked_eligible(const AttnArgs& a) {
 }
 
 size_t attn_masked_workspace_bytes(const AttnArgs& a) {
-    return static_cast<size_t>(a.rows) * bitmap_words(a.n_k) * sizeof(uint32_t);
+    // the bit rows (none when every row keeps all its visible keys)
+    return a.all_visible ? 0 : static_cast<size_t>(a.rows) * bitmap_words(a.n_k) * sizeof(uint32_t);
 }
 
 hipError_t launch_attn_masked(const AttnArgs& a, uint32_t* bm, hipStream_t st) {
+    const int B = a.rows / a.n_q;
+    const dim3 grid((a.n_q + kQB - 1) / kQB, a.Hq, B);
+    if (a.all_visible) {
+        hipLaunchKernelGGL(k_attn_masked_d128<true>, grid, dim3(256), 0, st, a, static_cast<const uint32_t*>(nullptr), 0);
+        return hipGetLastError();
+    }
     const int words = bitmap_words(a.n_k);
     const size_t lds = static_cast<size_t>(words) * sizeof(uint32_t);   // <= 32 KiB
     hipLaunchKernelGGL(k_sel_bitmap, dim3(a.rows), dim3(256), lds, st, a, bm, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int B = a.rows / a.n_q;
-    const dim3 grid((a.n_q + kQB - 1) / kQB, a.Hq, B);
-    hipLaunchKernelGGL(k_attn_masked_d128, grid, dim3(256), 0, st, a, static_cast<const uint32_t*>(bm), words);
+    hipLaunchKernelGGL(k_attn_masked_d128<false>, grid, dim3(256), 0, st, a, static_cast<const uint32_t*>(bm), words);
     return hipGetLastError();
 }
 

@@ -107,6 +107,15 @@ dsa_status_t check_topk(const dsa_problem_t* p) {
     return DSA_OK;
 }
 
+static_assert(DSA_ATTN_AUTO == dsa::ATTN_AUTO && DSA_ATTN_GATHER == dsa::ATTN_GATHER &&
+              DSA_ATTN_MASKED == dsa::ATTN_MASKED, "attention modes");
+
+// Shapes the masked (dense tile) kernels take.
+bool masked_shape(const dsa_problem_t* p) {
+    return p->attn_dtype == DSA_BF16 && p->kv_dtype == DSA_BF16 && !p->kv_latent && p->d_qk == 128 &&
+           p->d_v == 128;
+}
+
 dsa_status_t check_attn(const dsa_problem_t* p) {
     if (p->q_heads < 1 || p->kv_heads < 1 || p->q_heads % p->kv_heads)
         return fail(DSA_E_INVALID, "q_heads (%d) must be a positive multiple of kv_heads (%d)", p->q_heads, p->kv_heads);
@@ -132,6 +141,11 @@ dsa_status_t check_attn(const dsa_problem_t* p) {
     if (!p->q || !p->k) return fail(DSA_E_INVALID, "q and k are required");
     if (!(p->softmax_scale > 0.0f) || !std::isfinite(p->softmax_scale))
         return fail(DSA_E_INVALID, "softmax_scale must be finite and > 0");
+    if (p->attn_mode != DSA_ATTN_AUTO && p->attn_mode != DSA_ATTN_GATHER && p->attn_mode != DSA_ATTN_MASKED)
+        return fail(DSA_E_INVALID, "attn_mode %d is not a dsa_attn_mode_t", p->attn_mode);
+    if (p->attn_mode == DSA_ATTN_MASKED && (!masked_shape(p) || p->n_k > dsa::kMaskedMaxKeys))
+        return fail(DSA_E_UNSUPPORTED, "masked attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows "
+                    "and n_k <= %d", dsa::kMaskedMaxKeys);
     return DSA_OK;
 }
 
@@ -171,7 +185,24 @@ dsa::AttnArgs attn_args(const dsa_problem_t* p, const int32_t* idx, void* out, f
     a.k_scale = p->kv_dtype == DSA_FP8_E4M3 ? p->k_scale : nullptr;
     a.v_scale = p->kv_dtype == DSA_FP8_E4M3 && !p->kv_latent ? p->v_scale : nullptr;
     a.scale = p->softmax_scale; a.out = out; a.lse = lse;
+    a.mode = p->attn_mode; a.all_visible = false;
     return a;
+}
+
+// Last visible key of the rows [r0, r0 + nr) at most, when q_pos is NULL
+// (pos(t) = n_k - n_q + t); -1 ("unknown") when q_pos is given.
+int block_max_pos(const dsa_problem_t* p, int r0, int nr) {
+    if (p->q_pos) return -1;
+    const int last = r0 + nr - 1;
+    const int t_max = (r0 / p->n_q == last / p->n_q) ? last % p->n_q : p->n_q - 1;
+    return p->n_k - p->n_q + t_max;
+}
+
+// Every row of the block keeps all its visible keys (top_k >= pos(t) + 1):
+// the selection is 0..pos(t) whatever the scores.
+bool block_keeps_all(const dsa_problem_t* p, int r0, int nr) {
+    const int mp = block_max_pos(p, r0, nr);
+    return mp >= 0 && mp + 1 <= p->top_k;
 }
 
 // Rows of scores the fused paths produce per round.
@@ -230,6 +261,13 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
     auto mark = [&](int ph) { return device_status(timer_mark(ph, st), "phase timer"); };
     for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
         int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
+        if (block_keeps_all(p, r0, nr)) {
+            // no indexer and no top-k: the selection of every row is 0..pos(t)
+            s = device_status(dsa::launch_fill_prefix_idx(idx + static_cast<size_t>(r0) * p->top_k, r0, nr,
+                                                          p->n_q, p->n_k, p->top_k, st), "selection fill");
+            if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
+            continue;
+        }
         if (L.sampled) {
             dsa::SampledTopk t{};
             t.ix = index_args(p, r0, nr, nullptr);
@@ -262,6 +300,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
     }
     dsa::AttnArgs aa = attn_args(p, idx, out, lse);
+    aa.all_visible = block_keeps_all(p, 0, rows);
     s = device_status(dsa::launch_sparse_attn(aa, base + L.attn_off, st), "attention launch");
     if (s != DSA_OK) return s;
     return mark(DSA_PHASE_ATTN);
@@ -292,6 +331,13 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
                 return static_cast<size_t>(-1);
             }
             return fused_layout(p, true).total;
+        case DSA_OP_DENSE_ATTN:
+            if (check_attn(p) != DSA_OK) return static_cast<size_t>(-1);
+            if (!masked_shape(p)) {
+                fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows");
+                return static_cast<size_t>(-1);
+            }
+            return 0;
         default:
             fail(DSA_E_INVALID, "unknown op %d", op);
             return static_cast<size_t>(-1);
@@ -355,6 +401,20 @@ dsa_status_t dsa_decode(const dsa_problem_t* p, void* out, float* lse, int32_t* 
         return s;
     if (!out) return fail(DSA_E_INVALID, "out is required");
     return run_fused(p, out, lse, idx_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status_t dsa_dense_attn(const dsa_problem_t* p, void* out, float* lse, hipStream_t stream) {
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK) return s;
+    if (!masked_shape(p))
+        return fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows");
+    if (!out) return fail(DSA_E_INVALID, "out is required");
+    dsa::AttnArgs a = attn_args(p, nullptr, out, lse);
+    a.kk = 0;
+    a.mode = dsa::ATTN_MASKED;
+    a.all_visible = true;
+    return device_status(dsa::launch_attn_masked(a, nullptr, stream), "attention launch");
 }
 
 dsa_status_t dsa_phase_timing(int enable) {

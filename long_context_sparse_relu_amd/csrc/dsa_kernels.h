@@ -66,6 +66,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // histogram from the indexer needed).
 bool topk_row_lds(int n_k);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
+// idx[r][j] = j for j <= pos(row0 + r), else -1 (pos from n_k - n_q + t): the
+// top-k result of a row that keeps every visible key.
+hipError_t launch_fill_prefix_idx(int32_t* idx, int row0, int rows, int n_q, int n_k, int k, hipStream_t st);
+
+// Attention modes (dsa_attn_mode_t).
+enum AttnMode { ATTN_AUTO = 0, ATTN_GATHER = 1, ATTN_MASKED = 2 };
+constexpr int kMaskedMaxKeys = 1 << 18;  // keys of a selection bit row the masked path holds in LDS
 
 struct AttnArgs {
     int rows, n_q, n_k, kk;
@@ -81,6 +88,8 @@ struct AttnArgs {
     float scale;
     void* out;             // [rows, Hq, dv]
     float* lse;            // [rows, Hq] or null
+    int mode;              // AttnMode
+    bool all_visible;      // every row keeps all keys 0..pos(t) (idx may then be ignored)
 };
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st);
@@ -116,7 +125,9 @@ hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st);
 // per-slice partials of the split kernel), possibly 0.
 size_t attn_workspace_bytes(const AttnArgs& a);
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st);
-// Prefill rows as masked dense MFMA tiles (attn_masked.hip).
+// Prefill rows as masked dense MFMA tiles (attn_masked.hip).  With
+// a.all_visible the mask is causal only and no bit rows are built (bitmap
+// may be null).
 bool attn_masked_eligible(const AttnArgs& a);
 size_t attn_masked_workspace_bytes(const AttnArgs& a);
 hipError_t launch_attn_masked(const AttnArgs& a, uint32_t* bitmap, hipStream_t st);

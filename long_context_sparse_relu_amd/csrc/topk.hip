@@ -52,6 +52,21 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
     return hipGetLastError();
 }
 
+// A row with top_k >= pos(t) + 1 keeps all its visible keys: positions
+// 0..pos(t) in ascending order, then -1.  One workgroup per row.
+__global__ void k_fill_prefix_idx(int32_t* idx, int row0, int n_q, int n_k, int k) {
+    const int r = blockIdx.x;
+    const int pos = row_pos(nullptr, row0 + r, n_q, n_k);
+    int32_t* out = idx + static_cast<size_t>(r) * k;
+    for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j <= pos ? j : -1;
+}
+
+hipError_t launch_fill_prefix_idx(int32_t* idx, int row0, int rows, int n_q, int n_k, int k, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_prefix_idx, dim3(rows), dim3(256), 0, st, idx, row0, n_q, n_k, k);
+    return hipGetLastError();
+}
+
 __device__ __forceinline__ int row_visible(const TopkArgs& a, int row) {
     return row_pos(a.q_pos, row, a.n_q, a.n_k) + 1;   // 0..n_k
 }

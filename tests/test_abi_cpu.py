@@ -103,6 +103,9 @@ FAKE = ctypes.c_void_p(0x7F0000000000)
     (dict(kv_dtype=dsa.FP8_E4M3, k_scale=0x7F0000000000), dsa.E_INVALID),   # no v_scale
     (dict(kv_dtype=dsa.FP8_E4M3, attn_dtype=dsa.F32, k_scale=0x7F0000000000,
           v_scale=0x7F0000000000), dsa.E_UNSUPPORTED),                        # FP8 cache needs bf16 q
+    (dict(attn_mode=3), dsa.E_INVALID),
+    (dict(attn_mode=dsa.ATTN_MASKED, q_heads=4, kv_heads=1, kv_latent=1, d_qk=576, d_v=512, v=None),
+     dsa.E_UNSUPPORTED),                                                     # masked: d128 only
     (dict(softmax_scale=0.0), dsa.E_INVALID),
     (dict(softmax_scale=float("inf")), dsa.E_INVALID),
     (dict(n_q=2), dsa.E_INVALID),                   # decode takes one query row
@@ -112,6 +115,18 @@ def test_decode_validation(lib, over, status):
     st = lib.dsa_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == status, dsa.last_error()
     assert dsa.last_error()
+
+
+def test_dense_attn_validation(lib):
+    p = _problem(n_q=64, n_k=4096)
+    assert lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(p)) == 0
+    assert lib.dsa_dense_attn(ctypes.byref(p), None, None, None) == dsa.E_INVALID          # out missing
+    fp32 = _problem(attn_dtype=dsa.F32, kv_dtype=dsa.F32)
+    assert lib.dsa_dense_attn(ctypes.byref(fp32), FAKE, None, None) == dsa.E_UNSUPPORTED
+    assert lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(fp32)) == ctypes.c_size_t(-1).value
+    d64 = _problem(d_qk=64, d_v=64)
+    assert lib.dsa_dense_attn(ctypes.byref(d64), FAKE, None, None) == dsa.E_UNSUPPORTED
+    assert "dense" in dsa.last_error()
 
 
 def test_null_problem_and_outputs(lib):

@@ -416,3 +416,98 @@ def test_decode_1m_sampled():
     got = idx.cpu().numpy()
     hits = sum(int(s in set(got[b, 0].tolist())) for (b, s, t) in inp["needle_pairs"])
     assert hits >= 0.95 * len(inp["needle_pairs"]), f"needle recall {hits}/{len(inp['needle_pairs'])}"
+
+
+# --- masked MHA mode, dense causal attention and the dense fallback --------------------------
+
+def _attn_problem(inp, **kw):
+    return dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=inp["top_k"], q=inp["q"],
+                            k=inp["k"], v=inp["v"], softmax_scale=inp["scale"], **kw)
+
+
+@pytest.mark.parametrize("B,n_q,n_k,Hq,Hkv", [(2, 150, 400, 8, 2), (1, 300, 300, 4, 4), (3, 1, 2000, 8, 1)])
+def test_dense_attn_matches_oracle(B, n_q, n_k, Hq, Hkv):
+    """Causal attention over every visible key (ragged query blocks, a cached prefix, decode)."""
+    sp = custom_spec(name="dense", B=B, n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=8,
+                     q_heads=Hq, kv_heads=Hkv, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=11)
+    out, lse = dsa.dense_attn(_attn_problem(inp))
+    torch.cuda.synchronize()
+    ov = oracle_view(inp)
+    for b in range(B):
+        o_out, o_lse = oracle.dense_causal_attn(ov["q"][b], ov["k"][b], ov["v"][b], "bf16", inp["scale"],
+                                                ov["pos"][b].astype(np.int64))
+        check_attn(_host(out[b]), _host(lse[b]), o_out, o_lse, "bf16")
+
+
+def test_dense_attn_explicit_positions():
+    """q_pos rows, including one that sees nothing (out = 0, lse = -inf)."""
+    sp = custom_spec(name="dense_pos", B=1, n_q=70, n_k=500, idx_heads=4, idx_dtype="bf16", top_k=8,
+                     q_heads=4, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=12)
+    g = torch.Generator().manual_seed(3)
+    pos = torch.randint(-1, 500, (1, 70), generator=g, dtype=torch.int32)
+    pos[0, 5] = -1
+    out, lse = dsa.dense_attn(_attn_problem(inp, q_pos=pos.to(DEV)))
+    torch.cuda.synchronize()
+    ov = oracle_view(inp)
+    o_out, o_lse = oracle.dense_causal_attn(ov["q"][0], ov["k"][0], ov["v"][0], "bf16", inp["scale"],
+                                            pos[0].numpy().astype(np.int64))
+    check_attn(_host(out[0]), _host(lse[0]), o_out, o_lse, "bf16")
+    assert torch.isneginf(lse[0, 5]).all() and (out[0, 5] == 0).all()
+
+
+@pytest.mark.parametrize("n_q,n_k,k", [(200, 700, 100), (64, 3000, 512), (130, 130, 40)])
+def test_attention_modes_agree(n_q, n_k, k):
+    """AUTO, GATHER and MASKED compute the same attention over the same selection."""
+    sp = custom_spec(name="modes", B=2, n_q=n_q, n_k=n_k, idx_heads=8, idx_dtype="bf16", top_k=k,
+                     q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=13)
+    idxs, outs = [], []
+    for mode in (dsa.ATTN_AUTO, dsa.ATTN_GATHER, dsa.ATTN_MASKED):
+        prob = _attn_problem(inp, attn_mode=mode)
+        idx = torch.empty((2, n_q, k), dtype=torch.int32, device=DEV)
+        out, lse, _ = dsa.prefill(prob, idx_out=idx)
+        torch.cuda.synchronize()
+        idxs.append(idx)
+        outs.append((out, lse))
+    assert torch.equal(idxs[0], idxs[1]) and torch.equal(idxs[0], idxs[2])
+    ov = oracle_view(inp)
+    for b in range(2):
+        pos = ov["pos"][b].astype(np.int64)
+        o_out, o_lse = oracle.sparse_attn(ov["q"][b], ov["k"][b], ov["v"][b], idxs[0][b].cpu().numpy(), "bf16",
+                                          inp["scale"], pos)
+        for out, lse in outs:
+            check_attn(_host(out[b]), _host(lse[b]), o_out, o_lse, "bf16")
+
+
+def test_short_prompt_is_dense_attention():
+    """top_k >= every prefix: the selection is 0..t exactly and the output is dense attention."""
+    sp = custom_spec(name="short", B=2, n_q=500, n_k=500, idx_heads=16, idx_dtype="e4m3", top_k=512,
+                     q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=14)
+    prob = _problem(inp)
+    idx = torch.empty((2, 500, 512), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.prefill(prob, idx_out=idx)
+    d_out, d_lse = dsa.dense_attn(prob)
+    torch.cuda.synchronize()
+    j = torch.arange(512, device=DEV, dtype=torch.int32)
+    t = torch.arange(500, device=DEV, dtype=torch.int32)[:, None]
+    want = torch.where(j[None, :] <= t, j[None, :], torch.full_like(j[None, :], -1))
+    assert torch.equal(idx, want.expand(2, 500, 512))
+    assert torch.equal(out, d_out) and torch.equal(lse, d_lse)
+    ov = oracle_view(inp)
+    o_out, o_lse = oracle.dense_causal_attn(ov["q"][1], ov["k"][1], ov["v"][1], "bf16", inp["scale"],
+                                            ov["pos"][1].astype(np.int64))
+    check_attn(_host(out[1]), _host(lse[1]), o_out, o_lse, "bf16")
+
+
+def test_prefill_first_block_takes_dense_fallback():
+    """16K prefill, k = 4096: the first row block (rows t < 4096) skips the indexer and top-k."""
+    sp = custom_spec(name="fallback16k", B=1, n_q=16384, n_k=16384, idx_heads=16, idx_dtype="e4m3",
+                     top_k=4096, q_heads=4, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=15)
+    rows = [0, 1, 1000, 4095, 4096, 4097, 9000, 16383]
+    _, idx, _ = run_case(inp, [0], rows, fused="prefill")
+    got = idx[0, 4095].cpu()
+    assert torch.equal(got, torch.arange(4096, dtype=torch.int32))
