@@ -76,6 +76,113 @@ def _events_mean_us(fn, reps, stream):
     return 1000.0 * sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
 
 
+def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
+    """Masked MHA against gather attention, and DSA against dense attention, over L and k.
+
+    Part "prefill": one sequence of L tokens (indexer 16 FP8 heads, attention 32
+    bf16 heads of dim 128, MHA), for each k: the fused dsa_prefill step, its
+    attention alone in GATHER and in MASKED mode, and dsa_dense_attn.  Part
+    "chunk": n_q new queries over a cache of chunk_nk keys, k = ks[-1]: the
+    attention in both modes.  Each time is the median of `reps` calls, each
+    after a read of 1 GiB (so the gathered rows come from HBM, not a cache).
+    Prints one JSON line per point and a summary line.
+    """
+    from dsa_inputs import custom_spec, make_inputs
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        ts = []
+        for _ in range(n + 1):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(1000.0 * e0.elapsed_time(e1))
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    def problem(inp, k, mode):
+        return dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
+                                v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
+                                softmax_scale=inp["scale"], attn_mode=mode)
+
+    def attn_times(inp, k, idx, n):
+        res = {}
+        for name, mode in (("gather", dsa.ATTN_GATHER), ("masked", dsa.ATTN_MASKED)):
+            prob = problem(inp, k, mode)
+            out, lse = dsa._out_tensors(prob, None, None)
+            ws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_SPARSE_ATTN, prob)), dtype=torch.uint8, device=dev)
+            res[name] = timed(lambda: dsa.sparse_attn(prob, idx, out, lse, ws, stream), n)
+        return res
+
+    points = []
+    for L in ladder:
+        for k in ks:
+            sp = custom_spec(name=f"prefill_L{L}", B=1, n_q=L, n_k=L, idx_heads=16, idx_dim=128, idx_dtype="e4m3",
+                             top_k=k, q_heads=32, kv_heads=32, d_qk=128, d_v=128, attn_dtype="bf16",
+                             outlier_frac=0.001)
+            inp = make_inputs(sp, device=dev, seed=0)
+            prob = problem(inp, k, dsa.ATTN_AUTO)
+            out, lse = dsa._out_tensors(prob, None, None)
+            idx = torch.empty((1, L, k), dtype=torch.int32, device=dev)
+            ws = torch.empty(dsa.workspace_bytes(dsa.OP_PREFILL, prob), dtype=torch.uint8, device=dev)
+            n = reps if L <= 8192 else max(3, reps // 3)
+            dsa_us = timed(lambda: dsa.prefill(prob, out, lse, idx, ws, stream), n)
+            dsa.phase_timing(True)
+            try:
+                dsa.prefill(prob, out, lse, idx, ws, stream)
+                phases = dsa.phase_times()
+            finally:
+                dsa.phase_timing(False)
+            dws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_DENSE_ATTN, prob)), dtype=torch.uint8, device=dev)
+            dense_us = timed(lambda: dsa.dense_attn(prob, out, lse, dws, stream), n)
+            at = attn_times(inp, k, idx, n)
+            pt = {"sweep": "mask", "part": "prefill", "L": L, "k": k, "dsa_prefill_us": dsa_us,
+                  "dsa_phases_us": phases, "attn_gather_us": at["gather"], "attn_masked_us": at["masked"],
+                  "dense_attn_us": dense_us, "dsa_over_dense": dsa_us / dense_us}
+            points.append(pt)
+            print(json.dumps(pt), flush=True)
+            del inp, prob, out, lse, idx, ws, dws
+            torch.cuda.empty_cache()
+    k = ks[-1]
+    for hq, hkv in ((32, 32), (32, 4)):
+        for n_q in chunks:
+            sp = custom_spec(name=f"chunk{n_q}", B=1, n_q=n_q, n_k=chunk_nk, idx_heads=16, idx_dim=128,
+                             idx_dtype="e4m3", top_k=k, q_heads=hq, kv_heads=hkv, d_qk=128, d_v=128,
+                             attn_dtype="bf16")
+            inp = make_inputs(sp, device=dev, seed=0)
+            prob = problem(inp, k, dsa.ATTN_AUTO)
+            out, lse = dsa._out_tensors(prob, None, None)
+            idx = torch.empty((1, n_q, k), dtype=torch.int32, device=dev)
+            ws = torch.empty(dsa.workspace_bytes(dsa.OP_PREFILL, prob), dtype=torch.uint8, device=dev)
+            dsa_us = timed(lambda: dsa.prefill(prob, out, lse, idx, ws, stream), reps)
+            at = attn_times(inp, k, idx, reps)
+            dws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_DENSE_ATTN, prob)), dtype=torch.uint8, device=dev)
+            dense_us = timed(lambda: dsa.dense_attn(prob, out, lse, dws, stream), reps)
+            pt = {"sweep": "mask", "part": "chunk", "q_heads": hq, "kv_heads": hkv, "n_q": n_q, "n_k": chunk_nk,
+                  "k": k, "dsa_prefill_us": dsa_us, "attn_gather_us": at["gather"], "attn_masked_us": at["masked"],
+                  "dense_attn_us": dense_us}
+            points.append(pt)
+            print(json.dumps(pt), flush=True)
+            del inp, prob, idx, out, lse, ws, dws
+            torch.cuda.empty_cache()
+    summary = {"sweep": "mask", "summary": True}
+    for k in ks:
+        pre = [p for p in points if p["part"] == "prefill" and p["k"] == k]
+        wins = [p["L"] for p in pre if p["dsa_prefill_us"] < p["dense_attn_us"]]
+        summary[f"k{k}_smallest_L_where_dsa_beats_dense"] = min(wins) if wins else None
+        summary[f"k{k}_masked_faster_at_L"] = [p["L"] for p in pre if p["attn_masked_us"] < p["attn_gather_us"]]
+    for hq, hkv in ((32, 32), (32, 4)):
+        summary[f"chunk_{hq}x{hkv}_masked_faster_at_n_q"] = [
+            p["n_q"] for p in points if p["part"] == "chunk" and p["kv_heads"] == hkv
+            and p["attn_masked_us"] < p["attn_gather_us"]]
+    print(json.dumps(summary), flush=True)
+    return 0
+
+
 def _cpu_baseline(inp, n_seq, n_rows, min_s=10.0):
     """The oracle on n_seq sequences (decode) or n_rows evenly spread query rows (prefill)."""
     import oracle
@@ -116,6 +223,13 @@ def main(argv=None):
     ap.add_argument("--cpu-rows", type=int, default=48, help="query rows the oracle baseline runs (prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phase-reps", type=int, default=10)
+    ap.add_argument("--sweep", choices=["mask"], default=None,
+                    help="instead of the step benchmark: masked vs gather attention and DSA vs dense "
+                         "attention over a length ladder (JSON line per point)")
+    ap.add_argument("--ladder", default="1024,2048,4096,8192,16384,32768")
+    ap.add_argument("--ks", default="512,2048")
+    ap.add_argument("--chunks", default="16,64,256,1024,4096")
+    ap.add_argument("--chunk-nk", type=int, default=32768)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); a multi-GPU run is not part of "
@@ -128,6 +242,10 @@ def main(argv=None):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.sweep == "mask":
+        return _sweep_mask(dsa, torch, dev, [int(x) for x in args.ladder.split(",")],
+                           [int(x) for x in args.ks.split(",")], [int(x) for x in args.chunks.split(",")],
+                           args.chunk_nk, max(3, args.steps // 4))
     s = spec(args.workload)
     decode = s["n_q"] == 1
     print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)

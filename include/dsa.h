@@ -187,8 +187,10 @@ dsa_status_t dsa_decode(const dsa_problem_t *p, void *out, float *lse, int32_t *
  * pages measure DSA against.  Uses the main-attention fields only (q, k, v,
  * heads, dims, softmax_scale, q_pos); bf16, d_qk = d_v = 128, not latent,
  * bf16 KV (else DSA_E_UNSUPPORTED).  out: [B, n_q, Hq, d_v] bf16; lse:
- * [B, n_q, Hq] fp32 or NULL.  Needs no workspace (dsa_workspace_bytes = 0). */
-dsa_status_t dsa_dense_attn(const dsa_problem_t *p, void *out, float *lse, hipStream_t stream);
+ * [B, n_q, Hq] fp32 or NULL; workspace: dsa_workspace_bytes(DSA_OP_DENSE_ATTN)
+ * bytes (partial results when the key walk is split; may be 0). */
+dsa_status_t dsa_dense_attn(const dsa_problem_t *p, void *out, float *lse,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Phase timing of the fused entry points, for profiling.
  * dsa_phase_timing(1) makes every later dsa_prefill / dsa_decode call record

@@ -89,7 +89,7 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_decode.restype = ctypes.c_int
     lib.dsa_decode.argtypes = [P, vp, vp, vp, vp, sz, vp]
     lib.dsa_dense_attn.restype = ctypes.c_int
-    lib.dsa_dense_attn.argtypes = [P, vp, vp, vp]
+    lib.dsa_dense_attn.argtypes = [P, vp, vp, vp, sz, vp]
     lib.dsa_phase_timing.restype = ctypes.c_int
     lib.dsa_phase_timing.argtypes = [ctypes.c_int]
     lib.dsa_phase_times.restype = ctypes.c_int
@@ -309,10 +309,12 @@ def decode(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, s
     return _fused(load_library().dsa_decode, OP_DECODE, prob, out, lse, idx_out, workspace, stream)
 
 
-def dense_attn(prob: DSAProblem, out=None, lse=None, stream=None):
+def dense_attn(prob: DSAProblem, out=None, lse=None, workspace=None, stream=None):
     """(out, lse) of dense causal attention: every query over all its visible keys."""
     out, lse = _out_tensors(prob, out, lse)
-    _check(load_library().dsa_dense_attn(prob.ref(), _ptr(out), _ptr(lse), _stream(stream)))
+    ws = _workspace(OP_DENSE_ATTN, prob, workspace)
+    _check(load_library().dsa_dense_attn(prob.ref(), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
     return out, lse
 
 

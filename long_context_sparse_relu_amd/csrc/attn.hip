@@ -504,7 +504,7 @@ size_t attn_workspace_bytes(const AttnArgs& a) {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
-    if (attn_masked_eligible(a)) return launch_attn_masked(a, static_cast<uint32_t*>(ws), st);
+    if (attn_masked_eligible(a)) return launch_attn_masked(a, ws, st);
     if (gqa_d128_eligible(a)) {
         const int s = gqa_splits(a);
         const int len = gqa_slice_len(a, s);

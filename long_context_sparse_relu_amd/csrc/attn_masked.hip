@@ -38,7 +38,6 @@ constexpr int kKB = 64;            // keys per tile
 // 80 words per row puts the 4 keys 16 banks apart)
 constexpr int kStr = 136;          // K tile
 constexpr int kStrV = 160;         // V tile
-constexpr int kMinQ = 64;          // fewest query rows this path takes
 }
 
 // Words (uint32) per bit row: keys rounded up to 64.
@@ -89,18 +88,41 @@ __device__ __forceinline__ uint32_t causal_word(int pos, int key0) {
 
 // DENSE: every query keeps all its visible keys; the mask is causal and no
 // bit rows are read (bm may be null).
+// With ks > 1 the key tiles of each block are split into ks ranges of tps
+// tiles (blockIdx.z = b * ks + range) and each workgroup leaves its (max,
+// sum, unnormalised O) record per (row, head) in part for k_attn_merge.
 template <bool DENSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(AttnArgs a, const uint32_t* bm, int words) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(
+    AttnArgs a, const uint32_t* bm, int words, int ks, int tps, float* part) {
     // two buffers: the next tile is staged into one while the other is read
     // (one barrier per tile)
     __shared__ __align__(16) uint16_t k_all[2 * kKB * kStr];
     __shared__ __align__(16) uint16_t v_all[2 * kKB * kStrV];
     __shared__ int last_s[4];
 
+    // A stream = (sequence, key range, head): its query blocks read the same
+    // key tiles.  Consecutive workgroup ids go to the 8 XCDs in turn; when the
+    // streams divide by 8, stream sg and all its query blocks are given to
+    // XCD sg % 8, back to back, so the blocks in flight on an XCD walk the
+    // same tiles through its L2 (longest block first within a stream).
     const int nqb = (a.n_q + kQB - 1) / kQB;
-    const int qb = nqb - 1 - blockIdx.x;        // longest blocks first
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    const int streams = (a.rows / a.n_q) * ks * a.Hq;
+    int sg, j;
+    {
+        const int id = blockIdx.x;
+        if ((streams & 7) == 0) {
+            const int k8 = id >> 3;
+            sg = (k8 / nqb) * 8 + (id & 7);
+            j = k8 % nqb;
+        } else {
+            sg = id / nqb;
+            j = id % nqb;
+        }
+    }
+    const int qb = nqb - 1 - j;
+    const int h = sg % a.Hq;
+    const int split = (sg / a.Hq) % ks;
+    const int b = sg / (a.Hq * ks);
     const int G = a.Hq / a.Hkv;
     const int g = h / G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -129,7 +151,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __syncthreads();
     const int last = max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3]));
+    // this workgroup's key tiles [t0, t1) of the block's walk
     const int ntiles = last < 0 ? 0 : last / kKB + 1;
+    const int t0 = split * tps;
+    const int t1 = min(ntiles, t0 + tps);
 
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     const uint16_t* vp = static_cast<const uint16_t*>(a.v);
@@ -187,16 +212,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[d] = v16f{};
 
-    if (ntiles > 0) {
-        fetch(0);
+    if (t1 > t0) {
+        fetch(t0);
         stage(0);
     }
     uint32_t w0 = pw0, w1 = pw1;
     __builtin_amdgcn_s_waitcnt(0);              // prologue loads landed (see the indexer's tile loop)
     __syncthreads();
     int buf = 0;
-    for (int tile = 0; tile < ntiles; ++tile) {
-        fetch(tile + 1 < ntiles ? tile + 1 : tile);   // in flight during the multiply
+    for (int tile = t0; tile < t1; ++tile) {
+        fetch(tile + 1 < t1 ? tile + 1 : tile);   // in flight during the multiply
         const uint16_t* k_s = k_all + buf * kKB * kStr;
         const uint16_t* v_s = v_all + buf * kKB * kStrV;
         const bool any = __ballot((w0 | w1) != 0u) != 0ull;
@@ -276,7 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             }
         }
         // the other buffer was last read before the previous barrier
-        if (tile + 1 < ntiles) {
+        if (tile + 1 < t1) {
             stage(buf ^ 1);
             w0 = pw0;
             w1 = pw1;
@@ -288,6 +313,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const float l_tot = pair32_sum(l_part);
     if (!live_q) return;
     // o[d][r] = O^T[dim 32d + 8(r/4) + 4hh + r%4][query qc]
+    if (ks > 1) {
+        float* rec = part + ((static_cast<size_t>(row) * a.Hq + h) * ks + split) * (128 + 2);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 v;
+                v.x = o[d][4 * q4]; v.y = o[d][4 * q4 + 1]; v.z = o[d][4 * q4 + 2]; v.w = o[d][4 * q4 + 3];
+                // dims 32d + 8 q4 + 4hh .. +3; the record's O starts 2 floats in
+                float* dst = rec + 2 + 32 * d + 8 * q4 + 4 * hh;
+                dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+            }
+        if (hh == 0) {
+            rec[0] = m_ref == -__builtin_inff() ? -__builtin_inff() : m_ref * zscale;
+            rec[1] = l_tot;
+        }
+        return;
+    }
     uint16_t* outp = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(row) * a.Hq + h) * 128 + 4 * hh;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
@@ -306,38 +349,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         a.lse[static_cast<size_t>(row) * a.Hq + h] = l_tot > 0.0f ? (m_ref * zscale + log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
+// Costs that choose between the two forms in ATTN_AUTO, from rates measured
+// on MI355X (bf16, d = 128, cold caches): gathering rows of K and V (512 B
+// per kept (row, kv head, key)) runs at about 5.5 TB/s; the masked walk reads
+// every key tile up to a query block's last visible key once per query head
+// (about 4.5 TB/s) and does the dense tile math at about 800 TFLOP/s,
+// whichever is longer.  With few query rows per sequence the walk's reads
+// dominate and gathering wins; with GQA one gathered row serves all the
+// heads of its group, which the per-head walk does not share.
+static double gather_cost_us(const AttnArgs& a) {
+    const double kept = static_cast<double>(a.rows) * (a.all_visible ? 0.5 * a.n_k : a.kk);
+    return kept * a.Hkv * 512.0 / 5.5e6;
+}
+static double masked_cost_us(const AttnArgs& a) {
+    const int B = a.rows / a.n_q;
+    const int nqb = (a.n_q + kQB - 1) / kQB;
+    // key rows walked per query block: up to its last query's position
+    // (q_pos unknown on the host: n_k - n_q + t, the usual layout)
+    double walked = 0.0;
+    for (int qb = 0; qb < nqb; ++qb) {
+        const int t_last = (qb + 1) * kQB < a.n_q ? (qb + 1) * kQB - 1 : a.n_q - 1;
+        walked += static_cast<double>(a.n_k - a.n_q + t_last + 1);
+    }
+    const double bytes = static_cast<double>(B) * a.Hq * walked * 512.0;
+    const double flops = 4.0 * 128.0 * a.Hq * static_cast<double>(B) * kQB * walked;
+    const double t_bytes = bytes / 4.5e6, t_flops = flops / 8.0e8;
+    return t_bytes > t_flops ? t_bytes : t_flops;
+}
+
 bool attn_masked_eligible(const AttnArgs& a) {
     if (!(a.dtype == BF16 && a.kv_dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128)) return false;
     if (a.mode == ATTN_GATHER) return false;
-    if (a.all_visible) return a.mode == ATTN_MASKED || a.n_q >= kMinQ;   // causal mask, no bit rows
+    if (a.all_visible)                                       // causal mask, no bit rows
+        return a.mode == ATTN_MASKED || masked_cost_us(a) < gather_cost_us(a);
     if (a.n_k > kMaskedMaxKeys) return false;
     if (a.mode == ATTN_MASKED) return true;
-    if (a.n_q < kMinQ) return false;
-    // a key tile is shared by the block's 64 queries: worth it once a row keeps
-    // more than 1/64 of what it sees (the average prefix of this problem)
-    const double avg_vis = static_cast<double>(a.n_k) - 0.5 * a.n_q;
-    return static_cast<double>(a.kk) * kMinQ >= avg_vis;
+    return masked_cost_us(a) < gather_cost_us(a);
+}
+
+#ifndef DSA_MASKED_TARGET_WGS
+#define DSA_MASKED_TARGET_WGS 512
+#endif
+// Key-tile ranges per query block: with few (query block, head) pairs the
+// walk over the keys is split so that about two workgroups run per compute
+// unit, each range at least 8 tiles long.
+static int masked_splits(const AttnArgs& a) {
+    const int64_t wgs = static_cast<int64_t>((a.n_q + kQB - 1) / kQB) * a.Hq * (a.rows / a.n_q);
+    const int tiles = (a.n_k + kKB - 1) / kKB;
+    int s = static_cast<int>((DSA_MASKED_TARGET_WGS + wgs - 1) / wgs);
+    const int max_s = tiles / 8 > 64 ? 64 : tiles / 8;
+    if (s > max_s) s = max_s;
+    return s < 1 ? 1 : s;
+}
+
+static size_t bitmap_bytes(const AttnArgs& a) {
+    return a.all_visible ? 0 : (static_cast<size_t>(a.rows) * bitmap_words(a.n_k) * sizeof(uint32_t) + 255) & ~size_t(255);
 }
 
 size_t attn_masked_workspace_bytes(const AttnArgs& a) {
-    // the bit rows (none when every row keeps all its visible keys)
-    return a.all_visible ? 0 : static_cast<size_t>(a.rows) * bitmap_words(a.n_k) * sizeof(uint32_t);
+    // the bit rows (none when every row keeps all its visible keys), then the
+    // split records
+    const int s = masked_splits(a);
+    const size_t recs = s > 1 ? static_cast<size_t>(a.rows) * a.Hq * s * (128 + 2) * sizeof(float) : 0;
+    return bitmap_bytes(a) + recs;
 }
 
-hipError_t launch_attn_masked(const AttnArgs& a, uint32_t* bm, hipStream_t st) {
+hipError_t launch_attn_masked(const AttnArgs& a, void* ws, hipStream_t st) {
     const int B = a.rows / a.n_q;
-    const dim3 grid((a.n_q + kQB - 1) / kQB, a.Hq, B);
+    const int s = masked_splits(a);
+    const int tiles = (a.n_k + kKB - 1) / kKB;
+    const int tps = (tiles + s - 1) / s;
+    uint32_t* bm = static_cast<uint32_t*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + bitmap_bytes(a));
+    const dim3 grid(static_cast<unsigned>((a.n_q + kQB - 1) / kQB) * a.Hq * B * s);
+    hipError_t e;
     if (a.all_visible) {
-        hipLaunchKernelGGL(k_attn_masked_d128<true>, grid, dim3(256), 0, st, a, static_cast<const uint32_t*>(nullptr), 0);
-        return hipGetLastError();
+        hipLaunchKernelGGL(k_attn_masked_d128<true>, grid, dim3(256), 0, st, a,
+                           static_cast<const uint32_t*>(nullptr), 0, s, tps, part);
+    } else {
+        const int words = bitmap_words(a.n_k);
+        const size_t lds = static_cast<size_t>(words) * sizeof(uint32_t);   // <= 32 KiB
+        hipLaunchKernelGGL(k_sel_bitmap, dim3(a.rows), dim3(256), lds, st, a, bm, words);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_attn_masked_d128<false>, grid, dim3(256), 0, st, a,
+                           static_cast<const uint32_t*>(bm), words, s, tps, part);
     }
-    const int words = bitmap_words(a.n_k);
-    const size_t lds = static_cast<size_t>(words) * sizeof(uint32_t);   // <= 32 KiB
-    hipLaunchKernelGGL(k_sel_bitmap, dim3(a.rows), dim3(256), lds, st, a, bm, words);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_masked_d128<false>, grid, dim3(256), 0, st, a, static_cast<const uint32_t*>(bm), words);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess || s == 1) return e;
+    return launch_attn_merge(a, s, part, st);
 }
 
 }  // namespace dsa

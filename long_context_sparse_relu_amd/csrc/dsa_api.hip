@@ -189,6 +189,15 @@ dsa::AttnArgs attn_args(const dsa_problem_t* p, const int32_t* idx, void* out, f
     return a;
 }
 
+// Attention over every visible key (the causal-only masked kernels).
+dsa::AttnArgs dense_args(const dsa_problem_t* p, void* out, float* lse) {
+    dsa::AttnArgs a = attn_args(p, nullptr, out, lse);
+    a.kk = 0;
+    a.mode = dsa::ATTN_MASKED;
+    a.all_visible = true;
+    return a;
+}
+
 // Last visible key of the rows [r0, r0 + nr) at most, when q_pos is NULL
 // (pos(t) = n_k - n_q + t); -1 ("unknown") when q_pos is given.
 int block_max_pos(const dsa_problem_t* p, int r0, int nr) {
@@ -244,6 +253,7 @@ FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
     }
     L.attn_off = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t)) : 0);
     dsa::AttnArgs aa = attn_args(p, nullptr, nullptr, nullptr);
+    aa.all_visible = block_keeps_all(p, 0, rows_of(p));
     L.total = L.attn_off + align_up(dsa::attn_workspace_bytes(aa));
     return L;
 }
@@ -337,7 +347,7 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
                 fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows");
                 return static_cast<size_t>(-1);
             }
-            return 0;
+            return dsa::attn_masked_workspace_bytes(dense_args(p, nullptr, nullptr));
         default:
             fail(DSA_E_INVALID, "unknown op %d", op);
             return static_cast<size_t>(-1);
@@ -403,18 +413,19 @@ dsa_status_t dsa_decode(const dsa_problem_t* p, void* out, float* lse, int32_t* 
     return run_fused(p, out, lse, idx_out, workspace, workspace_bytes, stream);
 }
 
-dsa_status_t dsa_dense_attn(const dsa_problem_t* p, void* out, float* lse, hipStream_t stream) {
+dsa_status_t dsa_dense_attn(const dsa_problem_t* p, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
     g_last_error.clear();
     dsa_status_t s;
     if ((s = check_common(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK) return s;
     if (!masked_shape(p))
         return fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows");
     if (!out) return fail(DSA_E_INVALID, "out is required");
-    dsa::AttnArgs a = attn_args(p, nullptr, out, lse);
-    a.kk = 0;
-    a.mode = dsa::ATTN_MASKED;
-    a.all_visible = true;
-    return device_status(dsa::launch_attn_masked(a, nullptr, stream), "attention launch");
+    dsa::AttnArgs a = dense_args(p, out, lse);
+    const size_t need = dsa::attn_masked_workspace_bytes(a);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    return device_status(dsa::launch_attn_masked(a, workspace, stream), "attention launch");
 }
 
 dsa_status_t dsa_phase_timing(int enable) {

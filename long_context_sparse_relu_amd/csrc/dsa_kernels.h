@@ -125,12 +125,13 @@ hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st);
 // per-slice partials of the split kernel), possibly 0.
 size_t attn_workspace_bytes(const AttnArgs& a);
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st);
-// Prefill rows as masked dense MFMA tiles (attn_masked.hip).  With
-// a.all_visible the mask is causal only and no bit rows are built (bitmap
-// may be null).
+// Prefill rows as masked dense MFMA tiles (attn_masked.hip).  `ws` holds
+// attn_masked_workspace_bytes(a): the selection bit rows (none with
+// a.all_visible, where the mask is causal only), then the records of the
+// key-range splits (none when the walk is not split).
 bool attn_masked_eligible(const AttnArgs& a);
 size_t attn_masked_workspace_bytes(const AttnArgs& a);
-hipError_t launch_attn_masked(const AttnArgs& a, uint32_t* bitmap, hipStream_t st);
+hipError_t launch_attn_masked(const AttnArgs& a, void* ws, hipStream_t st);
 // MFMA kernel for wide rows / many heads per kv head (attn_wide.hip).
 bool attn_wide_eligible(const AttnArgs& a);
 size_t attn_wide_workspace_bytes(const AttnArgs& a);

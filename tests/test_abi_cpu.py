@@ -119,13 +119,15 @@ def test_decode_validation(lib, over, status):
 
 def test_dense_attn_validation(lib):
     p = _problem(n_q=64, n_k=4096)
-    assert lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(p)) == 0
-    assert lib.dsa_dense_attn(ctypes.byref(p), None, None, None) == dsa.E_INVALID          # out missing
+    need = lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(p))
+    assert 0 < need < ctypes.c_size_t(-1).value          # 2 rows x 32 heads: the key walk is split
+    assert lib.dsa_dense_attn(ctypes.byref(p), None, None, FAKE, need, None) == dsa.E_INVALID   # out missing
+    assert lib.dsa_dense_attn(ctypes.byref(p), FAKE, None, FAKE, need - 1, None) == dsa.E_WORKSPACE
     fp32 = _problem(attn_dtype=dsa.F32, kv_dtype=dsa.F32)
-    assert lib.dsa_dense_attn(ctypes.byref(fp32), FAKE, None, None) == dsa.E_UNSUPPORTED
+    assert lib.dsa_dense_attn(ctypes.byref(fp32), FAKE, None, FAKE, need, None) == dsa.E_UNSUPPORTED
     assert lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(fp32)) == ctypes.c_size_t(-1).value
     d64 = _problem(d_qk=64, d_v=64)
-    assert lib.dsa_dense_attn(ctypes.byref(d64), FAKE, None, None) == dsa.E_UNSUPPORTED
+    assert lib.dsa_dense_attn(ctypes.byref(d64), FAKE, None, FAKE, need, None) == dsa.E_UNSUPPORTED
     assert "dense" in dsa.last_error()
 
 

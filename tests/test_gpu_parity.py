@@ -457,7 +457,7 @@ def test_dense_attn_explicit_positions():
     assert torch.isneginf(lse[0, 5]).all() and (out[0, 5] == 0).all()
 
 
-@pytest.mark.parametrize("n_q,n_k,k", [(200, 700, 100), (64, 3000, 512), (130, 130, 40)])
+@pytest.mark.parametrize("n_q,n_k,k", [(200, 700, 100), (64, 3000, 512), (130, 130, 40), (32, 20000, 1024)])
 def test_attention_modes_agree(n_q, n_k, k):
     """AUTO, GATHER and MASKED compute the same attention over the same selection."""
     sp = custom_spec(name="modes", B=2, n_q=n_q, n_k=n_k, idx_heads=8, idx_dtype="bf16", top_k=k,
