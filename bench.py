@@ -183,6 +183,80 @@ def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
     return 0
 
 
+def _sweep_ladder(dsa, torch, dev, lengths, ks, reps):
+    """Decode time and bytes against context length L and k (one query per sequence).
+
+    The decode_128k layout (indexer 16 FP8 heads of dim 128, bf16 KV with 32
+    query heads over 4 kv heads of dim 128) at L tokens of context, 64
+    sequences up to 128K and 8 beyond (memory).  Per point: the fused
+    dsa_decode step and its phases, the algorithmic bytes (indexer keys and
+    scales once, kept K/V rows once), dsa_dense_attn over every key, and the
+    dense ideal (every K/V row read once at 8 TB/s).  Medians of `reps` calls,
+    each after a 1 GiB read.  One JSON line per point.
+    """
+    from dsa_inputs import custom_spec, make_inputs
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        ts = []
+        for _ in range(n + 1):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(1000.0 * e0.elapsed_time(e1))
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    for L in lengths:
+        B = 64 if L <= 131072 else 8
+        sp = custom_spec(name=f"decode_L{L}", B=B, n_q=1, n_k=L, idx_heads=16, idx_dim=128, idx_dtype="e4m3",
+                         top_k=max(ks), q_heads=32, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16")
+        print(f"[ladder] inputs L={L} B={B}", file=sys.stderr, flush=True)
+        inp = make_inputs(sp, device=dev, seed=0)
+        for k in ks:
+            prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
+                                    v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
+                                    softmax_scale=inp["scale"])
+            out, lse = dsa._out_tensors(prob, None, None)
+            idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+            ws = torch.empty(dsa.workspace_bytes(dsa.OP_DECODE, prob), dtype=torch.uint8, device=dev)
+            step_us = timed(lambda: dsa.decode(prob, out, lse, idx, ws, stream), reps)
+            dsa.phase_timing(True)
+            try:
+                acc = {}
+                for _ in range(reps):
+                    flush.sum()
+                    dsa.decode(prob, out, lse, idx, ws, stream)
+                    for n_, v_ in dsa.phase_times().items():
+                        acc[n_] = acc.get(n_, 0.0) + v_ / reps
+            finally:
+                dsa.phase_timing(False)
+            idx_bytes = B * L * (128 + 4) + B * (16 * 128 + 4 + 16 * 4)
+            gather_bytes = B * min(k, L) * 4 * 128 * 2 * 2
+            pt = {"sweep": "ladder", "L": L, "B": B, "k": k, "step_us": step_us,
+                  "q_tok_per_s": B / (step_us * 1e-6), "phases_us": acc,
+                  "indexer_bytes": idx_bytes, "gather_bytes": gather_bytes,
+                  "indexer_GBs": idx_bytes / (acc["index"] * 1e-6) / 1e9,
+                  "gather_GBs": gather_bytes / (acc["attn"] * 1e-6) / 1e9,
+                  "step_frac_of_hbm": (idx_bytes + gather_bytes) / (step_us * 1e-6) / 8e12}
+            if k == ks[0]:
+                dws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_DENSE_ATTN, prob)), dtype=torch.uint8,
+                                  device=dev)
+                pt["dense_attn_us"] = timed(lambda: dsa.dense_attn(prob, out, lse, dws, stream),
+                                            reps if L <= 131072 else 2)
+                del dws
+            pt["dense_ideal_us"] = B * L * 4 * 128 * 2 * 2 / 8e12 * 1e6
+            print(json.dumps(pt), flush=True)
+            del prob, out, lse, idx, ws
+        del inp
+        torch.cuda.empty_cache()
+    return 0
+
+
 def _cpu_baseline(inp, n_seq, n_rows, min_s=10.0):
     """The oracle on n_seq sequences (decode) or n_rows evenly spread query rows (prefill)."""
     import oracle
@@ -223,9 +297,12 @@ def main(argv=None):
     ap.add_argument("--cpu-rows", type=int, default=48, help="query rows the oracle baseline runs (prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phase-reps", type=int, default=10)
-    ap.add_argument("--sweep", choices=["mask"], default=None,
-                    help="instead of the step benchmark: masked vs gather attention and DSA vs dense "
-                         "attention over a length ladder (JSON line per point)")
+    ap.add_argument("--sweep", choices=["mask", "ladder"], default=None,
+                    help="instead of the step benchmark: 'mask' = masked vs gather attention and DSA vs dense "
+                         "attention in prefill; 'ladder' = decode time and bytes against context length and k "
+                         "(JSON line per point)")
+    ap.add_argument("--lengths", default="4096,16384,65536,131072,262144,524288,1048576")
+    ap.add_argument("--ladder-ks", default="256,512,2048")
     ap.add_argument("--ladder", default="1024,2048,4096,8192,16384,32768")
     ap.add_argument("--ks", default="512,2048")
     ap.add_argument("--chunks", default="16,64,256,1024,4096")
@@ -242,6 +319,9 @@ def main(argv=None):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.sweep == "ladder":
+        return _sweep_ladder(dsa, torch, dev, [int(x) for x in args.lengths.split(",")],
+                             [int(x) for x in args.ladder_ks.split(",")], max(3, args.steps // 4))
     if args.sweep == "mask":
         return _sweep_mask(dsa, torch, dev, [int(x) for x in args.ladder.split(",")],
                            [int(x) for x in args.ks.split(",")], [int(x) for x in args.chunks.split(",")],
