@@ -61,6 +61,8 @@ def _load():
     lib.ora_index_scores.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ora_topk.restype = None
     lib.ora_topk.argtypes = [i64, i64, vp, vp, i64, vp, vp]
+    lib.ora_select_backbone.restype = None
+    lib.ora_select_backbone.argtypes = [i64, i64, vp, vp, i64, i64, i64, vp, vp]
     lib.ora_sparse_attn.restype = None
     lib.ora_sparse_attn.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32,
                                     vp, vp, vp, vp, vp, dbl, vp, i64, vp, vp, vp]
@@ -141,6 +143,23 @@ def topk(scores, k: int, pos=None):
     idx = np.empty((n_q, k), dtype=np.int32)
     kth = np.empty(n_q, dtype=np.float64)
     _load().ora_topk(n_q, n_k, _ptr(scores), _ptr(pos), k, _ptr(idx), _ptr(kth))
+    return idx, kth
+
+
+def select_backbone(scores, k: int, sinks: int, window: int, pos=None):
+    """Top-k over the keys outside a forced set, united with that set.
+
+    The forced set of a row is its first `sinks` keys and its last `window`
+    visible keys; the m=min(k, #rest) best of the rest are added.  Returns
+    (idx [n_q, k+sinks+window] int32 ascending then -1, kth [n_q] fp64 = the
+    m-th best score of the rest, NaN if none).
+    """
+    scores = np.ascontiguousarray(scores, dtype=np.float64)
+    n_q, n_k = scores.shape
+    pos = _positions(pos, n_q, n_k)
+    idx = np.empty((n_q, k + sinks + window), dtype=np.int32)
+    kth = np.empty(n_q, dtype=np.float64)
+    _load().ora_select_backbone(n_q, n_k, _ptr(scores), _ptr(pos), k, sinks, window, _ptr(idx), _ptr(kth))
     return idx, kth
 
 
@@ -236,7 +255,11 @@ def dsa_forward(inp: dict, rows=None):
         iks = None if inp.get("ik_scale") is None else inp["ik_scale"][b]
         sc = index_scores(inp["iq"][b][ts], inp["ik"][b], inp["iw"][b][ts], inp["idx_dtype"],
                           iqs, iks, pos)
-        idx, kth = topk(sc, inp["top_k"], pos)
+        sinks, window = int(inp.get("sinks", 0)), int(inp.get("window", 0))
+        if sinks or window:
+            idx, kth = select_backbone(sc, inp["top_k"], sinks, window, pos)
+        else:
+            idx, kth = topk(sc, inp["top_k"], pos)
         v = None if inp.get("v") is None else inp["v"][b]
         kvs = {}
         if inp.get("kv_dtype", inp["attn_dtype"]) == "e4m3":

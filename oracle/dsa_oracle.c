@@ -213,6 +213,63 @@ void ora_topk(int64_t n_q, int64_t n_k, const double *scores, const int64_t *pos
 }
 
 /*
+ * Top-k with a structural backbone [SA: the sider.ai essay on DeepSeek Sparse
+ * Attention ("sparse-attention-that-isn-t-sparse-thinking"), sections
+ * "直覺：閃電索引器，而非割草機" and "DSA 可能如何選擇保留內容": keep a local window of
+ * neighbours and always-connected global tokens, add salience-chosen far
+ * tokens, attend over the union; V4 section "滑动窗口 KV Cache 与混合策略": the
+ * most recent tokens kept in full, older ones chosen by importance].  Per
+ * query row, with visible keys 0..pos:
+ *   forced  F = the first `sinks` keys and the last `window` visible keys;
+ *   C       = the visible keys outside F (sinks <= s <= pos - window);
+ *   picks   = the m = min(k, |C|) highest-scoring keys of C (lower index first
+ *             among equal scores);
+ *   idx row = F together with the picks, ascending, then -1, width
+ *             k + sinks + window.
+ *   kth     = the m-th highest score among the picks, NaN when m = 0.
+ * With sinks = window = 0 this is ora_topk.
+ */
+void ora_select_backbone(int64_t n_q, int64_t n_k, const double *scores, const int64_t *pos,
+                         int64_t k, int64_t sinks, int64_t window, int32_t *idx, double *kth)
+{
+    const int64_t width = k + sinks + window;
+    #pragma omp parallel
+    {
+        ora_pair *cand = (ora_pair *)malloc(sizeof(ora_pair) * (size_t)(n_k > 0 ? n_k : 1));
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_q; ++t) {
+            int64_t visible = pos[t] + 1;
+            if (visible > n_k) visible = n_k;
+            if (visible < 0) visible = 0;
+            int32_t *dst = idx + t * width;
+            int64_t n = 0;
+            /* the forced keys */
+            for (int64_t s = 0; s < visible; ++s)
+                if (s < sinks || s >= visible - window)
+                    dst[n++] = (int32_t)s;
+            /* the candidates and their m best */
+            int64_t nc = 0;
+            for (int64_t s = 0; s < visible; ++s)
+                if (!(s < sinks || s >= visible - window)) {
+                    cand[nc].score = scores[t * n_k + s];
+                    cand[nc].index = s;
+                    ++nc;
+                }
+            qsort(cand, (size_t)nc, sizeof(ora_pair), cmp_score_desc_index_asc);
+            int64_t m = nc < k ? nc : k;
+            for (int64_t j = 0; j < m; ++j)
+                dst[n++] = (int32_t)cand[j].index;
+            qsort(dst, (size_t)n, sizeof(int32_t), cmp_i32_asc);
+            for (int64_t j = n; j < width; ++j)
+                dst[j] = -1;
+            if (kth)
+                kth[t] = m > 0 ? cand[m - 1].score : NAN;
+        }
+        free(cand);
+    }
+}
+
+/*
  * Main attention over the selected rows only [DD §1: the main attention looks
  * at the selected subset; O(n*k)].  One sequence:
  *   q   [n_q, Hq, dqk]                      (dtype)

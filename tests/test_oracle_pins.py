@@ -183,6 +183,69 @@ def test_topk_brute_force_with_ties(seed):
         assert kth[t] == min(scores[t, i] for i in want[:m])
 
 
+def _brute_backbone(scores_row, visible, k, sinks, window):
+    """Forced first `sinks` and last `window` visible keys, plus the max-sum size-m subset of the rest
+    (ties -> lexicographically smallest), ascending, padded with -1 to k + sinks + window."""
+    forced = [s for s in range(visible) if s < sinks or s >= visible - window]
+    rest = [s for s in range(visible) if s not in forced]
+    m = min(k, len(rest))
+    best, best_sum = (), -math.inf
+    for comb in itertools.combinations(rest, m):          # lexicographic order of positions
+        tot = sum(scores_row[i] for i in comb)
+        if tot > best_sum:
+            best, best_sum = comb, tot
+    row = sorted(forced + list(best))
+    return row + [-1] * (k + sinks + window - len(row)), best
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_backbone_selection_brute_force(seed):
+    rng = np.random.default_rng(300 + seed)
+    L = int(rng.integers(1, 12))
+    k, sinks, window = (int(x) for x in rng.integers(0, 4, size=3))
+    k = max(k, 1)
+    scores = rng.integers(-2, 3, size=(L, L)).astype(np.float64)  # many exact ties
+    pos = np.arange(L)
+    for t in range(L):
+        scores[t, t + 1:] = -np.inf
+    idx, kth = oracle.select_backbone(scores, k, sinks, window, pos)
+    assert idx.shape == (L, k + sinks + window)
+    for t in range(L):
+        want, picks = _brute_backbone(scores[t], t + 1, k, sinks, window)
+        assert idx[t].tolist() == want, (t, sinks, window, k, scores[t], idx[t], want)
+        if picks:
+            assert kth[t] == min(scores[t, i] for i in picks)
+        else:
+            assert math.isnan(kth[t])
+
+
+def test_backbone_without_forced_keys_is_topk():
+    rng = np.random.default_rng(31)
+    sc = rng.standard_normal((40, 60))
+    pos = rng.integers(-1, 60, size=40)
+    a, ka = oracle.select_backbone(sc, 7, 0, 0, pos)
+    b, kb = oracle.topk(sc, 7, pos)
+    assert np.array_equal(a, b) and np.array_equal(ka, kb, equal_nan=True)
+
+
+def test_backbone_forced_keys_do_not_use_the_budget():
+    """The window holds the highest scores, yet the k picks all come from outside it."""
+    n = 50
+    sc = np.tile(np.arange(n, dtype=np.float64), (1, 1))        # score = position: recent keys score highest
+    idx, _ = oracle.select_backbone(sc, 5, 2, 10, [n - 1])
+    row = [s for s in idx[0].tolist() if s >= 0]
+    assert row == [0, 1] + list(range(35, 40)) + list(range(40, 50))
+
+
+def test_backbone_covering_everything_keeps_the_prefix():
+    rng = np.random.default_rng(32)
+    sc = rng.standard_normal((6, 30))
+    pos = np.array([0, 3, 10, 19, 25, 29])
+    idx, _ = oracle.select_backbone(sc, 10, 4, 16, pos)            # k + sinks + window = 30 >= every prefix
+    for t, p in enumerate(pos):
+        assert idx[t].tolist() == list(range(p + 1)) + [-1] * (30 - p - 1)
+
+
 def test_topk_all_zero_weights_selects_first_positions():
     rng = np.random.default_rng(8)
     iq, ik, iw = _rand_index_problem(rng, n_q=9, n_k=9)
