@@ -22,6 +22,16 @@
  *            I = sq*sk * sum_h w*ReLU(code.code) exactly (scales are > 0).
  *   top-k    m = min(top_k, pos(t)+1) keys with the highest I; among equal I
  *            the lower position wins; -0.0 equals +0.0.
+ *   backbone optional forced keys: the first sink_tokens keys and the last
+ *            local_window visible keys of each row are always kept, and the
+ *            top-k runs over the visible keys between them (m = min(top_k,
+ *            their count)); the selection is the union.  This is the local
+ *            window + global tokens + salience-chosen far tokens of "DeepSeek
+ *            Sparse Attention" (sider.ai essay "sparse-attention-that-isn-t-
+ *            sparse-thinking", section "DSA 可能如何選擇保留內容"), and the recent-
+ *            window KV of "DeepSeek-V4 百万 token 上下文的工程实现", section
+ *            "滑动窗口 KV Cache 与混合策略".  A selection row has W = top_k +
+ *            sink_tokens + local_window entries.
  *   attn     for each query head h (kv head g = h / (q_heads/kv_heads)):
  *            z_j = softmax_scale * q[t,h].k[s_j,g] over the kept rows s_j,
  *            out = sum_j softmax(z)_j * v[s_j,g], lse = log sum_j exp(z_j).
@@ -139,6 +149,9 @@ typedef struct {
 
     int32_t top_k;            /* k, 1..8192 */
     int32_t attn_mode;        /* dsa_attn_mode_t */
+    int32_t sink_tokens;      /* >= 0: the first sink_tokens keys are always kept (0 = none) */
+    int32_t local_window;     /* >= 0: the last local_window visible keys are always kept (0 = none);
+                                 top_k + sink_tokens + local_window <= 16384 */
 } dsa_problem_t;
 
 /* DSA_ABI_VERSION of the loaded library. */
@@ -155,22 +168,26 @@ dsa_status_t dsa_index_scores(const dsa_problem_t *p, float *scores, hipStream_t
 
 /* Top-k selector, unfused.  scores: [B, n_q, n_k] fp32 as written by
  * dsa_index_scores (entries past pos(t) are ignored whatever they hold);
- * idx: [B, n_q, top_k] int32, the m = min(top_k, pos(t)+1) kept positions in
- * ascending order, then -1.  Among equal scores the lower position wins. */
+ * idx: [B, n_q, W] int32 (W = top_k + sink_tokens + local_window), the kept
+ * positions in ascending order, then -1: the m = min(top_k, pos(t)+1) best
+ * keys, or with a backbone its forced keys and the best top_k between them.
+ * Among equal scores the lower position wins. */
 dsa_status_t dsa_topk(const dsa_problem_t *p, const float *scores, int32_t *idx,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Attention over the selected rows only, unfused.  idx: [B, n_q, kk] int32 with
- * kk = p->top_k (any entries; invalid ones skipped); out: [B, n_q, Hq, d_v] in
- * attn_dtype; lse: [B, n_q, Hq] fp32 natural-log sum-exp, or NULL. */
+/* Attention over the selected rows only, unfused.  idx: [B, n_q, W] int32 with
+ * W = top_k + sink_tokens + local_window (any entries; invalid ones skipped);
+ * out: [B, n_q, Hq, d_v] in attn_dtype; lse: [B, n_q, Hq] fp32 natural-log
+ * sum-exp, or NULL. */
 dsa_status_t dsa_sparse_attn(const dsa_problem_t *p, const int32_t *idx, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Fused prefill: indexer, top-k and sparse attention for every query row.  The
  * full [n_q, n_k] score matrix is never held in memory: scores are produced
  * and consumed one bounded block of query rows at a time inside the
- * workspace.  idx_out: [B, n_q, top_k] or NULL (then kept in the workspace).
- * A row with pos(t) + 1 <= top_k keeps every visible key whatever the scores,
+ * workspace.  idx_out: [B, n_q, W] (W = top_k + sink_tokens + local_window)
+ * or NULL (then kept in the workspace).
+ * A row with pos(t) + 1 <= W keeps every visible key whatever the scores,
  * so when q_pos is NULL, blocks of such rows skip the indexer and the top-k
  * (their selection is written as 0..pos(t) directly) and a problem made only
  * of such rows is dense causal attention. */

@@ -52,6 +52,7 @@ class Problem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("top_k", ctypes.c_int32),
         ("attn_mode", ctypes.c_int32),
+        ("sink_tokens", ctypes.c_int32), ("local_window", ctypes.c_int32),
     ]
 
 
@@ -139,6 +140,12 @@ class DSAProblem:
     def rows(self) -> int:
         return self.struct.batch * self.struct.n_q
 
+    @property
+    def sel_width(self) -> int:
+        """Entries of a selection row: top_k + sink_tokens + local_window."""
+        s = self.struct
+        return s.top_k + s.sink_tokens + s.local_window
+
     def ref(self):
         return ctypes.byref(self.struct)
 
@@ -159,7 +166,7 @@ def _contig(name, t, device, dtypes=None):
 
 def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik_scale=None,
                  q_pos=None, softmax_scale=None, latent_dv=None, k_scale=None, v_scale=None,
-                 attn_mode: int = ATTN_AUTO) -> DSAProblem:
+                 attn_mode: int = ATTN_AUTO, sink_tokens: int = 0, local_window: int = 0) -> DSAProblem:
     """Describe one batch: see include/dsa.h for the layouts.
 
     iq [B,n_q,H,128], ik [B,n_k,128] (fp32 | bf16 | float8_e4m3fn, same dtype),
@@ -169,6 +176,8 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     q_pos [B,n_q] int32 or None.  k and v have q's dtype, or float8_e4m3fn
     (an FP8 cache, q bf16) with k_scale [B,n_k,Hkv] and, unless latent,
     v_scale [B,n_k,Hkv] fp32.  attn_mode: ATTN_AUTO, ATTN_GATHER or ATTN_MASKED.
+    sink_tokens / local_window: the backbone's forced keys (the first sink_tokens
+    and last local_window visible keys), kept besides the top_k best between them.
     """
     device = iq.device
     idt = (torch.float32, torch.bfloat16, torch.float8_e4m3fn)
@@ -200,6 +209,7 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     p.ik_scale = None if ik_scale is None else ik_scale.data_ptr()
     p.top_k = int(top_k)
     p.attn_mode = int(attn_mode)
+    p.sink_tokens, p.local_window = int(sink_tokens), int(local_window)
     tensors = dict(iq=iq, ik=ik, iw=iw, iq_scale=iq_scale, ik_scale=ik_scale, q_pos=q_pos)
     if q is not None:
         adt = (torch.float32, torch.bfloat16)
@@ -265,10 +275,10 @@ def index_scores(prob: DSAProblem, scores=None, stream=None):
 
 
 def topk(prob: DSAProblem, scores, idx=None, workspace=None, stream=None):
-    """idx [B,n_q,top_k] int32: kept positions ascending, then -1."""
+    """idx [B,n_q,sel_width] int32: kept positions ascending, then -1."""
     s = prob.struct
     if idx is None:
-        idx = torch.empty((s.batch, s.n_q, s.top_k), dtype=torch.int32, device=prob.device)
+        idx = torch.empty((s.batch, s.n_q, prob.sel_width), dtype=torch.int32, device=prob.device)
     ws = _workspace(OP_TOPK, prob, workspace)
     _check(load_library().dsa_topk(prob.ref(), _ptr(scores), _ptr(idx), _ptr(ws), ws.numel(),
                                    _stream(stream)))

@@ -72,6 +72,7 @@ hipError_t timer_mark(int ph, hipStream_t st) {
 }
 
 constexpr int kMaxNk = 1 << 24;
+constexpr int kMaxSelWidth = 16384;   // entries of a selection row (top_k + sinks + window)
 constexpr size_t kAlign = 256;
 // Query rows whose scores the fused prefill keeps at once (bounded scratch).
 constexpr size_t kPrefillScoreBytes = size_t(256) << 20;
@@ -104,11 +105,16 @@ dsa_status_t check_index(const dsa_problem_t* p) {
 dsa_status_t check_topk(const dsa_problem_t* p) {
     if (p->top_k < 1 || p->top_k > dsa::kTopkMaxK)
         return fail(DSA_E_UNSUPPORTED, "top_k must be in 1..%d (got %d)", dsa::kTopkMaxK, p->top_k);
+    if (p->sink_tokens < 0 || p->local_window < 0)
+        return fail(DSA_E_INVALID, "sink_tokens and local_window must be >= 0 (got %d, %d)", p->sink_tokens,
+                    p->local_window);
+    if (static_cast<int64_t>(p->top_k) + p->sink_tokens + p->local_window > kMaxSelWidth)
+        return fail(DSA_E_UNSUPPORTED, "top_k + sink_tokens + local_window must be <= %d", kMaxSelWidth);
     return DSA_OK;
 }
 
-static_assert(DSA_ATTN_AUTO == dsa::ATTN_AUTO && DSA_ATTN_GATHER == dsa::ATTN_GATHER &&
-              DSA_ATTN_MASKED == dsa::ATTN_MASKED, "attention modes");
+static_assert(int(DSA_ATTN_AUTO) == int(dsa::ATTN_AUTO) && int(DSA_ATTN_GATHER) == int(dsa::ATTN_GATHER) &&
+              int(DSA_ATTN_MASKED) == int(dsa::ATTN_MASKED), "attention modes");
 
 // Shapes the masked (dense tile) kernels take.
 bool masked_shape(const dsa_problem_t* p) {
@@ -151,6 +157,10 @@ dsa_status_t check_attn(const dsa_problem_t* p) {
 
 int rows_of(const dsa_problem_t* p) { return p->batch * p->n_q; }
 
+// Entries of a selection row: the k picks plus a backbone's forced keys.
+int sel_width(const dsa_problem_t* p) { return p->top_k + p->sink_tokens + p->local_window; }
+bool has_backbone(const dsa_problem_t* p) { return p->sink_tokens > 0 || p->local_window > 0; }
+
 dsa::IndexArgs index_args(const dsa_problem_t* p, int row0, int rows, float* scores) {
     dsa::IndexArgs a{};
     a.rows = rows; a.row0 = row0;
@@ -168,6 +178,7 @@ dsa::TopkArgs topk_args(const dsa_problem_t* p, int row0, int rows, const float*
     dsa::TopkArgs a{};
     a.rows = rows; a.row0 = row0;
     a.n_q = p->n_q; a.n_k = p->n_k; a.k = p->top_k;
+    a.sinks = p->sink_tokens; a.window = p->local_window;
     a.q_pos = p->q_pos;
     a.scores = scores;
     a.idx = idx;
@@ -178,7 +189,7 @@ dsa::TopkArgs topk_args(const dsa_problem_t* p, int row0, int rows, const float*
 
 dsa::AttnArgs attn_args(const dsa_problem_t* p, const int32_t* idx, void* out, float* lse) {
     dsa::AttnArgs a{};
-    a.rows = rows_of(p); a.n_q = p->n_q; a.n_k = p->n_k; a.kk = p->top_k;
+    a.rows = rows_of(p); a.n_q = p->n_q; a.n_k = p->n_k; a.kk = sel_width(p);
     a.Hq = p->q_heads; a.Hkv = p->kv_heads; a.dqk = p->d_qk; a.dv = p->d_v;
     a.latent = p->kv_latent ? 1 : 0; a.dtype = p->attn_dtype; a.kv_dtype = p->kv_dtype;
     a.q = p->q; a.k = p->k; a.v = p->v; a.idx = idx; a.q_pos = p->q_pos;
@@ -207,11 +218,11 @@ int block_max_pos(const dsa_problem_t* p, int r0, int nr) {
     return p->n_k - p->n_q + t_max;
 }
 
-// Every row of the block keeps all its visible keys (top_k >= pos(t) + 1):
-// the selection is 0..pos(t) whatever the scores.
+// Every row of the block keeps all its visible keys (top_k + sinks + window
+// >= pos(t) + 1): the selection is 0..pos(t) whatever the scores.
 bool block_keeps_all(const dsa_problem_t* p, int r0, int nr) {
     const int mp = block_max_pos(p, r0, nr);
-    return mp >= 0 && mp + 1 <= p->top_k;
+    return mp >= 0 && mp + 1 <= sel_width(p);
 }
 
 // Rows of scores the fused paths produce per round.
@@ -230,13 +241,15 @@ bool use_sampled(const dsa_problem_t* p) {
     dsa::IndexArgs probe{};
     probe.dtype = p->idx_dtype;
     probe.H = p->idx_heads;
-    return p->n_q < 16 && dsa::index_fp8_path(probe) && dsa::topk_sampled_eligible(p->n_k, p->top_k);
+    // (the sampled select ranks every visible key: no backbone)
+    return p->n_q < 16 && !has_backbone(p) && dsa::index_fp8_path(probe) &&
+           dsa::topk_sampled_eligible(p->n_k, p->top_k);
 }
 
 struct FusedLayout {
     bool sampled;
     int block_rows;
-    size_t scores_off, topk_off, idx_off, attn_off, total;
+    size_t scores_off, topk_off, picks_off, idx_off, attn_off, total;
 };
 
 FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
@@ -249,13 +262,22 @@ FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
         L.idx_off = align_up(dsa::topk_sampled_workspace_bytes(L.block_rows, p->n_k));
     } else {
         L.topk_off = align_up(static_cast<size_t>(L.block_rows) * p->n_k * sizeof(float));
-        L.idx_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
+        L.picks_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
+        // a backbone's top-k picks of one block, before the union
+        L.idx_off = L.picks_off + (has_backbone(p) ? align_up(static_cast<size_t>(L.block_rows) * p->top_k *
+                                                              sizeof(int32_t)) : 0);
     }
-    L.attn_off = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t)) : 0);
+    L.attn_off = L.idx_off + (need_idx ? align_up(static_cast<size_t>(rows_of(p)) * sel_width(p) * sizeof(int32_t)) : 0);
     dsa::AttnArgs aa = attn_args(p, nullptr, nullptr, nullptr);
     aa.all_visible = block_keeps_all(p, 0, rows_of(p));
     L.total = L.attn_off + align_up(dsa::attn_workspace_bytes(aa));
     return L;
+}
+
+// dsa_topk's workspace: the select's own, then a backbone's picks.
+size_t topk_ws_bytes(const dsa_problem_t* p) {
+    const size_t sel = align_up(dsa::topk_workspace_bytes(rows_of(p), p->n_k));
+    return sel + (has_backbone(p) ? static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t) : 0);
 }
 
 dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,
@@ -273,8 +295,8 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
         if (block_keeps_all(p, r0, nr)) {
             // no indexer and no top-k: the selection of every row is 0..pos(t)
-            s = device_status(dsa::launch_fill_prefix_idx(idx + static_cast<size_t>(r0) * p->top_k, r0, nr,
-                                                          p->n_q, p->n_k, p->top_k, st), "selection fill");
+            s = device_status(dsa::launch_fill_prefix_idx(idx + static_cast<size_t>(r0) * sel_width(p), r0, nr,
+                                                          p->n_q, p->n_k, sel_width(p), st), "selection fill");
             if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
             continue;
         }
@@ -295,9 +317,12 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         float* scores = reinterpret_cast<float*>(base + L.scores_off);
         dsa::IndexArgs ia = index_args(p, r0, nr, scores);
         ia.visible_only = true;
-        dsa::TopkArgs ta = topk_args(p, r0, nr, scores, idx + static_cast<size_t>(r0) * p->top_k,
-                                     base + L.topk_off);
-        if (dsa::index_fills_hist(ia) && !dsa::topk_row_lds(p->n_k)) {
+        int32_t* picks = has_backbone(p) ? reinterpret_cast<int32_t*>(base + L.picks_off)
+                                         : idx + static_cast<size_t>(r0) * p->top_k;
+        dsa::TopkArgs ta = topk_args(p, r0, nr, scores, picks, base + L.topk_off);
+        // (the indexer's histogram counts the real scores; a backbone ranks its
+        // forced keys as -inf, so the top-k builds its own)
+        if (dsa::index_fills_hist(ia) && !dsa::topk_row_lds(p->n_k) && !has_backbone(p)) {
             // the indexer builds the first-digit histogram as it writes the scores
             ia.hist = ta.hist;
             ta.hist_ready = true;
@@ -307,6 +332,10 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         s = device_status(dsa::launch_index_scores(ia, st), "indexer launch");
         if (s != DSA_OK || (s = mark(DSA_PHASE_INDEX)) != DSA_OK) return s;
         s = device_status(dsa::launch_topk(ta, st), "top-k launch");
+        if (s == DSA_OK && has_backbone(p))
+            s = device_status(dsa::launch_union_backbone(picks, idx + static_cast<size_t>(r0) * sel_width(p), r0, nr,
+                                                         p->n_q, p->n_k, p->q_pos, p->top_k, p->sink_tokens,
+                                                         p->local_window, st), "backbone union");
         if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
     }
     dsa::AttnArgs aa = attn_args(p, idx, out, lse);
@@ -332,7 +361,7 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
             return dsa::attn_workspace_bytes(attn_args(p, nullptr, nullptr, nullptr));
         case DSA_OP_TOPK:
             if (check_topk(p) != DSA_OK) return static_cast<size_t>(-1);
-            return dsa::topk_workspace_bytes(rows_of(p), p->n_k);
+            return topk_ws_bytes(p);
         case DSA_OP_PREFILL:
         case DSA_OP_DECODE:
             if (check_topk(p) != DSA_OK) return static_cast<size_t>(-1);
@@ -369,11 +398,20 @@ dsa_status_t dsa_topk(const dsa_problem_t* p, const float* scores, int32_t* idx,
     dsa_status_t s;
     if ((s = check_common(p)) != DSA_OK || (s = check_topk(p)) != DSA_OK) return s;
     if (!scores || !idx) return fail(DSA_E_INVALID, "scores and idx are required");
-    size_t need = dsa::topk_workspace_bytes(rows_of(p), p->n_k);
+    size_t need = topk_ws_bytes(p);
     if (!workspace || workspace_bytes < need)
         return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
-    dsa::TopkArgs a = topk_args(p, 0, rows_of(p), scores, idx, workspace);
-    return device_status(dsa::launch_topk(a, stream), "top-k launch");
+    if (!has_backbone(p)) {
+        dsa::TopkArgs a = topk_args(p, 0, rows_of(p), scores, idx, workspace);
+        return device_status(dsa::launch_topk(a, stream), "top-k launch");
+    }
+    int32_t* picks = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) +
+                                                align_up(dsa::topk_workspace_bytes(rows_of(p), p->n_k)));
+    dsa::TopkArgs a = topk_args(p, 0, rows_of(p), scores, picks, workspace);
+    s = device_status(dsa::launch_topk(a, stream), "top-k launch");
+    if (s != DSA_OK) return s;
+    return device_status(dsa::launch_union_backbone(picks, idx, 0, rows_of(p), p->n_q, p->n_k, p->q_pos, p->top_k,
+                                                    p->sink_tokens, p->local_window, stream), "backbone union");
 }
 
 dsa_status_t dsa_sparse_attn(const dsa_problem_t* p, const int32_t* idx, void* out, float* lse,

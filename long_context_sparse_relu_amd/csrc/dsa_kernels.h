@@ -56,6 +56,7 @@ struct TopkArgs {
     uint64_t* cand;
     int cand_cap;
     bool hist_ready;       // hist..count were zeroed and the scores producer filled hist
+    int sinks, window;     // backbone: the first `sinks` and last `window` visible keys rank as -inf
 };
 
 size_t topk_workspace_bytes(int rows, int n_k);
@@ -69,6 +70,11 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 // idx[r][j] = j for j <= pos(row0 + r), else -1 (pos from n_k - n_q + t): the
 // top-k result of a row that keeps every visible key.
 hipError_t launch_fill_prefix_idx(int32_t* idx, int row0, int rows, int n_q, int n_k, int k, hipStream_t st);
+// Backbone union: idx[r] (width k + sinks + window) = the first min(sinks,
+// vis) keys, the picks[r] (width k, ascending) between the forced sets, the
+// last window keys, then -1.
+hipError_t launch_union_backbone(const int32_t* picks, int32_t* idx, int row0, int rows, int n_q, int n_k,
+                                 const int32_t* q_pos, int k, int sinks, int window, hipStream_t st);
 
 // Attention modes (dsa_attn_mode_t).
 enum AttnMode { ATTN_AUTO = 0, ATTN_GATHER = 1, ATTN_MASKED = 2 };

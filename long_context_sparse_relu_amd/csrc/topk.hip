@@ -67,8 +67,70 @@ hipError_t launch_fill_prefix_idx(int32_t* idx, int row0, int rows, int n_q, int
     return hipGetLastError();
 }
 
+// The union of a backbone selection: row r of idx (width k + sinks + window)
+// = the forced first keys 0..min(sinks, vis)-1, the picks that lie between
+// the forced sets (ascending in picks; a row with fewer than k such keys also
+// picked some forced ones, which are dropped), then the window keys
+// max(sinks, vis - window)..vis-1, then -1.  All three parts are ascending
+// and in that order, so the row is ascending.  One workgroup per row.
+__global__ __launch_bounds__(256) void k_union_backbone(const int32_t* picks, int32_t* idx, int row0, int n_q,
+                                                        int n_k, const int32_t* q_pos, int k, int sinks,
+                                                        int window) {
+    __shared__ int cnt[2][4];
+    const int r = blockIdx.x;
+    const int vis = row_pos(q_pos, row0 + r, n_q, n_k) + 1;
+    const int v = vis > 0 ? vis : 0;
+    const int ns = min(sinks, v);
+    const int wlo = max(sinks, v - window);
+    const int nw = max(0, v - wlo);
+    const int32_t* pr = picks + static_cast<size_t>(r) * k;
+    // picks below `sinks` come first and picks at or past v - window last
+    int below = 0, inside = 0;
+    for (int j = threadIdx.x; j < k; j += blockDim.x) {
+        const int p = pr[j];
+        below += p >= 0 && p < sinks;
+        inside += p >= sinks && p < v - window;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        below += __shfl_xor(below, o);
+        inside += __shfl_xor(inside, o);
+    }
+    if ((threadIdx.x & 63) == 0) { cnt[0][threadIdx.x >> 6] = below; cnt[1][threadIdx.x >> 6] = inside; }
+    __syncthreads();
+    const int a0 = cnt[0][0] + cnt[0][1] + cnt[0][2] + cnt[0][3];
+    const int np = cnt[1][0] + cnt[1][1] + cnt[1][2] + cnt[1][3];
+    const int width = k + sinks + window;
+    int32_t* out = idx + static_cast<size_t>(r) * width;
+    for (int j = threadIdx.x; j < width; j += blockDim.x) {
+        int val = -1;
+        if (j < ns) val = j;
+        else if (j < ns + np) val = pr[a0 + (j - ns)];
+        else if (j < ns + np + nw) val = wlo + (j - ns - np);
+        out[j] = val;
+    }
+}
+
+hipError_t launch_union_backbone(const int32_t* picks, int32_t* idx, int row0, int rows, int n_q, int n_k,
+                                 const int32_t* q_pos, int k, int sinks, int window, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_union_backbone, dim3(rows), dim3(256), 0, st, picks, idx, row0, n_q, n_k, q_pos, k,
+                       sinks, window);
+    return hipGetLastError();
+}
+
 __device__ __forceinline__ int row_visible(const TopkArgs& a, int row) {
     return row_pos(a.q_pos, row, a.n_q, a.n_k) + 1;   // 0..n_k
+}
+
+// A score as the selection ranks it: with a backbone, the forced keys of the
+// row (its first `sinks` and last `window` visible keys) rank as -inf, so the
+// k picks come from the keys between them whenever there are k of those; the
+// union step adds the forced keys and drops any forced key picked to fill k.
+// The load is unconditional (no branch around it).
+__device__ __forceinline__ float ranked(const TopkArgs& a, const float* sc, int s, int vis) {
+    const float x = sc[s];
+    return (s < a.sinks || s >= vis - a.window) ? -__builtin_inff() : x;
 }
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int s) {
@@ -90,7 +152,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topk_hist(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
         int s = c0 + u * kFilterThreads + threadIdx.x;
-        x[u] = s < c1 ? sc[s] : 0.0f;
+        x[u] = s < c1 ? ranked(a, sc, s, vis) : 0.0f;
     }
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
     __syncthreads();
@@ -141,7 +203,7 @@ __global__ __launch_bounds__(kFThreads) void k_topk_filter(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < kFPer; ++u) {
         int s = c0 + u * kFThreads + threadIdx.x;
-        x[u] = s < c1 ? sc[s] : 0.0f;
+        x[u] = s < c1 ? ranked(a, sc, s, vis) : 0.0f;
     }
     uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
     const int d0 = static_cast<int>(meta[M_D0]);
@@ -199,9 +261,11 @@ struct CandList {
 };
 struct CandRow {
     const float* sc; int n; int d0;
+    int lo, hi;                 // keys outside [lo, hi) rank as -inf (a backbone's forced keys)
     __device__ int size() const { return n; }
     __device__ bool get(int i, uint64_t* out) const {
-        uint32_t key = order_key(sc[i]);
+        const float x = sc[i];
+        uint32_t key = order_key(i < lo || i >= hi ? -__builtin_inff() : x);
         if (static_cast<int>(key >> 21) != d0) return false;
         *out = composite(key, i);
         return true;
@@ -278,7 +342,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
         }
     } else {
         // the list overflowed: read the row again, filtered to the d0 bin
-        CandRow row_src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, d0};
+        CandRow row_src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, d0, a.sinks, vis - a.window};
         for_each_candidate(row_src, [&](uint64_t c) {
             int dg = static_cast<int>(c >> 42);
             if (dg > d1 || (dg == d1 && whole_bin)) sink.put_c(c);
@@ -348,7 +412,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
     for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * kRowThreads) {
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = sc[min(i0 + u * kRowThreads, vis - 1)];
+        for (int u = 0; u < 8; ++u) v[u] = ranked(a, sc, min(i0 + u * kRowThreads, vis - 1), vis);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = i0 + u * kRowThreads;

@@ -67,3 +67,37 @@ def check_attn(gpu_out, gpu_lse, ora_out, ora_lse, dtype):
         lerr = np.abs(gl[fin] - ora_lse[fin]).max()
         assert lerr <= LSE_TOL[dtype], f"lse error {lerr}"
     return float(err)
+
+
+def check_backbone_row(gpu_idx, ora_idx, ora_scores, kth, pos, k, sinks, window):
+    """A backbone selection row: its forced keys exactly, then the top-k rule on the picks.
+
+    The forced keys are the first `sinks` and last `window` visible ones; the
+    picks are the kept keys between them, m = min(k, their count) of them,
+    compared with the oracle's under the same swap tolerance as check_topk_row.
+    Returns the number of allowed swaps.
+    """
+    gpu_idx = np.asarray(gpu_idx)
+    vis = max(0, min(pos + 1, len(ora_scores)))
+    forced = {s for s in range(vis) if s < sinks or s >= vis - window}
+    n_rest = vis - len(forced)
+    m = min(k, n_rest)
+    total = len(forced) + m
+    assert np.all(gpu_idx[total:] == -1), f"padding: {gpu_idx[total:][:8]}"
+    g = gpu_idx[:total]
+    assert np.all(g >= 0) and np.all(g <= pos), "kept positions must be visible"
+    assert np.all(np.diff(g) > 0), "kept positions must be distinct and ascending"
+    G = set(g.tolist())
+    assert forced <= G, f"forced keys missing: {sorted(forced - G)[:8]}"
+    O = set(int(x) for x in ora_idx[:total])
+    assert forced <= O
+    pg, po = G - forced, O - forced
+    assert len(pg) == len(po) == m
+    if pg == po:
+        return 0
+    only_o = np.array(sorted(po - pg))
+    only_g = np.array(sorted(pg - po))
+    tau = TAU_REL * abs(kth)
+    gap = ora_scores[only_o].max() - ora_scores[only_g].min()
+    assert gap < tau, (f"backbone swap beyond tolerance: dropped {only_o[:4]} kept {only_g[:4]}, tau {tau}")
+    return len(only_o)

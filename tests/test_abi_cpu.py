@@ -104,6 +104,9 @@ FAKE = ctypes.c_void_p(0x7F0000000000)
     (dict(kv_dtype=dsa.FP8_E4M3, attn_dtype=dsa.F32, k_scale=0x7F0000000000,
           v_scale=0x7F0000000000), dsa.E_UNSUPPORTED),                        # FP8 cache needs bf16 q
     (dict(attn_mode=3), dsa.E_INVALID),
+    (dict(sink_tokens=-1), dsa.E_INVALID),
+    (dict(local_window=-5), dsa.E_INVALID),
+    (dict(top_k=8192, local_window=8193), dsa.E_UNSUPPORTED),          # selection row over 16384 entries
     (dict(attn_mode=dsa.ATTN_MASKED, q_heads=4, kv_heads=1, kv_latent=1, d_qk=576, d_v=512, v=None),
      dsa.E_UNSUPPORTED),                                                     # masked: d128 only
     (dict(softmax_scale=0.0), dsa.E_INVALID),

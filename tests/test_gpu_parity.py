@@ -15,7 +15,7 @@ import torch
 import long_context_sparse_relu_amd as dsa
 import oracle
 from dsa_inputs import custom_spec, make_inputs, oracle_view, spec
-from parity import check_attn, check_scores, check_topk_row
+from parity import check_attn, check_backbone_row, check_scores, check_topk_row
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -26,7 +26,8 @@ def _problem(inp, row_sel=None):
     kw = dict(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=inp["top_k"], q=inp["q"],
               k=inp["k"], v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
               softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
-              k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
+              k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"),
+              sink_tokens=inp.get("sinks", 0), local_window=inp.get("window", 0))
     if row_sel is not None:
         sel = torch.as_tensor(row_sel, dtype=torch.long, device=DEV)
         for name in ("iq", "iw", "q", "iq_scale"):
@@ -73,13 +74,20 @@ def run_case(inp, seqs, rows, fused="prefill", check_e2e=True):
         iks = None if ov["ik_scale"] is None else ov["ik_scale"][j]
         ora_sc = oracle.index_scores(ov["iq"][j][rows], ov["ik"][j], ov["iw"][j][rows],
                                      inp["idx_dtype"], iqs, iks, pos)
-        ora_idx, kth = oracle.topk(ora_sc, k, pos)
+        sinks, window = inp.get("sinks", 0), inp.get("window", 0)
+        if sinks or window:
+            ora_idx, kth = oracle.select_backbone(ora_sc, k, sinks, window, pos)
+        else:
+            ora_idx, kth = oracle.topk(ora_sc, k, pos)
         g_sc = scores[b][rows].cpu().numpy()
         g_idx = idx[b][rows].cpu().numpy()
         same = []
         for r in range(len(rows)):
             stats["score_err"] = max(stats["score_err"], check_scores(g_sc[r], ora_sc[r], pos[r]))
-            n = check_topk_row(g_idx[r], ora_idx[r], ora_sc[r], kth[r], pos[r], k)
+            if sinks or window:
+                n = check_backbone_row(g_idx[r], ora_idx[r], ora_sc[r], kth[r], pos[r], k, sinks, window)
+            else:
+                n = check_topk_row(g_idx[r], ora_idx[r], ora_sc[r], kth[r], pos[r], k)
             swaps += n
             same.append(n == 0)
         # attention over the oracle's index set, through a q_pos sub-problem
@@ -89,7 +97,7 @@ def run_case(inp, seqs, rows, fused="prefill", check_e2e=True):
                         **{n: None if inp.get(n) is None else inp[n][b:b + 1]
                            for n in ("iq_scale", "ik_scale", "k_scale", "v_scale")}},
                        row_sel=rows)
-        o_idx_dev = torch.from_numpy(ora_idx).to(DEV).reshape(1, len(rows), k).contiguous()
+        o_idx_dev = torch.from_numpy(ora_idx).to(DEV).reshape(1, len(rows), ora_idx.shape[1]).contiguous()
         g_out, g_lse = dsa.sparse_attn(sub, o_idx_dev)
         torch.cuda.synchronize()
         v = None if ov["v"] is None else ov["v"][j]
@@ -150,6 +158,19 @@ EDGE_CASES = {
                          kv_heads=1, d_qk=576, d_v=512, latent=True, attn_dtype="bf16", kv_dtype="e4m3"),
     "fp8kv_generic_d64": dict(n_q=20, n_k=1500, idx_heads=4, top_k=77, q_heads=8, kv_heads=2,
                               d_qk=64, d_v=64, attn_dtype="bf16", idx_dtype="bf16", kv_dtype="e4m3"),
+    # backbone: forced first sink keys and last window keys, top-k between them
+    "backbone_prefill": dict(n_q=300, n_k=2000, idx_heads=8, idx_dtype="bf16", top_k=100, q_heads=8,
+                             kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16", sinks=4, window=64),
+    "backbone_decode_fp8": dict(B=4, n_q=1, n_k=50000, idx_heads=16, idx_dtype="e4m3", top_k=512, q_heads=32,
+                                kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16", sinks=16, window=2048),
+    "backbone_window_covers": dict(n_q=20, n_k=40, idx_heads=3, top_k=4, q_heads=2, kv_heads=2, d_qk=64,
+                                   d_v=64, sinks=2, window=30),
+    "backbone_sinks_only": dict(n_q=37, n_k=9000, idx_heads=4, top_k=100, q_heads=4, kv_heads=2, d_qk=64,
+                                d_v=64, sinks=8),
+    "backbone_long_rows": dict(n_q=16, n_k=40000, idx_heads=16, idx_dtype="e4m3", top_k=300, q_heads=8,
+                               kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16", sinks=3, window=1000),
+    "backbone_short_prompt": dict(B=2, n_q=200, n_k=200, idx_heads=8, idx_dtype="bf16", top_k=50, q_heads=4,
+                                  kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16", sinks=10, window=150),
 }
 
 
