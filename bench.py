@@ -334,9 +334,10 @@ def main(argv=None):
     prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
                             v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
                             softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
-                            k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                            sink_tokens=s.get("sinks", 0), local_window=s.get("window", 0))
     out, lse = dsa._out_tensors(prob, None, None)
-    idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, n_q, prob.sel_width), dtype=torch.int32, device=dev)
     op = dsa.OP_DECODE if decode else dsa.OP_PREFILL
     ws = torch.empty(dsa.workspace_bytes(op, prob), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -392,7 +393,7 @@ def main(argv=None):
                            + (4 * n_rows_kv if kvt == "e4m3" else 0))
     # visible keys and kept keys summed over every query row
     pairs = sum(N - n_q + t + 1 for t in range(n_q)) * B
-    kept = sum(min(k, N - n_q + t + 1) for t in range(n_q)) * B
+    kept = sum(min(prob.sel_width, N - n_q + t + 1) for t in range(n_q)) * B
     gather_bytes = kept * row
     attn_flops = 2 * kept * s["q_heads"] * (s["d_qk"] + s["d_v"])
     if decode:
@@ -445,7 +446,7 @@ def main(argv=None):
                    "idx_heads": H, "idx_dim": D, "idx_dtype": s["idx_dtype"],
                    "q_heads": s["q_heads"], "kv_heads": s["kv_heads"], "d_qk": s["d_qk"],
                    "d_v": s["d_v"], "latent": s["latent"], "attn_dtype": s["attn_dtype"],
-                   "kv_dtype": kvt},
+                   "kv_dtype": kvt, "sink_tokens": s.get("sinks", 0), "local_window": s.get("window", 0)},
         "roofline": roof,
         "attn_roofline": attn_roof,
         "step_roofline": step_roof,

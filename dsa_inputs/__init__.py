@@ -25,6 +25,9 @@ w ~ N(0,1)/2, main q/k/v ~ N(0,1), softmax scale 1/sqrt(d_qk)):
                     256 planted needles per sequence
   decode_128k_fp8kv decode_128k with the main KV cache stored as E4M3 codes
                     and one fp32 scale per (token, kv head) row
+  decode_128k_backbone  decode_128k with 4 sink tokens and a 4096-key local
+                    window kept besides the top-k (sinks / window fields)
+  decode_1m_window  decode_1m with an 8192-key local window
 
 Any spec may set kv_dtype="e4m3" (with attn_dtype "bf16"): the main k and v
 are drawn as above and stored as E4M3 codes with one fp32 scale (amax/448) per
@@ -63,6 +66,8 @@ CONFIGS: dict[str, dict] = {
                       attn_dtype="bf16", needles=256, outlier_frac=0.0, w_bf16=False),
 }
 CONFIGS["decode_128k_fp8kv"] = dict(CONFIGS["decode_128k"], kv_dtype="e4m3")
+CONFIGS["decode_128k_backbone"] = dict(CONFIGS["decode_128k"], sinks=4, window=4096)
+CONFIGS["decode_1m_window"] = dict(CONFIGS["decode_1m"], window=8192)
 
 _TORCH_STORE = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
 _TENSOR_IDS = {"iq": 1, "ik": 2, "iw": 3, "q": 4, "k": 5, "v": 6, "needle": 7, "outlier": 8}

@@ -170,6 +170,7 @@ dsa::IndexArgs index_args(const dsa_problem_t* p, int row0, int rows, float* sco
     a.iw = p->iw;
     a.q_pos = p->q_pos;
     a.scores = scores;
+    a.sinks = p->sink_tokens; a.window = p->local_window;
     return a;
 }
 
@@ -241,9 +242,7 @@ bool use_sampled(const dsa_problem_t* p) {
     dsa::IndexArgs probe{};
     probe.dtype = p->idx_dtype;
     probe.H = p->idx_heads;
-    // (the sampled select ranks every visible key: no backbone)
-    return p->n_q < 16 && !has_backbone(p) && dsa::index_fp8_path(probe) &&
-           dsa::topk_sampled_eligible(p->n_k, p->top_k);
+    return p->n_q < 16 && dsa::index_fp8_path(probe) && dsa::topk_sampled_eligible(p->n_k, p->top_k);
 }
 
 struct FusedLayout {
@@ -259,7 +258,9 @@ FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
     L.scores_off = 0;
     if (L.sampled) {
         L.topk_off = 0;
-        L.idx_off = align_up(dsa::topk_sampled_workspace_bytes(L.block_rows, p->n_k));
+        L.picks_off = align_up(dsa::topk_sampled_workspace_bytes(L.block_rows, p->n_k));
+        L.idx_off = L.picks_off + (has_backbone(p) ? align_up(static_cast<size_t>(L.block_rows) * p->top_k *
+                                                              sizeof(int32_t)) : 0);
     } else {
         L.topk_off = align_up(static_cast<size_t>(L.block_rows) * p->n_k * sizeof(float));
         L.picks_off = L.topk_off + align_up(dsa::topk_workspace_bytes(L.block_rows, p->n_k));
@@ -304,13 +305,19 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
             dsa::SampledTopk t{};
             t.ix = index_args(p, r0, nr, nullptr);
             t.ix.k = p->top_k;
-            t.idx = idx + static_cast<size_t>(r0) * p->top_k;
+            int32_t* picks = has_backbone(p) ? reinterpret_cast<int32_t*>(base + L.picks_off)
+                                             : idx + static_cast<size_t>(r0) * p->top_k;
+            t.idx = picks;
             dsa::topk_sampled_carve(base, nr, p->n_k, t);
             s = device_status(dsa::launch_topk_sample(t, st), "top-k sample launch");
             if (s != DSA_OK || (s = mark(DSA_PHASE_PREP)) != DSA_OK) return s;
             s = device_status(dsa::launch_index_candidates(t.ix, st), "indexer launch");
             if (s != DSA_OK || (s = mark(DSA_PHASE_INDEX)) != DSA_OK) return s;
             s = device_status(dsa::launch_topk_finish_sampled(t, st), "top-k launch");
+            if (s == DSA_OK && has_backbone(p))
+                s = device_status(dsa::launch_union_backbone(picks, idx + static_cast<size_t>(r0) * sel_width(p), r0,
+                                                             nr, p->n_q, p->n_k, p->q_pos, p->top_k, p->sink_tokens,
+                                                             p->local_window, st), "backbone union");
             if (s != DSA_OK || (s = mark(DSA_PHASE_TOPK)) != DSA_OK) return s;
             continue;
         }

@@ -27,6 +27,9 @@ struct IndexArgs {
     uint32_t* meta;      // [rows][kTopkMeta]
     uint64_t* cand;      // [rows][cand_cap]
     int cand_cap;
+    // backbone (candidate mode and the sampled top-k): only keys in
+    // [sinks, pos + 1 - window) are ranked
+    int sinks, window;
 };
 
 // Top-k workspace (device), per row r:

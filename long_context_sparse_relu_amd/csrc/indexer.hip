@@ -123,7 +123,8 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
     if constexpr (CAND) {
         if (threadIdx.x == 0) n_c = 0;
         k_low = meta[S_KLOW];
-        collect = pos + 1 > x.k;          // rows that keep every visible key need no candidates
+        // rows that keep every ranked key need no candidates
+        collect = pos + 1 - x.window - x.sinks > x.k;
     } else if (hist) {
         for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
     }
@@ -159,7 +160,7 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
             const bool mine = s < s_end;
             if constexpr (CAND) {
                 const uint32_t key = order_key(part);
-                const bool take = mine && collect && s <= pos && key >= k_low;
+                const bool take = mine && collect && s >= x.sinks && s <= pos - x.window && key >= k_low;
                 const uint64_t m = __ballot(take);
                 if (m) {
                     uint32_t base_slot = 0;

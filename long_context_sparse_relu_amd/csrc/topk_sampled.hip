@@ -44,15 +44,29 @@ struct Cand64Rel {
 };
 struct ScoreRow64 {
     const float* sc; int n;
+    int lo, hi;                 // keys outside [lo, hi) rank as -inf (a backbone's forced keys)
     __device__ int size() const { return n; }
-    __device__ bool get(int i, uint64_t* out) const { *out = composite64(order_key(sc[i]), i); return true; }
+    __device__ bool get(int i, uint64_t* out) const {
+        const float x = sc[i];
+        *out = composite64(order_key(i < lo || i >= hi ? -__builtin_inff() : x), i);
+        return true;
+    }
 };
 
+// The ranked keys of a row: [lo, lo + cnt) = the visible keys outside a
+// backbone's forced first `sinks` and last `window` ones (all visible keys
+// without a backbone).
+struct Ranked { int lo, cnt; };
+__device__ __forceinline__ Ranked ranked_keys(const IndexArgs& x, int pos) {
+    const int hi = pos + 1 - x.window;
+    return Ranked{x.sinks, hi > x.sinks ? hi - x.sinks : 0};
+}
+
 // The sample: kSampleKeys keys per row as runs of 16 consecutive keys spread
-// evenly over the visible prefix (all of it when it is shorter); sample j is
-// key j when m == vis, else run j/16 starts at (j/16) * gap.
-__device__ __forceinline__ int sample_key(int j, int m, int vis, int gap) {
-    return m == vis ? j : (j >> 4) * gap + (j & 15);
+// evenly over the ranked keys (all of them when there are fewer); sample j is
+// ranked key j when m == cnt, else run j/16 starts at (j/16) * gap.
+__device__ __forceinline__ int sample_key(int j, int m, int cnt, int gap) {
+    return m == cnt ? j : (j >> 4) * gap + (j & 15);
 }
 
 // Score the row's samples: grid (kSampleSplit, rows), each workgroup scores
@@ -61,7 +75,8 @@ __global__ __launch_bounds__(256) void k_topk_sample_score(SampledTopk t) {
     const IndexArgs& x = t.ix;
     const int lrow = blockIdx.y, row = x.row0 + lrow;
     const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
-    const int vis = pos + 1;
+    const Ranked rk = ranked_keys(x, pos);
+    const int vis = rk.cnt;                  // keys the sample spreads over, from rk.lo
     if (vis <= x.k) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, kg = lane >> 4;
@@ -71,8 +86,8 @@ __global__ __launch_bounds__(256) void k_topk_sample_score(SampledTopk t) {
     const int j0 = blockIdx.x * per;
     if (j0 >= m) return;
     const int b = row / x.n_q;
-    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
-    const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
+    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + (static_cast<size_t>(b) * x.n_k + rk.lo) * 128;
+    const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k + rk.lo;
     uint32_t* skey = t.samples + static_cast<size_t>(lrow) * kSampleKeys;
     static_assert(kSampleKeys / kSampleSplit == 4 * 64, "one group of 64 samples per wave");
     // block u of this wave holds samples j0 + 64*wave + 16u + (0..15); lane l
@@ -101,10 +116,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
     const IndexArgs& x = t.ix;
     const int lrow = blockIdx.x, row = x.row0 + lrow;
     const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
-    const int vis = pos + 1;
+    const int vis = ranked_keys(x, pos).cnt;   // keys ranked (and sampled)
     uint32_t* meta = x.meta + static_cast<size_t>(lrow) * kTopkMeta;
     if (threadIdx.x == 0) { meta[S_NCAND] = 0u; meta[S_OVF] = 0u; meta[S_FALLBACK] = 0u; }
-    if (vis <= x.k) {                      // every visible key is kept: nothing to bound
+    if (vis <= x.k) {                      // every ranked key is kept: nothing to bound
         if (threadIdx.x == 0) meta[S_KLOW] = 0xFFFFFFFFu;
         return;
     }
@@ -177,10 +192,11 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
     const int lrow = blockIdx.x, row = x.row0 + lrow;
     const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
     const int vis = pos + 1;
+    const Ranked rk = ranked_keys(x, pos);
     const int k = x.k;
     int32_t* out = t.idx + static_cast<size_t>(lrow) * k;
-    if (vis <= k) {
-        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < vis ? j : -1;
+    if (rk.cnt <= k) {                     // every ranked key is kept
+        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < rk.cnt ? rk.lo + j : -1;
         return;
     }
     uint64_t* cl = reinterpret_cast<uint64_t*>(smem);                       // [cand_cap]
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
         }
         __threadfence_block();
         __syncthreads();
-        ScoreRow64 src{sc, vis};
+        ScoreRow64 src{sc, vis, rk.lo, rk.lo + rk.cnt};
         radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
     }
     __syncthreads();

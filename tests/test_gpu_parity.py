@@ -169,6 +169,13 @@ EDGE_CASES = {
                                 d_v=64, sinks=8),
     "backbone_long_rows": dict(n_q=16, n_k=40000, idx_heads=16, idx_dtype="e4m3", top_k=300, q_heads=8,
                                kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16", sinks=3, window=1000),
+    # the sampled decode select over the ranked keys only
+    "backbone_sampled_small_rest": dict(B=2, n_q=1, n_k=12000, idx_heads=16, idx_dtype="e4m3", top_k=512,
+                                        q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16", sinks=4,
+                                        window=11700),
+    "backbone_sampled_needles": dict(B=3, n_q=1, n_k=60000, idx_heads=16, idx_dtype="e4m3", top_k=256,
+                                     q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16", sinks=2,
+                                     window=4096, needles=64),
     "backbone_short_prompt": dict(B=2, n_q=200, n_k=200, idx_heads=8, idx_dtype="bf16", top_k=50, q_heads=4,
                                   kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16", sinks=10, window=150),
 }
