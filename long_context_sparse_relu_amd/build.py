@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "topk_sampled.hip", "attn.hip", "attn_wide.hip", "attn_masked.hip"]
+SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "topk_sampled.hip", "attn.hip", "attn_wide.hip", "attn_masked.hip", "attn_latent.hip"]
 
 
 def hipcc() -> str:

@@ -498,6 +498,7 @@ size_t attn_workspace_bytes(const AttnArgs& a) {
         const int s = gqa_splits(a);
         return s > 1 ? static_cast<size_t>(a.rows) * a.Hq * s * (128 + 2) * sizeof(float) : 0;
     }
+    if (attn_latent_eligible(a)) return attn_latent_workspace_bytes(a);
     if (!attn_wide_eligible(a)) return 0;
     return attn_wide_workspace_bytes(a);
 }
@@ -529,6 +530,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
         if (e != hipSuccess || s == 1) return e;
         return launch_attn_merge(a, s, part, st);
     }
+    if (attn_latent_eligible(a)) return launch_attn_latent(a, static_cast<float*>(ws), st);
     if (attn_wide_eligible(a)) return launch_attn_wide(a, static_cast<float*>(ws), st);
     const size_t smem = (static_cast<size_t>(kGenHC) * a.dqk + static_cast<size_t>(kGenTK) * a.dqk +
                          static_cast<size_t>(kGenTK) * a.dv) * sizeof(float);

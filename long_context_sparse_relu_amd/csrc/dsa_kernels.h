@@ -141,6 +141,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st);
 bool attn_masked_eligible(const AttnArgs& a);
 size_t attn_masked_workspace_bytes(const AttnArgs& a);
 hipError_t launch_attn_masked(const AttnArgs& a, void* ws, hipStream_t st);
+// Shared latent rows (576 wide, value = first 512), bf16: one workgroup per
+// (row, 128 heads, slice of the index list) sharing each gathered tile in LDS
+// (attn_latent.hip).
+bool attn_latent_eligible(const AttnArgs& a);
+size_t attn_latent_workspace_bytes(const AttnArgs& a);
+hipError_t launch_attn_latent(const AttnArgs& a, float* part, hipStream_t st);
 // MFMA kernel for wide rows / many heads per kv head (attn_wide.hip).
 bool attn_wide_eligible(const AttnArgs& a);
 size_t attn_wide_workspace_bytes(const AttnArgs& a);
