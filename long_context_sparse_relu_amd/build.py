@@ -30,7 +30,7 @@ def hipcc() -> str:
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+          "-Wall", "-Wno-unused-function", "-Werror=uninitialized", "-I", INCLUDE, "-I", CSRC]
 
 
 def _compile(src: str) -> str:

@@ -75,7 +75,10 @@ constexpr int kMaxNk = 1 << 24;
 constexpr int kMaxSelWidth = 16384;   // entries of a selection row (top_k + sinks + window)
 constexpr size_t kAlign = 256;
 // Query rows whose scores the fused prefill keeps at once (bounded scratch).
-constexpr size_t kPrefillScoreBytes = size_t(256) << 20;
+#ifndef DSA_PREFILL_SCORE_MB
+#define DSA_PREFILL_SCORE_MB 256
+#endif
+constexpr size_t kPrefillScoreBytes = size_t(DSA_PREFILL_SCORE_MB) << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 

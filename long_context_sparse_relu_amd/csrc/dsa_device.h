@@ -62,6 +62,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // ReLU as the signed-integer max of the bit pattern with 0: a negative float
 // (or -0.0) has the sign bit set and becomes +0.0, a positive one is kept.
 // One VALU op, where fmaxf on an MFMA result also pays a NaN-quieting max.
+// Word 3 of a raw buffer resource (32-bit data format).  With stride 0 an
+// access at or past num_records bytes is out of range: a store there is
+// dropped and a load returns zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ int row_pos(const int32_t* q_pos, int row, int n_q, int n_k) {

@@ -6,6 +6,7 @@
 // sheratonhq.com, section 1).  With E4M3 inputs the per-token scales are
 // positive, so they factor out of the ReLU: I = sq[t]*sk[s]*sum_h w*ReLU(c_q.c_k)
 // where c are the decoded codes; the code products are exact in fp32.
+#include <type_traits>
 #include "dsa_kernels.h"
 #include "fp8_index.h"
 
@@ -204,23 +205,25 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
 
 // ---------------------------------------------------------------------------
 // Tiled path for prefill rows (FP8 E4M3 or bf16, up to 16 heads, d = 128).
-// Each workgroup takes kTQ consecutive query rows of one sequence (kQPW per
-// wave) and one chunk of kIdxChunk keys; the chunk's keys are staged 64 at a
-// time in LDS and shared by all kTQ queries, so every key row is fetched once
-// per kTQ queries, and each key operand read from LDS feeds kQPW MFMAs.  The
-// next tile is fetched into registers while the current one is scored.  Per
-// (query, 16 keys) the scores come from one v_mfma_scale_f32_16x16x128_f8f6f4
-// (FP8) or four v_mfma_f32_16x16x32_bf16 (bf16) with the heads as M; each lane
-// folds its four heads with ReLU and the head weights, and one reduce-scatter
-// over the four 16-key blocks of a tile finishes the head sums, leaving lane l
-// with the score of key l of the tile (one coalesced 256-byte store per query
-// and tile).  Keys past a query's last visible key are written as -inf only
-// when `write_future` (the unfused entry point).
+// Query rows go in blocks of kTQ consecutive rows of one sequence (kQPW per
+// wave).  A block scores the keys its rows see in tiles of 64, staged in LDS
+// and shared by all kTQ queries, so every key row is fetched once per kTQ
+// queries and each key operand read from LDS feeds kQPW MFMAs.  The
+// (block, tile) pairs of a launch, block-major, are cut into equal runs, one
+// per workgroup, and the grid is the number of workgroups the chip holds at
+// once: no workgroup waits for a dispatch slot, none is launched without
+// work, and a workgroup loads a block's queries once per run (one run, two
+// where its run crosses a block boundary).  The next tile is fetched into
+// registers while the current one is scored.  Per (query, 16 keys) the
+// scores come from one v_mfma_scale_f32_16x16x128_f8f6f4 (FP8) or four
+// v_mfma_f32_16x16x32_bf16 (bf16) with the heads as M; each lane folds its
+// four heads with ReLU and the head weights, and one reduce-scatter over the
+// four 16-key blocks of a tile finishes the head sums, leaving lane l with
+// the score of key l of the tile (one coalesced 256-byte store per query and
+// tile).  Keys past a query's last visible key are written as -inf only when
+// `write_future` (the unfused entry point): inside the block's tiles by the
+// scorer, past them by k_fill_future.
 // ---------------------------------------------------------------------------
-#ifndef DSA_TILED_CHUNK
-#define DSA_TILED_CHUNK 4096
-#endif
-constexpr int kIdxChunk = DSA_TILED_CHUNK;   // keys per workgroup
 #ifndef DSA_TILED_TILE
 #define DSA_TILED_TILE 64
 #endif
@@ -236,169 +239,304 @@ static_assert(kTileKeys % 64 == 0, "tiles are scored 64 keys at a time");
 template <int DT> struct TiledShape {
     static constexpr int QPW = DT == E4M3 ? DSA_TILED_F8_QPW : 2, TW = DT == E4M3 ? DSA_TILED_F8_TW : 4;
 };
+// fewest tiles a workgroup's piece gets when a launch has few, and the
+// piece length when a launch has many query blocks
+constexpr int kTiledMinRun = 4;
+#ifndef DSA_TILED_PIECE
+#define DSA_TILED_PIECE 64
+#endif
+constexpr int kTiledPiece = DSA_TILED_PIECE;
+
+// 64-key tiles of query block j of a launch over nrows rows: the tiles that
+// hold a key some row of the block sees.  base is the position of the
+// launch's first row (n_k - n_q + its index in the sequence); with explicit
+// positions (all_keys) every key counts as seen.
+__host__ __device__ inline int tiled_block_tiles(int j, int nrows, int kTQ, long long base, int n_k, bool all_keys) {
+    if (all_keys) return (n_k + 63) / 64;
+    const int rows_upto = (j + 1) * kTQ < nrows ? (j + 1) * kTQ : nrows;
+    long long vis = base + rows_upto;
+    if (vis > n_k) vis = n_k;
+    return vis > 0 ? static_cast<int>((vis + 63) / 64) : 0;
+}
 
 template <int DT>
 __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexArgs x, int t_first, int nrows,
-                                                                        int write_future) {
+                                                                        int piece, int write_future) {
     constexpr int kQPW = TiledShape<DT>::QPW, kTW = TiledShape<DT>::TW, kTQ = kQPW * kTW;
     constexpr int KROW = DT == E4M3 ? 128 : 256;           // bytes per key row
     constexpr int KSTR = KROW + 16;                         // padded LDS stride (conflict-free 16 B reads)
     constexpr int NC = DT == E4M3 ? 1 : 4;                  // MFMAs per 16 keys
     constexpr int LPT = kTileKeys * KROW / 16 / (kTW * 64); // 16-byte loads per thread per tile
     static_assert(LPT * kTW * 64 * 16 == kTileKeys * KROW, "a tile must split evenly over the threads");
-    __shared__ __align__(16) uint8_t k_s[kTileKeys * KSTR];
-    __shared__ float ks_s[kTileKeys];
-    __shared__ int last_s[kTW];
+    __shared__ __align__(16) uint8_t k_s[2][kTileKeys * KSTR];   // double-buffered key tile
+    __shared__ float ks_s[2][kTileKeys];
 
-    const int nqb = (nrows + kTQ - 1) / kTQ;
-    const int qb = nqb - 1 - static_cast<int>(blockIdx.y);  // longest query blocks first
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: rows and positions in SGPRs
     const int col = lane & 15, kg = lane >> 4;
     const int n_k = x.n_k, H = x.H;
 
-    // this wave's query rows (absolute row index t_first + qb*kTQ + kQPW*wave + q)
-    int rows[kQPW], pos[kQPW];
-    float w[kQPW][4], sq[kQPW];
-    v8i a8[DT == E4M3 ? kQPW : 1];
-    v8bf a16[DT == E4M3 ? 1 : kQPW][4];
-    unsigned livem = 0;                                      // bit q: row q exists
-    int mp = -1;
-#pragma unroll
-    for (int q = 0; q < kQPW; ++q) {
-        const int lr = qb * kTQ + wave * kQPW + q;          // row within the launch
-        const bool live = lr < nrows;
-        livem |= live ? 1u << q : 0u;
-        rows[q] = t_first + (live ? lr : 0);
-        pos[q] = live ? row_pos(x.q_pos, rows[q], x.n_q, n_k) : -1;  // may be negative for a live row
-        mp = max(mp, pos[q]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * kg + i;
-            w[q][i] = (live && h < H) ? x.iw[static_cast<size_t>(rows[q]) * H + h] : 0.0f;
-        }
-        if constexpr (DT == E4M3) {
-            sq[q] = live ? x.iq_scale[rows[q]] : 0.0f;
-            a8[q] = (live && col < H)
-                ? load_split32(static_cast<const uint8_t*>(x.iq) + (static_cast<size_t>(rows[q]) * H + col) * 128, kg)
-                : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        } else {
-            sq[q] = 1.0f;
-            const uint16_t* qrow = static_cast<const uint16_t*>(x.iq) + (static_cast<size_t>(rows[q]) * H + col) * 128 + kg * 32;
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                a16[q][c] = (live && col < H) ? *reinterpret_cast<const v8bf*>(qrow + c * 8) : v8bf{};
-        }
-    }
-    mp = max(mp, __shfl_xor(mp, 16));
-    mp = max(mp, __shfl_xor(mp, 32));
-    if (lane == 0) last_s[wave] = mp;
-    __syncthreads();
-    int last = last_s[0];
-#pragma unroll
-    for (int i = 1; i < kTW; ++i) last = max(last, last_s[i]);
     const int b = t_first / x.n_q;                           // every row of the launch is in sequence b
-    const int c0 = blockIdx.x * kIdxChunk;
-    const int c1 = min(c0 + kIdxChunk, n_k);
-    const int cvis = min(c1, last + 1);                      // keys some query of the block sees
-    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * n_k * KROW;
-    const float* ksb = DT == E4M3 ? x.ik_scale + static_cast<size_t>(b) * n_k : nullptr;
+    const long long base = static_cast<long long>(n_k) - x.n_q + t_first % x.n_q;
+    const bool all_keys = x.q_pos != nullptr;
+    const int nqb = (nrows + kTQ - 1) / kTQ;
 
-    v4i pre[LPT];
-    float pre_s = 0.0f;
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int i = threadIdx.x + u * kTW * 64;
-            const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
-            const int key = k0 + kr;
-            pre[u] = key < n_k ? *reinterpret_cast<const v4i*>(kb + static_cast<size_t>(key) * KROW + off)
-                               : v4i{0, 0, 0, 0};
+    // Score keys [c0, c1) of query block qb (c0 a multiple of 64).
+    auto run_segment = [&](const int qb, const int c0, const int c1) {
+        const int tid = static_cast<int>(threadIdx.x);
+        // the block's last visible key: positions run with the rows unless
+        // they are explicit (then a uniform pass over the block's rows)
+        int last = -1;
+        if (x.q_pos) {
+            for (int r = 0; r < kTQ; ++r) {
+                const int lr = qb * kTQ + r;
+                if (lr < nrows) last = max(last, row_pos(x.q_pos, t_first + lr, x.n_q, n_k));
+            }
+        } else {
+            last = row_pos(nullptr, t_first + min(qb * kTQ + kTQ, nrows) - 1, x.n_q, n_k);
         }
-        if constexpr (DT == E4M3) {
-            const int key = k0 + threadIdx.x;
-            pre_s = (threadIdx.x < kTileKeys && key < n_k) ? ksb[key] : 0.0f;
+        last = __builtin_amdgcn_readfirstlane(last);
+        const int cvis = min(c1, last + 1);                      // keys some query of the block sees
+        // -inf for keys [from, c1) of this wave's rows (the unfused entry point
+        // writes every key of a row)
+        auto write_inf = [&](int from) {
+            for (int q = 0; q < kQPW; ++q) {
+                const int lr = qb * kTQ + wave * kQPW + q;
+                if (lr >= nrows) continue;
+                float* out = x.scores + static_cast<size_t>(t_first + lr - x.row0) * n_k;
+                for (int s = from + lane; s < c1; s += 64) out[s] = -__builtin_inff();
+            }
+        };
+        if (c0 >= cvis) {                                        // uniform over the workgroup
+            if (write_future) write_inf(c0);
+            return;
         }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int i = threadIdx.x + u * kTW * 64;
-            const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
-            *reinterpret_cast<v4i*>(k_s + kr * KSTR + off) = pre[u];
-        }
-        if (DT == E4M3 && threadIdx.x < kTileKeys) ks_s[threadIdx.x] = pre_s;
-    };
 
-    if (c0 < cvis) {
-        fetch(c0);
-        stage();
-    }
-    // every prologue load (queries, weights, positions) has landed: otherwise
-    // the loop's first MFMA waits on all outstanding memory operations,
-    // including the previous tile's score stores, in every iteration
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int k0 = c0; k0 < cvis; k0 += kTileKeys) {
-        const bool more = k0 + kTileKeys < cvis;
-        if (more) fetch(k0 + kTileKeys);                     // in flight while this tile is scored
-#pragma unroll
-        for (int sub = 0; sub < kTileKeys / 64; ++sub) {
-        // key k0 + 64*sub + g16*16 + col sits in LDS row 64*sub + g16*16 + col;
-        // lane l scores key k0 + 64*sub + l
-        v8i b8[4];
-        v8bf b16[4][4];
-#pragma unroll
-        for (int g16 = 0; g16 < 4; ++g16) {
-            const uint8_t* kr = k_s + (sub * 64 + g16 * 16 + col) * KSTR;
+        // this wave's query rows (absolute row index t_first + qb*kTQ + kQPW*wave + q)
+        int rows[kQPW], pos[kQPW];
+        float w[kQPW][4], sq[kQPW];
+        v8i a8[DT == E4M3 ? kQPW : 1];
+        v8bf a16[DT == E4M3 ? 1 : kQPW][4];
+        unsigned livem = 0;                                      // bit q: row q exists
+    #pragma unroll
+        for (int q = 0; q < kQPW; ++q) {
+            const int lr = qb * kTQ + wave * kQPW + q;          // row within the launch
+            const bool live = lr < nrows;
+            livem |= live ? 1u << q : 0u;
+            rows[q] = t_first + (live ? lr : 0);
+            pos[q] = live ? row_pos(x.q_pos, rows[q], x.n_q, n_k) : -1;  // may be negative for a live row
+        }
+        // Every operand load is issued unconditionally (a missing row reads row
+        // t_first, heads past H read head H - 1) and masked afterwards, so one
+        // wait covers them all.
+        const int hq = min(col, H - 1);
+    #pragma unroll
+        for (int q = 0; q < kQPW; ++q) {
+            sq[q] = DT == E4M3 ? x.iq_scale[rows[q]] : 1.0f;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) w[q][i] = x.iw[static_cast<size_t>(rows[q]) * H + min(4 * kg + i, H - 1)];
             if constexpr (DT == E4M3) {
-                b8[g16] = load_split32(kr, kg);
+                a8[q] = load_split32(static_cast<const uint8_t*>(x.iq) + (static_cast<size_t>(rows[q]) * H + hq) * 128, kg);
             } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) b16[g16][c] = *reinterpret_cast<const v8bf*>(kr + kg * 64 + c * 16);
+                const uint16_t* qrow = static_cast<const uint16_t*>(x.iq) + (static_cast<size_t>(rows[q]) * H + hq) * 128 + kg * 32;
+    #pragma unroll
+                for (int c = 0; c < 4; ++c) a16[q][c] = *reinterpret_cast<const v8bf*>(qrow + c * 8);
             }
         }
-        const int s = k0 + sub * 64 + lane;
-        const float sk = DT == E4M3 ? ks_s[sub * 64 + lane] : 1.0f;
-#pragma unroll
+    #pragma unroll
         for (int q = 0; q < kQPW; ++q) {
-            float p[4];
-#pragma unroll
-            for (int g16 = 0; g16 < 4; ++g16) {
-                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (DT == E4M3) {
-                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8[q], b8[g16], acc, 0, 0, 0, 127, 0, 127);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < NC; ++c)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a16[q][c], b16[g16][c], acc, 0, 0, 0);
-                }
-                float part = w[q][0] * relu(acc[0]);
-                part = fmaf(w[q][1], relu(acc[1]), part);
-                part = fmaf(w[q][2], relu(acc[2]), part);
-                p[g16] = fmaf(w[q][3], relu(acc[3]), part);
-            }
-            const float part = reduce_scatter4(p[0], p[1], p[2], p[3]);
-            if (s < c1 && (livem >> q & 1u)) {
-                float* out = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
-                if (s <= pos[q]) out[s] = DT == E4M3 ? part * (sq[q] * sk) : part;
-                else if (write_future) out[s] = -__builtin_inff();
+            const bool live = livem >> q & 1u;
+            // the query's scale rides on its head weights: a score is then
+            // (sum over heads of (w * sq) * ReLU(q . k)) * sk
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) w[q][i] = (live && 4 * kg + i < H) ? w[q][i] * sq[q] : 0.0f;
+            if constexpr (DT == E4M3) {
+                if (!(live && col < H)) a8[q] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            } else {
+    #pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (!(live && col < H)) a16[q][c] = v8bf{};
             }
         }
-        }
-        if (more) {
-            __syncthreads();                                 // every wave is done with this tile
-            stage();
-        }
+        const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * n_k * KROW;
+        const float* ksb = DT == E4M3 ? x.ik_scale + static_cast<size_t>(b) * n_k : nullptr;
+        float* orow[kQPW];
+    #pragma unroll
+        for (int q = 0; q < kQPW; ++q) orow[q] = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
+
+        // Every tile load is issued unconditionally, from an address clamped to
+        // the last key, so no branch separates a load from its wait and the loop's
+        // one wait covers exactly the loads and stores of its own iteration.  Rows
+        // past n_k hold copies of the last key; their scores are never stored.
+        v4i pre[LPT];
+        float pre_s = 0.0f;
+        auto fetch = [&](int k0) {
+    #pragma unroll
+            for (int u = 0; u < LPT; ++u) {
+                const int i = tid + u * kTW * 64;
+                const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
+                pre[u] = *reinterpret_cast<const v4i*>(kb + static_cast<size_t>(min(k0 + kr, n_k - 1)) * KROW + off);
+            }
+            if constexpr (DT == E4M3) pre_s = ksb[min(k0 + static_cast<int>(tid % kTileKeys), n_k - 1)];
+        };
+        auto stage = [&](int nb) {
+    #pragma unroll
+            for (int u = 0; u < LPT; ++u) {
+                const int i = tid + u * kTW * 64;
+                const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
+                *reinterpret_cast<v4i*>(k_s[nb] + kr * KSTR + off) = pre[u];
+            }
+            if (DT == E4M3 && tid < kTileKeys) ks_s[nb][tid] = pre_s;
+        };
+        // Scores of the previous 64 keys, stored while the next 64 are scored.
+        // Stores count against the same in-order counter as the tile loads, so
+        // the four stores of a wave are issued unconditionally, after the loads
+        // of the next tile: the wait for those loads then leaves the stores in
+        // flight.  They are buffer stores, one resource per query row (no
+        // records for a missing row); a lane with nothing to store gets an
+        // offset past the row, which the hardware drops.
+        constexpr uint32_t kNoStore = 0x7fffffffu;
+        __amdgpu_buffer_rsrc_t orsrc[kQPW];
+    #pragma unroll
+        for (int q = 0; q < kQPW; ++q)
+            orsrc[q] = __builtin_amdgcn_make_buffer_rsrc(orow[q], 0, (livem >> q & 1u) ? n_k * 4 : 0, kBufferWord3);
+        float held[kQPW] = {};
+        uint32_t hoff[kQPW];                                     // byte offset of held[q] in its row, or kNoStore
+    #pragma unroll
+        for (int q = 0; q < kQPW; ++q) hoff[q] = kNoStore;
+        auto flush = [&]() {
+    #pragma unroll
+            for (int q = 0; q < kQPW; ++q)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[q]), orsrc[q], static_cast<int>(hoff[q]), 0, 0);
+        };
+        int minpos = pos[0];
+    #pragma unroll
+        for (int q = 1; q < kQPW; ++q) minpos = min(minpos, pos[q]);   // -1 when some row is missing
+
+        fetch(c0);
+        stage(0);
+        // every prologue load (queries, weights, positions) has landed before the loop
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    }
-    if (write_future) {
-        // keys of this chunk no query of the block sees
-        for (int q = 0; q < kQPW; ++q) {
-            if (!(livem >> q & 1u)) continue;
-            float* out = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
-            for (int s = max(c0, cvis) + lane; s < c1; s += 64) out[s] = -__builtin_inff();
+        int cur = 0;
+        for (int k0 = c0; k0 < cvis; k0 += kTileKeys) {
+            fetch(min(k0 + kTileKeys, cvis - 1));                // in flight while this tile is scored
+            // Score 64 keys starting at k0 + 64*sub.  FAST: every query of the
+            // wave sees all of them (the common case away from the diagonal), so
+            // no per-key visibility test or -inf is needed.
+            auto score64 = [&](int sub, auto fast_tag) {
+                constexpr bool FAST = decltype(fast_tag)::value;
+                // key k0 + 64*sub + g16*16 + col sits in LDS row 64*sub + g16*16 + col;
+                // lane l scores key k0 + 64*sub + l
+                v8i b8[4];
+                v8bf b16[4][4];
+    #pragma unroll
+                for (int g16 = 0; g16 < 4; ++g16) {
+                    const uint8_t* kr = k_s[cur] + (sub * 64 + g16 * 16 + col) * KSTR;
+                    if constexpr (DT == E4M3) {
+                        b8[g16] = load_split32(kr, kg);
+                    } else {
+    #pragma unroll
+                        for (int c = 0; c < 4; ++c) b16[g16][c] = *reinterpret_cast<const v8bf*>(kr + kg * 64 + c * 16);
+                    }
+                }
+                const int s = k0 + sub * 64 + lane;
+                const float sk = DT == E4M3 ? ks_s[cur][sub * 64 + lane] : 1.0f;
+                const uint32_t off = static_cast<uint32_t>(s) * 4u;
+    #pragma unroll
+                for (int q = 0; q < kQPW; ++q) {
+                    float p[4];
+    #pragma unroll
+                    for (int g16 = 0; g16 < 4; ++g16) {
+                        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                        if constexpr (DT == E4M3) {
+                            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8[q], b8[g16], acc, 0, 0, 0, 127, 0, 127);
+                        } else {
+    #pragma unroll
+                            for (int c = 0; c < NC; ++c)
+                                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a16[q][c], b16[g16][c], acc, 0, 0, 0);
+                        }
+                        float part = w[q][0] * relu(acc[0]);
+                        part = fmaf(w[q][1], relu(acc[1]), part);
+                        part = fmaf(w[q][2], relu(acc[2]), part);
+                        p[g16] = fmaf(w[q][3], relu(acc[3]), part);
+                    }
+                    const float part = reduce_scatter4(p[0], p[1], p[2], p[3]);
+                    const float score = DT == E4M3 ? part * sk : part;
+                    if constexpr (FAST) {
+                        held[q] = score;
+                        hoff[q] = off;
+                    } else {
+                        const bool vis = s <= pos[q];
+                        held[q] = vis ? score : -__builtin_inff();
+                        hoff[q] = (s < c1 && (vis || write_future)) ? off : kNoStore;
+                    }
+                }
+            };
+    #pragma unroll
+            for (int sub = 0; sub < kTileKeys / 64; ++sub) {
+                flush();                                         // on every path, so the tile wait can count past it
+                if (k0 + sub * 64 + 63 <= minpos) score64(sub, std::true_type{});
+                else score64(sub, std::false_type{});
+            }
+            // the next tile goes to the other buffer, which every wave finished
+            // reading before the barrier that ended the previous iteration; the
+            // scheduling barrier keeps the LDS writes (and the wait for the tile
+            // loads in front of them) after this tile's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            stage(cur ^ 1);
+            __syncthreads();
+            cur ^= 1;
         }
+        flush();
+        if (write_future) write_inf(cvis);                       // keys of this run no query of the block sees
+    };
+
+    // This workgroup's piece: block j's tiles are cut into pieces of at most
+    // `piece` tiles, and the pieces go to the workgroups in reverse block
+    // order (the longest blocks first).  To find the block holding piece p,
+    // lane l sums the piece counts of blocks [l*m, (l+1)*m) and the lanes
+    // take an inclusive prefix; the first lane whose prefix passes p walks
+    // its own blocks.  Every wave does this and gets the same answer.
+    const int p = static_cast<int>(gridDim.x - 1 - blockIdx.x);
+    int qb, t0, tj;
+    {
+        const int m = (nqb + 63) / 64;
+        int lsum = 0;
+        for (int i = 0; i < m; ++i) {
+            const int j = lane * m + i;
+            if (j < nqb) lsum += (tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys) + piece - 1) / piece;
+        }
+        int incl = lsum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        const int L = __ffsll(static_cast<long long>(__ballot(p < incl))) - 1;   // p < pieces: some lane ends past it
+        int acc = __shfl(incl - lsum, L);
+        int j = L * m;
+        tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
+        while (acc + (tj + piece - 1) / piece <= p) {
+            acc += (tj + piece - 1) / piece;
+            tj = tiled_block_tiles(++j, nrows, kTQ, base, n_k, all_keys);
+        }
+        qb = __builtin_amdgcn_readfirstlane(j);
+        tj = __builtin_amdgcn_readfirstlane(tj);
+        t0 = __builtin_amdgcn_readfirstlane((p - acc) * piece);
     }
+    run_segment(qb, 64 * t0, min(64 * min(t0 + piece, tj), n_k));
+}
+
+// -inf for keys [e, n_k) of every row of a launch, e the end of the row's
+// block's last key tile (the scorer writes the rest of the row).
+__global__ void k_fill_future(float* scores, int row_off, int nrows, int kTQ, long long base, int n_k, int all_keys) {
+    const int t = blockIdx.x;
+    if (t >= nrows) return;
+    const int tiles = tiled_block_tiles(t / kTQ, nrows, kTQ, base, n_k, all_keys != 0);
+    const int e = min(64 * tiles, n_k);
+    float* out = scores + static_cast<size_t>(row_off + t) * n_k;
+    for (int s = e + static_cast<int>(threadIdx.x); s < n_k; s += blockDim.x) out[s] = -__builtin_inff();
 }
 
 bool index_tiled_path(const IndexArgs& a) {
@@ -408,16 +546,44 @@ bool index_tiled_path(const IndexArgs& a) {
 template <int DT>
 static hipError_t launch_index_tiled_dt(const IndexArgs& a, bool write_future, hipStream_t st) {
     constexpr int kTW = TiledShape<DT>::TW, kTQ = TiledShape<DT>::QPW * kTW;
+    // workgroups the chip holds at once
+    static const int per_cu = [] {
+        int nb = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_index_tiled<DT>, kTW * 64, 0) == hipSuccess && nb > 0
+            ? nb : 1;
+    }();
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long long slots = static_cast<long long>(per_cu) * (cus > 0 ? cus : 1);
     // one launch per sequence the rows touch, so a query block never spans two
     int r = a.row0;
     const int r_end = a.row0 + a.rows;
     while (r < r_end) {
         const int seq_end = (r / a.n_q + 1) * a.n_q;
         const int n = min(r_end, seq_end) - r;
-        const dim3 grid((a.n_k + kIdxChunk - 1) / kIdxChunk, (n + kTQ - 1) / kTQ);
-        hipLaunchKernelGGL(k_index_tiled<DT>, grid, dim3(kTW * 64), 0, st, a, r, n, write_future ? 1 : 0);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        const long long base = static_cast<long long>(a.n_k) - a.n_q + r % a.n_q;
+        const bool all_keys = a.q_pos != nullptr;
+        const int nqb = (n + kTQ - 1) / kTQ;
+        long long total = 0;
+        for (int j = 0; j < nqb; ++j) total += tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys);
+        if (total > 0) {
+            // Few blocks (a fused row block): pieces sized so that they all run
+            // at once, one per resident workgroup.  Many blocks: pieces of
+            // kTiledPiece tiles over several rounds, longest blocks first.
+            long long piece = nqb * 2 <= slots ? (total + (slots - nqb) - 1) / (slots - nqb) : kTiledPiece;
+            if (piece < kTiledMinRun) piece = kTiledMinRun;
+            long long pieces = 0;
+            for (int j = 0; j < nqb; ++j) pieces += (tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys) + piece - 1) / piece;
+            hipLaunchKernelGGL(k_index_tiled<DT>, dim3(static_cast<unsigned>(pieces)), dim3(kTW * 64), 0, st, a, r, n,
+                               static_cast<int>(piece), write_future ? 1 : 0);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (write_future && !all_keys) {
+            hipLaunchKernelGGL(k_fill_future, dim3(n), dim3(256), 0, st, a.scores, r - a.row0, n, kTQ, base, a.n_k, 0);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         r += n;
     }
     return hipSuccess;
