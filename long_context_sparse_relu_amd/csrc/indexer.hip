@@ -6,6 +6,7 @@
 // sheratonhq.com, section 1).  With E4M3 inputs the per-token scales are
 // positive, so they factor out of the ReLU: I = sq[t]*sk[s]*sum_h w*ReLU(c_q.c_k)
 // where c are the decoded codes; the code products are exact in fp32.
+#include <climits>
 #include <type_traits>
 #include "dsa_kernels.h"
 #include "fp8_index.h"
@@ -208,13 +209,15 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
 // Query rows go in blocks of kTQ consecutive rows of one sequence (kQPW per
 // wave).  A block scores the keys its rows see in tiles of 64, staged in LDS
 // and shared by all kTQ queries, so every key row is fetched once per kTQ
-// queries and each key operand read from LDS feeds kQPW MFMAs.  The
-// (block, tile) pairs of a launch, block-major, are cut into equal runs, one
-// per workgroup, and the grid is the number of workgroups the chip holds at
-// once: no workgroup waits for a dispatch slot, none is launched without
-// work, and a workgroup loads a block's queries once per run (one run, two
-// where its run crosses a block boundary).  The next tile is fetched into
-// registers while the current one is scored.  Per (query, 16 keys) the
+// queries and each key operand read from LDS feeds kQPW MFMAs.  A launch
+// with few query blocks (a fused row block) cuts its (block, tile) pairs,
+// block-major, into equal runs, one per workgroup the chip holds at once, so
+// every workgroup starts at once and all finish together; a run crosses at
+// most one block boundary and loads a block's queries once.  A launch with
+// many blocks (a whole sequence) cuts each block into pieces of kTiledPiece
+// tiles, handed out longest blocks first over several rounds.  No workgroup
+// is launched without work.  The next tile is fetched into registers while
+// the current one is scored.  Per (query, 16 keys) the
 // scores come from one v_mfma_scale_f32_16x16x128_f8f6f4 (FP8) or four
 // v_mfma_f32_16x16x32_bf16 (bf16) with the heads as M; each lane folds its
 // four heads with ReLU and the head weights, and one reduce-scatter over the
@@ -239,7 +242,7 @@ static_assert(kTileKeys % 64 == 0, "tiles are scored 64 keys at a time");
 template <int DT> struct TiledShape {
     static constexpr int QPW = DT == E4M3 ? DSA_TILED_F8_QPW : 2, TW = DT == E4M3 ? DSA_TILED_F8_TW : 4;
 };
-// fewest tiles a workgroup's piece gets when a launch has few, and the
+// fewest tiles in a workgroup's run when a launch has few tiles, and the
 // piece length when a launch has many query blocks
 constexpr int kTiledMinRun = 4;
 #ifndef DSA_TILED_PIECE
@@ -261,7 +264,7 @@ __host__ __device__ inline int tiled_block_tiles(int j, int nrows, int kTQ, long
 
 template <int DT>
 __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexArgs x, int t_first, int nrows,
-                                                                        int piece, int write_future) {
+                                                                        int piece, long long total, int write_future) {
     constexpr int kQPW = TiledShape<DT>::QPW, kTW = TiledShape<DT>::TW, kTQ = kQPW * kTW;
     constexpr int KROW = DT == E4M3 ? 128 : 256;           // bytes per key row
     constexpr int KSTR = KROW + 16;                         // padded LDS stride (conflict-free 16 B reads)
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         v8i a8[DT == E4M3 ? kQPW : 1];
         v8bf a16[DT == E4M3 ? 1 : kQPW][4];
         unsigned livem = 0;                                      // bit q: row q exists
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < kQPW; ++q) {
             const int lr = qb * kTQ + wave * kQPW + q;          // row within the launch
             const bool live = lr < nrows;
@@ -330,30 +333,30 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         // t_first, heads past H read head H - 1) and masked afterwards, so one
         // wait covers them all.
         const int hq = min(col, H - 1);
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < kQPW; ++q) {
             sq[q] = DT == E4M3 ? x.iq_scale[rows[q]] : 1.0f;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) w[q][i] = x.iw[static_cast<size_t>(rows[q]) * H + min(4 * kg + i, H - 1)];
             if constexpr (DT == E4M3) {
                 a8[q] = load_split32(static_cast<const uint8_t*>(x.iq) + (static_cast<size_t>(rows[q]) * H + hq) * 128, kg);
             } else {
                 const uint16_t* qrow = static_cast<const uint16_t*>(x.iq) + (static_cast<size_t>(rows[q]) * H + hq) * 128 + kg * 32;
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < 4; ++c) a16[q][c] = *reinterpret_cast<const v8bf*>(qrow + c * 8);
             }
         }
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < kQPW; ++q) {
             const bool live = livem >> q & 1u;
             // the query's scale rides on its head weights: a score is then
             // (sum over heads of (w * sq) * ReLU(q . k)) * sk
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) w[q][i] = (live && 4 * kg + i < H) ? w[q][i] * sq[q] : 0.0f;
             if constexpr (DT == E4M3) {
                 if (!(live && col < H)) a8[q] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < 4; ++c)
                     if (!(live && col < H)) a16[q][c] = v8bf{};
             }
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * n_k * KROW;
         const float* ksb = DT == E4M3 ? x.ik_scale + static_cast<size_t>(b) * n_k : nullptr;
         float* orow[kQPW];
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < kQPW; ++q) orow[q] = x.scores + static_cast<size_t>(rows[q] - x.row0) * n_k;
 
         // Every tile load is issued unconditionally, from an address clamped to
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         v4i pre[LPT];
         float pre_s = 0.0f;
         auto fetch = [&](int k0) {
-    #pragma unroll
+#pragma unroll
             for (int u = 0; u < LPT; ++u) {
                 const int i = tid + u * kTW * 64;
                 const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
             if constexpr (DT == E4M3) pre_s = ksb[min(k0 + static_cast<int>(tid % kTileKeys), n_k - 1)];
         };
         auto stage = [&](int nb) {
-    #pragma unroll
+#pragma unroll
             for (int u = 0; u < LPT; ++u) {
                 const int i = tid + u * kTW * 64;
                 const int kr = i / (KROW / 16), off = (i % (KROW / 16)) * 16;
@@ -397,20 +400,20 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         // offset past the row, which the hardware drops.
         constexpr uint32_t kNoStore = 0x7fffffffu;
         __amdgpu_buffer_rsrc_t orsrc[kQPW];
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < kQPW; ++q)
             orsrc[q] = __builtin_amdgcn_make_buffer_rsrc(orow[q], 0, (livem >> q & 1u) ? n_k * 4 : 0, kBufferWord3);
         float held[kQPW] = {};
         uint32_t hoff[kQPW];                                     // byte offset of held[q] in its row, or kNoStore
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < kQPW; ++q) hoff[q] = kNoStore;
         auto flush = [&]() {
-    #pragma unroll
+#pragma unroll
             for (int q = 0; q < kQPW; ++q)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[q]), orsrc[q], static_cast<int>(hoff[q]), 0, 0);
         };
         int minpos = pos[0];
-    #pragma unroll
+#pragma unroll
         for (int q = 1; q < kQPW; ++q) minpos = min(minpos, pos[q]);   // -1 when some row is missing
 
         fetch(c0);
@@ -430,29 +433,29 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
                 // lane l scores key k0 + 64*sub + l
                 v8i b8[4];
                 v8bf b16[4][4];
-    #pragma unroll
+#pragma unroll
                 for (int g16 = 0; g16 < 4; ++g16) {
                     const uint8_t* kr = k_s[cur] + (sub * 64 + g16 * 16 + col) * KSTR;
                     if constexpr (DT == E4M3) {
                         b8[g16] = load_split32(kr, kg);
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int c = 0; c < 4; ++c) b16[g16][c] = *reinterpret_cast<const v8bf*>(kr + kg * 64 + c * 16);
                     }
                 }
                 const int s = k0 + sub * 64 + lane;
                 const float sk = DT == E4M3 ? ks_s[cur][sub * 64 + lane] : 1.0f;
                 const uint32_t off = static_cast<uint32_t>(s) * 4u;
-    #pragma unroll
+#pragma unroll
                 for (int q = 0; q < kQPW; ++q) {
                     float p[4];
-    #pragma unroll
+#pragma unroll
                     for (int g16 = 0; g16 < 4; ++g16) {
                         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
                         if constexpr (DT == E4M3) {
                             acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8[q], b8[g16], acc, 0, 0, 0, 127, 0, 127);
                         } else {
-    #pragma unroll
+#pragma unroll
                             for (int c = 0; c < NC; ++c)
                                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a16[q][c], b16[g16][c], acc, 0, 0, 0);
                         }
@@ -472,8 +475,22 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
                         hoff[q] = (s < c1 && (vis || write_future)) ? off : kNoStore;
                     }
                 }
+#ifndef DSA_TILED_NO_PINGPONG
+                // Ping-pong: each MFMA is issued before the ReLU-weight epilogue
+                // of the one before it, so the matrix core works through one
+                // product while the vector ALU folds the previous one (left to
+                // itself the scheduler runs each product and its epilogue back
+                // to back).
+                __builtin_amdgcn_sched_group_barrier(0x100, 8 * NC, 0);   // the tile's LDS operand reads
+                __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);       // product 0
+#pragma unroll
+                for (int i = 1; i < 4 * kQPW; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);   // product i
+                    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // epilogue of product i - 1
+                }
+#endif
             };
-    #pragma unroll
+#pragma unroll
             for (int sub = 0; sub < kTileKeys / 64; ++sub) {
                 flush();                                         // on every path, so the tile wait can count past it
                 if (k0 + sub * 64 + 63 <= minpos) score64(sub, std::true_type{});
@@ -492,40 +509,63 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         if (write_future) write_inf(cvis);                       // keys of this run no query of the block sees
     };
 
-    // This workgroup's piece: block j's tiles are cut into pieces of at most
-    // `piece` tiles, and the pieces go to the workgroups in reverse block
-    // order (the longest blocks first).  To find the block holding piece p,
-    // lane l sums the piece counts of blocks [l*m, (l+1)*m) and the lanes
-    // take an inclusive prefix; the first lane whose prefix passes p walks
-    // its own blocks.  Every wave does this and gets the same answer.
-    const int p = static_cast<int>(gridDim.x - 1 - blockIdx.x);
+    // This workgroup's share of the launch's (block, tile) pairs, block-major.
+    // Runs (piece == 0): tiles [total*w/G, total*(w+1)/G), which cross at most
+    // one block boundary (the launcher checks that no block is shorter than a
+    // run).  Pieces (piece > 0): block j's tiles cut into pieces of at most
+    // `piece` tiles, handed out in reverse block order (longest blocks first).
+    // Either way the first block is found the same way: lane l sums the counts
+    // (tiles or pieces) of blocks [l*m, (l+1)*m), the lanes take an inclusive
+    // prefix, and the first lane whose prefix passes the target walks its own
+    // blocks.  Every wave does this and gets the same answer.
+    const bool runs = piece == 0;
+    const long long target = runs ? total * blockIdx.x / gridDim.x : static_cast<long long>(gridDim.x - 1 - blockIdx.x);
+    const long long g_end = runs ? total * (blockIdx.x + 1) / gridDim.x : 0;
+    if (runs && target >= g_end) return;                      // uniform over the workgroup
+    auto units = [&](int j) {
+        const int tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
+        return runs ? tj : (tj + piece - 1) / piece;
+    };
     int qb, t0, tj;
     {
         const int m = (nqb + 63) / 64;
-        int lsum = 0;
+        long long lsum = 0;
         for (int i = 0; i < m; ++i) {
             const int j = lane * m + i;
-            if (j < nqb) lsum += (tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys) + piece - 1) / piece;
+            if (j < nqb) lsum += units(j);
         }
-        int incl = lsum;
+        long long incl = lsum;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d);
+            const long long v = __shfl_up(incl, d);
             if (lane >= d) incl += v;
         }
-        const int L = __ffsll(static_cast<long long>(__ballot(p < incl))) - 1;   // p < pieces: some lane ends past it
-        int acc = __shfl(incl - lsum, L);
+        const int L = __ffsll(static_cast<long long>(__ballot(target < incl))) - 1;   // target < all units
+        long long acc = __shfl(incl - lsum, L);
         int j = L * m;
-        tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
-        while (acc + (tj + piece - 1) / piece <= p) {
-            acc += (tj + piece - 1) / piece;
-            tj = tiled_block_tiles(++j, nrows, kTQ, base, n_k, all_keys);
+        int u = units(j);
+        while (acc + u <= target) {
+            acc += u;
+            u = units(++j);
         }
         qb = __builtin_amdgcn_readfirstlane(j);
-        tj = __builtin_amdgcn_readfirstlane(tj);
-        t0 = __builtin_amdgcn_readfirstlane((p - acc) * piece);
+        tj = __builtin_amdgcn_readfirstlane(tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys));
+        const int into = __builtin_amdgcn_readfirstlane(static_cast<int>(target - acc));
+        t0 = runs ? into : into * piece;
     }
-    run_segment(qb, 64 * t0, min(64 * min(t0 + piece, tj), n_k));
+    if (!runs) {
+        run_segment(qb, 64 * t0, min(64 * min(t0 + piece, tj), n_k));
+        return;
+    }
+    // a run: the rest of this block, then (if the run is longer) the head of
+    // the next block
+    const int ta = static_cast<int>(min(static_cast<long long>(tj - t0), g_end - target));
+    run_segment(qb, 64 * t0, min(64 * (t0 + ta), n_k));
+    const int tb = static_cast<int>(g_end - target - ta);
+    if (tb > 0) {
+        __syncthreads();                                      // the second segment restages both LDS buffers
+        run_segment(qb + 1, 0, min(64 * tb, n_k));
+    }
 }
 
 // -inf for keys [e, n_k) of every row of a launch, e the end of the row's
@@ -569,15 +609,26 @@ static hipError_t launch_index_tiled_dt(const IndexArgs& a, bool write_future, h
         long long total = 0;
         for (int j = 0; j < nqb; ++j) total += tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys);
         if (total > 0) {
-            // Few blocks (a fused row block): pieces sized so that they all run
-            // at once, one per resident workgroup.  Many blocks: pieces of
+            // Few blocks (a fused row block): equal runs, one per resident
+            // workgroup, when no block with keys is shorter than a run (a run
+            // then crosses at most one block boundary).  Otherwise pieces of
             // kTiledPiece tiles over several rounds, longest blocks first.
-            long long piece = nqb * 2 <= slots ? (total + (slots - nqb) - 1) / (slots - nqb) : kTiledPiece;
-            if (piece < kTiledMinRun) piece = kTiledMinRun;
-            long long pieces = 0;
-            for (int j = 0; j < nqb; ++j) pieces += (tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys) + piece - 1) / piece;
-            hipLaunchKernelGGL(k_index_tiled<DT>, dim3(static_cast<unsigned>(pieces)), dim3(kTW * 64), 0, st, a, r, n,
-                               static_cast<int>(piece), write_future ? 1 : 0);
+            long long wgs = (total + kTiledMinRun - 1) / kTiledMinRun;
+            if (wgs > slots) wgs = slots;
+            const long long run = (total + wgs - 1) / wgs;
+            int shortest = INT_MAX;
+            for (int j = 0; j < nqb; ++j) {
+                const int tj = tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys);
+                if (tj > 0 && tj < shortest) shortest = tj;
+            }
+            long long piece = 0;
+            if (nqb * 2 > slots || run > shortest) {
+                piece = kTiledPiece;
+                wgs = 0;
+                for (int j = 0; j < nqb; ++j) wgs += (tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys) + piece - 1) / piece;
+            }
+            hipLaunchKernelGGL(k_index_tiled<DT>, dim3(static_cast<unsigned>(wgs)), dim3(kTW * 64), 0, st, a, r, n,
+                               static_cast<int>(piece), total, write_future ? 1 : 0);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         if (write_future && !all_keys) {
