@@ -164,8 +164,9 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 // list is staged in LDS first, then wave w owns a contiguous 1/8 of it, 16
 // entries per block:
 //   S^T[key][head] = K Q^T  with 4 x v_mfma_f32_16x16x32_bf16: A = the 16
-//     gathered key rows (lane l: key l%16, its 64 contiguous bytes at
-//     64*(l/16)), B = Q^T held in registers for the whole loop;
+//     gathered key rows (lane l: key l%16; load c brings bytes
+//     64c + 16(l/16)..+16 of a bf16 row, so the 4 lanes of a key read one
+//     contiguous 64-byte run), B = Q^T held in registers for the whole loop;
 //   the result leaves each lane with 4 keys of one head (head l%16), so the
 //     online-softmax rescale is per lane and P^T is already the B operand of
 //   O^T[dim][head] += V^T P^T with 8 x v_mfma_f32_16x16x16_bf16, where the
@@ -256,12 +257,17 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
 
     const int32_t* idx_row = a.idx + static_cast<size_t>(row) * a.kk + jb;
 
+    // Dims of product c held by lane (col, kg): from a bf16 cache 32c + 8kg..+8,
+    // so that the 4 lanes of a key read one contiguous 64-byte run per load
+    // (16 keys x 64 B per load instruction); from an E4M3 cache 32kg + 8c..+8
+    // (a lane widens its own 32 contiguous code bytes).  Q takes the same order.
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     v8bf qb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+        const int dim0 = KV8 ? kg * 32 + c * 8 : c * 32 + kg * 8;
         if (col < G)
-            qb[c] = *reinterpret_cast<const v8bf*>(qp + (static_cast<size_t>(row) * a.Hq + g * G + col) * 128 + kg * 32 + c * 8);
+            qb[c] = *reinterpret_cast<const v8bf*>(qp + (static_cast<size_t>(row) * a.Hq + g * G + col) * 128 + dim0);
         else
             qb[c] = v8bf{};
     }
@@ -270,11 +276,12 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     const int j_begin = wave * per;
     const int j_end = min(j_begin + per, nj);
     const int nblk = j_end > j_begin ? (j_end - j_begin + 15) / 16 : 0;
-    // this lane's 32 dims of kv head g: bytes [32*kg, 32*kg + 32) (E4M3) or
-    // elements of it (bf16) within each 128-dim row
+    // this lane's 32 dims of kv head g within each 128-dim row: E4M3 bytes
+    // [32kg, 32kg + 32); bf16 elements 8kg..8kg+8 of each 32-dim group (the
+    // loads add 64 bytes per group)
     constexpr int ESZ = KV8 ? 1 : 2;
     const size_t row_bytes = static_cast<size_t>(a.Hkv) * 128 * ESZ;
-    const size_t base_off = static_cast<size_t>(b) * a.n_k * row_bytes + (g * 128 + kg * 32) * ESZ;
+    const size_t base_off = static_cast<size_t>(b) * a.n_k * row_bytes + g * 128 * ESZ + (KV8 ? kg * 32 : kg * 16);
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + base_off;
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + base_off;
     const size_t sc_base = static_cast<size_t>(b) * a.n_k * a.Hkv + g;
@@ -321,17 +328,20 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
             d.k[0] = ks[0]; d.k[1] = ks[1]; d.v[0] = vs[0]; d.v[1] = vs[1];
             d.ks = *kq; d.vs = *vq;
         } else {
-            const v8bf* ks = reinterpret_cast<const v8bf*>(kbase + sr * row_bytes);
-            const v8bf* vs = reinterpret_cast<const v8bf*>(vbase + sr * row_bytes);
+            const unsigned char* ks = kbase + sr * row_bytes;
+            const unsigned char* vs = vbase + sr * row_bytes;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) { d.k[c] = ks[c]; d.v[c] = vs[c]; }
+            for (int c = 0; c < 4; ++c) {
+                d.k[c] = *reinterpret_cast<const v8bf*>(ks + 64 * c);
+                d.v[c] = *reinterpret_cast<const v8bf*>(vs + 64 * c);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
     auto stage_values = [&](const v8bf* vc) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<v8bf*>(v_s + col * kGqaVStride + kg * 32 + c * 8) = vc[c];
+            *reinterpret_cast<v8bf*>(v_s + col * kGqaVStride + (KV8 ? kg * 32 + c * 8 : c * 32 + kg * 8)) = vc[c];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
