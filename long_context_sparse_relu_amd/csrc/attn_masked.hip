@@ -271,16 +271,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             {
                 float psum = 0.0f;
                 v8bf pb[4];
+                const v2bf kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const float pa0 = __builtin_amdgcn_exp2f(fmaf(sa[r], zscale, -mz));
                     const float pa1 = __builtin_amdgcn_exp2f(fmaf(sa[r + 1], zscale, -mz));
                     const float pc0 = __builtin_amdgcn_exp2f(fmaf(sb[r], zscale, -mz));
                     const float pc1 = __builtin_amdgcn_exp2f(fmaf(sb[r + 1], zscale, -mz));
-                    psum += (pa0 + pa1) + (pc0 + pc1);
                     // pairs convert with one v_cvt_pk_bf16_f32 (round to nearest even)
                     const v2bf qa = __builtin_convertvector((v2f){pa0, pa1}, v2bf);
                     const v2bf qc = __builtin_convertvector((v2f){pc0, pc1}, v2bf);
+                    // the denominator sums the same bf16 weights P.V multiplies,
+                    // two per v_dot2c_f32_bf16
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(qa, kOnes2, psum, false);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(qc, kOnes2, psum, false);
                     pb[r >> 3][r & 7] = qa[0];               // keys 0..31: chunks 0, 1
                     pb[r >> 3][(r & 7) + 1] = qa[1];
                     pb[2 + (r >> 3)][r & 7] = qc[0];         // keys 32..63: chunks 2, 3
