@@ -31,11 +31,15 @@ def hipcc() -> str:
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-Werror=uninitialized", "-I", INCLUDE, "-I", CSRC]
+# Per-source flags.  The masked attention runs its kernels with IEEE mode off:
+# the online softmax takes maxima of scores and -inf, never of NaN, and in
+# IEEE mode every max first quiets its operands (one extra VALU op each).
+EXTRA = {"attn_masked.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
