@@ -26,7 +26,7 @@
 namespace dsa {
 
 constexpr int kSampleThreads = 512;
-constexpr int kSFinishThreads = 512;
+constexpr int kSFinishThreads = 1024;
 
 bool topk_sampled_eligible(int n_k, int k) {
     return static_cast<int64_t>(n_k) >= 16 * static_cast<int64_t>(k) && n_k >= kSampleKeys;
