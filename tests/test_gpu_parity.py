@@ -190,6 +190,24 @@ def test_edge_case(name):
     run_case(inp, list(range(fields.get("B", 1))), list(range(n_q)), fused=fused)
 
 
+@pytest.mark.parametrize("n_q,n_k,idt", [(3001, 3001, "e4m3"), (301, 9001, "e4m3"), (2003, 6003, "bf16")])
+def test_tiled_indexer_work_splits(n_q, n_k, idt):
+    """The tiled indexer's split of (query block, key tile) pairs over workgroups:
+    a prefill from scratch (the first query blocks see one key tile, so the
+    launch falls back from equal runs to pieces), a prefix (equal runs that
+    cross block boundaries) and bf16 blocks of 8 rows; rows on both sides of
+    block boundaries are checked, scores (-inf past each row's position),
+    selections and attention, fused against unfused."""
+    sp = custom_spec(name=f"splits_{n_q}_{n_k}_{idt}", n_q=n_q, n_k=n_k, idx_heads=16, idx_dtype=idt, top_k=256,
+                     q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=31)
+    tq = 32 if idt == "e4m3" else 8
+    nqb = (n_q + tq - 1) // tq
+    edges = [r for blk in (1, 2, nqb // 2, nqb - 1) for r in (blk * tq - 1, blk * tq) if 0 <= r < n_q]
+    rows = sorted(set([0, 1, n_q - 1] + edges + list(_sample_rows(n_q, 12, 7))))
+    run_case(inp, [0], rows, fused="prefill")
+
+
 def test_all_zero_weights_pick_lowest_positions():
     """All scores tie at 0: the lower position must win, exactly."""
     sp = custom_spec(name="zero_w", B=2, n_q=3, n_k=10000, idx_heads=16, idx_dtype="e4m3", top_k=2048,
