@@ -234,6 +234,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[c], sa, 0, 0, 0);
                 sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qv[c], sb, 0, 0, 0);
             }
+            // The softmax below runs at raised wave priority and P.V at the
+            // normal one, so where one SIMD's two waves (of different
+            // workgroups) reach these parts at once, the VALU work issues
+            // first while the other wave's MFMAs keep the matrix core busy.
+            __builtin_amdgcn_s_setprio(1);
             // the query's bits: key 8(r/4) + 4hh + r%4 of each half; a
             // sign-extended one-bit field selects the score or -inf
             const int ma = static_cast<int>(w0 >> (4 * hh)), mb = static_cast<int>(w1 >> (4 * hh));
@@ -291,6 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     pb[2 + (r >> 3)][(r & 7) + 1] = qc[1];
                 }
                 l_part += psum;
+                __builtin_amdgcn_s_setprio(0);
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
                     const uint16_t* vr = v_s + (16 * c16 + tr_key) * kStrV + tr_dim;
