@@ -391,6 +391,30 @@ struct LdsRel {
     }
 };
 
+// Radix select over a row's order keys in LDS and the ordered write of the
+// kept positions (the whole block; vis > k; kmin, kmax: the keys' range).
+__device__ __forceinline__ void select_lds_row(const TopkArgs& a, uint32_t* keys, int vis, uint32_t kmin, uint32_t kmax,
+                               uint32_t* lh, uint32_t* bm, uint32_t* wsum, uint32_t* n_list, int32_t* out) {
+    const int k = a.k;
+    const uint32_t range = kmax - kmin;
+    const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
+    const int sh = bits > 11 ? bits - 11 : 0;
+    int shifts[6], widths[6], np = 1;
+    shifts[0] = 32 + sh;
+    widths[0] = 11;
+    for (int below = 32 + sh; below > 0 && np < 6; ++np) {
+        const int w = below < 11 ? below : 11;
+        below -= w;
+        shifts[np] = below;
+        widths[np] = w;
+    }
+    const int nwords = (vis + 31) >> 5;
+    Sink sink{bm, nullptr, n_list, static_cast<uint32_t>(k)};
+    LdsRel src{keys, vis, kmin};
+    radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
+    write_ordered(sink, nwords, 1, k, out, wsum);
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
     extern __shared__ uint32_t keys[];                        // [min(n_k, kRowLdsMax)]
     __shared__ uint32_t lh[kTopkBins];
@@ -436,22 +460,73 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
     if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
     __syncthreads();
     for (int w = 0; w < kRowThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
-    const uint32_t range = kmax - kmin;
-    const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
-    const int sh = bits > 11 ? bits - 11 : 0;
-    int shifts[6], widths[6], np = 1;
-    shifts[0] = 32 + sh;
-    widths[0] = 11;
-    for (int below = 32 + sh; below > 0 && np < 6; ++np) {
-        const int w = below < 11 ? below : 11;
-        below -= w;
-        shifts[np] = below;
-        widths[np] = w;
+    select_lds_row(a, keys, vis, kmin, kmax, lh, bm, wsum, &n_list, out);
+}
+
+// Rows longer than half the LDS limit leave room for one workgroup per
+// compute unit, so nothing hides a row's load behind another row's select.
+// This persistent form does it inside the workgroup: workgroup w takes rows
+// w, w + gridDim.x, ...; while it selects one row, the next row's scores
+// (kRowPerThread per thread) are already in flight into registers.
+constexpr int kRowPerThread = kRowLdsMax / kRowThreads;
+__global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
+    extern __shared__ uint32_t keys[];                        // [kRowLdsMax]
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t bm[kRowLdsMax / 32];
+    __shared__ uint32_t wsum[kRowThreads / 64 + 2];
+    __shared__ uint32_t wmin[kRowThreads / 64], wmax[kRowThreads / 64];
+    __shared__ uint32_t n_list;
+    float v[kRowPerThread];
+    // issue the loads of row lrow's scores: entry u of thread t is key
+    // t + u * kRowThreads; entries past vis re-read the last score and are not
+    // stored.  The loads are unconditional and nothing reads them until the
+    // next row's keys are stored, so no wait separates them.
+    auto fetch = [&](int lrow, int vis) {
+        const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+#pragma unroll
+        for (int u = 0; u < kRowPerThread; ++u) v[u] = sc[min(static_cast<int>(threadIdx.x) + u * kRowThreads, vis - 1)];
+    };
+    int lrow = blockIdx.x;
+    int vis = lrow < a.rows ? row_visible(a, a.row0 + lrow) : 0;
+    if (lrow < a.rows && vis > a.k) fetch(lrow, vis);
+    for (; lrow < a.rows; lrow += gridDim.x) {
+        const int next = lrow + gridDim.x;
+        const int vis_next = next < a.rows ? row_visible(a, a.row0 + next) : 0;
+        int32_t* out = a.idx + static_cast<size_t>(lrow) * a.k;
+        if (vis <= a.k) {
+            for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < vis ? j : -1;
+            if (next < a.rows && vis_next > a.k) fetch(next, vis_next);
+        } else {
+            uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+            for (int u = 0; u < kRowPerThread; ++u) {
+                const int i = static_cast<int>(threadIdx.x) + u * kRowThreads;
+                if (i < vis) {
+                    // a backbone's forced keys rank as -inf (as ranked() does)
+                    const float x = (i < a.sinks || i >= vis - a.window) ? -__builtin_inff() : v[u];
+                    const uint32_t kk = order_key(x);
+                    keys[i] = kk;
+                    kmin = min(kmin, kk);
+                    kmax = max(kmax, kk);
+                }
+            }
+            const int nwords = (vis + 31) >> 5;
+            for (int i = threadIdx.x; i < nwords; i += kRowThreads) bm[i] = 0u;
+            if (threadIdx.x == 0) n_list = 0;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+                kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+            }
+            if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
+            __syncthreads();
+            for (int w = 0; w < kRowThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
+            if (next < a.rows && vis_next > a.k) fetch(next, vis_next);   // lands during the select
+            select_lds_row(a, keys, vis, kmin, kmax, lh, bm, wsum, &n_list, out);
+        }
+        __syncthreads();                    // the next row's keys reuse the LDS
+        vis = vis_next;
     }
-    Sink sink{bm, nullptr, &n_list, static_cast<uint32_t>(k)};
-    LdsRel src{keys, vis, kmin};
-    radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
-    write_ordered(sink, nwords, 1, k, out, wsum);
 }
 
 size_t topk_workspace_bytes(int rows, int n_k) {
@@ -487,6 +562,21 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
             const int t_max = a.row0 / a.n_q == last / a.n_q ? last % a.n_q : a.n_q - 1;
             vis_max = min(a.n_k, a.n_k - a.n_q + t_max + 1);
             if (vis_max < 1) vis_max = 1;
+        }
+        if (vis_max > kRowLdsMax / 2) {
+            const void* fn = reinterpret_cast<const void*>(k_topk_row_lds_next);
+            const size_t smem = static_cast<size_t>(kRowLdsMax) * sizeof(uint32_t);
+            if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem))) !=
+                hipSuccess)
+                return e;
+            int per_cu = 0, dev = 0, cus = 0;
+            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kRowThreads, smem)) != hipSuccess) return e;
+            if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+            if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+            const long long slots = static_cast<long long>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+            const dim3 grid(static_cast<unsigned>(a.rows < slots ? a.rows : slots));
+            hipLaunchKernelGGL(k_topk_row_lds_next, grid, dim3(kRowThreads), smem, st, a);
+            return hipGetLastError();
         }
         const size_t smem = static_cast<size_t>(vis_max) * sizeof(uint32_t);
         if (smem > 64 * 1024) {

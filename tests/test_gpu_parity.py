@@ -21,13 +21,17 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
 
 
+def _problem_kwargs(inp):
+    return dict(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=inp["top_k"], q=inp["q"],
+                k=inp["k"], v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
+                softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
+                k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"),
+                sink_tokens=inp.get("sinks", 0), local_window=inp.get("window", 0))
+
+
 def _problem(inp, row_sel=None):
     """dsa problem for the whole batch, or for query rows `row_sel` (via q_pos)."""
-    kw = dict(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=inp["top_k"], q=inp["q"],
-              k=inp["k"], v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-              softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
-              k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"),
-              sink_tokens=inp.get("sinks", 0), local_window=inp.get("window", 0))
+    kw = _problem_kwargs(inp)
     if row_sel is not None:
         sel = torch.as_tensor(row_sel, dtype=torch.long, device=DEV)
         for name in ("iq", "iw", "q", "iq_scale"):
@@ -331,6 +335,38 @@ def test_decode_is_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a[2], b[2])
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("sinks,window", [(0, 0), (3, 500)])
+def test_topk_long_rows_many_per_workgroup(sinks, window):
+    """dsa_topk over rows longer than 16K keys (one row fills most of a
+    compute unit's LDS, so each workgroup selects several rows in turn and
+    loads the next while selecting the current): 700 rows of explicit
+    positions, some short enough to keep every key, over seeded fp32 scores
+    quantised to 2^-10 so exact ties are common.  The kept sets must equal
+    the oracle's exactly (the same scores on both sides; ties to the lower
+    position), with and without a backbone."""
+    n_q, n_k, k = 700, 20000, 1000
+    sp = custom_spec(name="long_rows", n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=k,
+                     q_heads=2, kv_heads=1, d_qk=64, d_v=64, attn_dtype="bf16", sinks=sinks, window=window)
+    inp = make_inputs(sp, device=DEV, seed=41)
+    g = torch.Generator().manual_seed(41)
+    pos = torch.randint(n_k // 2, n_k, (1, n_q), generator=g, dtype=torch.int32)
+    pos[0, :40] = torch.randint(0, k + sinks + window, (40,), generator=g, dtype=torch.int32)
+    pos[0, -1] = n_k - 1
+    scores = torch.round(torch.randn((1, n_q, n_k), generator=g) * 1024.0) / 1024.0
+    prob = dsa.make_problem(**_problem_kwargs(inp), q_pos=pos.to(DEV))
+    idx = dsa.topk(prob, scores.to(DEV))
+    torch.cuda.synchronize()
+    sc = scores[0].double().numpy()
+    p_np = pos[0].numpy().astype(np.int64)
+    if sinks or window:
+        o_idx, _ = oracle.select_backbone(sc, k, sinks, window, p_np)
+    else:
+        o_idx, _ = oracle.topk(sc, k, p_np)
+    g_idx = idx[0].cpu().numpy()
+    bad = [r for r in range(n_q) if not np.array_equal(g_idx[r], o_idx[r])]
+    assert not bad, f"rows {bad[:5]} differ (of {len(bad)})"
 
 
 def test_workspace_too_small_is_rejected():
