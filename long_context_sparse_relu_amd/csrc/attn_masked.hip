@@ -79,6 +79,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+// A pointer that is the same in every lane, held as such (buffer resources
+// must be uniform, and the compiler cannot always prove it).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // The 32 bits of keys key0..key0+31 that a causal mask admits for a query
 // whose last visible key is pos.
 __device__ __forceinline__ uint32_t causal_word(int pos, int key0) {
@@ -150,7 +159,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         qv[c] = live_q ? x : v8bf{};
     }
     __syncthreads();
-    const int last = max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3]));
+    // (uniform; read from LDS, so named uniform for the tile offsets below)
+    const int last = __builtin_amdgcn_readfirstlane(max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3])));
     // this workgroup's key tiles [t0, t1) of the block's walk
     const int ntiles = last < 0 ? 0 : last / kKB + 1;
     const int t0 = split * tps;
@@ -163,21 +173,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const uint16_t* vbase = vp + static_cast<size_t>(b) * a.n_k * rstride + g * 128;
     const uint32_t* brow = DENSE ? nullptr : bm + static_cast<size_t>(row) * words;
 
-    // loader: 256 threads x 4 rows x 16 B of K and of V per tile; rows past
-    // n_k read row n_k-1 and are zeroed when staged
+    // loader: 256 threads x 4 rows x 16 B of K and of V per tile, as buffer
+    // loads: the thread's byte offset within a tile is fixed, the tile's
+    // offset is one scalar, and rows past n_k lie past the buffer's end and
+    // read as zeros (one sequence's K or V spans n_k * Hkv * 256 bytes, below
+    // 2^31 for every shape the masked kernels take)
     const int lrow = threadIdx.x >> 4;          // 0..15, plus 16 per step
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
+    const int row_bytes = static_cast<int>(rstride) * 2;
+    const int kv_bytes = __builtin_amdgcn_readfirstlane((a.n_k - 1) * row_bytes + 256);
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbase), 0, kv_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbase), 0, kv_bytes, kBufferWord3);
+    int voff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) voff[r] = (lrow + 16 * r) * row_bytes + lcol * 2;
     v8bf pk[4], pv[4];
     uint32_t pw0 = 0u, pw1 = 0u;
-    int pkey0 = 0;
-    auto fetch = [&](int tile) {
-        pkey0 = tile * kKB;
+    // (the resources go in by value: a captured reference would pass them
+    // through memory, and a resource read from memory is not known uniform)
+    auto fetch_kv = [&](int tile, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr) {
+        const int soff = __builtin_amdgcn_readfirstlane(tile * kKB * row_bytes);   // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const size_t key = static_cast<size_t>(min(pkey0 + lrow + 16 * r, a.n_k - 1));
-            pk[r] = *reinterpret_cast<const v8bf*>(kbase + key * rstride + lcol);
-            pv[r] = *reinterpret_cast<const v8bf*>(vbase + key * rstride + lcol);
+            const v4i xk = __builtin_amdgcn_raw_buffer_load_b128(kr, voff[r], soff, 0);
+            const v4i xv = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[r], soff, 0);
+            __builtin_memcpy(&pk[r], &xk, sizeof xk);
+            __builtin_memcpy(&pv[r], &xv, sizeof xv);
         }
+        const int pkey0 = tile * kKB;
         uint32_t x0, x1;
         if constexpr (DENSE) {
             x0 = causal_word(pos, pkey0);
@@ -189,15 +212,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         pw0 = live_q ? x0 : 0u;
         pw1 = live_q ? x1 : 0u;
     };
+    auto fetch = [&](int tile) { fetch_kv(tile, krsrc, vrsrc); };
     auto stage = [&](int buf) {
         uint16_t* ks = k_all + buf * kKB * kStr;
         uint16_t* vs = v_all + buf * kKB * kStrV;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int kr = lrow + 16 * r;
-            const bool in = pkey0 + kr < a.n_k;
-            *reinterpret_cast<v8bf*>(&ks[kr * kStr + lcol]) = in ? pk[r] : v8bf{};
-            *reinterpret_cast<v8bf*>(&vs[kr * kStrV + lcol]) = in ? pv[r] : v8bf{};
+            *reinterpret_cast<v8bf*>(&ks[kr * kStr + lcol]) = pk[r];
+            *reinterpret_cast<v8bf*>(&vs[kr * kStrV + lcol]) = pv[r];
         }
     };
     // this lane's addresses for the transposing V reads: group dims 16*(lane/16 % 2),
