@@ -309,8 +309,8 @@ def main(argv=None):
     ap.add_argument("--chunk-nk", type=int, default=32768)
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); a multi-GPU run is not part of "
-              "this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU path",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -82,7 +82,7 @@ typedef struct ihipStream_t *hipStream_t;
 typedef enum {
     DSA_OK = 0,
     DSA_E_INVALID = -1,      /* null required pointer, non-positive size, bad combination */
-    DSA_E_UNSUPPORTED = -2,  /* valid problem outside what this build implements */
+    DSA_E_UNSUPPORTED = -2,  /* valid problem the library has no kernel for */
     DSA_E_WORKSPACE = -3,    /* workspace missing or smaller than dsa_workspace_bytes() */
     DSA_E_DEVICE = -4        /* a HIP launch failed; see dsa_last_error() */
 } dsa_status_t;

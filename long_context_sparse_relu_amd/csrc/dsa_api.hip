@@ -505,7 +505,7 @@ const char* dsa_status_str(dsa_status_t status) {
     switch (status) {
         case DSA_OK: return "DSA_OK";
         case DSA_E_INVALID: return "DSA_E_INVALID: invalid argument";
-        case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: valid problem outside this build";
+        case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: valid problem the library has no kernel for";
         case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing or too small";
         case DSA_E_DEVICE: return "DSA_E_DEVICE: HIP launch failed";
         default: return "unknown dsa_status_t";
