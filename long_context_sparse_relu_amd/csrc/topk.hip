@@ -569,11 +569,16 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
             if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem))) !=
                 hipSuccess)
                 return e;
-            int per_cu = 0, dev = 0, cus = 0;
-            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kRowThreads, smem)) != hipSuccess) return e;
+            // workgroups the chip holds at once (one per CU at this LDS size)
+            static const int per_cu = [fn, smem] {
+                int nb = 0;
+                return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kRowThreads, smem) == hipSuccess && nb > 0
+                    ? nb : 1;
+            }();
+            int dev = 0, cus = 0;
             if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
             if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-            const long long slots = static_cast<long long>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+            const long long slots = static_cast<long long>(per_cu) * (cus > 0 ? cus : 1);
             const dim3 grid(static_cast<unsigned>(a.rows < slots ? a.rows : slots));
             hipLaunchKernelGGL(k_topk_row_lds_next, grid, dim3(kRowThreads), smem, st, a);
             return hipGetLastError();
