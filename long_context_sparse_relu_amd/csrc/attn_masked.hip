@@ -5,12 +5,12 @@
 // same attention over each query's selected keys: a softmax over the keys a
 // mask admits equals the softmax over the kept subset.  In prefill, the
 // selections of neighbouring queries overlap so much that reading every key
-// tile once per block of 64 queries moves far fewer bytes than gathering k
-// rows per query (a row kept by 1/64 of the queries of a block is already
+// tile once per block of 256 queries moves far fewer bytes than gathering k
+// rows per query (a row kept by 1/256 of the queries of a block is already
 // cheaper as a tile), so prefill rows take this path:
 //   bitmap  one workgroup per query row turns its index list into a bit row
 //           over the keys (bit s set <=> s kept);
-//   attend  one workgroup per (block of 128 queries, query head), 4 waves of
+//   attend  one workgroup per (block of 256 queries, query head), 8 waves of
 //           32 queries each, walks the key tiles of 64 up to the block's
 //           last visible key.  Per tile and wave: S^T = K Q^T on
 //           v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T in registers), the
@@ -30,7 +30,10 @@ namespace dsa {
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kQB = 128;           // queries per workgroup (32 per wave)
+constexpr int kMW = 8;                 // waves per workgroup
+constexpr int kQB = 32 * kMW;          // queries per workgroup (32 per wave)
+constexpr int kLoadRows = 16 / kMW;    // 16-byte pieces of a 64-key K (and V) tile per thread
+constexpr int kLoadStride = 4 * kMW;   // key rows between them
 constexpr int kKB = 64;            // keys per tile
 // LDS row strides (bf16), one bank pattern per access: the K tile is read a
 // row per lane (16-byte reads; 68 words per row spread 16 rows over all 64
@@ -101,13 +104,13 @@ __device__ __forceinline__ uint32_t causal_word(int pos, int key0) {
 // tiles (blockIdx.z = b * ks + range) and each workgroup leaves its (max,
 // sum, unnormalised O) record per (row, head) in part for k_attn_merge.
 template <bool DENSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(
+__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_masked_d128(
     AttnArgs a, const uint32_t* bm, int words, int ks, int tps, float* part) {
     // two buffers: the next tile is staged into one while the other is read
     // (one barrier per tile)
     __shared__ __align__(16) uint16_t k_all[2 * kKB * kStr];
     __shared__ __align__(16) uint16_t v_all[2 * kKB * kStrV];
-    __shared__ int last_s[4];
+    __shared__ int last_s[kMW];
 
     // A stream = (sequence, key range, head): its query blocks read the same
     // key tiles.  Consecutive workgroup ids go to the 8 XCDs in turn; when the
@@ -160,7 +163,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __syncthreads();
     // (uniform; read from LDS, so named uniform for the tile offsets below)
-    const int last = __builtin_amdgcn_readfirstlane(max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3])));
+    int last_all = last_s[0];
+#pragma unroll
+    for (int w = 1; w < kMW; ++w) last_all = max(last_all, last_s[w]);
+    const int last = __builtin_amdgcn_readfirstlane(last_all);
     // this workgroup's key tiles [t0, t1) of the block's walk
     const int ntiles = last < 0 ? 0 : last / kKB + 1;
     const int t0 = split * tps;
@@ -178,23 +184,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // offset is one scalar, and rows past n_k lie past the buffer's end and
     // read as zeros (one sequence's K or V spans n_k * Hkv * 256 bytes, below
     // 2^31 for every shape the masked kernels take)
-    const int lrow = threadIdx.x >> 4;          // 0..15, plus 16 per step
+    const int lrow = threadIdx.x >> 4;          // 0..4*kMW-1, plus kLoadStride per step
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
     const int row_bytes = static_cast<int>(rstride) * 2;
     const int kv_bytes = __builtin_amdgcn_readfirstlane((a.n_k - 1) * row_bytes + 256);
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbase), 0, kv_bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbase), 0, kv_bytes, kBufferWord3);
-    int voff[4];
+    int voff[kLoadRows];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) voff[r] = (lrow + 16 * r) * row_bytes + lcol * 2;
-    v8bf pk[4], pv[4];
+    for (int r = 0; r < kLoadRows; ++r) voff[r] = (lrow + kLoadStride * r) * row_bytes + lcol * 2;
+    v8bf pk[kLoadRows], pv[kLoadRows];
     uint32_t pw0 = 0u, pw1 = 0u;
     // (the resources go in by value: a captured reference would pass them
     // through memory, and a resource read from memory is not known uniform)
     auto fetch_kv = [&](int tile, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr) {
         const int soff = __builtin_amdgcn_readfirstlane(tile * kKB * row_bytes);   // uniform
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < kLoadRows; ++r) {
             const v4i xk = __builtin_amdgcn_raw_buffer_load_b128(kr, voff[r], soff, 0);
             const v4i xv = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[r], soff, 0);
             __builtin_memcpy(&pk[r], &xk, sizeof xk);
@@ -217,8 +223,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         uint16_t* ks = k_all + buf * kKB * kStr;
         uint16_t* vs = v_all + buf * kKB * kStrV;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int kr = lrow + 16 * r;
+        for (int r = 0; r < kLoadRows; ++r) {
+            const int kr = lrow + kLoadStride * r;
             *reinterpret_cast<v8bf*>(&ks[kr * kStr + lcol]) = pk[r];
             *reinterpret_cast<v8bf*>(&vs[kr * kStrV + lcol]) = pv[r];
         }
@@ -457,14 +463,14 @@ hipError_t launch_attn_masked(const AttnArgs& a, void* ws, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>((a.n_q + kQB - 1) / kQB) * a.Hq * B * s);
     hipError_t e;
     if (a.all_visible) {
-        hipLaunchKernelGGL(k_attn_masked_d128<true>, grid, dim3(256), 0, st, a,
+        hipLaunchKernelGGL(k_attn_masked_d128<true>, grid, dim3(64 * kMW), 0, st, a,
                            static_cast<const uint32_t*>(nullptr), 0, s, tps, part);
     } else {
         const int words = bitmap_words(a.n_k);
         const size_t lds = static_cast<size_t>(words) * sizeof(uint32_t);   // <= 32 KiB
         hipLaunchKernelGGL(k_sel_bitmap, dim3(a.rows), dim3(256), lds, st, a, bm, words);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_attn_masked_d128<false>, grid, dim3(256), 0, st, a,
+        hipLaunchKernelGGL(k_attn_masked_d128<false>, grid, dim3(64 * kMW), 0, st, a,
                            static_cast<const uint32_t*>(bm), words, s, tps, part);
     }
     if ((e = hipGetLastError()) != hipSuccess || s == 1) return e;
