@@ -112,7 +112,8 @@ typedef enum {
     DSA_ATTN_GATHER = 1,     /* gather each query's kept rows */
     DSA_ATTN_MASKED = 2      /* masked MHA: every key tile up to the block's last visible
                                 key, the selection as a mask (bf16, d_qk = d_v = 128,
-                                not latent, bf16 KV; else DSA_E_UNSUPPORTED) */
+                                not latent, bf16 KV, n_k * Hkv * 256 B below 2 GiB;
+                                else DSA_E_UNSUPPORTED) */
 } dsa_attn_mode_t;
 
 /* One problem: B sequences, each with n_q query rows and n_k key rows. */
@@ -203,7 +204,7 @@ dsa_status_t dsa_decode(const dsa_problem_t *p, void *out, float *lse, int32_t *
  * attention DSA reduces to when top_k >= pos(t) + 1 and the baseline the
  * pages measure DSA against.  Uses the main-attention fields only (q, k, v,
  * heads, dims, softmax_scale, q_pos); bf16, d_qk = d_v = 128, not latent,
- * bf16 KV (else DSA_E_UNSUPPORTED).  out: [B, n_q, Hq, d_v] bf16; lse:
+ * bf16 KV, n_k * Hkv * 256 B below 2 GiB (else DSA_E_UNSUPPORTED).  out: [B, n_q, Hq, d_v] bf16; lse:
  * [B, n_q, Hq] fp32 or NULL; workspace: dsa_workspace_bytes(DSA_OP_DENSE_ATTN)
  * bytes (partial results when the key walk is split; may be 0). */
 dsa_status_t dsa_dense_attn(const dsa_problem_t *p, void *out, float *lse,

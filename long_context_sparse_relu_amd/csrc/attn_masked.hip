@@ -183,7 +183,7 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
     // loads: the thread's byte offset within a tile is fixed, the tile's
     // offset is one scalar, and rows past n_k lie past the buffer's end and
     // read as zeros (one sequence's K or V spans n_k * Hkv * 256 bytes, below
-    // 2^31 for every shape the masked kernels take)
+    // 2^31: masked_kv_fits is part of every way into these kernels)
     const int lrow = threadIdx.x >> 4;          // 0..4*kMW-1, plus kLoadStride per step
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
     const int row_bytes = static_cast<int>(rstride) * 2;
@@ -418,6 +418,7 @@ static double masked_cost_us(const AttnArgs& a) {
 
 bool attn_masked_eligible(const AttnArgs& a) {
     if (!(a.dtype == BF16 && a.kv_dtype == BF16 && !a.latent && a.dqk == 128 && a.dv == 128)) return false;
+    if (!masked_kv_fits(a.n_k, a.Hkv)) return false;
     if (a.mode == ATTN_GATHER) return false;
     if (a.all_visible)                                       // causal mask, no bit rows
         return a.mode == ATTN_MASKED || masked_cost_us(a) < gather_cost_us(a);

@@ -122,7 +122,7 @@ static_assert(int(DSA_ATTN_AUTO) == int(dsa::ATTN_AUTO) && int(DSA_ATTN_GATHER) 
 // Shapes the masked (dense tile) kernels take.
 bool masked_shape(const dsa_problem_t* p) {
     return p->attn_dtype == DSA_BF16 && p->kv_dtype == DSA_BF16 && !p->kv_latent && p->d_qk == 128 &&
-           p->d_v == 128;
+           p->d_v == 128 && dsa::masked_kv_fits(p->n_k, p->kv_heads);
 }
 
 dsa_status_t check_attn(const dsa_problem_t* p) {
@@ -153,8 +153,8 @@ dsa_status_t check_attn(const dsa_problem_t* p) {
     if (p->attn_mode != DSA_ATTN_AUTO && p->attn_mode != DSA_ATTN_GATHER && p->attn_mode != DSA_ATTN_MASKED)
         return fail(DSA_E_INVALID, "attn_mode %d is not a dsa_attn_mode_t", p->attn_mode);
     if (p->attn_mode == DSA_ATTN_MASKED && (!masked_shape(p) || p->n_k > dsa::kMaskedMaxKeys))
-        return fail(DSA_E_UNSUPPORTED, "masked attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows "
-                    "and n_k <= %d", dsa::kMaskedMaxKeys);
+        return fail(DSA_E_UNSUPPORTED, "masked attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows, "
+                    "n_k <= %d and n_k * kv_heads * 256 B below 2 GiB", dsa::kMaskedMaxKeys);
     return DSA_OK;
 }
 
@@ -383,7 +383,8 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
         case DSA_OP_DENSE_ATTN:
             if (check_attn(p) != DSA_OK) return static_cast<size_t>(-1);
             if (!masked_shape(p)) {
-                fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows");
+                fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows "
+                     "and n_k * kv_heads * 256 B below 2 GiB");
                 return static_cast<size_t>(-1);
             }
             return dsa::attn_masked_workspace_bytes(dense_args(p, nullptr, nullptr));
@@ -467,7 +468,8 @@ dsa_status_t dsa_dense_attn(const dsa_problem_t* p, void* out, float* lse, void*
     dsa_status_t s;
     if ((s = check_common(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK) return s;
     if (!masked_shape(p))
-        return fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows");
+        return fail(DSA_E_UNSUPPORTED, "dense attention needs bf16 q and KV, d_qk = d_v = 128, no latent rows "
+                    "and n_k * kv_heads * 256 B below 2 GiB");
     if (!out) return fail(DSA_E_INVALID, "out is required");
     dsa::AttnArgs a = dense_args(p, out, lse);
     const size_t need = dsa::attn_masked_workspace_bytes(a);

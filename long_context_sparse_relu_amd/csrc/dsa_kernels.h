@@ -82,6 +82,11 @@ hipError_t launch_union_backbone(const int32_t* picks, int32_t* idx, int row0, i
 // Attention modes (dsa_attn_mode_t).
 enum AttnMode { ATTN_AUTO = 0, ATTN_GATHER = 1, ATTN_MASKED = 2 };
 constexpr int kMaskedMaxKeys = 1 << 18;  // keys of a selection bit row the masked path holds in LDS
+// The masked kernels address one sequence's K and V rows (n_k x Hkv x 256
+// bytes each) with 32-bit buffer offsets: the span must stay below 2^31.
+inline bool masked_kv_fits(int n_k, int Hkv) {
+    return static_cast<int64_t>(n_k) * Hkv * 256 < (static_cast<int64_t>(1) << 31);
+}
 
 struct AttnArgs {
     int rows, n_q, n_k, kk;

@@ -132,6 +132,17 @@ def test_dense_attn_validation(lib):
     d64 = _problem(d_qk=64, d_v=64)
     assert lib.dsa_dense_attn(ctypes.byref(d64), FAKE, None, FAKE, need, None) == dsa.E_UNSUPPORTED
     assert "dense" in dsa.last_error()
+    # the masked kernels address a sequence's K and V with 32-bit offsets:
+    # n_k * kv_heads * 256 B must stay below 2 GiB (here exactly 2 GiB)
+    huge = _problem(n_q=64, n_k=1 << 20, kv_heads=8, q_heads=8)
+    assert lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(huge)) == ctypes.c_size_t(-1).value
+    assert lib.dsa_dense_attn(ctypes.byref(huge), FAKE, None, FAKE, 1 << 40, None) == dsa.E_UNSUPPORTED
+    assert "2 GiB" in dsa.last_error()
+    masked = _problem(n_q=64, n_k=1 << 18, kv_heads=32, q_heads=32, attn_mode=dsa.ATTN_MASKED)
+    assert lib.dsa_sparse_attn(ctypes.byref(masked), FAKE, FAKE, None, FAKE, 1 << 40, None) == dsa.E_UNSUPPORTED
+    assert "2 GiB" in dsa.last_error()
+    fits = _problem(n_q=64, n_k=(1 << 20) - 64, kv_heads=8, q_heads=8)
+    assert lib.dsa_workspace_bytes(dsa.OP_DENSE_ATTN, ctypes.byref(fits)) != ctypes.c_size_t(-1).value
 
 
 def test_null_problem_and_outputs(lib):
