@@ -415,11 +415,12 @@ __device__ __forceinline__ void select_lds_row(const TopkArgs& a, uint32_t* keys
     write_ordered(sink, nwords, 1, k, out, wsum);
 }
 
-__global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
+template <int T>
+__global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
     extern __shared__ uint32_t keys[];                        // [min(n_k, kRowLdsMax)]
     __shared__ uint32_t lh[kTopkBins];
     __shared__ uint32_t bm[kRowLdsMax / 32];
-    __shared__ uint32_t wsum[kRowThreads / 64 + 2];
+    __shared__ uint32_t wsum[T / 64 + 2];
     __shared__ uint32_t n_list;
     const int lrow = blockIdx.x, row = a.row0 + lrow;
     const int vis = row_visible(a, row);
@@ -433,13 +434,13 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
     // the row's keys, eight loads in flight per thread (indices past vis
     // re-read the last score and are not stored)
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * kRowThreads) {
+    for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * T) {
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = ranked(a, sc, min(i0 + u * kRowThreads, vis - 1), vis);
+        for (int u = 0; u < 8; ++u) v[u] = ranked(a, sc, min(i0 + u * T, vis - 1), vis);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kRowThreads;
+            const int i = i0 + u * T;
             if (i < vis) {
                 const uint32_t kk = order_key(v[u]);
                 keys[i] = kk;
@@ -449,17 +450,17 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds(TopkArgs a) {
         }
     }
     const int nwords = (vis + 31) >> 5;
-    for (int i = threadIdx.x; i < nwords; i += kRowThreads) bm[i] = 0u;
+    for (int i = threadIdx.x; i < nwords; i += T) bm[i] = 0u;
     if (threadIdx.x == 0) n_list = 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
         kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
     }
-    __shared__ uint32_t wmin[kRowThreads / 64], wmax[kRowThreads / 64];
+    __shared__ uint32_t wmin[T / 64], wmax[T / 64];
     if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
     __syncthreads();
-    for (int w = 0; w < kRowThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
+    for (int w = 0; w < T / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
     select_lds_row(a, keys, vis, kmin, kmax, lh, bm, wsum, &n_list, out);
 }
 
@@ -584,12 +585,18 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
             return hipGetLastError();
         }
         const size_t smem = static_cast<size_t>(vis_max) * sizeof(uint32_t);
+        // rows of up to 8K keys leave LDS for three workgroups per CU, which
+        // 1024-thread workgroups cannot reach (two fill the CU's waves)
+        if (vis_max <= kRowLdsMax / 4) {
+            hipLaunchKernelGGL(k_topk_row_lds<512>, dim3(a.rows), dim3(512), smem, st, a);
+            return hipGetLastError();
+        }
         if (smem > 64 * 1024) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_row_lds),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_row_lds<kRowThreads>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(k_topk_row_lds, dim3(a.rows), dim3(kRowThreads), smem, st, a);
+        hipLaunchKernelGGL(k_topk_row_lds<kRowThreads>, dim3(a.rows), dim3(kRowThreads), smem, st, a);
         return hipGetLastError();
     }
     const dim3 grid((a.n_k + kChunk - 1) / kChunk, a.rows);
