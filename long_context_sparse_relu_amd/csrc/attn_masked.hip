@@ -401,17 +401,23 @@ static double gather_cost_us(const AttnArgs& a) {
     return kept * a.Hkv * 512.0 / 5.5e6;
 }
 static double masked_cost_us(const AttnArgs& a) {
+    // The rates were fitted with the walk counted per 128 queries; the kernel
+    // now walks per 256 (faster on long prefills), but counting per 256 halves
+    // the modelled bytes of a short chunk and picks the walk where gathering
+    // measured faster (GQA chunks of 256-1024 queries over 32K keys), so the
+    // count stays per 128.
+    constexpr int kCostQB = 128;
     const int B = a.rows / a.n_q;
-    const int nqb = (a.n_q + kQB - 1) / kQB;
+    const int nqb = (a.n_q + kCostQB - 1) / kCostQB;
     // key rows walked per query block: up to its last query's position
     // (q_pos unknown on the host: n_k - n_q + t, the usual layout)
     double walked = 0.0;
     for (int qb = 0; qb < nqb; ++qb) {
-        const int t_last = (qb + 1) * kQB < a.n_q ? (qb + 1) * kQB - 1 : a.n_q - 1;
+        const int t_last = (qb + 1) * kCostQB < a.n_q ? (qb + 1) * kCostQB - 1 : a.n_q - 1;
         walked += static_cast<double>(a.n_k - a.n_q + t_last + 1);
     }
     const double bytes = static_cast<double>(B) * a.Hq * walked * 512.0;
-    const double flops = 4.0 * 128.0 * a.Hq * static_cast<double>(B) * kQB * walked;
+    const double flops = 4.0 * 128.0 * a.Hq * static_cast<double>(B) * kCostQB * walked;
     const double t_bytes = bytes / 4.5e6, t_flops = flops / 8.0e8;
     return t_bytes > t_flops ? t_bytes : t_flops;
 }
