@@ -337,16 +337,18 @@ def test_decode_is_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("n_k", [20000, 6000])
 @pytest.mark.parametrize("sinks,window", [(0, 0), (3, 500)])
-def test_topk_long_rows_many_per_workgroup(sinks, window):
-    """dsa_topk over rows longer than 16K keys (one row fills most of a
-    compute unit's LDS, so each workgroup selects several rows in turn and
-    loads the next while selecting the current): 700 rows of explicit
-    positions, some short enough to keep every key, over seeded fp32 scores
-    quantised to 2^-10 so exact ties are common.  The kept sets must equal
-    the oracle's exactly (the same scores on both sides; ties to the lower
-    position), with and without a backbone."""
-    n_q, n_k, k = 700, 20000, 1000
+def test_topk_long_rows_many_per_workgroup(sinks, window, n_k):
+    """dsa_topk over LDS-resident rows with explicit positions: rows of up to
+    20000 keys (over 16K: one row fills most of a compute unit's LDS, so each
+    workgroup selects several rows in turn and loads the next while selecting
+    the current) and of up to 6000 (the 512-thread select, three rows per
+    compute unit).  700 rows, some short enough to keep every key, over
+    seeded fp32 scores quantised to 2^-10 so exact ties are common.  The kept
+    sets must equal the oracle's exactly (the same scores on both sides; ties
+    to the lower position), with and without a backbone."""
+    n_q, k = 700, 1000
     sp = custom_spec(name="long_rows", n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=k,
                      q_heads=2, kv_heads=1, d_qk=64, d_v=64, attn_dtype="bf16", sinks=sinks, window=window)
     inp = make_inputs(sp, device=DEV, seed=41)
