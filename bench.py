@@ -109,13 +109,14 @@ def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
                                 v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
                                 softmax_scale=inp["scale"], attn_mode=mode)
 
-    def attn_times(inp, k, idx, n):
+    def attn_times(inp, k, idx, n, n_gather=None):
         res = {}
         for name, mode in (("gather", dsa.ATTN_GATHER), ("masked", dsa.ATTN_MASKED)):
             prob = problem(inp, k, mode)
             out, lse = dsa._out_tensors(prob, None, None)
             ws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_SPARSE_ATTN, prob)), dtype=torch.uint8, device=dev)
-            res[name] = timed(lambda: dsa.sparse_attn(prob, idx, out, lse, ws, stream), n)
+            reps_ = n_gather if (name == "gather" and n_gather) else n
+            res[name] = timed(lambda: dsa.sparse_attn(prob, idx, out, lse, ws, stream), reps_)
         return res
 
     points = []
@@ -129,7 +130,9 @@ def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
             out, lse = dsa._out_tensors(prob, None, None)
             idx = torch.empty((1, L, k), dtype=torch.int32, device=dev)
             ws = torch.empty(dsa.workspace_bytes(dsa.OP_PREFILL, prob), dtype=torch.uint8, device=dev)
-            n = reps if L <= 8192 else max(3, reps // 3)
+            # long prefills: fewer timed calls (a gathered MHA prefill at 128K
+            # reads about 4 TB)
+            n = reps if L <= 8192 else (max(3, reps // 3) if L <= 32768 else 2)
             dsa_us = timed(lambda: dsa.prefill(prob, out, lse, idx, ws, stream), n)
             dsa.phase_timing(True)
             try:
@@ -139,7 +142,7 @@ def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
                 dsa.phase_timing(False)
             dws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_DENSE_ATTN, prob)), dtype=torch.uint8, device=dev)
             dense_us = timed(lambda: dsa.dense_attn(prob, out, lse, dws, stream), n)
-            at = attn_times(inp, k, idx, n)
+            at = attn_times(inp, k, idx, n, n_gather=1 if L > 32768 else None)
             pt = {"sweep": "mask", "part": "prefill", "L": L, "k": k, "dsa_prefill_us": dsa_us,
                   "dsa_phases_us": phases, "attn_gather_us": at["gather"], "attn_masked_us": at["masked"],
                   "dense_attn_us": dense_us, "dsa_over_dense": dsa_us / dense_us}
@@ -257,10 +260,24 @@ def _sweep_ladder(dsa, torch, dev, lengths, ks, reps):
     return 0
 
 
+def _cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _cpu_baseline(inp, n_seq, n_rows, min_s=10.0):
-    """The oracle on n_seq sequences (decode) or n_rows evenly spread query rows (prefill)."""
+    """The oracle on n_seq sequences (decode) or n_rows evenly spread query rows
+    (prefill), on every host CPU this process may run on."""
     import oracle
     from dsa_inputs import oracle_view
+    oracle.set_num_threads(len(os.sched_getaffinity(0)))
     threads = oracle.num_threads()
     if inp["n_q"] == 1:
         seqs = list(range(min(n_seq, inp["B"])))
@@ -283,6 +300,7 @@ def _cpu_baseline(inp, n_seq, n_rows, min_s=10.0):
         total += time.perf_counter() - t0
         reps += 1
     return {"value": reps * count / total, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "cpus_available": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
             "sample": f"{what}, whole path in fp64: indexer, top-k, attention; {reps} pass(es), {total:.2f} s"}
 
 
@@ -303,7 +321,7 @@ def main(argv=None):
                          "(JSON line per point)")
     ap.add_argument("--lengths", default="4096,16384,65536,131072,262144,524288,1048576")
     ap.add_argument("--ladder-ks", default="256,512,2048")
-    ap.add_argument("--ladder", default="1024,2048,4096,8192,16384,32768")
+    ap.add_argument("--ladder", default="1024,2048,4096,8192,16384,32768,65536,131072")
     ap.add_argument("--ks", default="512,2048")
     ap.add_argument("--chunks", default="16,64,256,1024,4096")
     ap.add_argument("--chunk-nk", type=int, default=32768)
@@ -375,13 +393,17 @@ def main(argv=None):
     fused_us = {name: v / reps for name, v in acc.items()}
     idx_us_fused = fused_us["index"]
 
-    # unfused phases, each its own launch sequence on the same stream
-    scores = torch.empty((B, n_q, N), dtype=torch.float32, device=dev)
-    tws = torch.empty(dsa.workspace_bytes(dsa.OP_TOPK, prob), dtype=torch.uint8, device=dev)
-    aws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_SPARSE_ATTN, prob)), dtype=torch.uint8, device=dev)
-    idx_us = _events_mean_us(lambda: dsa.index_scores(prob, scores, stream), reps, stream)
-    topk_us = _events_mean_us(lambda: dsa.topk(prob, scores, idx, tws, stream), reps, stream)
-    attn_us = _events_mean_us(lambda: dsa.sparse_attn(prob, idx, out, lse, aws, stream), reps, stream)
+    # unfused phases, each its own launch sequence on the same stream (only
+    # where the full score matrix the unfused indexer writes is at most 8 GiB)
+    unfused = B * n_q * N * 4 <= (8 << 30)
+    if unfused:
+        scores = torch.empty((B, n_q, N), dtype=torch.float32, device=dev)
+        tws = torch.empty(dsa.workspace_bytes(dsa.OP_TOPK, prob), dtype=torch.uint8, device=dev)
+        aws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_SPARSE_ATTN, prob)), dtype=torch.uint8, device=dev)
+        idx_us = _events_mean_us(lambda: dsa.index_scores(prob, scores, stream), reps, stream)
+        topk_us = _events_mean_us(lambda: dsa.topk(prob, scores, idx, tws, stream), reps, stream)
+        attn_us = _events_mean_us(lambda: dsa.sparse_attn(prob, idx, out, lse, aws, stream), reps, stream)
+        del scores, tws, aws
 
     H, D = s["idx_heads"], s["idx_dim"]
     kbytes = {"f32": 4, "bf16": 2, "e4m3": 1}[s["idx_dtype"]]
@@ -453,7 +475,7 @@ def main(argv=None):
         "fused_phases_us": fused_us,
         "phases_us": {"index_scores": idx_us, "topk": topk_us, "sparse_attn": attn_us,
                       "gather_GBs": gather_bytes / (attn_us * 1e-6) / 1e9,
-                      "attn_TFLOPs": attn_flops / (attn_us * 1e-6) / 1e12},
+                      "attn_TFLOPs": attn_flops / (attn_us * 1e-6) / 1e12} if unfused else None,
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline", file=sys.stderr, flush=True)

@@ -23,6 +23,8 @@ w ~ N(0,1)/2, main q/k/v ~ N(0,1), softmax scale 1/sqrt(d_qk)):
                     E4M3, k=512, one shared latent bf16 row of width 576 per
                     token (value = first 512 entries), 128 query heads,
                     256 planted needles per sequence
+  prefill_fp8_128k  prefill_fp8_32k's shapes at L=131072 (128K context, k=2048,
+                    about 1.6% of the longest prefix)
   decode_128k_fp8kv decode_128k with the main KV cache stored as E4M3 codes
                     and one fp32 scale per (token, kv head) row
   decode_128k_backbone  decode_128k with 4 sink tokens and a 4096-key local
@@ -65,6 +67,7 @@ CONFIGS: dict[str, dict] = {
                       top_k=512, q_heads=128, kv_heads=1, d_qk=576, d_v=512, latent=True,
                       attn_dtype="bf16", needles=256, outlier_frac=0.0, w_bf16=False),
 }
+CONFIGS["prefill_fp8_128k"] = dict(CONFIGS["prefill_fp8_32k"], n_q=131072, n_k=131072)
 CONFIGS["decode_128k_fp8kv"] = dict(CONFIGS["decode_128k"], kv_dtype="e4m3")
 CONFIGS["decode_128k_backbone"] = dict(CONFIGS["decode_128k"], sinks=4, window=4096)
 CONFIGS["decode_1m_window"] = dict(CONFIGS["decode_1m"], window=8192)

@@ -547,8 +547,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     const void* fn = a.dtype == F32        ? reinterpret_cast<const void*>(k_attn_generic<F32, F32>)
                      : a.kv_dtype == E4M3  ? reinterpret_cast<const void*>(k_attn_generic<BF16, E4M3>)
                                            : reinterpret_cast<const void*>(k_attn_generic<BF16, BF16>);
-    if (smem > 64 * 1024) {   // the latent shape stages ~104 KiB of rows
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    {   // (the latent shape stages ~104 KiB of rows)
+        hipError_t e = allow_dyn_lds(fn, smem);
         if (e != hipSuccess) return e;
     }
     dim3 grid((G + kGenHC - 1) / kGenHC, a.Hkv, a.rows);

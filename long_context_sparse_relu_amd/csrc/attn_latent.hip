@@ -225,8 +225,7 @@ hipError_t launch_attn_latent(const AttnArgs& a, float* part, hipStream_t st) {
     const int slice = ((a.kk + s - 1) / s + kLatKeys - 1) / kLatKeys * kLatKeys;
     const size_t idx_lds = static_cast<size_t>(slice) * sizeof(int32_t);   // <= 64 KiB
     if (idx_lds + sizeof(uint16_t) * 2 * kLatKeys * kLatStr > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_latent),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(idx_lds));
+        hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(k_attn_latent), idx_lds);
         if (e != hipSuccess) return e;
     }
     const dim3 grid(static_cast<unsigned>(a.rows) * hgroups * s);

@@ -180,29 +180,35 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint32_t* brow = DENSE ? nullptr : bm + static_cast<size_t>(row) * words;
 
     // loader: 256 threads x 4 rows x 16 B of K and of V per tile, as buffer
-    // loads: the thread's byte offset within a tile is fixed, the tile's
-    // offset is one scalar, and rows past n_k lie past the buffer's end and
-    // read as zeros (one sequence's K or V spans n_k * Hkv * 256 bytes, below
-    // 2^31: masked_kv_fits is part of every way into these kernels)
+    // loads with a fixed per-thread offset within the tile.  Each tile gets
+    // its own resources, based at the tile's first row and ending at the
+    // sequence's last row (the range check covers the per-thread offset only,
+    // not a scalar offset), so rows past n_k read as zeros whatever memory
+    // follows the tensor.  One sequence's K or V spans n_k * Hkv * 256 bytes,
+    // below 2^31: masked_kv_fits is part of every way into these kernels.
     const int lrow = threadIdx.x >> 4;          // 0..4*kMW-1, plus kLoadStride per step
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
     const int row_bytes = static_cast<int>(rstride) * 2;
     const int kv_bytes = __builtin_amdgcn_readfirstlane((a.n_k - 1) * row_bytes + 256);
-    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbase), 0, kv_bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbase), 0, kv_bytes, kBufferWord3);
+    const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
+    const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
     int voff[kLoadRows];
 #pragma unroll
     for (int r = 0; r < kLoadRows; ++r) voff[r] = (lrow + kLoadStride * r) * row_bytes + lcol * 2;
     v8bf pk[kLoadRows], pv[kLoadRows];
     uint32_t pw0 = 0u, pw1 = 0u;
-    // (the resources go in by value: a captured reference would pass them
-    // through memory, and a resource read from memory is not known uniform)
-    auto fetch_kv = [&](int tile, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr) {
-        const int soff = __builtin_amdgcn_readfirstlane(tile * kKB * row_bytes);   // uniform
+    auto fetch = [&](int tile) {
+        // tile * 64 <= n_k - 1, so the tile's offset is below kv_bytes
+        const int toff = __builtin_amdgcn_readfirstlane(tile * kKB * row_bytes);
+        const int rem = __builtin_amdgcn_readfirstlane(kv_bytes - toff);
+        const __amdgpu_buffer_rsrc_t kr =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbytes + toff), 0, rem, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t vr =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbytes + toff), 0, rem, kBufferWord3);
 #pragma unroll
         for (int r = 0; r < kLoadRows; ++r) {
-            const v4i xk = __builtin_amdgcn_raw_buffer_load_b128(kr, voff[r], soff, 0);
-            const v4i xv = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[r], soff, 0);
+            const v4i xk = __builtin_amdgcn_raw_buffer_load_b128(kr, voff[r], 0, 0);
+            const v4i xv = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[r], 0, 0);
             __builtin_memcpy(&pk[r], &xk, sizeof xk);
             __builtin_memcpy(&pv[r], &xv, sizeof xv);
         }
@@ -218,7 +224,6 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
         pw0 = live_q ? x0 : 0u;
         pw1 = live_q ? x1 : 0u;
     };
-    auto fetch = [&](int tile) { fetch_kv(tile, krsrc, vrsrc); };
     auto stage = [&](int buf) {
         uint16_t* ks = k_all + buf * kKB * kStr;
         uint16_t* vs = v_all + buf * kKB * kStrV;

@@ -332,7 +332,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         dsa::TopkArgs ta = topk_args(p, r0, nr, scores, picks, base + L.topk_off);
         // (the indexer's histogram counts the real scores; a backbone ranks its
         // forced keys as -inf, so the top-k builds its own)
-        if (dsa::index_fills_hist(ia) && !dsa::topk_row_lds(p->n_k) && !has_backbone(p)) {
+        if (dsa::index_fills_hist(ia) && !dsa::topk_rows_fit_lds(ta) && !has_backbone(p)) {
             // the indexer builds the first-digit histogram as it writes the scores
             ia.hist = ta.hist;
             ta.hist_ready = true;
@@ -357,6 +357,35 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
 
 }  // namespace
 
+namespace dsa {
+
+hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;             // below the default limit
+    struct Entry { int device; const void* fn; size_t bytes; };
+    static std::mutex mu;
+    static std::vector<Entry> set;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    for (Entry& x : set) {
+        if (x.device != dev || x.fn != fn) continue;
+        if (bytes <= x.bytes) return hipSuccess;
+        if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes))) !=
+            hipSuccess)
+            return e;
+        x.bytes = bytes;
+        return hipSuccess;
+    }
+    if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes))) !=
+        hipSuccess)
+        return e;
+    set.push_back(Entry{dev, fn, bytes});
+    return hipSuccess;
+}
+
+}  // namespace dsa
+
 extern "C" {
 
 int dsa_abi_version(void) { return DSA_ABI_VERSION; }
@@ -374,7 +403,9 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
             return topk_ws_bytes(p);
         case DSA_OP_PREFILL:
         case DSA_OP_DECODE:
-            if (check_topk(p) != DSA_OK) return static_cast<size_t>(-1);
+            // the same checks as the entry points: the layout divides by head counts
+            if (check_index(p) != DSA_OK || check_topk(p) != DSA_OK || check_attn(p) != DSA_OK)
+                return static_cast<size_t>(-1);
             if (op == DSA_OP_DECODE && p->n_q != 1) {
                 fail(DSA_E_INVALID, "dsa_decode takes n_q == 1 (got %d)", p->n_q);
                 return static_cast<size_t>(-1);

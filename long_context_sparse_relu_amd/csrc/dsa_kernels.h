@@ -66,9 +66,10 @@ size_t topk_workspace_bytes(int rows, int n_k);
 int topk_cand_cap(int n_k);
 void topk_carve(void* ws, int rows, int n_k, TopkArgs& a);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-// Rows of at most this many keys are selected by one workgroup from LDS (no
-// histogram from the indexer needed).
-bool topk_row_lds(int n_k);
+// True when every row of the launch is short enough (32K visible keys) to be
+// selected by one workgroup from LDS; launch_topk then neither reads nor
+// clears the histograms.
+bool topk_rows_fit_lds(const TopkArgs& a);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 // idx[r][j] = j for j <= pos(row0 + r), else -1 (pos from n_k - n_q + t): the
 // top-k result of a row that keeps every visible key.
@@ -105,6 +106,11 @@ struct AttnArgs {
     int mode;              // AttnMode
     bool all_visible;      // every row keeps all keys 0..pos(t) (idx may then be ignored)
 };
+
+// Lets kernel `fn` take `bytes` of dynamic LDS on the current device.  The
+// attribute is set once per (device, kernel, size reached so far): later
+// launches that need no more LDS than an earlier one make no HIP call.
+hipError_t allow_dyn_lds(const void* fn, size_t bytes);
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t st);
 // True when launch_index_scores accumulates a.hist (the top-k's first-digit

@@ -380,7 +380,6 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 constexpr int kRowLdsMax = 32768;       // scores a row may hold in LDS (128 KiB)
 constexpr int kRowThreads = 1024;
 
-bool topk_row_lds(int n_k) { return n_k <= kRowLdsMax; }
 
 struct LdsRel {
     const uint32_t* key; int n; uint32_t base;
@@ -552,24 +551,31 @@ void topk_carve(void* ws, int rows, int n_k, TopkArgs& a) {
 // `a.rows` rows starting at absolute row a.row0; scores, idx and the
 // workspace are indexed from the first of them.  Unless a.hist_ready, the
 // workspace's counters are cleared and the digit-0 histogram built here.
+// The longest visible prefix among the rows of a launch: known on the host
+// when positions are implicit (pos = n_k - n_q + t), else n_k.
+static int launch_vis_max(const TopkArgs& a) {
+    int vis_max = a.n_k;
+    if (!a.q_pos && a.rows > 0) {
+        const int last = a.row0 + a.rows - 1;
+        const int t_max = a.row0 / a.n_q == last / a.n_q ? last % a.n_q : a.n_q - 1;
+        vis_max = min(a.n_k, a.n_k - a.n_q + t_max + 1);
+        if (vis_max < 1) vis_max = 1;
+    }
+    return vis_max;
+}
+
+bool topk_rows_fit_lds(const TopkArgs& a) { return launch_vis_max(a) <= kRowLdsMax; }
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipError_t e;
-    if (topk_row_lds(a.n_k)) {
-        // LDS for the longest visible prefix among the rows: known on the
-        // host when positions are implicit (pos = n_k - n_q + t), else n_k
-        int vis_max = a.n_k;
-        if (!a.q_pos && a.rows > 0) {
-            const int last = a.row0 + a.rows - 1;
-            const int t_max = a.row0 / a.n_q == last / a.n_q ? last % a.n_q : a.n_q - 1;
-            vis_max = min(a.n_k, a.n_k - a.n_q + t_max + 1);
-            if (vis_max < 1) vis_max = 1;
-        }
+    // rows of at most kRowLdsMax visible keys (all rows of a short prefill,
+    // the early row blocks of a long one) are selected from LDS
+    const int vis_max = launch_vis_max(a);
+    if (vis_max <= kRowLdsMax) {
         if (vis_max > kRowLdsMax / 2) {
             const void* fn = reinterpret_cast<const void*>(k_topk_row_lds_next);
             const size_t smem = static_cast<size_t>(kRowLdsMax) * sizeof(uint32_t);
-            if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem))) !=
-                hipSuccess)
-                return e;
+            if ((e = allow_dyn_lds(fn, smem)) != hipSuccess) return e;
             // workgroups the chip holds at once (one per CU at this LDS size)
             static const int per_cu = [fn, smem] {
                 int nb = 0;
@@ -591,11 +597,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
             hipLaunchKernelGGL(k_topk_row_lds<512>, dim3(a.rows), dim3(512), smem, st, a);
             return hipGetLastError();
         }
-        if (smem > 64 * 1024) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_row_lds<kRowThreads>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-            if (e != hipSuccess) return e;
-        }
+        if ((e = allow_dyn_lds(reinterpret_cast<const void*>(k_topk_row_lds<kRowThreads>), smem)) != hipSuccess)
+            return e;
         hipLaunchKernelGGL(k_topk_row_lds<kRowThreads>, dim3(a.rows), dim3(kRowThreads), smem, st, a);
         return hipGetLastError();
     }
@@ -611,11 +614,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_topk_filter, fgrid, dim3(kFThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t smem = finish_lds_bytes(a);
-    if (smem > 64 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-        if (e != hipSuccess) return e;
-    }
+    if ((e = allow_dyn_lds(reinterpret_cast<const void*>(k_topk_finish), smem)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_topk_finish, dim3(a.rows), dim3(kFinishThreads), smem, st, a);
     return hipGetLastError();
 }

@@ -331,9 +331,8 @@ hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st) {
     const size_t tail = t.ix.n_k <= kBitmapMaxKeys ? static_cast<size_t>((t.ix.n_k + 31) >> 5) * 4
                                                    : static_cast<size_t>(kpad) * 4;
     const size_t smem = static_cast<size_t>(t.ix.cand_cap) * sizeof(uint64_t) + tail;
-    if (smem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish_sampled),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    {
+        hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(k_topk_finish_sampled), smem);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_topk_finish_sampled, dim3(t.ix.rows), dim3(kSFinishThreads), smem, st, t);

@@ -53,6 +53,8 @@ def _load():
     i64, dbl, vp, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
     lib.ora_num_threads.restype = ctypes.c_int
     lib.ora_num_threads.argtypes = []
+    lib.ora_set_num_threads.restype = None
+    lib.ora_set_num_threads.argtypes = [ctypes.c_int]
     lib.ora_e4m3_value.restype = dbl
     lib.ora_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.ora_bf16_value.restype = dbl
@@ -99,6 +101,11 @@ def _positions(pos, n_q, n_k):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().ora_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Sets the OpenMP threads of the oracle's parallel loops (n >= 1)."""
+    _load().ora_set_num_threads(int(n))
 
 
 def e4m3_value(code: int) -> float:

@@ -56,6 +56,16 @@ int ora_num_threads(void)
 #endif
 }
 
+/* Sets the thread count of the parallel loops below (n >= 1). */
+void ora_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* OCP FP8 E4M3 ("E4M3FN"): 1 sign bit, 4 exponent bits with bias 7, 3
  * mantissa bits.  Exponent field 0 encodes subnormals m/8 * 2^-6.  There is no
  * infinity; exponent 15 with mantissa 7 is NaN, so the largest finite value is

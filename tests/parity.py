@@ -56,17 +56,31 @@ def check_topk_row(gpu_idx, ora_idx, ora_scores, kth, pos, k):
     return len(only_o)
 
 
-def check_attn(gpu_out, gpu_lse, ora_out, ora_lse, dtype):
+def attn_errors(gpu_out, gpu_lse, ora_out, ora_lse):
+    """Observed errors of an attention result: out max-abs, out max-abs relative
+    to max|oracle out| (a diagnostic), and lse max-abs over non-empty rows."""
     gpu_out = np.asarray(gpu_out, dtype=np.float64)
-    err = np.abs(gpu_out - ora_out).max() if gpu_out.size else 0.0
-    assert err <= OUT_TOL[dtype], f"attention max-abs error {err} > {OUT_TOL[dtype]}"
+    err = float(np.abs(gpu_out - ora_out).max()) if gpu_out.size else 0.0
+    scale = float(np.abs(ora_out).max()) if gpu_out.size else 0.0
+    gl = np.asarray(gpu_lse, dtype=np.float64)
+    fin = np.isfinite(ora_lse)
+    lerr = float(np.abs(gl[fin] - ora_lse[fin]).max()) if fin.any() else 0.0
+    return {"out": err, "out_rel": err / scale if scale > 0 else 0.0, "lse": lerr}
+
+
+def check_attn(gpu_out, gpu_lse, ora_out, ora_lse, dtype, errors=None):
+    """Asserts the attention rule; returns the out max-abs error.  With
+    `errors` (a dict) the observed errors are also folded into it (max)."""
+    e = attn_errors(gpu_out, gpu_lse, ora_out, ora_lse)
+    assert e["out"] <= OUT_TOL[dtype], f"attention max-abs error {e['out']} > {OUT_TOL[dtype]}"
     gl = np.asarray(gpu_lse, dtype=np.float64)
     fin = np.isfinite(ora_lse)
     assert np.array_equal(np.isneginf(gl), ~fin), "empty rows must give lse = -inf"
-    if fin.any():
-        lerr = np.abs(gl[fin] - ora_lse[fin]).max()
-        assert lerr <= LSE_TOL[dtype], f"lse error {lerr}"
-    return float(err)
+    assert e["lse"] <= LSE_TOL[dtype], f"lse error {e['lse']}"
+    if errors is not None:
+        for key, v in e.items():
+            errors[key] = max(errors.get(key, 0.0), v)
+    return e["out"]
 
 
 def check_backbone_row(gpu_idx, ora_idx, ora_scores, kth, pos, k, sinks, window):

@@ -170,6 +170,18 @@ def test_workspace_sizes_and_shortfall(lib):
     assert lib.dsa_workspace_bytes(dsa.OP_DECODE, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
 
 
+@pytest.mark.parametrize("op", [dsa.OP_PREFILL, dsa.OP_DECODE])
+@pytest.mark.parametrize("over", [dict(q_heads=0), dict(kv_heads=0), dict(kv_heads=5), dict(idx_heads=0),
+                                  dict(idx_dim=64), dict(iw=None), dict(attn_dtype=7), dict(q=None)])
+def test_fused_workspace_query_validates_like_the_entry_points(lib, op, over):
+    """dsa_workspace_bytes for the fused ops runs the entry points' checks:
+    a problem the call would reject sizes to SIZE_MAX (never a crash, e.g. a
+    division by a zero head count while laying out the workspace)."""
+    p = _problem(**over)
+    assert lib.dsa_workspace_bytes(op, ctypes.byref(p)) == ctypes.c_size_t(-1).value
+    assert dsa.last_error()
+
+
 def test_binding_rejects_missing_library(tmp_path):
     saved = dsa._lib
     dsa._lib = None
