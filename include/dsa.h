@@ -200,6 +200,23 @@ dsa_status_t dsa_prefill(const dsa_problem_t *p, void *out, float *lse, int32_t 
 dsa_status_t dsa_decode(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Fused decode that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Inputs, outputs and results are
+ * those of dsa_decode (the same kernels run).  Its scratch is a static array
+ * of DSA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; the kernels clear what must start at zero, and the
+ * array keeps whatever the last call left.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams or other
+ * threads) race and must not be made.  A problem whose scratch need (the
+ * bytes dsa_workspace_bytes(DSA_OP_DECODE) reports, less the selection when
+ * idx_out is given) exceeds DSA_NOALLOC_SCRATCH_BYTES returns
+ * DSA_E_UNSUPPORTED before anything is enqueued.  The phase timer does not
+ * record these calls. */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status_t dsa_decode_noalloc(const dsa_problem_t *p, void *out, float *lse, int32_t *idx_out,
+                                hipStream_t stream);
+
 /* Dense causal attention: every query row over all its visible keys, the
  * attention DSA reduces to when top_k >= pos(t) + 1 and the baseline the
  * pages measure DSA against.  Uses the main-attention fields only (q, k, v,

@@ -30,8 +30,9 @@ ABI_VERSION = 2
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
 EXPORTED = ("dsa_abi_version", "dsa_workspace_bytes", "dsa_index_scores", "dsa_topk",
-            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_dense_attn", "dsa_phase_timing", "dsa_phase_times",
-            "dsa_status_str", "dsa_last_error")
+            "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_decode_noalloc", "dsa_dense_attn",
+            "dsa_phase_timing", "dsa_phase_times", "dsa_status_str", "dsa_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # dsa_phase_t, in order
 PHASES = ("prep", "index", "topk", "attn")
 
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp]
     lib.dsa_decode.restype = ctypes.c_int
     lib.dsa_decode.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.dsa_decode_noalloc.restype = ctypes.c_int
+    lib.dsa_decode_noalloc.argtypes = [P, vp, vp, vp, vp]
     lib.dsa_dense_attn.restype = ctypes.c_int
     lib.dsa_dense_attn.argtypes = [P, vp, vp, vp, sz, vp]
     lib.dsa_phase_timing.restype = ctypes.c_int
@@ -317,6 +320,14 @@ def prefill(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, 
 
 def decode(prob: DSAProblem, out=None, lse=None, idx_out=None, workspace=None, stream=None):
     return _fused(load_library().dsa_decode, OP_DECODE, prob, out, lse, idx_out, workspace, stream)
+
+
+def decode_noalloc(prob: DSAProblem, out=None, lse=None, idx_out=None, stream=None):
+    """dsa_decode on the library's static per-GPU scratch (no workspace).  Calls
+    on one GPU must not overlap; out/lse are allocated here only when not given."""
+    out, lse = _out_tensors(prob, out, lse)
+    _check(load_library().dsa_decode_noalloc(prob.ref(), _ptr(out), _ptr(lse), _ptr(idx_out), _stream(stream)))
+    return out, lse, idx_out
 
 
 def dense_attn(prob: DSAProblem, out=None, lse=None, workspace=None, stream=None):

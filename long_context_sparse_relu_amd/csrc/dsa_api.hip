@@ -284,17 +284,18 @@ size_t topk_ws_bytes(const dsa_problem_t* p) {
     return sel + (has_backbone(p) ? static_cast<size_t>(rows_of(p)) * p->top_k * sizeof(int32_t) : 0);
 }
 
+// timed = false: the phase timer is bypassed (it creates HIP events).
 dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,
-                       void* ws, size_t ws_bytes, hipStream_t st) {
+                       void* ws, size_t ws_bytes, hipStream_t st, bool timed = true) {
     FusedLayout L = fused_layout(p, idx_out == nullptr);
     if (!ws || ws_bytes < L.total)
         return fail(DSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
     unsigned char* base = static_cast<unsigned char*>(ws);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx_off);
     const int rows = rows_of(p);
-    dsa_status_t s = device_status(timer_mark(-1, st), "phase timer");
+    dsa_status_t s = timed ? device_status(timer_mark(-1, st), "phase timer") : DSA_OK;
     if (s != DSA_OK) return s;
-    auto mark = [&](int ph) { return device_status(timer_mark(ph, st), "phase timer"); };
+    auto mark = [&](int ph) { return timed ? device_status(timer_mark(ph, st), "phase timer") : DSA_OK; };
     for (int r0 = 0; r0 < rows; r0 += L.block_rows) {
         int nr = rows - r0 < L.block_rows ? rows - r0 : L.block_rows;
         if (block_keeps_all(p, r0, nr)) {
@@ -353,6 +354,37 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
     s = device_status(dsa::launch_sparse_attn(aa, base + L.attn_off, st), "attention launch");
     if (s != DSA_OK) return s;
     return mark(DSA_PHASE_ATTN);
+}
+
+// Scratch of dsa_decode_noalloc.  Each GPU the library runs on holds its own
+// copy of this array until the process ends.  On the host its name is a
+// stand-in, not a device address: host code uses only the address
+// hipGetSymbolAddress returns for the current device (kept per device below).
+__device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device with that
+// device current.
+dsa_status_t scratch_ptr(void** out) {
+    int dev = 0;
+    dsa_status_t s = device_status(hipGetDevice(&dev), "hipGetDevice");
+    if (s != DSA_OK) return s;
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(DSA_E_UNSUPPORTED, "device %d is beyond the %d devices the static scratch serves", dev,
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        s = device_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (s != DSA_OK) return s;
+        if (!ptr) return fail(DSA_E_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
 }
 
 }  // namespace
@@ -491,6 +523,25 @@ dsa_status_t dsa_decode(const dsa_problem_t* p, void* out, float* lse, int32_t* 
         return s;
     if (!out) return fail(DSA_E_INVALID, "out is required");
     return run_fused(p, out, lse, idx_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status_t dsa_decode_noalloc(const dsa_problem_t* p, void* out, float* lse, int32_t* idx_out,
+                                hipStream_t stream) {
+    g_last_error.clear();
+    dsa_status_t s;
+    if ((s = check_common(p)) != DSA_OK) return s;
+    if (p->n_q != 1) return fail(DSA_E_INVALID, "dsa_decode_noalloc takes n_q == 1 (got %d)", p->n_q);
+    if ((s = check_index(p)) != DSA_OK || (s = check_topk(p)) != DSA_OK || (s = check_attn(p)) != DSA_OK)
+        return s;
+    if (!out) return fail(DSA_E_INVALID, "out is required");
+    const size_t need = fused_layout(p, idx_out == nullptr).total;
+    if (need > static_cast<size_t>(DSA_NOALLOC_SCRATCH_BYTES))
+        return fail(DSA_E_UNSUPPORTED, "dsa_decode_noalloc: this problem needs %zu bytes of scratch and the "
+                    "static scratch holds %zu; call dsa_decode with a workspace instead", need,
+                    static_cast<size_t>(DSA_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if ((s = scratch_ptr(&ws)) != DSA_OK) return s;
+    return run_fused(p, out, lse, idx_out, ws, DSA_NOALLOC_SCRATCH_BYTES, stream, /*timed=*/false);
 }
 
 dsa_status_t dsa_dense_attn(const dsa_problem_t* p, void* out, float* lse, void* workspace,

@@ -182,6 +182,18 @@ def test_fused_workspace_query_validates_like_the_entry_points(lib, op, over):
     assert dsa.last_error()
 
 
+def test_noalloc_decode_rejects_problems_beyond_its_scratch(lib):
+    """dsa_decode_noalloc validates like dsa_decode and refuses, before any
+    device call, a problem whose scratch need exceeds the static array."""
+    assert lib.dsa_decode_noalloc(ctypes.byref(_problem(n_q=2)), FAKE, FAKE, FAKE, None) == dsa.E_INVALID
+    assert lib.dsa_decode_noalloc(ctypes.byref(_problem()), None, FAKE, FAKE, None) == dsa.E_INVALID
+    big = _problem(batch=64, n_k=1 << 20)
+    need = lib.dsa_workspace_bytes(dsa.OP_DECODE, ctypes.byref(big))
+    assert need > dsa.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_decode_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, None) == dsa.E_UNSUPPORTED
+    assert "scratch" in dsa.last_error()
+
+
 def test_binding_rejects_missing_library(tmp_path):
     saved = dsa._lib
     dsa._lib = None
