@@ -262,6 +262,64 @@ __host__ __device__ inline int tiled_block_tiles(int j, int nrows, int kTQ, long
     return vis > 0 ? static_cast<int>((vis + 63) / 64) : 0;
 }
 
+// This workgroup's share of a launch's (query block, key tile) pairs,
+// block-major.  Runs (piece == 0): tiles [total*w/G, total*(w+1)/G), which
+// cross at most one block boundary (the launcher checks that no block is
+// shorter than a run): ta tiles of block qb from tile t0, then tb tiles of
+// block qb + 1.  Pieces (piece > 0): block j's tiles cut into pieces of at
+// most `piece` tiles, handed out in reverse block order (longest blocks
+// first).  Either way the first block is found the same way: lane l sums the
+// counts (tiles or pieces) of blocks [l*m, (l+1)*m), the lanes take an
+// inclusive prefix, and the first lane whose prefix passes the target walks
+// its own blocks.  Every wave does this and gets the same answer.  Returns
+// false when the workgroup has no work.
+struct TiledWork { int qb, t0, tj, ta, tb, piece; };
+
+template <int kTQ>
+__device__ __forceinline__ bool tiled_work_start(int lane, int nrows, long long base, int n_k, bool all_keys,
+                                                 int piece, long long total, TiledWork& w) {
+    const int nqb = (nrows + kTQ - 1) / kTQ;
+    const bool runs = piece == 0;
+    const long long target = runs ? total * blockIdx.x / gridDim.x : static_cast<long long>(gridDim.x - 1 - blockIdx.x);
+    const long long g_end = runs ? total * (blockIdx.x + 1) / gridDim.x : 0;
+    if (runs && target >= g_end) return false;               // uniform over the workgroup
+    auto units = [&](int j) {
+        const int tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
+        return runs ? tj : (tj + piece - 1) / piece;
+    };
+    const int m = (nqb + 63) / 64;
+    long long lsum = 0;
+    for (int i = 0; i < m; ++i) {
+        const int j = lane * m + i;
+        if (j < nqb) lsum += units(j);
+    }
+    long long incl = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const long long v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    const int L = __ffsll(static_cast<long long>(__ballot(target < incl))) - 1;   // target < all units
+    long long acc = __shfl(incl - lsum, L);
+    int j = L * m;
+    int u = units(j);
+    while (acc + u <= target) {
+        acc += u;
+        u = units(++j);
+    }
+    w.qb = __builtin_amdgcn_readfirstlane(j);
+    w.tj = __builtin_amdgcn_readfirstlane(tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys));
+    const int into = __builtin_amdgcn_readfirstlane(static_cast<int>(target - acc));
+    w.piece = piece;
+    w.t0 = runs ? into : into * piece;
+    w.ta = w.tb = 0;
+    if (runs) {
+        w.ta = static_cast<int>(min(static_cast<long long>(w.tj - w.t0), g_end - target));
+        w.tb = static_cast<int>(g_end - target - w.ta);
+    }
+    return true;
+}
+
 template <int DT>
 __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexArgs x, int t_first, int nrows,
                                                                         int piece, long long total, int write_future) {
@@ -282,7 +340,6 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
     const int b = t_first / x.n_q;                           // every row of the launch is in sequence b
     const long long base = static_cast<long long>(n_k) - x.n_q + t_first % x.n_q;
     const bool all_keys = x.q_pos != nullptr;
-    const int nqb = (nrows + kTQ - 1) / kTQ;
 
     // Score keys [c0, c1) of query block qb (c0 a multiple of 64).
     auto run_segment = [&](const int qb, const int c0, const int c1) {
@@ -509,62 +566,315 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
         if (write_future) write_inf(cvis);                       // keys of this run no query of the block sees
     };
 
-    // This workgroup's share of the launch's (block, tile) pairs, block-major.
-    // Runs (piece == 0): tiles [total*w/G, total*(w+1)/G), which cross at most
-    // one block boundary (the launcher checks that no block is shorter than a
-    // run).  Pieces (piece > 0): block j's tiles cut into pieces of at most
-    // `piece` tiles, handed out in reverse block order (longest blocks first).
-    // Either way the first block is found the same way: lane l sums the counts
-    // (tiles or pieces) of blocks [l*m, (l+1)*m), the lanes take an inclusive
-    // prefix, and the first lane whose prefix passes the target walks its own
-    // blocks.  Every wave does this and gets the same answer.
-    const bool runs = piece == 0;
-    const long long target = runs ? total * blockIdx.x / gridDim.x : static_cast<long long>(gridDim.x - 1 - blockIdx.x);
-    const long long g_end = runs ? total * (blockIdx.x + 1) / gridDim.x : 0;
-    if (runs && target >= g_end) return;                      // uniform over the workgroup
-    auto units = [&](int j) {
-        const int tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
-        return runs ? tj : (tj + piece - 1) / piece;
-    };
-    int qb, t0, tj;
-    {
-        const int m = (nqb + 63) / 64;
-        long long lsum = 0;
-        for (int i = 0; i < m; ++i) {
-            const int j = lane * m + i;
-            if (j < nqb) lsum += units(j);
-        }
-        long long incl = lsum;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const long long v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-        }
-        const int L = __ffsll(static_cast<long long>(__ballot(target < incl))) - 1;   // target < all units
-        long long acc = __shfl(incl - lsum, L);
-        int j = L * m;
-        int u = units(j);
-        while (acc + u <= target) {
-            acc += u;
-            u = units(++j);
-        }
-        qb = __builtin_amdgcn_readfirstlane(j);
-        tj = __builtin_amdgcn_readfirstlane(tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys));
-        const int into = __builtin_amdgcn_readfirstlane(static_cast<int>(target - acc));
-        t0 = runs ? into : into * piece;
-    }
-    if (!runs) {
-        run_segment(qb, 64 * t0, min(64 * min(t0 + piece, tj), n_k));
+    TiledWork w;
+    if (!tiled_work_start<kTQ>(lane, nrows, base, n_k, all_keys, piece, total, w)) return;
+    if (w.piece > 0) {
+        run_segment(w.qb, 64 * w.t0, min(64 * min(w.t0 + w.piece, w.tj), n_k));
         return;
     }
     // a run: the rest of this block, then (if the run is longer) the head of
     // the next block
-    const int ta = static_cast<int>(min(static_cast<long long>(tj - t0), g_end - target));
-    run_segment(qb, 64 * t0, min(64 * (t0 + ta), n_k));
-    const int tb = static_cast<int>(g_end - target - ta);
-    if (tb > 0) {
+    run_segment(w.qb, 64 * w.t0, min(64 * (w.t0 + w.ta), n_k));
+    if (w.tb > 0) {
         __syncthreads();                                      // the second segment restages both LDS buffers
-        run_segment(qb + 1, 0, min(64 * tb, n_k));
+        run_segment(w.qb + 1, 0, min(64 * w.tb, n_k));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 prefill path with the query rows as the rows of the MFMA.  A wave holds
+// RG groups of 16 query rows with every head's operand in registers (16
+// heads x 8 registers per group); per head and 16 keys one
+// v_mfma_scale_f32_16x16x128_f8f6f4 gives that head's 16 x 16 dot products,
+// lane l holding queries 4(l/16)..4(l/16)+3 of key l%16.  Each lane folds its
+// four products with ReLU and the head weight (one integer max and one FMA
+// each) into four running sums, so the sum over heads needs no exchange
+// between lanes and the only vector work per product is those two
+// instructions.  The waves of a workgroup share each 64-key tile staged in
+// LDS.  The head weights times the query scales sit in LDS ([head][query])
+// and are read as one 16-byte broadcast per head and group.  Work split and
+// stores as in k_index_tiled.
+// ---------------------------------------------------------------------------
+#ifndef DSA_Q16_RG
+#define DSA_Q16_RG 1
+#endif
+constexpr int kQ16RG = DSA_Q16_RG;                   // groups of 16 query rows per wave
+constexpr int kQ16W = kQ16RG == 1 ? 8 : 4;           // waves per workgroup (one workgroup per CU)
+constexpr int kQ16Q = 16 * kQ16RG * kQ16W;           // query rows per workgroup (block)
+
+__global__ __launch_bounds__(kQ16W * 64) __attribute__((amdgpu_waves_per_eu(kQ16W / 4)))
+void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long total, int write_future) {
+    constexpr int RG = kQ16RG;
+    constexpr int KSTR = 144;                                // padded LDS stride of a 128-byte key row
+    constexpr int PIECES = 64 * 128 / 16 / (kQ16W * 64);     // 16-byte pieces of a key tile per thread
+    __shared__ __align__(16) uint8_t k_s[2][64 * KSTR];      // double-buffered key tile
+    __shared__ float ks_s[2][64];
+    __shared__ __align__(16) float w_s[16 * kQ16Q];          // [head][query]: w * sq (0 past H or nrows)
+
+    const int lane = threadIdx.x & 63;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, kg = lane >> 4;
+    const int n_k = x.n_k, H = x.H;
+    const int b = t_first / x.n_q;                           // every row of the launch is in sequence b
+    const long long base = static_cast<long long>(n_k) - x.n_q + t_first % x.n_q;
+    const bool all_keys = x.q_pos != nullptr;
+    const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * n_k * 128;
+    const float* ksb = x.ik_scale + static_cast<size_t>(b) * n_k;
+    constexpr uint32_t kNoStore = 0x7FFFFFF0u;               // past any row range (<= 2^30 bytes): dropped
+    const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto run_segment = [&](const int qb, const int c0, const int c1) {
+        // the block's last visible key (every wave computes it)
+        int last = -1;
+        for (int r = lane; r < kQ16Q; r += 64) {
+            const int lr = qb * kQ16Q + r;
+            if (lr < nrows) last = max(last, row_pos(x.q_pos, t_first + lr, x.n_q, n_k));
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) last = max(last, __shfl_xor(last, o));
+        last = __builtin_amdgcn_readfirstlane(last);
+        const int cvis = min(c1, last + 1);                  // keys some query of the block sees
+
+        // row group g of this wave: block rows r0[g] .. r0[g] + nlive[g] - 1
+        int r0[RG], nlive[RG], pos[RG][4], wmin = INT_MAX, wmax = -1;
+        __amdgpu_buffer_rsrc_t orsrc[RG];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            r0[g] = qb * kQ16Q + 16 * (wave * RG + g);
+            nlive[g] = __builtin_amdgcn_readfirstlane(max(0, min(16, nrows - r0[g])));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = 4 * kg + i;
+                pos[g][i] = q < nlive[g] ? row_pos(x.q_pos, t_first + r0[g] + q, x.n_q, n_k) : -1;
+                if (q < nlive[g]) { wmin = min(wmin, pos[g][i]); wmax = max(wmax, pos[g][i]); }
+            }
+            // stores: one resource over the group's live rows (missing rows lie past its end)
+            float* grow = x.scores + static_cast<size_t>(t_first + r0[g] - x.row0) * n_k;
+            orsrc[g] = __builtin_amdgcn_make_buffer_rsrc(grow, 0, nlive[g] > 0 ? nlive[g] * n_k * 4 : 0, kBufferWord3);
+        }
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {
+            wmin = min(wmin, __shfl_xor(wmin, o));
+            wmax = max(wmax, __shfl_xor(wmax, o));
+        }
+        wmin = __builtin_amdgcn_readfirstlane(wmin);         // first and last key every / any row of the wave sees
+        wmax = __builtin_amdgcn_readfirstlane(wmax);
+        uint32_t roff[4];                                    // lane's byte offset of output row 4kg + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) roff[i] = static_cast<uint32_t>(4 * kg + i) * static_cast<uint32_t>(n_k) * 4u;
+
+        auto store_inf = [&](int from) {                     // -inf for keys [from, c1) of every row
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    for (int s0 = from; s0 < c1; s0 += 16)
+                        if (s0 + col < c1)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_inff()), orsrc[g],
+                                                                  static_cast<int>(roff[i] + (s0 + col) * 4u), 0, 0);
+        };
+        if (c0 >= cvis) {                                    // uniform over the workgroup
+            if (write_future) store_inf(c0);
+            return;
+        }
+
+        // operands: head h of row r0[g] + col (zero for a missing row or a head
+        // past H); loads issued unconditionally from a valid row
+        v8i a[RG][16];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int arow = t_first + (nlive[g] > 0 ? r0[g] + min(col, nlive[g] - 1) : 0);
+#pragma unroll
+            for (int h = 0; h < 16; ++h)
+                a[g][h] = load_split32(static_cast<const uint8_t*>(x.iq) + (static_cast<size_t>(arow) * H + min(h, H - 1)) * 128, kg);
+        }
+        // weights of the block's rows, times their query scales
+        for (int e = tid; e < 16 * kQ16Q; e += kQ16W * 64) {
+            const int h = e / kQ16Q, q = e % kQ16Q;
+            const int lr = qb * kQ16Q + q;
+            const int row = t_first + min(lr, nrows - 1);
+            const float wv = x.iw[static_cast<size_t>(row) * H + min(h, H - 1)] * x.iq_scale[row];
+            w_s[e] = (lr < nrows && h < H) ? wv : 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int h = 0; h < 16; ++h)
+                if (!(col < nlive[g] && h < H)) a[g][h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+
+        // tile loads: PIECES 16-byte pieces per thread, clamped to the last key
+        v4i pre[PIECES];
+        float pre_s = 0.0f;
+        auto fetch = [&](int k0) {
+#pragma unroll
+            for (int p = 0; p < PIECES; ++p) {
+                const int e = tid + p * kQ16W * 64, kr = e >> 3, off = (e & 7) * 16;
+                pre[p] = *reinterpret_cast<const v4i*>(kb + static_cast<size_t>(min(k0 + kr, n_k - 1)) * 128 + off);
+            }
+            pre_s = ksb[min(k0 + (tid & 63), n_k - 1)];
+        };
+        auto stage = [&](int nb) {
+#pragma unroll
+            for (int p = 0; p < PIECES; ++p) {
+                const int e = tid + p * kQ16W * 64, kr = e >> 3, off = (e & 7) * 16;
+                *reinterpret_cast<v4i*>(k_s[nb] + kr * KSTR + off) = pre[p];
+            }
+            if (tid < 64) ks_s[nb][tid] = pre_s;
+        };
+
+        // scores of the previous tile, stored while the next is scored (16 per
+        // group and lane, issued after the next tile's loads)
+        float held[RG][16];
+        uint32_t hbase = kNoStore;                           // (k0 + col) * 4 of the held tile
+        uint32_t hmask[RG];                                  // bit 4u + i: store held[g][4u + i]
+        bool hall = false;                                   // uniform: store every held value
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            hmask[g] = 0u;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) held[g][j] = 0.0f;
+        }
+        auto flush = [&]() {
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                if (hall) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[g][4 * u + i]), orsrc[g],
+                                                                  static_cast<int>(roff[i] + hbase + 64u * u), 0, 0);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t off = (hmask[g] >> (4 * u + i) & 1u) ? roff[i] + hbase + 64u * u : kNoStore;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[g][4 * u + i]), orsrc[g],
+                                                                  static_cast<int>(off), 0, 0);
+                        }
+                }
+            }
+        };
+
+        fetch(c0);
+        stage(0);
+        __builtin_amdgcn_s_waitcnt(0);                       // prologue loads (operands, weights) landed
+        __syncthreads();
+        int cur = 0;
+        for (int k0 = c0; k0 < cvis; k0 += 64) {
+            fetch(min(k0 + 64, cvis - 1));                   // in flight while this tile is scored
+            flush();
+            if (k0 <= wmax) {                                // uniform: some row of the wave sees the tile
+                v8i bk[4];
+                float sk[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    bk[u] = load_split32(k_s[cur] + (16 * u + col) * KSTR, kg);
+                    sk[u] = ks_s[cur][16 * u + col];
+                }
+                float acc[RG][16];
+#pragma unroll
+                for (int g = 0; g < RG; ++g)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+                // product j = (4h + u) * RG + g.  Software pipeline: product j + 1
+                // is issued before the ReLU-weight fold of product j, so the
+                // matrix core works through one product while the vector ALU
+                // folds the one before; head h + 1's weights are read while head
+                // h is folded.  One scheduling region per product.
+                constexpr int NP = 64 * RG;
+                const float* wrow = &w_s[16 * wave * RG + 4 * kg];
+                v4f wv[RG], wn[RG];
+#pragma unroll
+                for (int g = 0; g < RG; ++g) wn[g] = wv[g] = *reinterpret_cast<const v4f*>(wrow + 16 * g);
+                v4f dcur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0][0], bk[0], zero4, 0, 0, 0, 127, 0, 127);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 1; j <= NP; ++j) {
+                    v4f dnext = zero4;
+                    if (j < NP) {
+                        const int g = j % RG, u = (j / RG) & 3, h = j / (4 * RG);
+                        dnext = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[g][h], bk[u], zero4, 0, 0, 0,
+                                                                                 127, 0, 127);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                    const int jp = j - 1;
+                    const int gp = jp % RG, up = (jp / RG) & 3, hp = jp / (4 * RG);
+                    if (jp % (4 * RG) == 0 && hp + 1 < 16) {      // the next head's weights
+#pragma unroll
+                        for (int g = 0; g < RG; ++g)
+                            wn[g] = *reinterpret_cast<const v4f*>(wrow + (hp + 1) * kQ16Q + 16 * g);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[gp][4 * up + i] = fmaf(wv[gp][i], relu(dcur[i]), acc[gp][4 * up + i]);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (jp % (4 * RG) == 4 * RG - 1) {
+#pragma unroll
+                        for (int g = 0; g < RG; ++g) wv[g] = wn[g];
+                    }
+                    dcur = dnext;
+                }
+                const bool fast = k0 + 63 < c1 && k0 + 63 <= wmin;   // uniform: every key of every row
+                hbase = static_cast<uint32_t>(k0 + col) * 4u;
+                hall = fast;
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    if (fast) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) held[g][4 * u + i] = acc[g][4 * u + i] * sk[u];
+                    } else {
+                        hmask[g] = 0u;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int sidx = k0 + 16 * u + col;
+                                const bool vis = sidx <= pos[g][i];
+                                held[g][4 * u + i] = vis ? acc[g][4 * u + i] * sk[u] : -__builtin_inff();
+                                hmask[g] |= (sidx < c1 && (vis || write_future)) ? 1u << (4 * u + i) : 0u;
+                            }
+                    }
+                }
+            } else {                                         // no row of the wave sees the tile
+                hbase = static_cast<uint32_t>(k0 + col) * 4u;
+                hall = false;
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    hmask[g] = 0u;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            held[g][4 * u + i] = -__builtin_inff();
+                            hmask[g] |= (write_future && k0 + 16 * u + col < c1) ? 1u << (4 * u + i) : 0u;
+                        }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            stage(cur ^ 1);
+            __syncthreads();
+            cur ^= 1;
+        }
+        flush();
+        if (write_future) store_inf(cvis);                   // keys of this segment no query of the block sees
+    };
+
+    TiledWork w;
+    if (!tiled_work_start<kQ16Q>(lane, nrows, base, n_k, all_keys, piece, total, w)) return;
+    if (w.piece > 0) {
+        run_segment(w.qb, 64 * w.t0, min(64 * min(w.t0 + w.piece, w.tj), n_k));
+        return;
+    }
+    run_segment(w.qb, 64 * w.t0, min(64 * (w.t0 + w.ta), n_k));
+    if (w.tb > 0) {
+        __syncthreads();                                      // the second segment restages both LDS buffers
+        run_segment(w.qb + 1, 0, min(64 * w.tb, n_k));
     }
 }
 
@@ -583,20 +893,24 @@ bool index_tiled_path(const IndexArgs& a) {
     return (a.dtype == E4M3 || a.dtype == BF16) && a.H <= 16 && a.n_q >= 16;
 }
 
-template <int DT>
-static hipError_t launch_index_tiled_dt(const IndexArgs& a, bool write_future, hipStream_t st) {
-    constexpr int kTW = TiledShape<DT>::TW, kTQ = TiledShape<DT>::QPW * kTW;
+// Launch of a tiled prefill kernel (query blocks of kTQ rows, `threads` per
+// workgroup) over the rows of `a`; `fn` is k_index_tiled<DT> or
+// k_index_fp8_q16, which take the same arguments.
+typedef void (*TiledKernel)(IndexArgs, int, int, int, long long, int);
+
+static hipError_t launch_tiled(TiledKernel fn, int kTQ, int threads, int& per_cu_cache, const IndexArgs& a,
+                               bool write_future, hipStream_t st) {
     // workgroups the chip holds at once
-    static const int per_cu = [] {
+    if (per_cu_cache == 0) {
         int nb = 0;
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_index_tiled<DT>, kTW * 64, 0) == hipSuccess && nb > 0
-            ? nb : 1;
-    }();
+        per_cu_cache = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), threads,
+                                                                    0) == hipSuccess && nb > 0 ? nb : 1;
+    }
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const long long slots = static_cast<long long>(per_cu) * (cus > 0 ? cus : 1);
+    const long long slots = static_cast<long long>(per_cu_cache) * (cus > 0 ? cus : 1);
     // one launch per sequence the rows touch, so a query block never spans two
     int r = a.row0;
     const int r_end = a.row0 + a.rows;
@@ -627,7 +941,7 @@ static hipError_t launch_index_tiled_dt(const IndexArgs& a, bool write_future, h
                 wgs = 0;
                 for (int j = 0; j < nqb; ++j) wgs += (tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys) + piece - 1) / piece;
             }
-            hipLaunchKernelGGL(k_index_tiled<DT>, dim3(static_cast<unsigned>(wgs)), dim3(kTW * 64), 0, st, a, r, n,
+            hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(wgs)), dim3(threads), 0, st, a, r, n,
                                static_cast<int>(piece), total, write_future ? 1 : 0);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
@@ -640,9 +954,19 @@ static hipError_t launch_index_tiled_dt(const IndexArgs& a, bool write_future, h
     return hipSuccess;
 }
 
+#ifndef DSA_TILED_FP8_Q16
+#define DSA_TILED_FP8_Q16 1
+#endif
 hipError_t launch_index_tiled(const IndexArgs& a, bool write_future, hipStream_t st) {
-    return a.dtype == E4M3 ? launch_index_tiled_dt<E4M3>(a, write_future, st)
-                           : launch_index_tiled_dt<BF16>(a, write_future, st);
+    static int occ_q16 = 0, occ_f8 = 0, occ_bf = 0;
+    if (a.dtype == E4M3) {
+        if (DSA_TILED_FP8_Q16)
+            return launch_tiled(k_index_fp8_q16, kQ16Q, kQ16W * 64, occ_q16, a, write_future, st);
+        constexpr int tw = TiledShape<E4M3>::TW;
+        return launch_tiled(k_index_tiled<E4M3>, TiledShape<E4M3>::QPW * tw, tw * 64, occ_f8, a, write_future, st);
+    }
+    constexpr int tw = TiledShape<BF16>::TW;
+    return launch_tiled(k_index_tiled<BF16>, TiledShape<BF16>::QPW * tw, tw * 64, occ_bf, a, write_future, st);
 }
 
 // ---------------------------------------------------------------------------

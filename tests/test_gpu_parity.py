@@ -174,6 +174,9 @@ EDGE_CASES = {
                                d_qk=128, d_v=128, attn_dtype="bf16"),
     "fp8_odd_heads": dict(B=3, n_q=4, n_k=5000, idx_heads=5, idx_dtype="e4m3", top_k=300, q_heads=24,
                           kv_heads=3, d_qk=128, d_v=128, attn_dtype="bf16"),
+    # FP8 prefill rows with fewer than 16 indexer heads (the tiled kernel pads them with zeros)
+    "fp8_tiled_odd_heads": dict(n_q=150, n_k=3000, idx_heads=5, idx_dtype="e4m3", top_k=300, q_heads=8,
+                                kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16"),
     "fp8_gqa_decode_ragged": dict(B=5, n_q=1, n_k=12345, idx_heads=16, idx_dtype="e4m3", top_k=2048,
                                   q_heads=32, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16"),
     "latent_small": dict(B=2, n_q=1, n_k=4000, idx_heads=16, idx_dtype="e4m3", top_k=512, q_heads=20,
@@ -230,7 +233,8 @@ def test_edge_case(name):
     run_case(inp, list(range(fields.get("B", 1))), list(range(n_q)), fused=fused)
 
 
-@pytest.mark.parametrize("n_q,n_k,idt", [(3001, 3001, "e4m3"), (301, 9001, "e4m3"), (2003, 6003, "bf16")])
+@pytest.mark.parametrize("n_q,n_k,idt", [(3001, 3001, "e4m3"), (301, 9001, "e4m3"), (2003, 6003, "bf16"),
+                                         (700, 5000, "e4m3")])
 def test_tiled_indexer_work_splits(n_q, n_k, idt):
     """The tiled indexer's split of (query block, key tile) pairs over workgroups:
     a prefill from scratch (the first query blocks see one key tile, so the
@@ -241,7 +245,7 @@ def test_tiled_indexer_work_splits(n_q, n_k, idt):
     sp = custom_spec(name=f"splits_{n_q}_{n_k}_{idt}", n_q=n_q, n_k=n_k, idx_heads=16, idx_dtype=idt, top_k=256,
                      q_heads=8, kv_heads=2, d_qk=128, d_v=128, attn_dtype="bf16")
     inp = make_inputs(sp, device=DEV, seed=31)
-    tq = 32 if idt == "e4m3" else 8
+    tq = 128 if idt == "e4m3" else 8                 # rows per query block of the FP8 / bf16 kernels
     nqb = (n_q + tq - 1) // tq
     edges = [r for blk in (1, 2, nqb // 2, nqb - 1) for r in (blk * tq - 1, blk * tq) if 0 <= r < n_q]
     rows = sorted(set([0, 1, n_q - 1] + edges + list(_sample_rows(n_q, 12, 7))))
