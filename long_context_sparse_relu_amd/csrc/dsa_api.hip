@@ -333,7 +333,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
         dsa::TopkArgs ta = topk_args(p, r0, nr, scores, picks, base + L.topk_off);
         // (the indexer's histogram counts the real scores; a backbone ranks its
         // forced keys as -inf, so the top-k builds its own)
-        if (dsa::index_fills_hist(ia) && !dsa::topk_rows_fit_lds(ta) && !has_backbone(p)) {
+        if (dsa::index_fills_hist(ia) && dsa::topk_uses_hist(ta) && !has_backbone(p)) {
             // the indexer builds the first-digit histogram as it writes the scores
             ia.hist = ta.hist;
             ta.hist_ready = true;

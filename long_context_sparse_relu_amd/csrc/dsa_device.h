@@ -59,6 +59,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// (order key << 32 | ~position): larger means higher score, then lower position.
+__device__ __forceinline__ uint64_t composite64(uint32_t key, int s) {
+    return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(s));
+}
+
 // Word 3 of a raw buffer resource (32-bit data format).  With stride 0 an
 // access whose per-lane offset (plus the instruction's immediate offset) is at
 // or past num_records bytes is out of range: a store there is dropped and a

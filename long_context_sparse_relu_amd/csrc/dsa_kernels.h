@@ -66,10 +66,10 @@ size_t topk_workspace_bytes(int rows, int n_k);
 int topk_cand_cap(int n_k);
 void topk_carve(void* ws, int rows, int n_k, TopkArgs& a);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-// True when every row of the launch is short enough (32K visible keys) to be
-// selected by one workgroup from LDS; launch_topk then neither reads nor
-// clears the histograms.
-bool topk_rows_fit_lds(const TopkArgs& a);
+// True when launch_topk selects through the digit-0 histograms (rows too long
+// for the LDS select, too few for the sampled candidate lists); otherwise it
+// neither reads nor clears them.
+bool topk_uses_hist(const TopkArgs& a);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 // idx[r][j] = j for j <= pos(row0 + r), else -1 (pos from n_k - n_q + t): the
 // top-k result of a row that keeps every visible key.

@@ -76,9 +76,4 @@ __device__ __forceinline__ float fp8_score4(const Fp8Query& q, const v8i* bv, fl
     return reduce_scatter4(p[0], p[1], p[2], p[3]) * (q.sq * sk);
 }
 
-// (order key << 32 | ~position): larger means higher score, then lower position.
-__device__ __forceinline__ uint64_t composite64(uint32_t key, int s) {
-    return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(s));
-}
-
 }  // namespace dsa

@@ -529,6 +529,191 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Rows of scores in memory much longer than k (prefill rows past a few
+// thousand keys; dsa_topk over many such rows).  One workgroup per row:
+//   sample  kRcSample order keys of the row -- runs of 16 consecutive keys
+//           spread evenly over it, so every load is one 64-byte piece -- and a
+//           lower bound k_low of their r-th largest, r ~ 1.5 k * samples /
+//           visible keys + 24, about the (1.5 k + 24 * visible / samples)-th
+//           largest key of the row;
+//   collect one pass over the row keeps the keys at or above k_low as
+//           (order key << 32 | ~position) in an LDS list (wave ballots, one
+//           LDS atomic per wave and load);
+//   select  the exact k largest of the list, radix-selected on the keys
+//           relative to k_low (ties to the lower position), written in
+//           ascending order through an LDS bitmap of the row.
+// A list with at least k entries holds the k largest keys whatever the
+// sample was (any key left out is below k_low, and k listed keys are not).
+// A row whose list came out shorter than k, or overflowed, is selected again
+// from its scores in memory (radix passes over the whole row), so the result
+// never depends on the sample.
+// ---------------------------------------------------------------------------
+constexpr int kRcThreads = 512;
+constexpr int kRcSample = 4096;
+
+__global__ __launch_bounds__(kRcThreads) void k_topk_row_cand(TopkArgs a, int cap) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint64_t* cl = reinterpret_cast<uint64_t*>(smem);              // [cap] candidates
+    uint32_t* skey = reinterpret_cast<uint32_t*>(smem);            // [kRcSample] samples, dead before collection
+    uint32_t* tail = reinterpret_cast<uint32_t*>(cl + cap);        // bitmap of the row, or the list of kept keys
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t wsum[kRcThreads / 64 + 2];
+    __shared__ uint32_t wmin[kRcThreads / 64], wmax[kRcThreads / 64];
+    __shared__ uint32_t n_c, n_list;
+    const int lrow = blockIdx.x, row = a.row0 + lrow;
+    const int vis = row_visible(a, row);
+    const int k = a.k;
+    const int lane = threadIdx.x & 63;
+    int32_t* out = a.idx + static_cast<size_t>(lrow) * k;
+    if (vis <= k) {                                                // every visible key is kept
+        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < vis ? j : -1;
+        return;
+    }
+    const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+
+    // the sample (all visible keys when there are at most kRcSample)
+    const int m = vis < kRcSample ? vis : kRcSample;
+    const int gap = vis / ((m + 15) / 16);                         // >= 16 unless m == vis
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    {
+        constexpr int kPer = kRcSample / kRcThreads;
+        float v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {                           // loads first (past m: sample m - 1, unused)
+            const int j = min(static_cast<int>(threadIdx.x) + u * kRcThreads, m - 1);
+            v[u] = ranked(a, sc, m == vis ? j : (j >> 4) * gap + (j & 15), vis);
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int j = threadIdx.x + u * kRcThreads;
+            if (j < m) {
+                const uint32_t kk = order_key(v[u]);
+                skey[j] = kk;
+                kmin = min(kmin, kk);
+                kmax = max(kmax, kk);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    }
+    if (lane == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
+    __syncthreads();
+    for (int w = 0; w < kRcThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
+    const int64_t want = (3 * static_cast<int64_t>(m) * k + 2 * static_cast<int64_t>(vis) - 1) /
+                         (2 * static_cast<int64_t>(vis)) + 24;
+    const uint32_t k_low = want < m ? lower_bound_rth(skey, m, static_cast<uint32_t>(want), kmin, kmax, lh, wsum)
+                                    : 0u;
+    __syncthreads();                                               // the samples are dead from here
+
+    // collect the keys at or above k_low
+    const bool use_bitmap = a.n_k <= kBitmapMaxKeys;
+    const int nwords = (vis + 31) >> 5;
+    int kpad = 1;
+    while (kpad < k) kpad <<= 1;
+    if (use_bitmap) {
+        for (int i = threadIdx.x; i < nwords; i += blockDim.x) tail[i] = 0u;
+    } else {
+        for (int i = threadIdx.x; i < kpad; i += blockDim.x) tail[i] = 0x7FFFFFFFu;
+    }
+    if (threadIdx.x == 0) { n_c = 0u; n_list = 0u; }
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    // one wave-wide append of this lane's key s if it takes it
+    auto append = [&](int s, float x) {
+        const float r = (s < a.sinks || s >= vis - a.window) ? -__builtin_inff() : x;
+        const uint32_t key = order_key(r);
+        const bool take = s < vis && key >= k_low;
+        const uint64_t msk = __ballot(take);
+        if (msk) {
+            uint32_t base_slot = 0;
+            if (lane == 0) base_slot = atomicAdd(&n_c, static_cast<uint32_t>(__popcll(msk)));
+            base_slot = __shfl(base_slot, 0);
+            const uint32_t slot = base_slot + static_cast<uint32_t>(__popcll(msk & below));
+            if (take && slot < static_cast<uint32_t>(cap)) cl[slot] = composite64(key, s);
+        }
+    };
+    // (lane 0 of a wave has the wave's lowest index, so it is active whenever
+    // any lane of the wave is; every load is issued before any key is used)
+    if ((a.n_k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0) {
+        // rows start 16-byte aligned: 16-byte loads of four keys; groups past
+        // vis re-read the last group (inside the row: 4 * ceil(vis / 4) <= n_k)
+        const int nv4 = (vis + 3) >> 2;
+        for (int g0 = threadIdx.x; g0 < nv4; g0 += 8 * kRcThreads) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = *reinterpret_cast<const float4*>(sc + 4 * min(g0 + u * kRcThreads, nv4 - 1));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = 4 * (g0 + u * kRcThreads);
+                append(s, v[u].x);
+                append(s + 1, v[u].y);
+                append(s + 2, v[u].z);
+                append(s + 3, v[u].w);
+            }
+        }
+    } else {
+        for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * kRcThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = sc[min(i0 + u * kRcThreads, vis - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) append(i0 + u * kRcThreads, v[u]);
+        }
+    }
+    __syncthreads();
+    const uint32_t n = n_c;
+    Sink sink{use_bitmap ? tail : nullptr, reinterpret_cast<int32_t*>(tail), &n_list, static_cast<uint32_t>(k)};
+    if (n >= static_cast<uint32_t>(k) && n <= static_cast<uint32_t>(cap)) {
+        uint32_t cmax = 0u;
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) cmax = max(cmax, static_cast<uint32_t>(cl[i] >> 32));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(cmax), o)));
+        if (lane == 0) wmax[threadIdx.x >> 6] = cmax;
+        __syncthreads();
+        for (int w = 0; w < kRcThreads / 64; ++w) cmax = max(cmax, wmax[w]);
+        // digits of ((key - k_low) << 32 | ~position): the first over the top
+        // 11 bits of the candidates' key range, then 11 bits at a time
+        const uint32_t range = cmax - k_low;
+        const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
+        const int sh = bits > 11 ? bits - 11 : 0;
+        int shifts[6], widths[6], np = 1;
+        shifts[0] = 32 + sh;
+        widths[0] = 11;
+        for (int rest = 32 + sh; rest > 0 && np < 6; ++np) {
+            const int w = rest < 11 ? rest : 11;
+            rest -= w;
+            shifts[np] = rest;
+            widths[np] = w;
+        }
+        Cand64Rel src{cl, static_cast<int>(n), static_cast<uint64_t>(k_low) << 32};
+        radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
+    } else {
+        // digits of the full 64-bit composite
+        const int shifts64[6] = {53, 42, 32, 21, 10, 0};
+        const int widths64[6] = {11, 11, 10, 11, 11, 10};
+        ScoreRow64 src{sc, vis, a.sinks, vis - a.window};
+        radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
+    }
+    __syncthreads();
+    write_ordered(sink, nwords, kpad, k, out, wsum);
+}
+
+// Candidate list capacity for a launch whose rows have at most vis_max keys:
+// about 1.6 x the expected list length, at least the sample's size.
+static int row_cand_cap(int k, int vis_max) {
+    const int64_t expect = (3 * static_cast<int64_t>(k)) / 2 + 24 * ((vis_max + kRcSample - 1) / kRcSample);
+    int64_t cap = (expect * 8) / 5 + 512;
+    cap = (cap + 255) & ~static_cast<int64_t>(255);
+    if (cap < kRcSample / 2) cap = kRcSample / 2;                 // the samples alias the list
+    if (cap > kTopkCandCapMax) cap = kTopkCandCapMax;
+    return static_cast<int>(cap);
+}
+
 size_t topk_workspace_bytes(int rows, int n_k) {
     size_t r = static_cast<size_t>(rows);
     size_t zeroed = align256(r * (2 * kTopkBins + kTopkMeta) * sizeof(uint32_t));
@@ -564,13 +749,42 @@ static int launch_vis_max(const TopkArgs& a) {
     return vis_max;
 }
 
-bool topk_rows_fit_lds(const TopkArgs& a) { return launch_vis_max(a) <= kRowLdsMax; }
+
+// Launches of many rows, some much longer than k, select through sampled
+// candidate lists (k_topk_row_cand) when some row exceeds kRowLdsMax keys
+// (measured: rows of up to 32K keys select faster whole in LDS, 1.92 against
+// 2.21 ms on the 32K prefill; DSA_TOPK_ROWCAND_LDS = 1 sends them here too).
+#ifndef DSA_TOPK_ROWCAND_LDS
+#define DSA_TOPK_ROWCAND_LDS 0
+#endif
+constexpr int kRowCandMinRows = 128;
+static bool use_row_cand(const TopkArgs& a, int vis_max) {
+    if (a.rows < kRowCandMinRows || a.k > 4096) return false;
+    if (static_cast<int64_t>(vis_max) < 4 * static_cast<int64_t>(a.k) || vis_max < 2 * kRcSample) return false;
+    return DSA_TOPK_ROWCAND_LDS || vis_max > kRowLdsMax;
+}
+
+bool topk_uses_hist(const TopkArgs& a) {
+    const int vis_max = launch_vis_max(a);
+    return !use_row_cand(a, vis_max) && vis_max > kRowLdsMax;
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipError_t e;
+    const int vis_max = launch_vis_max(a);
+    if (use_row_cand(a, vis_max)) {
+        const int cap = row_cand_cap(a.k, vis_max);
+        int kpad = 1;
+        while (kpad < a.k) kpad <<= 1;
+        const size_t tail = a.n_k <= kBitmapMaxKeys ? static_cast<size_t>((a.n_k + 31) >> 5) * 4
+                                                    : static_cast<size_t>(kpad) * 4;
+        const size_t smem = static_cast<size_t>(cap) * sizeof(uint64_t) + tail;
+        if ((e = allow_dyn_lds(reinterpret_cast<const void*>(k_topk_row_cand), smem)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_topk_row_cand, dim3(a.rows), dim3(kRcThreads), smem, st, a, cap);
+        return hipGetLastError();
+    }
     // rows of at most kRowLdsMax visible keys (all rows of a short prefill,
     // the early row blocks of a long one) are selected from LDS
-    const int vis_max = launch_vis_max(a);
     if (vis_max <= kRowLdsMax) {
         if (vis_max > kRowLdsMax / 2) {
             const void* fn = reinterpret_cast<const void*>(k_topk_row_lds_next);

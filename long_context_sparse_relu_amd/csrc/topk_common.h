@@ -110,6 +110,26 @@ __device__ __forceinline__ void for_each_candidate(const Src& src, F&& f) {
     }
 }
 
+// Candidates relative to the row's bound: every candidate has key >= k_low,
+// so subtracting (k_low << 32) keeps the order and leaves small keys whose
+// top digit spreads the candidates over the histogram instead of piling them
+// into the one or two bins just above the bound.
+struct Cand64Rel {
+    const uint64_t* c; int n; uint64_t base;
+    __device__ int size() const { return n; }
+    __device__ bool get(int i, uint64_t* out) const { *out = c[i] - base; return true; }
+};
+// A score row in memory as 64-bit composites (order key << 32 | ~position).
+struct ScoreRow64 {
+    const float* sc; int n;
+    int lo, hi;                 // keys outside [lo, hi) rank as -inf (a backbone's forced keys)
+    __device__ int size() const { return n; }
+    __device__ bool get(int i, uint64_t* out) const {
+        const float x = sc[i];
+        *out = composite64(order_key(i < lo || i >= hi ? -__builtin_inff() : x), i);
+        return true;
+    }
+};
 // Where the finish puts kept positions: bits of an LDS bitmap over the row
 // (rows up to kBitmapMaxKeys keys; read back in position order), or an LDS
 // list sorted afterwards.
@@ -166,6 +186,41 @@ __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, 
         if ((c >> done_shift) >= prefix) sink.put_c(c);
     });
     __syncthreads();
+}
+
+// A lower bound on the r-th largest of the m order keys skey[0..m) (LDS),
+// at two 11-bit digits of resolution: digit 0 spans the top 11 bits of the
+// keys' range [kmin, kmax], digit 1 the next 11 below it; the result is kmin
+// plus the r-th largest key's two digits (lower bits cleared), so at least r
+// keys are >= it.  Whole block; requires 1 <= r <= m; `lh` has kTopkBins
+// entries, `wsum` one slot per wave plus two.
+__device__ inline uint32_t lower_bound_rth(const uint32_t* skey, int m, uint32_t r, uint32_t kmin, uint32_t kmax,
+                                           uint32_t* lh, uint32_t* wsum) {
+    const uint32_t range = kmax - kmin;
+    const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
+    const int sh1 = bits > 11 ? bits - 11 : 0;
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[(skey[j] - kmin) >> sh1], 1u);
+    __syncthreads();
+    int d0; uint32_t gt0;
+    find_threshold_bin(lh, kTopkBins, r, wsum, &d0, &gt0);
+    uint32_t k_low = kmin + (static_cast<uint32_t>(d0) << sh1);
+    if (sh1 > 0) {
+        const int sh2 = sh1 > 11 ? sh1 - 11 : 0;
+        const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+        __syncthreads();
+        for (int j = threadIdx.x; j < m; j += blockDim.x) {
+            const uint32_t rel = skey[j] - kmin;
+            if (static_cast<int>(rel >> sh1) == d0) atomicAdd(&lh[(rel >> sh2) & mask2], 1u);
+        }
+        __syncthreads();
+        int d1; uint32_t gt1;
+        find_threshold_bin(lh, kTopkBins, r - gt0, wsum, &d1, &gt1);
+        k_low += static_cast<uint32_t>(d1) << sh2;
+    }
+    return k_low;
 }
 
 // Write the k kept positions of a row in ascending order from the sink's

@@ -33,25 +33,6 @@ bool topk_sampled_eligible(int n_k, int k) {
 }
 
 
-// Candidates relative to the row's bound: every candidate has key >= k_low,
-// so subtracting (k_low << 32) keeps the order and leaves small keys whose
-// top digit spreads the candidates over the histogram instead of piling them
-// into the one or two bins just above the bound.
-struct Cand64Rel {
-    const uint64_t* c; int n; uint64_t base;
-    __device__ int size() const { return n; }
-    __device__ bool get(int i, uint64_t* out) const { *out = c[i] - base; return true; }
-};
-struct ScoreRow64 {
-    const float* sc; int n;
-    int lo, hi;                 // keys outside [lo, hi) rank as -inf (a backbone's forced keys)
-    __device__ int size() const { return n; }
-    __device__ bool get(int i, uint64_t* out) const {
-        const float x = sc[i];
-        *out = composite64(order_key(i < lo || i >= hi ? -__builtin_inff() : x), i);
-        return true;
-    }
-};
 
 // The ranked keys of a row: [lo, lo + cnt) = the visible keys outside a
 // backbone's forced first `sinks` and last `window` ones (all visible keys
@@ -137,7 +118,6 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
         const int j = threadIdx.x + u * kSampleThreads;
         if (j < m) { skey[j] = v[u]; kmin = min(kmin, v[u]); kmax = max(kmax, v[u]); }
     }
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
@@ -149,35 +129,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
     for (int w = 0; w < kSampleThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
     const int64_t want = (3 * static_cast<int64_t>(m) * x.k + 2 * static_cast<int64_t>(vis) - 1) /
                          (2 * static_cast<int64_t>(vis)) + 24;
-    uint32_t k_low = 0u;                   // every visible key a candidate
-    if (want < m) {
-        // two 11-bit digits of (key - kmin), the first over the top of the
-        // samples' range: the bound is the floor of the r-th largest sample
-        // at that resolution
-        const uint32_t r = static_cast<uint32_t>(want);
-        const uint32_t range = kmax - kmin;
-        const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
-        const int sh1 = bits > 11 ? bits - 11 : 0;
-        for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[(skey[j] - kmin) >> sh1], 1u);
-        __syncthreads();
-        int d0; uint32_t gt0;
-        find_threshold_bin(lh, kTopkBins, r, wsum, &d0, &gt0);
-        k_low = kmin + (static_cast<uint32_t>(d0) << sh1);
-        if (sh1 > 0) {
-            const int sh2 = sh1 > 11 ? sh1 - 11 : 0;
-            const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
-            for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-            __syncthreads();
-            for (int j = threadIdx.x; j < m; j += blockDim.x) {
-                const uint32_t rel = skey[j] - kmin;
-                if (static_cast<int>(rel >> sh1) == d0) atomicAdd(&lh[(rel >> sh2) & mask2], 1u);
-            }
-            __syncthreads();
-            int d1; uint32_t gt1;
-            find_threshold_bin(lh, kTopkBins, r - gt0, wsum, &d1, &gt1);
-            k_low += static_cast<uint32_t>(d1) << sh2;
-        }
-    }
+    // the floor of the r-th largest sample at two 11-bit digits of resolution
+    // (every visible key a candidate when r reaches the sample size)
+    const uint32_t k_low = want < m ? lower_bound_rth(skey, m, static_cast<uint32_t>(want), kmin, kmax, lh, wsum)
+                                    : 0u;
     if (threadIdx.x == 0) meta[S_KLOW] = k_low;
 }
 

@@ -411,6 +411,36 @@ def test_topk_long_rows_many_per_workgroup(sinks, window, n_k):
     assert not bad, f"rows {bad[:5]} differ (of {len(bad)})"
 
 
+@pytest.mark.parametrize("case", ["all_tied", "sample_overstates"])
+def test_topk_candidate_lists_fall_back_to_the_whole_row(case):
+    """dsa_topk over 300 rows of 20000 keys selects through sampled candidate
+    lists.  Two rows patterns defeat the sample, and the row must then be
+    selected again from its scores: every score equal (every key is a
+    candidate, far more than the list holds; the lowest positions win), and
+    a row whose sampled runs of 16 keys score 1.0 where only 400 keys do (the
+    list ends shorter than k).  The kept sets must equal the oracle's exactly."""
+    n_q, n_k, k = 300, 20000, 1000
+    sp = custom_spec(name="cand_fallback", n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=k,
+                     q_heads=2, kv_heads=1, d_qk=64, d_v=64, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=43)
+    pos = torch.full((1, n_q), n_k - 1, dtype=torch.int32)
+    if case == "all_tied":
+        scores = torch.full((1, n_q, n_k), 0.25)
+    else:
+        # the sampled keys: runs of 16 from multiples of n_k // 256; 25 runs score 1.0
+        scores = torch.full((1, n_q, n_k), 0.5)
+        gap = n_k // 256
+        for j in range(25):
+            scores[0, :, 3 * j * gap:3 * j * gap + 16] = 1.0
+    prob = dsa.make_problem(**_problem_kwargs(inp), q_pos=pos.to(DEV))
+    idx = dsa.topk(prob, scores.to(DEV))
+    torch.cuda.synchronize()
+    o_idx, _ = oracle.topk(scores[0].double().numpy(), k, pos[0].numpy().astype(np.int64))
+    g_idx = idx[0].cpu().numpy()
+    bad = [r for r in range(n_q) if not np.array_equal(g_idx[r], o_idx[r])]
+    assert not bad, f"rows {bad[:5]} differ (of {len(bad)})"
+
+
 def test_workspace_too_small_is_rejected():
     sp = custom_spec(name="ws", B=1, n_q=1, n_k=5000, idx_heads=16, idx_dtype="e4m3", top_k=64,
                      q_heads=4, kv_heads=4, d_qk=128, d_v=128, attn_dtype="bf16")
