@@ -25,6 +25,42 @@ __device__ __forceinline__ v8i load_split32(const uint8_t* row, int g) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Whole-line loads of 64 key rows (8 KiB) in the order the memory system
+// streams best: instruction j brings keys base + 8j .. base + 8j + 7 whole,
+// lane l holding bytes [16(l%8), +16) of key base + 8j + l/8, marked
+// non-temporal (the keys are read once).  Key indices are clamped to lim.
+// (Loads that cover only half of each 128-byte line, as load_split32's do,
+// stream slower and lose more from the non-temporal hint.)
+__device__ __forceinline__ void load_keys64_lines(const uint8_t* kb, int base, int lim, int lane, v4i* r) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int key = min(base + 8 * j + (lane >> 3), lim);
+        r[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(kb + static_cast<size_t>(key) * 128) + (lane & 7));
+    }
+}
+
+// The MFMA operand of keys base + 16u .. base + 16u + 15 out of those lines,
+// exactly as load_split32 lays it out (lane (c, g) = (l%16, l/16) holds bytes
+// [16g, +16) and [64 + 16g, +16) of key c): each dword is fetched from the
+// lane that loaded it with ds_bpermute, from the line of keys 0-7 or 8-15 of
+// the block.
+__device__ __forceinline__ v8i keys_block_operand(const v4i* r, int u, int lane) {
+    const int c = lane & 15, g = lane >> 4;
+    const int a0 = (8 * (c & 7) + g) * 4, a1 = a0 + 16;     // byte addresses of the source lanes
+    const bool upper = c >= 8;
+    v8i out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int x0 = __builtin_amdgcn_ds_bpermute(a0, r[2 * u][d]);
+        const int y0 = __builtin_amdgcn_ds_bpermute(a0, r[2 * u + 1][d]);
+        const int x1 = __builtin_amdgcn_ds_bpermute(a1, r[2 * u][d]);
+        const int y1 = __builtin_amdgcn_ds_bpermute(a1, r[2 * u + 1][d]);
+        out[d] = upper ? y0 : x0;
+        out[4 + d] = upper ? y1 : x1;
+    }
+    return out;
+}
+
 // A query row's operands as one lane holds them.
 struct Fp8Query {
     v8i a;        // head (lane % 16) code bytes, zero for heads >= H

@@ -147,17 +147,20 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
     // reads the chunk's last visible key (key 0 when it has none) and its
     // score is discarded, so no branch separates a load from its use.
     const int lim = max(0, min(s_end, pos + 1) - 1);
-    auto load_batch = [&](int base, v8i* bv, float* sk) {
+    // whole-line loads of the batch's 64 U/4 keys and their scales
+    auto load_batch = [&](int base, v4i* lines, float* sk) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            bv[u] = load_split32(kb + static_cast<size_t>(min(base + u * 16 + col, lim)) * 128, kg);
+        for (int g = 0; g < U / 4; ++g) load_keys64_lines(kb, base + 64 * g, lim, lane, lines + 8 * g);
 #pragma unroll
-        for (int g = 0; g < U / 4; ++g) sk[g] = ksb[min(base + g * 64 + lane, lim)];
+        for (int g = 0; g < U / 4; ++g) sk[g] = __builtin_nontemporal_load(ksb + min(base + g * 64 + lane, lim));
     };
-    auto score_batch = [&](int base, const v8i* bv, const float* sk) {
+    auto score_batch = [&](int base, const v4i* lines, const float* sk) {
 #pragma unroll
         for (int g = 0; g < U / 4; ++g) {
-            const float part = fp8_score4(q, bv + 4 * g, sk[g]);
+            v8i bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bv[u] = keys_block_operand(lines + 8 * g, u, lane);
+            const float part = fp8_score4(q, bv, sk[g]);
             const int s = base + g * 64 + lane;
             const bool mine = s < s_end;
             if constexpr (CAND) {
@@ -180,10 +183,10 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
     };
 
     for (int base = s_begin + wave * 16 * U; base < s_end; base += step) {
-        v8i bv[U];
+        v4i lines[2 * U];
         float sk[U / 4];
-        load_batch(base, bv, sk);
-        score_batch(base, bv, sk);
+        load_batch(base, lines, sk);
+        score_batch(base, lines, sk);
     }
     if constexpr (CAND) {
         __syncthreads();
