@@ -40,7 +40,11 @@ struct IndexArgs {
 // hist, hist1 and count are contiguous (zero_words words) and must start at 0.
 constexpr int kTopkBins = 2048;
 constexpr int kTopkMeta = 4;
-constexpr int kIdxCandBuf = 1024;        // candidates one indexer workgroup can hold in LDS
+// Candidates one decode-indexer workgroup (8192 keys) holds in LDS: about
+// 2.5 times the most a workgroup expects when the row has 16 k keys (the
+// shortest row the sampled top-k takes); more overflow the row to its exact
+// recompute.
+constexpr int kIdxCandBuf = 2048;
 // Row metadata of the sampled top-k (TopkArgs::count / IndexArgs::meta).
 enum { S_NCAND = 0, S_KLOW = 1, S_OVF = 2, S_FALLBACK = 3 };
 constexpr int kTopkCandCapMax = 12288;   // candidates per row kept for the LDS select

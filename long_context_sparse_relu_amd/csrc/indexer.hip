@@ -87,20 +87,22 @@ __global__ __launch_bounds__(256) void k_index_generic(
 //               gathered per workgroup in LDS and appended to the row's
 //               candidate list as (key << 32 | ~position).
 // ---------------------------------------------------------------------------
-// Launch shape (measured on decode_128k: register prefetch of the next step,
-// other chunk sizes, wave counts and interleaved chunks were all slower or
-// equal).
+// Launch shape, measured on decode_128k and decode_1m with the whole-line
+// loads: 8192 keys per workgroup of 4 waves with a 128-register budget
+// (indexer 166 us) against 4096 keys at 64 registers (183 us); 16384 keys,
+// 8 waves per workgroup, other budgets and register prefetch of the next
+// batch were equal or slower.
 #ifndef DSA_IDX_U
 #define DSA_IDX_U 4          // blocks of 16 keys each wave loads per step
 #endif
 #ifndef DSA_IDX_KPB
-#define DSA_IDX_KPB 4096     // keys per workgroup
+#define DSA_IDX_KPB 8192     // keys per workgroup
 #endif
 #ifndef DSA_IDX_WAVES
 #define DSA_IDX_WAVES 4      // waves per workgroup
 #endif
 #ifndef DSA_IDX_OCC
-#define DSA_IDX_OCC 8        // waves per SIMD the register budget must allow
+#define DSA_IDX_OCC 4        // waves per SIMD the register budget must allow
 #endif
 
 template <int U, bool CAND>
@@ -182,11 +184,32 @@ void k_index_fp8_mfma(IndexArgs x, int keys_per_block) {
         }
     };
 
-    for (int base = s_begin + wave * 16 * U; base < s_end; base += step) {
+#ifndef DSA_IDX_PREFETCH
+#define DSA_IDX_PREFETCH 0
+#endif
+    if (DSA_IDX_PREFETCH) {
+        // the next batch's loads are in flight while this one is scored
         v4i lines[2 * U];
         float sk[U / 4];
+        int base = s_begin + wave * 16 * U;
         load_batch(base, lines, sk);
-        score_batch(base, lines, sk);
+        for (; base < s_end; base += step) {
+            v4i nlines[2 * U];
+            float nsk[U / 4];
+            load_batch(base + step, nlines, nsk);          // clamped to lim past the chunk
+            score_batch(base, lines, sk);
+#pragma unroll
+            for (int j = 0; j < 2 * U; ++j) lines[j] = nlines[j];
+#pragma unroll
+            for (int g = 0; g < U / 4; ++g) sk[g] = nsk[g];
+        }
+    } else {
+        for (int base = s_begin + wave * 16 * U; base < s_end; base += step) {
+            v4i lines[2 * U];
+            float sk[U / 4];
+            load_batch(base, lines, sk);
+            score_batch(base, lines, sk);
+        }
     }
     if constexpr (CAND) {
         __syncthreads();
