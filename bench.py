@@ -64,15 +64,22 @@ def _traffic(kernel_key):
     return int(rec["bytes_per_launch"])
 
 
-def _events_mean_us(fn, reps, stream):
+def _events_mean_us(fn, reps, stream, host=None):
+    """Mean GPU microseconds of fn (HIP events on `stream` around each call); with
+    a dict `host`, host['us'] gets the mean host time of enqueueing one call."""
     import torch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    h = 0.0
     for i in range(reps):
         starts[i].record(stream)
+        t = time.perf_counter()
         fn()
+        h += time.perf_counter() - t
         ends[i].record(stream)
     torch.cuda.synchronize()
+    if host is not None:
+        host["us"] = 1e6 * h / reps
     return 1000.0 * sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
 
 
@@ -314,6 +321,10 @@ def main(argv=None):
     ap.add_argument("--cpu-sample", type=int, default=64, help="sequences the oracle baseline runs (decode)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="query rows the oracle baseline runs (prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--zero-weight-rows", type=int, default=0,
+                    help="zero the indexer head weights of the first R query rows: every score of such a row ties "
+                         "at 0, so a decode row overflows its sampled candidate list and is recomputed in full "
+                         "(times that fallback; the workload is then not the benchmark's)")
     ap.add_argument("--phase-reps", type=int, default=10)
     ap.add_argument("--sweep", choices=["mask", "ladder"], default=None,
                     help="instead of the step benchmark: 'mask' = masked vs gather attention and DSA vs dense "
@@ -349,6 +360,8 @@ def main(argv=None):
     print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
     inp = make_inputs(s, device=dev, seed=args.seed)
     B, N, k, n_q = s["B"], s["n_k"], s["top_k"], s["n_q"]
+    if args.zero_weight_rows:
+        inp["iw"].view(B * n_q, -1)[:args.zero_weight_rows].zero_()
     prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
                             v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
                             softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
@@ -373,8 +386,10 @@ def main(argv=None):
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
+    th = time.perf_counter()
     for _ in range(args.steps):
         step()
+    host_step_us = 1e6 * (time.perf_counter() - th) / args.steps   # enqueue time, the GPU runs behind
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
@@ -400,9 +415,10 @@ def main(argv=None):
         scores = torch.empty((B, n_q, N), dtype=torch.float32, device=dev)
         tws = torch.empty(dsa.workspace_bytes(dsa.OP_TOPK, prob), dtype=torch.uint8, device=dev)
         aws = torch.empty(max(1, dsa.workspace_bytes(dsa.OP_SPARSE_ATTN, prob)), dtype=torch.uint8, device=dev)
-        idx_us = _events_mean_us(lambda: dsa.index_scores(prob, scores, stream), reps, stream)
-        topk_us = _events_mean_us(lambda: dsa.topk(prob, scores, idx, tws, stream), reps, stream)
-        attn_us = _events_mean_us(lambda: dsa.sparse_attn(prob, idx, out, lse, aws, stream), reps, stream)
+        hi, ht, ha = {}, {}, {}
+        idx_us = _events_mean_us(lambda: dsa.index_scores(prob, scores, stream), reps, stream, hi)
+        topk_us = _events_mean_us(lambda: dsa.topk(prob, scores, idx, tws, stream), reps, stream, ht)
+        attn_us = _events_mean_us(lambda: dsa.sparse_attn(prob, idx, out, lse, aws, stream), reps, stream, ha)
         del scores, tws, aws
 
     H, D = s["idx_heads"], s["idx_dim"]
@@ -464,7 +480,8 @@ def main(argv=None):
         "dtype": f"{s['idx_dtype']}-indexer/{s['attn_dtype']}-attn"
                  + (f"/{kvt}-kv" if kvt != s["attn_dtype"] else ""),
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "n_q": n_q, "context": N, "top_k": k,
+        "config": {"workload": args.workload + (f"+{args.zero_weight_rows}_zero_weight_rows"
+                                                 if args.zero_weight_rows else ""), "batch": B, "n_q": n_q, "context": N, "top_k": k,
                    "idx_heads": H, "idx_dim": D, "idx_dtype": s["idx_dtype"],
                    "q_heads": s["q_heads"], "kv_heads": s["kv_heads"], "d_qk": s["d_qk"],
                    "d_v": s["d_v"], "latent": s["latent"], "attn_dtype": s["attn_dtype"],
@@ -476,6 +493,11 @@ def main(argv=None):
         "phases_us": {"index_scores": idx_us, "topk": topk_us, "sparse_attn": attn_us,
                       "gather_GBs": gather_bytes / (attn_us * 1e-6) / 1e9,
                       "attn_TFLOPs": attn_flops / (attn_us * 1e-6) / 1e12} if unfused else None,
+        # host time of enqueueing one call (binding + C ABI + launches), against
+        # the GPU time above: the fused step is GPU-bound when it is smaller
+        "host_enqueue_us": {"fused_step": host_step_us,
+                            **({"index_scores": hi["us"], "topk": ht["us"], "sparse_attn": ha["us"]}
+                               if unfused else {})},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline", file=sys.stderr, flush=True)
