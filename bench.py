@@ -456,7 +456,8 @@ def main(argv=None):
         idx_flops = 2 * pairs * H * D
         peak = {"e4m3": 5000.0, "bf16": 2500.0, "f32": 157.3}[s["idx_dtype"]]
         achieved = idx_flops / (idx_us_fused * 1e-6) / 1e12
-        kern = "k_index_tiled" if (s["idx_dtype"] != "f32" and n_q >= 16 and H <= 16) else "k_index_generic"
+        kern = ("k_index_generic" if not (s["idx_dtype"] != "f32" and n_q >= 16 and H <= 16)
+                else "k_index_fp8_q16" if s["idx_dtype"] == "e4m3" else "k_index_tiled")
         roof = {"bound": "mfma" if s["idx_dtype"] != "f32" else "alu", "kernel": kern, "achieved": achieved,
                 "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                 "algorithmic_flops": idx_flops, "mean_us": idx_us_fused}
@@ -464,6 +465,9 @@ def main(argv=None):
                      attn_flops / (fused_us["attn"] * 1e-6) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
                      "algorithmic_flops": attn_flops, "mean_us": fused_us["attn"]}
         attn_roof["frac"] = attn_roof["achieved"] / 2500.0
+        # the masked walk computes whole causal tiles: its executed work is the dense causal product
+        attn_roof["dense_equivalent_flops"] = 2 * pairs * s["q_heads"] * (s["d_qk"] + s["d_v"])
+        attn_roof["dense_equivalent_frac"] = attn_roof["dense_equivalent_flops"] / (fused_us["attn"] * 1e6) / 2500.0
         step_roof = {"indexer_flops": idx_flops, "attention_flops": attn_flops,
                      "ideal_us_at_peaks": idx_flops / (peak * 1e6) + attn_flops / (2500.0 * 1e6)}
     res = {
