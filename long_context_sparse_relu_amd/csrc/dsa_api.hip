@@ -261,7 +261,7 @@ FusedLayout fused_layout(const dsa_problem_t* p, bool need_idx) {
     L.scores_off = 0;
     if (L.sampled) {
         L.topk_off = 0;
-        L.picks_off = align_up(dsa::topk_sampled_workspace_bytes(L.block_rows, p->n_k));
+        L.picks_off = align_up(dsa::topk_sampled_workspace_bytes(L.block_rows, p->n_k, p->top_k));
         L.idx_off = L.picks_off + (has_backbone(p) ? align_up(static_cast<size_t>(L.block_rows) * p->top_k *
                                                               sizeof(int32_t)) : 0);
     } else {
@@ -312,7 +312,7 @@ dsa_status_t run_fused(const dsa_problem_t* p, void* out, float* lse, int32_t* i
             int32_t* picks = has_backbone(p) ? reinterpret_cast<int32_t*>(base + L.picks_off)
                                              : idx + static_cast<size_t>(r0) * p->top_k;
             t.idx = picks;
-            dsa::topk_sampled_carve(base, nr, p->n_k, t);
+            dsa::topk_sampled_carve(base, nr, p->n_k, p->top_k, t);
             s = device_status(dsa::launch_topk_sample(t, st), "top-k sample launch");
             if (s != DSA_OK || (s = mark(DSA_PHASE_PREP)) != DSA_OK) return s;
             s = device_status(dsa::launch_index_candidates(t.ix, st), "indexer launch");

@@ -35,18 +35,20 @@ struct IndexArgs {
 // Top-k workspace (device), per row r:
 //   hist  [rows][2048] uint32  counts of digit 0 (key bits 31..21)
 //   hist1 [rows][2048] uint32  counts of digit 1 (key bits 20..10) in the threshold bin
-//   count [rows][4]    uint32  {kept above, candidates, digit-0 bin, count above it}
+//   count [rows][8]    uint32  {kept above, candidates, digit-0 bin, count above it, unused}
 //   cand  [rows][cap]  uint64  (low 21 key bits << 32 | ~position) candidates
 // hist, hist1 and count are contiguous (zero_words words) and must start at 0.
 constexpr int kTopkBins = 2048;
-constexpr int kTopkMeta = 4;
+constexpr int kTopkMeta = 8;
 // Candidates one decode-indexer workgroup (8192 keys) holds in LDS: about
 // 2.5 times the most a workgroup expects when the row has 16 k keys (the
 // shortest row the sampled top-k takes); more overflow the row to its exact
 // recompute.
 constexpr int kIdxCandBuf = 2048;
 // Row metadata of the sampled top-k (TopkArgs::count / IndexArgs::meta).
-enum { S_NCAND = 0, S_KLOW = 1, S_OVF = 2, S_FALLBACK = 3 };
+// A row that falls back: S_DONE counts the finish workgroups that have
+// finished their slice, S_NWIN the slice winners they appended.
+enum { S_NCAND = 0, S_KLOW = 1, S_OVF = 2, S_FALLBACK = 3, S_DONE = 4, S_NWIN = 5 };
 constexpr int kTopkCandCapMax = 12288;   // candidates per row kept for the LDS select
 constexpr int kTopkMaxK = 8192;
 
@@ -136,13 +138,15 @@ struct SampledTopk {
     int32_t* idx;          // [rows, k]
     uint32_t* samples;     // [rows, kSampleKeys] order keys of the sampled scores
     float* scratch;        // [rows, n_k] fp32, used only by a recomputed row
+    uint64_t* win;         // [rows, win_cap] the slice winners of a recomputed row
+    int win_cap;
 };
 constexpr int kSampleKeys = 4096;       // keys sampled per row
 constexpr int kSampleSplit = 16;        // workgroups scoring one row's sample
 constexpr int kSampledCandCap = 12288;  // candidates per row
 bool topk_sampled_eligible(int n_k, int k);
-size_t topk_sampled_workspace_bytes(int rows, int n_k);
-void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t);
+size_t topk_sampled_workspace_bytes(int rows, int n_k, int k);
+void topk_sampled_carve(void* ws, int rows, int n_k, int k, SampledTopk& t);
 hipError_t launch_topk_sample(const SampledTopk& t, hipStream_t st);
 hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st);
 // Attention over index sets; `ws` holds attn_workspace_bytes(a) bytes (the

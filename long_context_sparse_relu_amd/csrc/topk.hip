@@ -22,7 +22,9 @@
 //             in ascending order (through an LDS bitmap of the row, or a
 //             bitonic sort for rows too long for one).
 // The score row is read twice (hist, filter) or once when the indexer built
-// the histogram.
+// the histogram.  A row whose digit-0 bin overflows its candidate list (a
+// mass of equal scores) is selected again in the finish from its whole score
+// row.
 #include "topk_common.h"
 
 namespace dsa {
@@ -251,27 +253,12 @@ __global__ __launch_bounds__(kFThreads) void k_topk_filter(TopkArgs a) {
     }
 }
 
-// Candidate sources for the finishing select: a list (LDS or global), or,
-// when the digit-0 bin overflowed the list, the score row itself filtered to
-// that bin.
+// The finishing select's candidates: a list in LDS or global memory.
 struct CandList {
     const uint64_t* c; int n;
     __device__ int size() const { return n; }
     __device__ bool get(int i, uint64_t* out) const { *out = c[i]; return true; }
 };
-struct CandRow {
-    const float* sc; int n; int d0;
-    int lo, hi;                 // keys outside [lo, hi) rank as -inf (a backbone's forced keys)
-    __device__ int size() const { return n; }
-    __device__ bool get(int i, uint64_t* out) const {
-        const float x = sc[i];
-        uint32_t key = order_key(i < lo || i >= hi ? -__builtin_inff() : x);
-        if (static_cast<int>(key >> 21) != d0) return false;
-        *out = composite(key, i);
-        return true;
-    }
-};
-
 // Candidates whose top composite digit (key bits 20..10) is d1 share the
 // first 22 key bits; radix-select the k_rem largest of them on the remaining
 // digits and keep them.
@@ -314,7 +301,6 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
     }
     const uint32_t* meta = a.count + static_cast<size_t>(lrow) * kTopkMeta;
     const uint32_t gt0 = meta[M_GT0];
-    const int d0 = static_cast<int>(meta[M_D0]);
     const uint32_t n_cand = meta[M_CAND];
     copy_to_lds(lh, a.hist1 + static_cast<size_t>(lrow) * kTopkBins, kTopkBins);
     if (threadIdx.x == 0) { n_list = 0; n_grp = 0; }
@@ -341,14 +327,17 @@ __global__ __launch_bounds__(kFinishThreads) void k_topk_finish(TopkArgs a) {
             select_in_bin(src, d1, k2, lh, wsum, sink);
         }
     } else {
-        // the list overflowed: read the row again, filtered to the d0 bin
-        CandRow row_src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, d0, a.sinks, vis - a.window};
-        for_each_candidate(row_src, [&](uint64_t c) {
-            int dg = static_cast<int>(c >> 42);
-            if (dg > d1 || (dg == d1 && whole_bin)) sink.put_c(c);
-        });
-        __syncthreads();
-        if (!whole_bin) select_in_bin(row_src, d1, k2, lh, wsum, sink);
+        // the list overflowed (a mass of equal or nearly equal scores): select
+        // the row again from all of its scores, on the composite bits that
+        // vary among them, starting from an empty sink
+        if (use_bitmap) {
+            for (int i = threadIdx.x; i < nwords; i += blockDim.x) tail[i] = 0u;
+        } else {
+            for (int i = threadIdx.x; i < kpad; i += blockDim.x) tail[i] = 0x7FFFFFFFu;
+        }
+        if (threadIdx.x == 0) n_list = 0;
+        ScoreRow64 row_src{a.scores + static_cast<size_t>(lrow) * a.n_k, vis, a.sinks, vis - a.window};
+        radix_select_spread(row_src, static_cast<uint32_t>(a.k), lh, wsum, sink);
     }
     __syncthreads();
     write_ordered(sink, nwords, kpad, a.k, out, wsum);
@@ -693,11 +682,9 @@ __global__ __launch_bounds__(kRcThreads) void k_topk_row_cand(TopkArgs a, int ca
         Cand64Rel src{cl, static_cast<int>(n), static_cast<uint64_t>(k_low) << 32};
         radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
     } else {
-        // digits of the full 64-bit composite
-        const int shifts64[6] = {53, 42, 32, 21, 10, 0};
-        const int widths64[6] = {11, 11, 10, 11, 11, 10};
+        // the whole row, on the bits of the composite that vary
         ScoreRow64 src{sc, vis, a.sinks, vis - a.window};
-        radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
+        radix_select_spread(src, static_cast<uint32_t>(k), lh, wsum, sink);
     }
     __syncthreads();
     write_ordered(sink, nwords, kpad, k, out, wsum);
@@ -791,7 +778,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
             const size_t smem = static_cast<size_t>(kRowLdsMax) * sizeof(uint32_t);
             if ((e = allow_dyn_lds(fn, smem)) != hipSuccess) return e;
             // workgroups the chip holds at once (one per CU at this LDS size)
-            static const int per_cu = [fn, smem] {
+            static const int per_cu = [fn] {
                 int nb = 0;
                 return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kRowThreads, smem) == hipSuccess && nb > 0
                     ? nb : 1;

@@ -119,10 +119,12 @@ struct Cand64Rel {
     __device__ int size() const { return n; }
     __device__ bool get(int i, uint64_t* out) const { *out = c[i] - base; return true; }
 };
-// A score row in memory as 64-bit composites (order key << 32 | ~position).
+// A score row in memory as 64-bit composites (order key << 32 | ~position),
+// visited over positions [first, n).
 struct ScoreRow64 {
     const float* sc; int n;
     int lo, hi;                 // keys outside [lo, hi) rank as -inf (a backbone's forced keys)
+    int first = 0;
     __device__ int size() const { return n; }
     __device__ bool get(int i, uint64_t* out) const {
         const float x = sc[i];
@@ -130,6 +132,63 @@ struct ScoreRow64 {
         return true;
     }
 };
+// Score rows are visited four scores per load over their 16-byte aligned
+// part (eight loads in flight per thread), the ends one by one.
+template <class F>
+__device__ __forceinline__ void for_each_candidate(const ScoreRow64& src, F&& f) {
+    const int n = src.n, T = blockDim.x;
+    auto one = [&](int i) {
+        uint64_t c;
+        src.get(i, &c);
+        f(c);
+    };
+    if ((reinterpret_cast<uintptr_t>(src.sc) & 15) != 0) {
+        for (int i = src.first + threadIdx.x; i < n; i += T) one(i);
+        return;
+    }
+    const int g0 = (src.first + 3) >> 2, g1 = n >> 2;      // whole float4 groups
+    if (g0 >= g1) {
+        for (int i = src.first + threadIdx.x; i < n; i += T) one(i);
+        return;
+    }
+    for (int i = src.first + threadIdx.x; i < 4 * g0; i += T) one(i);
+    const float4* v = reinterpret_cast<const float4*>(src.sc);
+    auto visit = [&](const float4& x, int i4) {
+        const float e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int s = 4 * i4 + c;
+            f(composite64(order_key(s < src.lo || s >= src.hi ? -__builtin_inff() : e[c]), s));
+        }
+    };
+    int i = g0 + threadIdx.x;
+    for (; i + 7 * T < g1; i += 8 * T) {
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = v[i + u * T];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) visit(x[u], i + u * T);
+    }
+    for (; i < g1; i += T) visit(v[i], i);
+    for (int j = 4 * g1 + threadIdx.x; j < n; j += T) one(j);
+}
+
+// One count per hit lane into the LDS histogram `lh`; when every hit lane of
+// the wave falls in the same bin (rows of tied scores put all of them there)
+// the first hit lane adds the wave's count in one atomic instead of up to 64
+// serialised ones on one address.
+__device__ __forceinline__ void lds_count(uint32_t* lh, bool hit, uint32_t bin) {
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(bin);
+    const uint64_t hits = __ballot(hit);
+    const uint64_t same = __ballot(hit && bin == lb);
+    if (same == hits) {
+        if (hit && (threadIdx.x & 63) == __ffsll(static_cast<unsigned long long>(hits)) - 1)
+            atomicAdd(&lh[lb], static_cast<uint32_t>(__popcll(hits)));
+    } else if (hit) {
+        atomicAdd(&lh[bin], 1u);
+    }
+}
+
 // Where the finish puts kept positions: bits of an LDS bitmap over the row
 // (rows up to kBitmapMaxKeys keys; read back in position order), or an LDS
 // list sorted afterwards.
@@ -149,6 +208,27 @@ struct Sink {
     __device__ void put_c(uint64_t c) const {
         put(static_cast<int>(~static_cast<uint32_t>(c & 0xFFFFFFFFull)));
     }
+    __device__ void put_if(bool take, uint64_t c) const {
+        if (take) put_c(c);
+    }
+};
+// A sink that appends the kept composites themselves to a list in global
+// memory at out[0..cap): one LDS counter, bumped once per wave.
+struct ListSink64 {
+    uint64_t* out;
+    uint32_t* n;       // LDS, starts at 0
+    uint32_t cap;
+    __device__ void put_if(bool take, uint64_t c) const {
+        const uint64_t m = __ballot(take);
+        if (!m) return;
+        const int lane = threadIdx.x & 63;
+        const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+        uint32_t base = 0;
+        if (lane == leader) base = atomicAdd(n, static_cast<uint32_t>(__popcll(m)));
+        base = __shfl(base, leader);
+        const uint32_t slot = base + static_cast<uint32_t>(__popcll(m & ((1ull << lane) - 1ull)));
+        if (take && slot < cap) out[slot] = c;
+    }
 };
 
 // Radix-select the k_rem largest composites of `src` on the digits
@@ -158,9 +238,9 @@ struct Sink {
 // `sink`.  Candidates whose fixed bits differ from `prefix` are ignored.
 // Requires at least k_rem matching candidates and a unique composite per
 // candidate (the position is part of it), so the last digit always resolves.
-template <class Src>
+template <class Src, class SinkT>
 __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, const int* widths, int npass,
-                             uint64_t prefix, uint32_t* lh, uint32_t* wsum, const Sink& sink)
+                             uint64_t prefix, uint32_t* lh, uint32_t* wsum, const SinkT& sink)
 {
     int done_shift = shifts[0] + widths[0];
     for (int p = 0; p < npass; ++p) {
@@ -170,7 +250,7 @@ __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, 
         for (int i = threadIdx.x; i < nb; i += blockDim.x) lh[i] = 0u;
         __syncthreads();
         for_each_candidate(src, [&](uint64_t c) {
-            if (top >= 64 || (c >> top) == prefix) atomicAdd(&lh[(c >> sh) & (nb - 1)], 1u);
+            lds_count(lh, top >= 64 || (c >> top) == prefix, static_cast<uint32_t>((c >> sh) & (nb - 1)));
         });
         __syncthreads();
         int d; uint32_t gt;
@@ -182,10 +262,45 @@ __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, 
         __syncthreads();
         if (done) break;
     }
-    for_each_candidate(src, [&](uint64_t c) {
-        if ((c >> done_shift) >= prefix) sink.put_c(c);
-    });
+    for_each_candidate(src, [&](uint64_t c) { sink.put_if((c >> done_shift) >= prefix, c); });
     __syncthreads();
+}
+
+// radix_select over full 64-bit composites whose digits start below the
+// highest bit in which the candidates differ: one pass finds their minimum
+// and maximum, the bits above their first difference are fixed, and 11-bit
+// digits cover the rest.  Rows of tied scores then take only the passes over
+// the position bits.  `lh` (kTopkBins entries) and `wsum` as radix_select.
+template <class Src, class SinkT>
+__device__ void radix_select_spread(const Src& src, uint32_t k, uint32_t* lh, uint32_t* wsum, const SinkT& sink) {
+    uint64_t lo = ~0ull, hi = 0ull;
+    for_each_candidate(src, [&](uint64_t c) { lo = c < lo ? c : lo; hi = c > hi ? c : hi; });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    uint64_t* red = reinterpret_cast<uint64_t*>(lh);        // lh is free until the select
+    if (lane == 0) { red[2 * wave] = lo; red[2 * wave + 1] = hi; }
+    __syncthreads();
+    for (int w = 0; w < nwaves; ++w) {
+        const uint64_t l2 = red[2 * w], h2 = red[2 * w + 1];
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+    }
+    __syncthreads();
+    const uint64_t diff = lo ^ hi;
+    const int bits = diff ? 64 - __clzll(static_cast<long long>(diff)) : 1;   // the bits that vary
+    int shifts[6], widths[6], np = 0;
+    for (int below = bits; below > 0 && np < 6; ++np) {
+        const int w = below < 11 ? below : 11;
+        below -= w;
+        shifts[np] = below;
+        widths[np] = w;
+    }
+    radix_select(src, k, shifts, widths, np, bits >= 64 ? 0ull : hi >> bits, lh, wsum, sink);
 }
 
 // A lower bound on the r-th largest of the m order keys skey[0..m) (LDS),

@@ -18,8 +18,10 @@
 //           candidates on (order key, ~position) -- ties go to the lower
 //           position -- and writes the positions in ascending order.
 // If a row ends with fewer than k candidates or more than the list holds, the
-// finish workgroup recomputes that row's scores in full and selects from all
-// of them, so the result never depends on how good the sample was.
+// finish recomputes that row's scores in full, spread over several
+// workgroups that each keep the top k of their slice, and the last of them
+// selects the row's k from those, so the result never depends on how good
+// the sample was.
 #include "fp8_index.h"
 #include "topk_common.h"
 
@@ -27,6 +29,18 @@ namespace dsa {
 
 constexpr int kSampleThreads = 512;
 constexpr int kSFinishThreads = 1024;
+// Workgroups per row of the finish: one selects from the candidates; a row
+// that falls back is recomputed by all of them, a slice of at least
+// kFinishSliceKeys keys each, up to kFinishPartsMax workgroups.
+constexpr int kFinishSliceKeys = 16384;
+// s_waitcnt immediate that waits for every outstanding vector memory access
+// of the wave (vmcnt = 0, the other counters unconstrained).
+constexpr int kWaitVmem = 0x0F70;
+constexpr int kFinishPartsMax = 64;
+static int finish_parts(int n_k) {
+    const int p = (n_k + kFinishSliceKeys - 1) / kFinishSliceKeys;
+    return p < 1 ? 1 : p > kFinishPartsMax ? kFinishPartsMax : p;
+}
 
 bool topk_sampled_eligible(int n_k, int k) {
     return static_cast<int64_t>(n_k) >= 16 * static_cast<int64_t>(k) && n_k >= kSampleKeys;
@@ -99,7 +113,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
     const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
     const int vis = ranked_keys(x, pos).cnt;   // keys ranked (and sampled)
     uint32_t* meta = x.meta + static_cast<size_t>(lrow) * kTopkMeta;
-    if (threadIdx.x == 0) { meta[S_NCAND] = 0u; meta[S_OVF] = 0u; meta[S_FALLBACK] = 0u; }
+    if (threadIdx.x == 0) { meta[S_NCAND] = 0u; meta[S_OVF] = 0u; meta[S_FALLBACK] = 0u; meta[S_DONE] = 0u; meta[S_NWIN] = 0u; }
     if (vis <= x.k) {                      // every ranked key is kept: nothing to bound
         if (threadIdx.x == 0) meta[S_KLOW] = 0xFFFFFFFFu;
         return;
@@ -137,21 +151,28 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
 }
 
 // Exact top-k over the candidate list (or the recomputed row), then the
-// positions in ascending order.
+// positions in ascending order.  Grid (rows, parts): workgroup (r, 0)
+// selects row r from its candidates; the others return at once unless the
+// row falls back, and then all `parts` workgroups of the row recompute one
+// slice of its scores each, and the last of them to finish selects from the
+// whole row.
 __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(SampledTopk t) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ uint32_t lh[kTopkBins];
     __shared__ uint32_t wsum[kSFinishThreads / 64 + 2];
     __shared__ uint32_t n_list;
+    __shared__ uint32_t last, win_base;
     const IndexArgs& x = t.ix;
     const int lrow = blockIdx.x, row = x.row0 + lrow;
+    const int part = blockIdx.y, nparts = gridDim.y;
     const int pos = row_pos(x.q_pos, row, x.n_q, x.n_k);
     const int vis = pos + 1;
     const Ranked rk = ranked_keys(x, pos);
     const int k = x.k;
     int32_t* out = t.idx + static_cast<size_t>(lrow) * k;
     if (rk.cnt <= k) {                     // every ranked key is kept
-        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < rk.cnt ? rk.lo + j : -1;
+        if (part == 0)
+            for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < rk.cnt ? rk.lo + j : -1;
         return;
     }
     uint64_t* cl = reinterpret_cast<uint64_t*>(smem);                       // [cand_cap]
@@ -161,15 +182,16 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
     int kpad = 1;
     while (kpad < k) kpad <<= 1;
     Sink sink{use_bitmap ? tail : nullptr, reinterpret_cast<int32_t*>(tail), &n_list, static_cast<uint32_t>(k)};
-    if (use_bitmap) {
-        for (int i = threadIdx.x; i < nwords; i += blockDim.x) tail[i] = 0u;
-    } else {
-        for (int i = threadIdx.x; i < kpad; i += blockDim.x) tail[i] = 0x7FFFFFFFu;
-    }
-    if (threadIdx.x == 0) n_list = 0;
-    // digits of the 64-bit (order key << 32 | ~position) composite
-    const int shifts64[6] = {53, 42, 32, 21, 10, 0};
-    const int widths64[6] = {11, 11, 10, 11, 11, 10};
+    // the sink starts empty (ordered before its first use by the select's
+    // first barrier)
+    auto clear_sink = [&]() {
+        if (use_bitmap) {
+            for (int i = threadIdx.x; i < nwords; i += blockDim.x) tail[i] = 0u;
+        } else {
+            for (int i = threadIdx.x; i < kpad; i += blockDim.x) tail[i] = 0x7FFFFFFFu;
+        }
+        if (threadIdx.x == 0) n_list = 0;
+    };
     uint32_t* meta = x.meta + static_cast<size_t>(lrow) * kTopkMeta;
     // the first kSpecLoads*blockDim.x list entries are fetched together with the
     // counters, before the list's length is known (entries past it are ignored;
@@ -178,12 +200,16 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
     static_assert(kSpecLoads * kSFinishThreads <= kSampledCandCap, "speculative reads stay inside the list");
     const uint64_t* cg = x.cand + static_cast<size_t>(lrow) * x.cand_cap;
     uint64_t spec[kSpecLoads];
+    if (part == 0) {
 #pragma unroll
-    for (int u = 0; u < kSpecLoads; ++u) spec[u] = cg[threadIdx.x + u * kSFinishThreads];
+        for (int u = 0; u < kSpecLoads; ++u) spec[u] = cg[threadIdx.x + u * kSFinishThreads];
+    }
     const uint32_t n = meta[S_NCAND];
     const uint32_t k_low = meta[S_KLOW];
     const bool ok = meta[S_OVF] == 0u && n >= static_cast<uint32_t>(k) && n <= static_cast<uint32_t>(x.cand_cap);
     if (ok) {
+        if (part != 0) return;
+        clear_sink();
         uint32_t kmax = 0u;
 #pragma unroll
         for (int u = 0; u < kSpecLoads; ++u) {
@@ -219,30 +245,74 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
         Cand64Rel src{cl, static_cast<int>(n), static_cast<uint64_t>(k_low) << 32};
         radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
     } else {
-        // recompute this row's scores in full, then select from all of them
-        if (threadIdx.x == 0) meta[S_FALLBACK] = 1u;
+        // recompute this row's scores in full, slice `part` of nparts here:
+        // each wave scores 128 keys per step with whole-line loads
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-        const int col = lane & 15;
         const int b = row / x.n_q;
         const Fp8Query q = load_fp8_query(static_cast<const uint8_t*>(x.iq), x.iq_scale, x.iw, row, x.H, lane);
         const uint8_t* kb = static_cast<const uint8_t*>(x.ik) + static_cast<size_t>(b) * x.n_k * 128;
         const float* ksb = x.ik_scale + static_cast<size_t>(b) * x.n_k;
         float* sc = t.scratch + static_cast<size_t>(lrow) * x.n_k;
-        for (int base = wave * 64; base < vis; base += nwaves * 64) {   // uniform per wave
-            v8i bv[4];
+        const int slice = (((vis + nparts - 1) / nparts) + 127) & ~127;
+        const int s0 = part * slice, s1 = min(vis, s0 + slice);
+        for (int base = s0 + wave * 128; base < s1; base += nwaves * 128) {   // uniform per wave
+            v4i lines[16];
+            float sk[2];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int s = base + u * 16 + col;
-                bv[u] = load_fp8_key(kb, s, s < vis, lane);
+            for (int g = 0; g < 2; ++g) {
+                load_keys64_lines(kb, base + 64 * g, vis - 1, lane, lines + 8 * g);
+                sk[g] = ksb[min(base + 64 * g + lane, vis - 1)];
             }
-            const int s = base + lane;
-            const float score = fp8_score4(q, bv, s < vis ? ksb[s] : 0.0f);
-            if (s < vis) sc[s] = score;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                v8i bv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) bv[u] = keys_block_operand(lines + 8 * g, u, lane);
+                const float score = fp8_score4(q, bv, sk[g]);
+                const int s = base + 64 * g + lane;
+                if (s < s1) sc[s] = score;
+            }
         }
         __threadfence_block();
         __syncthreads();
-        ScoreRow64 src{sc, vis, rk.lo, rk.lo + rk.cnt};
-        radix_select(src, static_cast<uint32_t>(k), shifts64, widths64, 6, 0ull, lh, wsum, sink);
+        // this slice's top k (all of its ranked keys when it has no more) go
+        // to the row's winner list; the top k of the row are among them
+        const int r0 = max(s0, rk.lo), r1 = min(s1, rk.lo + rk.cnt);
+        const int cnt = r1 > r0 ? r1 - r0 : 0;
+        const uint32_t take = static_cast<uint32_t>(min(cnt, k));
+        uint64_t* win = t.win + static_cast<size_t>(lrow) * t.win_cap;
+        if (threadIdx.x == 0) {
+            n_list = 0;
+            win_base = take ? atomicAdd(&meta[S_NWIN], take) : 0u;
+        }
+        __syncthreads();
+        if (cnt > k) {
+            ScoreRow64 src{sc, r1, rk.lo, rk.lo + rk.cnt, r0};
+            ListSink64 ls{win + win_base, &n_list, take};
+            radix_select_spread(src, static_cast<uint32_t>(k), lh, wsum, ls);
+        } else {
+            for (int s = r0 + threadIdx.x; s < r1; s += blockDim.x)
+                win[win_base + static_cast<uint32_t>(s - r0)] = composite64(order_key(sc[s]), s);
+        }
+        // publish the winners: every wave waits until its stores have reached
+        // the L2, then one thread releases them at device scope (a device
+        // fence writes back the whole L2, so one per workgroup, not one per
+        // wave) and counts the workgroup in; the last of the row's
+        // workgroups to arrive acquires and merges
+        __builtin_amdgcn_s_waitcnt(kWaitVmem);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            if (part == 0) meta[S_FALLBACK] = 1u;
+            __threadfence();
+            last = atomicAdd(&meta[S_DONE], 1u) == static_cast<uint32_t>(nparts - 1) ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!last) return;
+        __threadfence();
+        const uint32_t nw = __hip_atomic_load(&meta[S_NWIN], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        clear_sink();
+        Cand64Rel src{win, static_cast<int>(nw), 0ull};
+        radix_select_spread(src, static_cast<uint32_t>(k), lh, wsum, sink);
     }
     __syncthreads();
     write_ordered(sink, nwords, kpad, k, out, wsum);
@@ -250,15 +320,16 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
 
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-size_t topk_sampled_workspace_bytes(int rows, int n_k) {
+size_t topk_sampled_workspace_bytes(int rows, int n_k, int k) {
     const size_t r = static_cast<size_t>(rows);
     return align256(r * kTopkMeta * sizeof(uint32_t)) +
            align256(r * kSampledCandCap * sizeof(uint64_t)) +
            align256(r * kSampleKeys * sizeof(uint32_t)) +
-           align256(r * static_cast<size_t>(n_k) * sizeof(float));
+           align256(r * static_cast<size_t>(n_k) * sizeof(float)) +
+           align256(r * static_cast<size_t>(finish_parts(n_k)) * k * sizeof(uint64_t));
 }
 
-void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t) {
+void topk_sampled_carve(void* ws, int rows, int n_k, int k, SampledTopk& t) {
     unsigned char* p = static_cast<unsigned char*>(ws);
     const size_t r = static_cast<size_t>(rows);
     t.ix.meta = reinterpret_cast<uint32_t*>(p);
@@ -269,7 +340,9 @@ void topk_sampled_carve(void* ws, int rows, int n_k, SampledTopk& t) {
     t.samples = reinterpret_cast<uint32_t*>(p);
     p += align256(r * kSampleKeys * sizeof(uint32_t));
     t.scratch = reinterpret_cast<float*>(p);
-    (void)n_k;
+    p += align256(r * static_cast<size_t>(n_k) * sizeof(float));
+    t.win = reinterpret_cast<uint64_t*>(p);
+    t.win_cap = finish_parts(n_k) * k;
 }
 
 hipError_t launch_topk_sample(const SampledTopk& t, hipStream_t st) {
@@ -290,7 +363,7 @@ hipError_t launch_topk_finish_sampled(const SampledTopk& t, hipStream_t st) {
         hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(k_topk_finish_sampled), smem);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_topk_finish_sampled, dim3(t.ix.rows), dim3(kSFinishThreads), smem, st, t);
+    hipLaunchKernelGGL(k_topk_finish_sampled, dim3(t.ix.rows, finish_parts(t.ix.n_k)), dim3(kSFinishThreads), smem, st, t);
     return hipGetLastError();
 }
 

@@ -590,6 +590,23 @@ def test_decode_1m_sampled():
     assert hits >= 0.95 * len(inp["needle_pairs"]), f"needle recall {hits}/{len(inp['needle_pairs'])}"
 
 
+@pytest.mark.parametrize("workload,zero_rows", [("decode_128k", [5, 17]), ("decode_1m", [3])])
+def test_decode_rows_recomputed_in_full_at_full_size(workload, zero_rows):
+    """Rows whose indexer head weights are all zero score 0 at every key: every
+    key is a candidate, the row's list overflows and the finish recomputes the
+    whole row over several workgroups, then selects the lowest k positions.
+    The benchmarked shapes, with the other rows on the candidate path beside
+    them; fused, unfused and oracle must agree."""
+    inp = make_inputs(spec(workload), device=DEV, seed=0)
+    inp["name"] = f"{workload}_zero_weight_rows"
+    for b in zero_rows:
+        inp["iw"][b].zero_()
+    stats, idx, _ = run_case(inp, zero_rows + [0], [0], fused="decode")
+    k = inp["top_k"]
+    for b in zero_rows:
+        assert idx[b, 0].cpu().tolist() == list(range(k))
+
+
 # --- masked MHA mode, dense causal attention and the dense fallback --------------------------
 
 def _attn_problem(inp, **kw):
