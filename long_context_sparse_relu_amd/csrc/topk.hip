@@ -403,10 +403,136 @@ __device__ __forceinline__ void select_lds_row(const TopkArgs& a, uint32_t* keys
     write_ordered(sink, nwords, 1, k, out, wsum);
 }
 
+// Keys of one bin that the comparison ranking below takes (they sit in the
+// histogram's LDS once the bin is known: kTopkBins words = this many 64-bit
+// entries).
+constexpr int kLinListCap = kTopkBins / 2;
+
+// Exact top k of a row whose scores (float bits; a backbone's forced keys
+// already -inf) sit in LDS at sbits[0, vis), vis > k: the k largest by
+// (score descending, position ascending), written in ascending order.
+//   histogram  a digit linear in the score over the row's finite range
+//              [smin, smax] (2048 bins; -inf and smin fall in bin 0): the
+//              digit never decreases as the score grows, so the threshold bin
+//              d0 and the count above it give the exact split;
+//   split      keys of bins above d0 are kept (bitmap), keys of bin d0 go to
+//              a list as (order key << 32 | ~position);
+//   rank       each listed key counts the listed keys that beat it; the
+//              k - (count above d0) best are kept.
+// On rows whose scores are nearly equal (finite range 0, or more than
+// kLinListCap keys in bin d0) the scores are turned into order keys in place
+// and radix-selected instead.  Whole block; smin, smax block-uniform.
+__device__ void select_lds_row_lin(const TopkArgs& a, uint32_t* sbits, int vis, float smin, float smax,
+                                   uint32_t* lh, uint32_t* bm, uint32_t* wsum, uint32_t* n_list, int32_t* out) {
+    const int k = a.k;
+    const int T = blockDim.x;
+    const int nwords = (vis + 31) >> 5;
+    float scale = smax > smin && smin > -__builtin_inff() && smax < __builtin_inff()
+                      ? static_cast<float>(kTopkBins) / (smax - smin) : 0.0f;
+    const bool spread = scale > 0.0f && scale < __builtin_inff();
+    auto digit = [&](float x) {
+        return x <= smin ? 0 : min(kTopkBins - 1, static_cast<int>((x - smin) * scale));
+    };
+    int d0 = 0;
+    uint32_t gt0 = 0, n0 = 0;
+    if (spread) {
+        for (int i = threadIdx.x; i < kTopkBins; i += T) lh[i] = 0u;
+        __syncthreads();
+        for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * T) {      // eight reads in flight
+            uint32_t x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = sbits[min(i0 + u * T, vis - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * T < vis) atomicAdd(&lh[digit(__uint_as_float(x[u]))], 1u);
+        }
+        __syncthreads();
+        find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(k), wsum, &d0, &gt0);
+        n0 = lh[d0];
+        __syncthreads();                          // every thread has read lh[d0] (the list reuses lh)
+    }
+    if (!spread || n0 > static_cast<uint32_t>(kLinListCap)) {
+        // nearly equal scores: radix select over order keys
+        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+        for (int i = threadIdx.x; i < vis; i += T) {
+            const uint32_t kk = order_key(__uint_as_float(sbits[i]));
+            sbits[i] = kk;
+            kmin = min(kmin, kk);
+            kmax = max(kmax, kk);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+            kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+        }
+        uint32_t* wred = lh;                      // free until the select clears it
+        if ((threadIdx.x & 63) == 0) { wred[2 * (threadIdx.x >> 6)] = kmin; wred[2 * (threadIdx.x >> 6) + 1] = kmax; }
+        __syncthreads();
+        for (int w = 0; w < T / 64; ++w) { kmin = min(kmin, wred[2 * w]); kmax = max(kmax, wred[2 * w + 1]); }
+        __syncthreads();
+        select_lds_row(a, sbits, vis, kmin, kmax, lh, bm, wsum, n_list, out);
+        return;
+    }
+    // split: bins above d0 kept, bin d0 listed
+    uint64_t* list = reinterpret_cast<uint64_t*>(lh);
+    const int lane = threadIdx.x & 63;
+    for (int j0 = 0; j0 < vis; j0 += 4 * T) {    // uniform trip count (ballots below); four reads in flight
+        uint32_t xs[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xs[u] = sbits[min(j0 + u * T + static_cast<int>(threadIdx.x), vis - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i0 = j0 + u * T;
+            const int i = i0 + static_cast<int>(threadIdx.x);
+            const float x = i < vis ? __uint_as_float(xs[u]) : -__builtin_inff();
+            const int d = i < vis ? digit(x) : -1;
+            // a wave covers 64 consecutive positions from a multiple of 64: two
+            // whole bitmap words, which only this wave writes in this pass
+            const uint64_t above = __ballot(d > d0);
+            if ((lane & 31) == 0) {
+                const uint32_t bits = static_cast<uint32_t>(lane == 0 ? above : above >> 32);
+                if (bits) bm[i >> 5] = bits;
+            }
+            const bool take = d == d0;
+            const uint64_t m = __ballot(take);
+            if (m) {
+                const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+                uint32_t base = 0;
+                if (lane == leader) base = atomicAdd(n_list, static_cast<uint32_t>(__popcll(m)));
+                base = __shfl(base, leader);
+                if (take) list[base + __popcll(m & ((1ull << lane) - 1ull))] = composite64(order_key(x), i);
+            }
+        }
+    }
+    __syncthreads();
+    // rank: the k - gt0 best of the n0 listed keys (composites are distinct)
+    const uint32_t k_rem = static_cast<uint32_t>(k) - gt0;
+    for (uint32_t t = threadIdx.x; t < n0; t += T) {
+        const uint64_t c = list[t];
+        uint32_t beat = 0;
+        uint32_t j = 0;
+        for (; j + 8 <= n0; j += 8) {            // eight reads in flight
+            uint64_t y[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) y[u] = list[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) beat += y[u] > c ? 1u : 0u;
+        }
+        for (; j < n0; ++j) beat += list[j] > c ? 1u : 0u;
+        if (beat < k_rem) {
+            const int pos = static_cast<int>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
+            atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+        }
+    }
+    __syncthreads();
+    Sink sink{bm, nullptr, n_list, static_cast<uint32_t>(k)};
+    write_ordered(sink, nwords, 1, k, out, wsum);
+}
+
 template <int T>
 __global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
     extern __shared__ uint32_t keys[];                        // [min(n_k, kRowLdsMax)]
-    __shared__ uint32_t lh[kTopkBins];
+    __shared__ __align__(16) uint32_t lh[kTopkBins];          // (8-byte list entries in the select)
     __shared__ uint32_t bm[kRowLdsMax / 32];
     __shared__ uint32_t wsum[T / 64 + 2];
     __shared__ uint32_t n_list;
@@ -419,9 +545,9 @@ __global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
         return;
     }
     const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
-    // the row's keys, eight loads in flight per thread (indices past vis
-    // re-read the last score and are not stored)
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    // the row's scores, eight loads in flight per thread (indices past vis
+    // re-read the last score and are not stored), and their finite range
+    float smin = __builtin_inff(), smax = -__builtin_inff();
     for (int i0 = threadIdx.x; i0 < vis; i0 += 8 * T) {
         float v[8];
 #pragma unroll
@@ -430,10 +556,9 @@ __global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
         for (int u = 0; u < 8; ++u) {
             const int i = i0 + u * T;
             if (i < vis) {
-                const uint32_t kk = order_key(v[u]);
-                keys[i] = kk;
-                kmin = min(kmin, kk);
-                kmax = max(kmax, kk);
+                keys[i] = __float_as_uint(v[u]);
+                if (v[u] > -__builtin_inff()) smin = fminf(smin, v[u]);
+                smax = fmaxf(smax, v[u]);
             }
         }
     }
@@ -442,14 +567,14 @@ __global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
     if (threadIdx.x == 0) n_list = 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+        smin = fminf(smin, __shfl_xor(smin, o));
+        smax = fmaxf(smax, __shfl_xor(smax, o));
     }
-    __shared__ uint32_t wmin[T / 64], wmax[T / 64];
-    if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
+    __shared__ float wmin[T / 64], wmax[T / 64];
+    if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = smin; wmax[threadIdx.x >> 6] = smax; }
     __syncthreads();
-    for (int w = 0; w < T / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
-    select_lds_row(a, keys, vis, kmin, kmax, lh, bm, wsum, &n_list, out);
+    for (int w = 0; w < T / 64; ++w) { smin = fminf(smin, wmin[w]); smax = fmaxf(smax, wmax[w]); }
+    select_lds_row_lin(a, keys, vis, smin, smax, lh, bm, wsum, &n_list, out);
 }
 
 // Rows longer than half the LDS limit leave room for one workgroup per
@@ -460,10 +585,10 @@ __global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
 constexpr int kRowPerThread = kRowLdsMax / kRowThreads;
 __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
     extern __shared__ uint32_t keys[];                        // [kRowLdsMax]
-    __shared__ uint32_t lh[kTopkBins];
+    __shared__ __align__(16) uint32_t lh[kTopkBins];          // (8-byte list entries in the select)
     __shared__ uint32_t bm[kRowLdsMax / 32];
     __shared__ uint32_t wsum[kRowThreads / 64 + 2];
-    __shared__ uint32_t wmin[kRowThreads / 64], wmax[kRowThreads / 64];
+    __shared__ float wmin[kRowThreads / 64], wmax[kRowThreads / 64];
     __shared__ uint32_t n_list;
     float v[kRowPerThread];
     // issue the loads of row lrow's scores: entry u of thread t is key
@@ -486,17 +611,16 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
             for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < vis ? j : -1;
             if (next < a.rows && vis_next > a.k) fetch(next, vis_next);
         } else {
-            uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+            float smin = __builtin_inff(), smax = -__builtin_inff();
 #pragma unroll
             for (int u = 0; u < kRowPerThread; ++u) {
                 const int i = static_cast<int>(threadIdx.x) + u * kRowThreads;
                 if (i < vis) {
                     // a backbone's forced keys rank as -inf (as ranked() does)
                     const float x = (i < a.sinks || i >= vis - a.window) ? -__builtin_inff() : v[u];
-                    const uint32_t kk = order_key(x);
-                    keys[i] = kk;
-                    kmin = min(kmin, kk);
-                    kmax = max(kmax, kk);
+                    keys[i] = __float_as_uint(x);
+                    if (x > -__builtin_inff()) smin = fminf(smin, x);
+                    smax = fmaxf(smax, x);
                 }
             }
             const int nwords = (vis + 31) >> 5;
@@ -504,14 +628,14 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
             if (threadIdx.x == 0) n_list = 0;
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
-                kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-                kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+                smin = fminf(smin, __shfl_xor(smin, o));
+                smax = fmaxf(smax, __shfl_xor(smax, o));
             }
-            if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
+            if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = smin; wmax[threadIdx.x >> 6] = smax; }
             __syncthreads();
-            for (int w = 0; w < kRowThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }
+            for (int w = 0; w < kRowThreads / 64; ++w) { smin = fminf(smin, wmin[w]); smax = fmaxf(smax, wmax[w]); }
             if (next < a.rows && vis_next > a.k) fetch(next, vis_next);   // lands during the select
-            select_lds_row(a, keys, vis, kmin, kmax, lh, bm, wsum, &n_list, out);
+            select_lds_row_lin(a, keys, vis, smin, smax, lh, bm, wsum, &n_list, out);
         }
         __syncthreads();                    // the next row's keys reuse the LDS
         vis = vis_next;

@@ -238,7 +238,10 @@ struct ListSink64 {
 // `sink`.  Candidates whose fixed bits differ from `prefix` are ignored.
 // Requires at least k_rem matching candidates and a unique composite per
 // candidate (the position is part of it), so the last digit always resolves.
-template <class Src, class SinkT>
+// With AGG the histogram adds are aggregated per wave (lds_count): worth its
+// extra instructions only where whole waves tend to hit one bin (whole rows
+// of tied scores).
+template <bool AGG = false, class Src, class SinkT>
 __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, const int* widths, int npass,
                              uint64_t prefix, uint32_t* lh, uint32_t* wsum, const SinkT& sink)
 {
@@ -250,7 +253,10 @@ __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, 
         for (int i = threadIdx.x; i < nb; i += blockDim.x) lh[i] = 0u;
         __syncthreads();
         for_each_candidate(src, [&](uint64_t c) {
-            lds_count(lh, top >= 64 || (c >> top) == prefix, static_cast<uint32_t>((c >> sh) & (nb - 1)));
+            const bool hit = top >= 64 || (c >> top) == prefix;
+            const uint32_t bin = static_cast<uint32_t>((c >> sh) & (nb - 1));
+            if constexpr (AGG) lds_count(lh, hit, bin);
+            else if (hit) atomicAdd(&lh[bin], 1u);
         });
         __syncthreads();
         int d; uint32_t gt;
@@ -300,7 +306,7 @@ __device__ void radix_select_spread(const Src& src, uint32_t k, uint32_t* lh, ui
         shifts[np] = below;
         widths[np] = w;
     }
-    radix_select(src, k, shifts, widths, np, bits >= 64 ? 0ull : hi >> bits, lh, wsum, sink);
+    radix_select<true>(src, k, shifts, widths, np, bits >= 64 ? 0ull : hi >> bits, lh, wsum, sink);
 }
 
 // A lower bound on the r-th largest of the m order keys skey[0..m) (LDS),

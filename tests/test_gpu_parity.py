@@ -411,6 +411,40 @@ def test_topk_long_rows_many_per_workgroup(sinks, window, n_k):
     assert not bad, f"rows {bad[:5]} differ (of {len(bad)})"
 
 
+@pytest.mark.parametrize("n_k", [12000, 24000])
+def test_topk_lds_rows_with_skewed_scores(n_k):
+    """dsa_topk over rows selected in LDS (12000 keys: one row per workgroup;
+    24000: the persistent form), each row exact against the oracle.  The
+    select bins scores linearly over each row's finite range, so the rows
+    cycle through distributions that stress that: Gaussian; one huge outlier
+    (every other key in the lowest bin: the order-key radix select takes
+    over); a heavy tail; two values with ties across the threshold; and
+    -inf scores mixed in."""
+    n_q, k = 300, 1000
+    sp = custom_spec(name="lds_skew", n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=k,
+                     q_heads=2, kv_heads=1, d_qk=64, d_v=64, attn_dtype="bf16")
+    inp = make_inputs(sp, device=DEV, seed=47)
+    g = torch.Generator().manual_seed(47)
+    pos = torch.randint(n_k // 2, n_k, (1, n_q), generator=g, dtype=torch.int32)
+    pos[0, -1] = n_k - 1
+    sc = torch.randn((n_q, n_k), generator=g)
+    kind = torch.arange(n_q) % 5
+    sc[kind == 1, 7] = 1e30
+    sc[kind == 2] = torch.exp(3.0 * sc[kind == 2])
+    two = torch.where(torch.rand((n_q, n_k), generator=g) < 0.05, 1.0, 0.5)
+    sc[kind == 3] = two[kind == 3]
+    ninf = torch.rand((n_q, n_k), generator=g) < 0.3
+    sc[(kind == 4).unsqueeze(1) & ninf] = -float("inf")
+    scores = sc.unsqueeze(0).float()
+    prob = dsa.make_problem(**_problem_kwargs(inp), q_pos=pos.to(DEV))
+    idx = dsa.topk(prob, scores.to(DEV))
+    torch.cuda.synchronize()
+    o_idx, _ = oracle.topk(scores[0].double().numpy(), k, pos[0].numpy().astype(np.int64))
+    g_idx = idx[0].cpu().numpy()
+    bad = [r for r in range(n_q) if not np.array_equal(g_idx[r], o_idx[r])]
+    assert not bad, f"rows {bad[:5]} differ (of {len(bad)})"
+
+
 @pytest.mark.parametrize("case", ["all_tied", "sample_overstates"])
 def test_topk_candidate_lists_fall_back_to_the_whole_row(case):
     """dsa_topk over 300 rows of 20000 keys selects through sampled candidate
