@@ -94,7 +94,7 @@ def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
     after a read of 1 GiB (so the gathered rows come from HBM, not a cache).
     Prints one JSON line per point and a summary line.
     """
-    from dsa_inputs import custom_spec, make_inputs
+    from dsa_inputs import custom_spec, kv_args, make_inputs
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
@@ -112,9 +112,9 @@ def _sweep_mask(dsa, torch, dev, ladder, ks, chunks, chunk_nk, reps):
         return ts[len(ts) // 2]
 
     def problem(inp, k, mode):
-        return dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
-                                v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-                                softmax_scale=inp["scale"], attn_mode=mode)
+        return dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"],
+                                iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
+                                softmax_scale=inp["scale"], attn_mode=mode, **kv_args(inp))
 
     def attn_times(inp, k, idx, n, n_gather=None):
         res = {}
@@ -204,7 +204,7 @@ def _sweep_ladder(dsa, torch, dev, lengths, ks, reps):
     dense ideal (every K/V row read once at 8 TB/s).  Medians of `reps` calls,
     each after a 1 GiB read.  One JSON line per point.
     """
-    from dsa_inputs import custom_spec, make_inputs
+    from dsa_inputs import custom_spec, kv_args, make_inputs
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
@@ -228,9 +228,9 @@ def _sweep_ladder(dsa, torch, dev, lengths, ks, reps):
         print(f"[ladder] inputs L={L} B={B}", file=sys.stderr, flush=True)
         inp = make_inputs(sp, device=dev, seed=0)
         for k in ks:
-            prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
-                                    v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-                                    softmax_scale=inp["scale"])
+            prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"],
+                                    iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
+                                    softmax_scale=inp["scale"], **kv_args(inp))
             out, lse = dsa._out_tensors(prob, None, None)
             idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
             ws = torch.empty(dsa.workspace_bytes(dsa.OP_DECODE, prob), dtype=torch.uint8, device=dev)
@@ -344,7 +344,7 @@ def main(argv=None):
 
     import torch
     import long_context_sparse_relu_amd as dsa
-    from dsa_inputs import spec, make_inputs
+    from dsa_inputs import kv_args, make_inputs, spec
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -362,11 +362,9 @@ def main(argv=None):
     B, N, k, n_q = s["B"], s["n_k"], s["top_k"], s["n_q"]
     if args.zero_weight_rows:
         inp["iw"].view(B * n_q, -1)[:args.zero_weight_rows].zero_()
-    prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"], k=inp["k"],
-                            v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-                            softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
-                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                            sink_tokens=s.get("sinks", 0), local_window=s.get("window", 0))
+    prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=k, q=inp["q"],
+                            iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"], softmax_scale=inp["scale"],
+                            sink_tokens=s.get("sinks", 0), local_window=s.get("window", 0), **kv_args(inp))
     out, lse = dsa._out_tensors(prob, None, None)
     idx = torch.empty((B, n_q, prob.sel_width), dtype=torch.int32, device=dev)
     op = dsa.OP_DECODE if decode else dsa.OP_PREFILL

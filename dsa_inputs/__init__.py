@@ -34,7 +34,8 @@ w ~ N(0,1)/2, main q/k/v ~ N(0,1), softmax scale 1/sqrt(d_qk)):
 Any spec may set kv_dtype="e4m3" (with attn_dtype "bf16"): the main k and v
 are drawn as above and stored as E4M3 codes with one fp32 scale (amax/448) per
 (token, kv head) row, in k_scale / v_scale [B,n_k,Hkv] (latent rows: k_scale
-only).
+only), and packed as the library takes them, token records of codes then
+scales (k_rec / v_rec; kv_args gives a problem's k / v arguments either way).
 
 A needle is an indexer key made a noisy copy of one query's strongest head:
 for a random key position s and a query t >= s, h = argmax_h w[t,h] (the query
@@ -115,6 +116,28 @@ def quantize_e4m3_per_row(x: torch.Tensor):
     return y.to(torch.float8_e4m3fn), scale.to(torch.float32)
 
 
+def pack_fp8_kv_records(codes: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """An FP8 cache's token records: codes [B,n_k,Hkv,d] float8_e4m3fn and
+    scales [B,n_k,Hkv] fp32 -> uint8 [B,n_k,rec], each token's Hkv*d code
+    bytes, then its Hkv fp32 scales (little-endian), then zeros up to a
+    multiple of 16 bytes (the layout the library's header defines)."""
+    B, n_k, Hkv, d = codes.shape
+    rec = (Hkv * d + 4 * Hkv + 15) // 16 * 16
+    out = torch.zeros((B, n_k, rec), dtype=torch.uint8, device=codes.device)
+    out[:, :, :Hkv * d] = codes.contiguous().view(torch.uint8).reshape(B, n_k, Hkv * d)
+    out[:, :, Hkv * d:Hkv * d + 4 * Hkv] = scale.contiguous().view(torch.uint8).reshape(B, n_k, 4 * Hkv)
+    return out
+
+
+def kv_args(inp: dict) -> dict:
+    """The main k / v arguments of a problem over `inp`: the tensors as drawn,
+    or an FP8 cache's token records with kv_heads and d_v."""
+    if inp["kv_dtype"] != "e4m3":
+        return dict(k=inp["k"], v=inp["v"], latent_dv=inp["latent_dv"])
+    return dict(k=inp["k_rec"], v=inp["v_rec"], latent_dv=inp["latent_dv"], kv_heads=inp["kv_heads"],
+                d_v=None if inp["v"] is None else inp["d_v"])
+
+
 def make_inputs(s: dict, device="cpu", seed: int = 0) -> dict:
     """Draw one input set for spec `s` on `device`.
 
@@ -122,6 +145,8 @@ def make_inputs(s: dict, device="cpu", seed: int = 0) -> dict:
       iq [B,n_q,H,D], iq_scale [B,n_q] (E4M3 only), ik [B,n_k,D], ik_scale [B,n_k],
       iw [B,n_q,H] fp32, q [B,n_q,Hq,dqk], k [B,n_k,Hkv,dqk], v [B,n_k,Hkv,dv] or
       None (latent), k_scale / v_scale [B,n_k,Hkv] (E4M3 cache only, else None),
+      and for an E4M3 cache k_rec / v_rec, the same as token records
+      (pack_fp8_kv_records; v_rec None when latent),
       pos [B,n_q] int32 (last visible key: n_k-n_q+t),
     and the scalars of the spec plus `scale` = 1/sqrt(d_qk).
     """
@@ -188,6 +213,9 @@ def make_inputs(s: dict, device="cpu", seed: int = 0) -> dict:
     out["v"] = torch.stack(v_l) if not latent else None
     out["k_scale"] = torch.stack(ks_l) if ks_l else None
     out["v_scale"] = torch.stack(vs_l) if vs_l else None
+    if kvt == "e4m3":
+        out["k_rec"] = pack_fp8_kv_records(out["k"], out["k_scale"])
+        out["v_rec"] = None if latent else pack_fp8_kv_records(out["v"], out["v_scale"])
     out["needle_pairs"] = needle_pairs
     return out
 

@@ -41,10 +41,13 @@
  *            the cache format "DeepSeek-V4 百万 token 上下文的工程实现" names
  *            in its section on the sliding-window KV cache and mixed strategy
  *            (FP8 instead of FP16, half the memory).  Each (token, kv head) row
- *            is its E4M3 codes times one fp32 scale: k[s,g] = k_scale[s,g] *
- *            code, v[s,g] = v_scale[s,g] * code; a latent value row is part of
- *            its key row and takes k_scale.  The attention above runs on those
- *            decoded values.
+ *            is its E4M3 codes times one fp32 scale: k[s,g] = ks[s,g] * code,
+ *            v[s,g] = vs[s,g] * code; a latent value row is part of its key
+ *            row and takes ks.  The attention above runs on those decoded
+ *            values.  The pages fix no layout for the scales; here each
+ *            token's scales sit right after its codes in one record (see
+ *            DSA_FP8_KV_RECORD_BYTES below), so a gathered token's scale comes
+ *            from the same memory page as its codes.
  *
  * Memory and ownership.  Every pointer inside dsa_problem_t and every output
  * pointer is DEVICE memory owned by the caller, contiguous and row-major in
@@ -77,7 +80,14 @@ extern "C" {
 /* Same typedef as HIP's own header, so both may be included together. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
+
+/* Bytes of one token's record in an FP8 (DSA_FP8_E4M3) k or v cache with
+ * `heads` kv heads of `dim` entries: bytes [0, heads*dim) are the E4M3 codes,
+ * head g at g*dim; then `heads` little-endian fp32 scales, head g's at
+ * heads*dim + 4*g; then zero padding to a multiple of 16 bytes.  Records of a
+ * sequence are contiguous: token s of sequence b at (b*n_k + s) * record. */
+#define DSA_FP8_KV_RECORD_BYTES(heads, dim) ((((heads) * (dim) + 4 * (heads)) + 15) / 16 * 16)
 
 typedef enum {
     DSA_OK = 0,
@@ -142,10 +152,11 @@ typedef struct {
     int32_t attn_dtype;       /* DSA_F32 or DSA_BF16, for q and out */
     int32_t kv_dtype;         /* dtype of k and v: attn_dtype, or DSA_FP8_E4M3 when attn_dtype is DSA_BF16 */
     const void *q;            /* [B, n_q, Hq, d_qk] */
-    const void *k;            /* [B, n_k, Hkv, d_qk] */
-    const void *v;            /* [B, n_k, Hkv, d_v], NULL when kv_latent */
-    const float *k_scale;     /* [B, n_k, Hkv] fp32 scale of each k row (FP8 cache only, else NULL) */
-    const float *v_scale;     /* [B, n_k, Hkv] fp32 scale of each v row (FP8 cache without kv_latent, else NULL) */
+    const void *k;            /* [B, n_k, Hkv, d_qk]; FP8: [B, n_k] records of DSA_FP8_KV_RECORD_BYTES(Hkv, d_qk) */
+    const void *v;            /* [B, n_k, Hkv, d_v]; FP8: [B, n_k] records of DSA_FP8_KV_RECORD_BYTES(Hkv, d_v);
+                                 NULL when kv_latent */
+    const float *k_scale;     /* reserved: must be NULL (FP8 scales live in the k records) */
+    const float *v_scale;     /* reserved: must be NULL (FP8 scales live in the v records) */
     float softmax_scale;      /* > 0, e.g. 1/sqrt(d_qk) */
 
     int32_t top_k;            /* k, 1..8192 */

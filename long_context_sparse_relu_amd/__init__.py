@@ -25,7 +25,7 @@ OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE = 0, -1, -2, -3, -4
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE_ATTN = 0, 1, 2, 3, 4, 5
 ATTN_AUTO, ATTN_GATHER, ATTN_MASKED = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
@@ -167,8 +167,13 @@ def _contig(name, t, device, dtypes=None):
     return t
 
 
+def fp8_kv_record_bytes(heads: int, dim: int) -> int:
+    """Bytes of one token's record in an FP8 k or v cache (DSA_FP8_KV_RECORD_BYTES)."""
+    return (heads * dim + 4 * heads + 15) // 16 * 16
+
+
 def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik_scale=None,
-                 q_pos=None, softmax_scale=None, latent_dv=None, k_scale=None, v_scale=None,
+                 q_pos=None, softmax_scale=None, latent_dv=None, kv_heads=None, d_v=None,
                  attn_mode: int = ATTN_AUTO, sink_tokens: int = 0, local_window: int = 0) -> DSAProblem:
     """Describe one batch: see include/dsa.h for the layouts.
 
@@ -176,11 +181,13 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     iq_scale [B,n_q] / ik_scale [B,n_k] fp32 for FP8, iw [B,n_q,H] fp32,
     q [B,n_q,Hq,dqk], k [B,n_k,Hkv,dqk], v [B,n_k,Hkv,dv] or None with
     latent_dv (then the value is k[..., :latent_dv] and Hkv must be 1),
-    q_pos [B,n_q] int32 or None.  k and v have q's dtype, or float8_e4m3fn
-    (an FP8 cache, q bf16) with k_scale [B,n_k,Hkv] and, unless latent,
-    v_scale [B,n_k,Hkv] fp32.  attn_mode: ATTN_AUTO, ATTN_GATHER or ATTN_MASKED.
-    sink_tokens / local_window: the backbone's forced keys (the first sink_tokens
-    and last local_window visible keys), kept besides the top_k best between them.
+    q_pos [B,n_q] int32 or None.  k and v have q's dtype, or are an FP8 cache
+    (q bf16): uint8 token records [B,n_k,fp8_kv_record_bytes(Hkv, dqk)] for k
+    and [B,n_k,fp8_kv_record_bytes(Hkv, dv)] for v (codes, then the scales),
+    with kv_heads = Hkv and, unless latent, d_v given.  attn_mode: ATTN_AUTO,
+    ATTN_GATHER or ATTN_MASKED.  sink_tokens / local_window: the backbone's
+    forced keys (the first sink_tokens and last local_window visible keys),
+    kept besides the top_k best between them.
     """
     device = iq.device
     idt = (torch.float32, torch.bfloat16, torch.float8_e4m3fn)
@@ -217,40 +224,48 @@ def make_problem(*, iq, ik, iw, top_k, q=None, k=None, v=None, iq_scale=None, ik
     if q is not None:
         adt = (torch.float32, torch.bfloat16)
         q = _contig("q", q, device, adt)
-        kvt = (q.dtype, torch.float8_e4m3fn) if q.dtype == torch.bfloat16 else (q.dtype,)
-        k = _contig("k", k, device, kvt)
+        if q.dim() != 4 or q.shape[:2] != (B, n_q):
+            raise ValueError(f"q must be [B,n_q,Hq,dqk], got {tuple(q.shape)}")
+        Hq, dqk = q.shape[2], q.shape[3]
+        fp8 = k is not None and k.dtype == torch.uint8
+        if fp8:
+            if q.dtype != torch.bfloat16:
+                raise TypeError("an FP8 KV cache goes with bf16 q")
+            if kv_heads is None:
+                raise ValueError("an FP8 KV cache (uint8 token records) needs kv_heads")
+            Hkv = int(kv_heads)
+            k = _contig("k", k, device, (torch.uint8,))
+            if k.shape != (B, n_k, fp8_kv_record_bytes(Hkv, dqk)):
+                raise ValueError(f"k records must be [B,n_k,{fp8_kv_record_bytes(Hkv, dqk)}], got {tuple(k.shape)}")
+        else:
+            k = _contig("k", k, device, (q.dtype,))
+            if k.dim() != 4 or k.shape[:2] != (B, n_k) or k.shape[3] != dqk:
+                raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}")
+            Hkv = k.shape[2]
         v = _contig("v", v, device, (k.dtype,))
-        k_scale = _contig("k_scale", k_scale, device, (torch.float32,))
-        v_scale = _contig("v_scale", v_scale, device, (torch.float32,))
-        if q.dim() != 4 or k.dim() != 4:
-            raise ValueError("q must be [B,n_q,Hq,dqk] and k [B,n_k,Hkv,dqk]")
-        if q.shape[:2] != (B, n_q) or k.shape[:2] != (B, n_k) or k.shape[3] != q.shape[3]:
-            raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}")
-        Hq, dqk, Hkv = q.shape[2], q.shape[3], k.shape[2]
         if v is None:
             if latent_dv is None:
                 raise ValueError("v is None: pass latent_dv for latent key/value rows")
             dv, latent = int(latent_dv), 1
+        elif fp8:
+            if d_v is None:
+                raise ValueError("FP8 value records need d_v")
+            dv, latent = int(d_v), 0
+            if v.shape != (B, n_k, fp8_kv_record_bytes(Hkv, dv)):
+                raise ValueError(f"v records must be [B,n_k,{fp8_kv_record_bytes(Hkv, dv)}], got {tuple(v.shape)}")
         else:
             if v.dim() != 4 or v.shape[:3] != (B, n_k, Hkv):
                 raise ValueError(f"v must be [B,n_k,Hkv,dv], got {tuple(v.shape)}")
             dv, latent = v.shape[3], 0
-        if k.dtype == torch.float8_e4m3fn:
-            if k_scale is None or (not latent and v_scale is None):
-                raise ValueError("an FP8 KV cache needs k_scale (and v_scale unless latent)")
-            if k_scale.shape != (B, n_k, Hkv) or (v_scale is not None and v_scale.shape != (B, n_k, Hkv)):
-                raise ValueError("k_scale and v_scale must be [B,n_k,Hkv]")
-        elif k_scale is not None or v_scale is not None:
-            raise ValueError("k_scale / v_scale are for an FP8 (float8_e4m3fn) KV cache only")
         p.q_heads, p.kv_heads, p.d_qk, p.d_v, p.kv_latent = Hq, Hkv, dqk, dv, latent
         p.attn_dtype = _DTYPE_CODE[q.dtype]
-        p.kv_dtype = _DTYPE_CODE[k.dtype]
+        p.kv_dtype = FP8_E4M3 if fp8 else _DTYPE_CODE[k.dtype]
         p.q, p.k = q.data_ptr(), k.data_ptr()
         p.v = None if v is None else v.data_ptr()
-        p.k_scale = None if k_scale is None else k_scale.data_ptr()
-        p.v_scale = None if v_scale is None else v_scale.data_ptr()
+        p.k_scale = None
+        p.v_scale = None
         p.softmax_scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(dqk)
-        tensors.update(q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale)
+        tensors.update(q=q, k=k, v=v)
     return DSAProblem(p, tensors, device)
 
 

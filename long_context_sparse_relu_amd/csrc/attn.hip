@@ -46,8 +46,14 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
     const int pos = row_pos(a.q_pos, row, a.n_q, a.n_k);
     const int tid = threadIdx.x;
     const int dqk = a.dqk, dv = a.dv;
-    const size_t kv_row_stride = static_cast<size_t>(a.Hkv) * dqk;    // k row (all kv heads)
-    const size_t v_row_stride = static_cast<size_t>(a.Hkv) * dv;
+    // elements per token of k and v (all kv heads); an E4M3 cache's token
+    // records hold the codes first, then the scales, and may be padded
+    const size_t kv_row_stride = KDT == E4M3 ? static_cast<size_t>(a.k_rec) : static_cast<size_t>(a.Hkv) * dqk;
+    const size_t v_row_stride = KDT == E4M3 ? static_cast<size_t>(a.v_rec) : static_cast<size_t>(a.Hkv) * dv;
+    auto rec_scale = [&](const void* base, size_t r, size_t stride, int dim, int head) {
+        return *reinterpret_cast<const float*>(static_cast<const unsigned char*>(base) + r * stride +
+                                               static_cast<size_t>(a.Hkv) * dim + 4 * head);
+    };
 
     for (int i = tid; i < kGenHC * dqk; i += blockDim.x) {
         int h = i / dqk, d = i % dqk;
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
             if (s >= 0) {
                 const size_t r = static_cast<size_t>(b) * a.n_k + s;
                 val = load_as_f32<KDT>(a.k, r * kv_row_stride + g * dqk + d);
-                if constexpr (KDT == E4M3) val *= a.k_scale[r * a.Hkv + g];
+                if constexpr (KDT == E4M3) val *= rec_scale(a.k, r, kv_row_stride, dqk, g);
             }
             k_s[i] = val;
         }
@@ -85,10 +91,10 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
                 const size_t r = static_cast<size_t>(b) * a.n_k + s;
                 if (a.latent) {
                     val = load_as_f32<KDT>(a.k, r * kv_row_stride + d);
-                    if constexpr (KDT == E4M3) val *= a.k_scale[r];
+                    if constexpr (KDT == E4M3) val *= rec_scale(a.k, r, kv_row_stride, dqk, 0);
                 } else {
                     val = load_as_f32<KDT>(a.v, r * v_row_stride + g * dv + d);
-                    if constexpr (KDT == E4M3) val *= a.v_scale[r * a.Hkv + g];
+                    if constexpr (KDT == E4M3) val *= rec_scale(a.v, r, v_row_stride, dv, g);
                 }
             }
             v_s[i] = val;
@@ -178,6 +184,10 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 #ifndef DSA_ATTN_DEPTH
 #define DSA_ATTN_DEPTH 1
 #endif
+// (an E4M3 block carries half the bytes of a bf16 one)
+#ifndef DSA_ATTN_DEPTH8
+#define DSA_ATTN_DEPTH8 DSA_ATTN_DEPTH
+#endif
 #ifndef DSA_ATTN_WAVES
 #define DSA_ATTN_WAVES 8
 #endif
@@ -226,9 +236,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     // One workgroup per (kv head, row, slice).  Consecutive workgroup ids go to
     // the 8 XCDs in turn; when the (row, slice) units divide by 8, the ids are
     // mapped so that the kv heads of one unit land on the same XCD, back to
-    // back: they gather the same tokens, and the row scales of an E4M3 cache
-    // (one 16-byte group per token for 4 kv heads) are then read into that
-    // XCD's L2 once instead of once per kv head.
+    // back: they gather the same tokens, and the scales of an E4M3 cache's
+    // token record (one 16-byte group after the codes of its 4 kv heads) are
+    // then read into that XCD's L2 once instead of once per kv head.
     int g, unit;
     {
         const int id = blockIdx.x;
@@ -279,12 +289,15 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
     // this lane's 32 dims of kv head g within each 128-dim row: E4M3 bytes
     // [32kg, 32kg + 32); bf16 elements 8kg..8kg+8 of each 32-dim group (the
     // loads add 64 bytes per group)
+    // (an E4M3 cache: token records of codes then scales; kv head g's scale
+    // sits 4g bytes past the Hkv * 128 code bytes)
     constexpr int ESZ = KV8 ? 1 : 2;
-    const size_t row_bytes = static_cast<size_t>(a.Hkv) * 128 * ESZ;
-    const size_t base_off = static_cast<size_t>(b) * a.n_k * row_bytes + g * 128 * ESZ + (KV8 ? kg * 32 : kg * 16);
-    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + base_off;
-    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + base_off;
-    const size_t sc_base = static_cast<size_t>(b) * a.n_k * a.Hkv + g;
+    const size_t k_bytes = KV8 ? static_cast<size_t>(a.k_rec) : static_cast<size_t>(a.Hkv) * 128 * ESZ;
+    const size_t v_bytes = KV8 ? static_cast<size_t>(a.v_rec) : k_bytes;
+    const size_t lane_off = g * 128 * ESZ + (KV8 ? kg * 32 : kg * 16);
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + static_cast<size_t>(b) * a.n_k * k_bytes;
+    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + static_cast<size_t>(b) * a.n_k * v_bytes;
+    const size_t sc_off = static_cast<size_t>(a.Hkv) * 128 + 4 * g;
 
     float m_run = -__builtin_inff();
     float l_part = 0.0f;
@@ -321,15 +334,16 @@ __global__ __launch_bounds__(kGqaWaves * 64) void k_attn_bf16_d128(AttnArgs a, i
         // that the wait counts agree on every path into the loop
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (KV8) {
-            const v4i* ks = reinterpret_cast<const v4i*>(kbase + sr * row_bytes);
-            const v4i* vs = reinterpret_cast<const v4i*>(vbase + sr * row_bytes);
-            const float* kq = a.k_scale + sc_base + sr * a.Hkv;
-            const float* vq = a.v_scale + sc_base + sr * a.Hkv;
+            const unsigned char* kr = kbase + sr * k_bytes;
+            const unsigned char* vr = vbase + sr * v_bytes;
+            const v4i* ks = reinterpret_cast<const v4i*>(kr + lane_off);
+            const v4i* vs = reinterpret_cast<const v4i*>(vr + lane_off);
             d.k[0] = ks[0]; d.k[1] = ks[1]; d.v[0] = vs[0]; d.v[1] = vs[1];
-            d.ks = *kq; d.vs = *vq;
+            d.ks = *reinterpret_cast<const float*>(kr + sc_off);
+            d.vs = *reinterpret_cast<const float*>(vr + sc_off);
         } else {
-            const unsigned char* ks = kbase + sr * row_bytes;
-            const unsigned char* vs = vbase + sr * row_bytes;
+            const unsigned char* ks = kbase + sr * k_bytes + lane_off;
+            const unsigned char* vs = vbase + sr * v_bytes + lane_off;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 d.k[c] = *reinterpret_cast<const v8bf*>(ks + 64 * c);
@@ -530,7 +544,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
             const int nr = a.rows - r0 < chunk ? a.rows - r0 : chunk;
             const dim3 grid(static_cast<unsigned>(per_row * nr));
             if (a.kv_dtype == E4M3)
-                hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, true>), grid, dim3(kGqaWaves * 64), idx_lds,
+                hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH8, true>), grid, dim3(kGqaWaves * 64), idx_lds,
                                    st, a, r0, nr, s, len, part);
             else
                 hipLaunchKernelGGL((k_attn_bf16_d128<DSA_ATTN_DEPTH, false>), grid, dim3(kGqaWaves * 64), idx_lds,

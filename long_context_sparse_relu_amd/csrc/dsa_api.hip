@@ -133,8 +133,9 @@ dsa_status_t check_attn(const dsa_problem_t* p) {
     if (p->kv_dtype == DSA_FP8_E4M3) {
         if (p->attn_dtype != DSA_BF16)
             return fail(DSA_E_UNSUPPORTED, "an FP8 KV cache needs attn_dtype DSA_BF16");
-        if (!p->k_scale || (!p->kv_latent && !p->v_scale))
-            return fail(DSA_E_INVALID, "an FP8 KV cache needs k_scale (and v_scale unless kv_latent)");
+        if (p->k_scale || p->v_scale)
+            return fail(DSA_E_INVALID, "k_scale and v_scale are reserved (NULL): an FP8 cache keeps its scales "
+                                       "in its token records");
     } else if (p->kv_dtype != p->attn_dtype) {
         return fail(DSA_E_INVALID, "kv_dtype (%d) must equal attn_dtype (%d) or be DSA_FP8_E4M3",
                     p->kv_dtype, p->attn_dtype);
@@ -197,8 +198,10 @@ dsa::AttnArgs attn_args(const dsa_problem_t* p, const int32_t* idx, void* out, f
     a.Hq = p->q_heads; a.Hkv = p->kv_heads; a.dqk = p->d_qk; a.dv = p->d_v;
     a.latent = p->kv_latent ? 1 : 0; a.dtype = p->attn_dtype; a.kv_dtype = p->kv_dtype;
     a.q = p->q; a.k = p->k; a.v = p->v; a.idx = idx; a.q_pos = p->q_pos;
-    a.k_scale = p->kv_dtype == DSA_FP8_E4M3 ? p->k_scale : nullptr;
-    a.v_scale = p->kv_dtype == DSA_FP8_E4M3 && !p->kv_latent ? p->v_scale : nullptr;
+    if (p->kv_dtype == DSA_FP8_E4M3) {
+        a.k_rec = DSA_FP8_KV_RECORD_BYTES(p->kv_heads, p->d_qk);
+        a.v_rec = p->kv_latent ? 0 : DSA_FP8_KV_RECORD_BYTES(p->kv_heads, p->d_v);
+    }
     a.scale = p->softmax_scale; a.out = out; a.lse = lse;
     a.mode = p->attn_mode; a.all_visible = false;
     return a;

@@ -100,10 +100,9 @@ struct AttnArgs {
     int Hq, Hkv, dqk, dv, latent, dtype;
     int kv_dtype;          // dtype of k and v: dtype, or E4M3 (then dtype is BF16)
     const void* q;
-    const void* k;
-    const void* v;
-    const float* k_scale;  // [rows of k, Hkv] per-row scales of an E4M3 cache, else null
-    const float* v_scale;  // the same for v (null for latent rows, which use k_scale)
+    const void* k;         // E4M3: token records of k_rec bytes (codes of every kv head, then their scales)
+    const void* v;         // E4M3: token records of v_rec bytes (latent rows: none, values use k's)
+    int k_rec, v_rec;      // E4M3 record bytes (DSA_FP8_KV_RECORD_BYTES), else 0
     const int32_t* idx;    // [rows, kk]
     const int32_t* q_pos;
     float scale;

@@ -62,6 +62,34 @@ def test_struct_layout_matches_header(tmp_path):
     assert int(got["sizeof"]) == ctypes.sizeof(dsa.Problem)
 
 
+def test_fp8_kv_record_layout(tmp_path):
+    """The header's record size macro, the binding's and the input packer agree:
+    each token's codes, then its per-head fp32 scales, then zeros to 16 bytes."""
+    import torch
+    from dsa_inputs import pack_fp8_kv_records
+    cases = [(4, 128), (1, 576), (1, 512), (2, 64), (3, 128), (8, 128)]
+    src = tmp_path / "rec.c"
+    body = "\n".join(f'    printf("%d\\n", DSA_FP8_KV_RECORD_BYTES({h}, {d}));' for h, d in cases)
+    src.write_text("#include <stdio.h>\n#include \"dsa.h\"\nint main(void){\n" + body + "\n    return 0;\n}\n")
+    exe = tmp_path / "rec"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    for (h, d), n in zip(cases, got):
+        assert n == dsa.fp8_kv_record_bytes(h, d)
+        assert n % 16 == 0 and h * d + 4 * h <= n < h * d + 4 * h + 16
+    g = torch.Generator().manual_seed(5)
+    codes = (torch.randn((2, 3, 3, 8), generator=g) * 4).to(torch.float8_e4m3fn)
+    scale = torch.rand((2, 3, 3), generator=g) + 0.5
+    rec = pack_fp8_kv_records(codes, scale)
+    assert rec.shape == (2, 3, dsa.fp8_kv_record_bytes(3, 8)) and rec.dtype == torch.uint8
+    for b in range(2):
+        for s in range(3):
+            r = rec[b, s]
+            assert torch.equal(r[:24], codes[b, s].reshape(-1).view(torch.uint8))
+            assert torch.equal(r[24:36].view(torch.float32), scale[b, s])
+            assert torch.all(r[36:] == 0)
+
+
 def _problem(**over):
     p = dsa.Problem()
     p.batch, p.n_q, p.n_k = 2, 1, 4096
@@ -99,10 +127,9 @@ FAKE = ctypes.c_void_p(0x7F0000000000)
     (dict(d_qk=1024), dsa.E_UNSUPPORTED),
     (dict(attn_dtype=dsa.FP8_E4M3), dsa.E_UNSUPPORTED),
     (dict(kv_dtype=dsa.F32), dsa.E_INVALID),         # neither attn_dtype nor FP8
-    (dict(kv_dtype=dsa.FP8_E4M3), dsa.E_INVALID),    # FP8 cache without scales
-    (dict(kv_dtype=dsa.FP8_E4M3, k_scale=0x7F0000000000), dsa.E_INVALID),   # no v_scale
-    (dict(kv_dtype=dsa.FP8_E4M3, attn_dtype=dsa.F32, k_scale=0x7F0000000000,
-          v_scale=0x7F0000000000), dsa.E_UNSUPPORTED),                        # FP8 cache needs bf16 q
+    (dict(kv_dtype=dsa.FP8_E4M3, k_scale=0x7F0000000000), dsa.E_INVALID),   # scales live in the records
+    (dict(kv_dtype=dsa.FP8_E4M3, v_scale=0x7F0000000000), dsa.E_INVALID),
+    (dict(kv_dtype=dsa.FP8_E4M3, attn_dtype=dsa.F32), dsa.E_UNSUPPORTED),   # FP8 cache needs bf16 q
     (dict(attn_mode=3), dsa.E_INVALID),
     (dict(sink_tokens=-1), dsa.E_INVALID),
     (dict(local_window=-5), dsa.E_INVALID),

@@ -17,7 +17,7 @@ import torch
 
 import long_context_sparse_relu_amd as dsa
 import oracle
-from dsa_inputs import custom_spec, make_inputs, oracle_view, spec
+from dsa_inputs import custom_spec, kv_args, make_inputs, oracle_view, pack_fp8_kv_records, spec
 from parity import check_attn, check_backbone_row, check_scores, check_topk_row
 
 pytestmark = pytest.mark.gpu
@@ -26,11 +26,9 @@ DEV = torch.device("cuda", 0)
 
 def _problem_kwargs(inp):
     return dict(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=inp["top_k"], q=inp["q"],
-                k=inp["k"], v=inp["v"], iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"],
-                softmax_scale=inp["scale"], latent_dv=inp["latent_dv"],
-                k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"),
+                iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"], softmax_scale=inp["scale"],
                 sink_tokens=inp.get("sinks", 0), local_window=inp.get("window", 0),
-                attn_mode=inp.get("attn_mode", dsa.ATTN_AUTO))
+                attn_mode=inp.get("attn_mode", dsa.ATTN_AUTO), **kv_args(inp))
 
 
 def _problem(inp, row_sel=None):
@@ -113,7 +111,7 @@ def run_case(inp, seqs, rows, fused="prefill", check_e2e=True, unfused=True):
                                   ("iq", "iw", "q", "k", "ik", "pos")},
                         "v": None if inp["v"] is None else inp["v"][b:b + 1],
                         **{n: None if inp.get(n) is None else inp[n][b:b + 1]
-                           for n in ("iq_scale", "ik_scale", "k_scale", "v_scale")}},
+                           for n in ("iq_scale", "ik_scale", "k_scale", "v_scale", "k_rec", "v_rec")}},
                        row_sel=rows)
         if unfused:
             g_sc = scores[b][rows].cpu().numpy()
@@ -604,6 +602,7 @@ def test_fp8kv_scales_act_per_row():
     inp2 = dict(inp)
     inp2["v_scale"] = inp["v_scale"].clone()
     inp2["v_scale"][0, s] *= 64.0
+    inp2["v_rec"] = pack_fp8_kv_records(inp2["v"], inp2["v_scale"])
     out1, lse1 = dsa.sparse_attn(_problem(inp2), idx)
     torch.cuda.synchronize()
     assert torch.equal(lse0, lse1), "the value scale must not touch the softmax"
