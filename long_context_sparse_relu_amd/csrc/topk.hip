@@ -643,6 +643,362 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Rows of more than half the LDS limit (persistent, one workgroup per CU).
+// A row's scores arrive in LDS straight from memory (global_load_lds), and the
+// next row's are loaded while the current one finishes.  Per row:
+//   sample    every eighth key (key t + (8m + (t mod 8)) * 1024 for thread t,
+//             m < 4), up to 4096 scores; their finite range and a 2048-bin
+//             histogram of g(x) = (x - min) * 2048 / range;
+//   bracket   the bins d_hi >= d_lo holding the sample's r_hi-th and r_lo-th
+//             largest score, r = k * samples / visible keys -/+ 4 standard
+//             deviations (binomial) and 2;
+//   classify  every key by the same map g: g >= d_hi + 1 -> above (bitmap
+//             bit, one ballot per 64 keys), d_lo <= g < d_hi + 1 -> listed as
+//             (score, position) in its wave's LDS region, below -> dropped;
+//             the next row's chunks are loaded during it;
+//   select    if fewer than k keys are above and at least k are above or
+//             listed (which proves the bracket holds the k-th key), the k -
+//             above best listed keys: a 256-bin histogram of a second map
+//             linear over the bracket, and its threshold bin ranked exactly by
+//             (order key << 32 | ~position).
+// g and the second map never decrease as the score grows, so "above" keys beat
+// every listed key and listed keys beat every dropped one: the result is the
+// exact top k whatever the sample.  When the counts do not prove the bracket
+// (or a wave's region overflows) the row, still in LDS, is selected in full
+// there (select_lds_row_lin); a threshold bin too large to rank by comparison
+// is radix-selected from the list.
+// ---------------------------------------------------------------------------
+#ifndef DSA_TOPK_ROW_REG
+#define DSA_TOPK_ROW_REG 1
+#endif
+constexpr int kRegThreads = 1024;
+constexpr int kRegPer = kRowLdsMax / kRegThreads;   // 32 keys per thread
+constexpr int kRegRegion = 128;     // list entries per wave
+constexpr int kRegBins2 = 256;      // second-level bins over the bracket
+constexpr int kRegTieCap = (kTopkBins - kRegBins2) / 2;   // threshold-bin entries ranked (8-byte entries in lh past the bins)
+
+// The second-level digit of a listed score: linear over the bracket [lo2,
+// d_hi + 1) of the first map t = x * scale + off, clamped to the bins.
+__device__ __forceinline__ int reg_digit2(uint32_t bits, float scale, float off, float lo2, float scale2) {
+    const float t = fmaf(__uint_as_float(bits), scale, off);
+    return max(0, min(kRegBins2 - 1, static_cast<int>((t - lo2) * scale2)));
+}
+// The listed keys (wave regions of (score bits, position) pairs, wc1[w] in
+// region w) whose second-level digit is d2, as composites (order key << 32 |
+// ~position).
+struct RegTieSrc {
+    const uint32_t* lpair; const uint32_t* wc1; int region; int total;
+    float scale, off, lo2, scale2; int d2;
+    __device__ int size() const { return total; }
+    __device__ bool get(int i, uint64_t* out) const {
+        int w = 0;
+        while (i >= static_cast<int>(wc1[w])) { i -= static_cast<int>(wc1[w]); ++w; }
+        const uint32_t bits = lpair[2 * (w * region + i)];
+        const int pos = static_cast<int>(lpair[2 * (w * region + i) + 1]);
+        if (reg_digit2(bits, scale, off, lo2, scale2) != d2) return false;
+        *out = composite64(order_key(__uint_as_float(bits)), pos);
+        return true;
+    }
+};
+
+__global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
+    // (static: the compiler then knows that no other LDS array overlaps the
+    // loads in flight into keys and waits for them only where keys is read)
+    __shared__ __align__(16) uint32_t keys[kRowLdsMax];        // the row's scores
+    __shared__ __align__(16) uint32_t lh[kTopkBins];
+    __shared__ uint32_t bm[kRowLdsMax / 32];
+    constexpr int T = kRegThreads, P = kRegPer, NW = kRegThreads / 64;
+    __shared__ uint32_t lpair[NW * kRegRegion * 2];            // per wave: (score bits, position) pairs
+    __shared__ int fres[4];
+    __shared__ uint32_t wsum[NW + 2];
+    __shared__ float wmin[NW], wmax[NW];
+    __shared__ uint32_t wc0[NW], wc1[NW];
+    __shared__ uint32_t n_list;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float kNaN = __uint_as_float(0x7FC00000u);
+    // The thread index through an empty asm, taken afresh for each use:
+    // per-key positions are then recomputed where they are needed (one add
+    // each) instead of being kept alive or hoisted out of the row loop.
+    auto fresh_tid = [&]() {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+    // Row lrow's scores into keys[] (completion is awaited at the row's
+    // start): instruction u of wave w copies keys [u * T + 64 w, +64), lane l
+    // one key (positions past vis re-read the last visible score).  Each
+    // wave reads only these slices of keys[] (the sample and the classify
+    // below), so chunk u of the next row can follow as soon as the wave has
+    // classified chunk u of the current one.
+    auto load_chunk = [&](const float* sc, int vis, int u, int t0, int wbase) {
+        __builtin_amdgcn_global_load_lds(sc + min(t0 + u * T, vis - 1),
+                                         (__attribute__((address_space(3))) void*)(keys + u * T + wbase), 4, 0, 0);
+    };
+    auto prefetch = [&](int lrow, int vis) {
+        const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+        const int t0 = fresh_tid();
+        const int wbase = __builtin_amdgcn_readfirstlane(t0 & ~63);
+#pragma unroll
+        for (int u = 0; u < P; ++u) load_chunk(sc, vis, u, t0, wbase);
+    };
+    int lrow = blockIdx.x;
+    int vis = lrow < a.rows ? row_visible(a, a.row0 + lrow) : 0;
+    if (lrow < a.rows && vis > a.k) prefetch(lrow, vis);
+    for (; lrow < a.rows; lrow += gridDim.x) {
+        const int next = lrow + gridDim.x;
+        const int vis_next = next < a.rows ? row_visible(a, a.row0 + next) : 0;
+        const bool fetch_next = next < a.rows && vis_next > a.k;
+        int32_t* out = a.idx + static_cast<size_t>(lrow) * a.k;
+        const uint32_t k = static_cast<uint32_t>(a.k);
+        if (vis <= a.k) {
+            for (int j = tid; j < a.k; j += T) out[j] = j < vis ? j : -1;
+            if (fetch_next) prefetch(next, vis_next);
+            vis = vis_next;
+            continue;
+        }
+        // this row's scores have landed in keys[] (every wave's part)
+        __builtin_amdgcn_s_waitcnt(kWaitVmem);
+        lds_barrier();
+        // a key as ranked: absent (past vis) NaN, a backbone's forced keys -inf
+        auto key_at = [&](int i) {
+            const float y = __uint_as_float(keys[i]);
+            return i >= vis ? kNaN : (i < a.sinks || i >= vis - a.window) ? -__builtin_inff() : y;
+        };
+        const int nwords = (vis + 31) >> 5;
+
+        // sample: key t + (8m + (t & 7)) * T of thread t
+        float smp[4];
+        float smin = __builtin_inff(), smax = -__builtin_inff();
+        uint32_t ns_w = 0;
+        {
+            const int tr = fresh_tid();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = tr + (8 * m + (tr & 7)) * T;
+                const bool pres = i < vis;
+                const float sv = key_at(min(i, kRowLdsMax - 1));
+                smp[m] = pres ? sv : kNaN;
+                ns_w += static_cast<uint32_t>(__popcll(__ballot(pres)));
+                if (pres && sv > -__builtin_inff()) smin = fminf(smin, sv);
+                if (pres) smax = fmaxf(smax, sv);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            smin = fminf(smin, __shfl_xor(smin, o));
+            smax = fmaxf(smax, __shfl_xor(smax, o));
+        }
+        if (lane == 0) { wmin[wave] = smin; wmax[wave] = smax; wc0[wave] = ns_w; }
+        for (int i = tid; i < kTopkBins; i += T) lh[i] = 0u;
+        if (tid == 0) n_list = 0;
+        lds_barrier();
+        uint32_t ns = 0;
+        for (int w = 0; w < NW; ++w) { smin = fminf(smin, wmin[w]); smax = fmaxf(smax, wmax[w]); ns += wc0[w]; }
+        const float scale = static_cast<float>(kTopkBins) / (smax - smin);
+        const float off = -smin * scale;
+        // block-uniform: the sampled path holds (else the whole-row select)
+        bool fast = smax > smin && scale > 0.0f && scale < __builtin_inff();
+        int d_hi = kTopkBins - 1, d_lo = 0;
+        uint32_t above_all = 0, listed = 0;
+        const bool classified = fast;          // the classify (and the next row's loads) ran
+        if (fast) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (smp[m] == smp[m]) {
+                    const float t = fmaf(smp[m], scale, off);
+                    atomicAdd(&lh[max(0, min(kTopkBins - 1, static_cast<int>(t)))], 1u);
+                }
+            lds_barrier();
+            // bracket
+            const float ks = static_cast<float>(k) * static_cast<float>(ns) / static_cast<float>(vis);
+            const float sd = sqrtf(ks);
+            const int r_hi = static_cast<int>(floorf(ks - 4.0f * sd - 2.0f));
+            const int r_lo = static_cast<int>(ceilf(ks + 4.0f * sd + 2.0f));
+            float th = __builtin_inff(), tl = -__builtin_inff();
+            if (wave == 0)
+                wave_find_bins<kTopkBins>(lh, static_cast<uint32_t>(max(r_hi, 1)),
+                                          static_cast<uint32_t>(min(r_lo, static_cast<int>(ns))), fres);
+            lds_barrier();
+            if (r_hi >= 1) {
+                d_hi = fres[0];
+                th = static_cast<float>(d_hi + 1);
+            }
+            if (r_lo <= static_cast<int>(ns)) {
+                d_lo = fres[2];
+                if (d_lo > 0) tl = static_cast<float>(d_lo);
+            }
+            // classify: lane 2u (2u + 1) of bw gathers the low (high) bitmap
+            // word of this wave's 64 keys of chunk u
+            uint32_t n_above = 0, cnt = 0;
+            int bw = 0;
+            const int tc = fresh_tid();
+            uint32_t* lreg = lpair + 2 * (tc >> 6) * kRegRegion;   // this wave's region
+            const float* nsc = a.scores + static_cast<size_t>(fetch_next ? next : lrow) * a.n_k;
+            const int wbase = __builtin_amdgcn_readfirstlane(tc & ~63);
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                if (u * T < vis) {
+                    // (chunks holding no absent or forced key skip those tests)
+                    float xv;
+                    if (u * T >= a.sinks && (u + 1) * T <= vis - a.window)
+                        xv = __uint_as_float(keys[tc + u * T]);
+                    else
+                        xv = key_at(tc + u * T);
+                    const float t = fmaf(xv, scale, off);
+                    const bool ab = t >= th;
+                    const bool tk = t >= tl && !ab;
+                    const uint64_t above = __ballot(ab);
+                    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(bw) : "s"(static_cast<uint32_t>(above)), "n"(2 * u));
+                    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(bw) : "s"(static_cast<uint32_t>(above >> 32)), "n"(2 * u + 1));
+                    n_above += static_cast<uint32_t>(__popcll(above));
+                    const uint64_t take = __ballot(tk);
+                    if (take) {
+                        if (tk) {
+                            // (past the region's end every entry lands on its last slot;
+                            // the count then exceeds the region and the row takes the
+                            // fallback, so those entries are never read)
+                            const uint32_t slot = min(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(take >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(take), cnt)),
+                                                      static_cast<uint32_t>(kRegRegion - 1));
+                            lreg[2 * slot] = __float_as_uint(xv);
+                            lreg[2 * slot + 1] = static_cast<uint32_t>(tc + u * T);
+                        }
+                        cnt += static_cast<uint32_t>(__popcll(take));
+                    }
+                }
+                // this wave is done with its slice of chunk u (the scores above
+                // were used, so their reads have completed): the next row's
+                // chunk u follows
+                if (fetch_next) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_chunk(nsc, vis_next, u, tc, wbase);
+                }
+            }
+            {
+                const int nchunk = (vis + T - 1) / T;
+                if (lane < 2 * nchunk) bm[(lane >> 1) * (T / 32) + 2 * (tc >> 6) + (lane & 1)] = static_cast<uint32_t>(bw);
+            }
+            if (lane == 0) { wc0[wave] = n_above; wc1[wave] = cnt; }
+            lds_barrier();
+            // the waves' counts, one per lane, summed across the wave
+            uint32_t c0 = lane < NW ? wc0[lane] : 0u, c1 = lane < NW ? wc1[lane] : 0u;
+            uint32_t ovf = c1 > static_cast<uint32_t>(kRegRegion) ? 1u : 0u;
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) {
+                c0 += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c0), o));
+                c1 += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c1), o));
+                ovf |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(ovf), o));
+            }
+            above_all = __builtin_amdgcn_readfirstlane(c0);
+            listed = __builtin_amdgcn_readfirstlane(c1);
+            fast = !__builtin_amdgcn_readfirstlane(ovf) && above_all <= k && above_all + listed >= k;
+        }
+        if (!fast) {
+            // the whole row selected in LDS; if the classify ran, the next row's
+            // loads have replaced it: they complete, the row is loaded again,
+            // and the next row follows once more after the select
+            if (classified && fetch_next) {
+                __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                lds_barrier();
+                prefetch(lrow, vis);
+                __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                lds_barrier();
+            }
+            float rmin = __builtin_inff(), rmax = -__builtin_inff();
+            {
+                const int tf = fresh_tid();
+                for (int u = 0; u < P; ++u) {
+                    const int i = tf + u * T;
+                    if (i < vis) {
+                        const float xv = key_at(i);
+                        if (xv != __uint_as_float(keys[i])) keys[i] = __float_as_uint(xv);   // forced keys
+                        if (xv > -__builtin_inff()) rmin = fminf(rmin, xv);
+                        rmax = fmaxf(rmax, xv);
+                    }
+                }
+            }
+            for (int i = tid; i < nwords; i += T) bm[i] = 0u;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                rmin = fminf(rmin, __shfl_xor(rmin, o));
+                rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+            }
+            __syncthreads();                  // every thread has read the sample's range
+            if (lane == 0) { wmin[wave] = rmin; wmax[wave] = rmax; }
+            if (tid == 0) n_list = 0;
+            __syncthreads();
+            for (int w = 0; w < NW; ++w) { rmin = fminf(rmin, wmin[w]); rmax = fmaxf(rmax, wmax[w]); }
+            select_lds_row_lin(a, keys, vis, rmin, rmax, lh, bm, wsum, &n_list, out);
+            __syncthreads();                  // every wave is done with keys[]
+            if (fetch_next) prefetch(next, vis_next);
+            vis = vis_next;
+            continue;
+        }
+        if (above_all < k) {
+            // the k - above best listed keys; second map linear over [d_lo, d_hi + 1)
+            const uint32_t k_rem = k - above_all;
+            const float lo2 = static_cast<float>(d_lo);
+            const float scale2 = static_cast<float>(kRegBins2) / (static_cast<float>(d_hi + 1) - lo2);
+            auto digit2 = [&](uint32_t bits) { return reg_digit2(bits, scale, off, lo2, scale2); };
+            // (the arrays indexed directly, not through pointers, so the
+            // compiler sees that they do not overlap the loads in flight)
+            const int lb = 2 * wave * kRegRegion;
+            const int mine = static_cast<int>(wc1[wave]);     // this wave's region
+            for (int i = tid; i < kRegBins2; i += T) lh[i] = 0u;
+            lds_barrier();
+            for (int j = lane; j < mine; j += 64) lds_add(&lh[digit2(lpair[lb + 2 * j])], 1u);
+            lds_barrier();
+            if (wave == 0) wave_find_bins<kRegBins2>(lh, k_rem, k_rem, fres);
+            lds_barrier();
+            const int d2 = fres[0];
+            const uint32_t gt2 = static_cast<uint32_t>(fres[1]);
+            // the threshold bin's keys: (order key, ~position) word pairs in lh past the bins
+            constexpr int TB = kRegBins2;
+            for (int j = lane; j < mine; j += 64) {
+                const uint32_t bits = lpair[lb + 2 * j];
+                const int pos = static_cast<int>(lpair[lb + 2 * j + 1]);
+                const int d = digit2(bits);
+                if (d > d2) {
+                    lds_or(&bm[pos >> 5], 1u << (pos & 31));
+                } else if (d == d2) {
+                    const uint32_t sl = lds_add_rtn(&n_list, 1u);
+                    if (sl < static_cast<uint32_t>(kRegTieCap)) {
+                        lh[TB + 2 * sl] = order_key(__uint_as_float(bits));
+                        lh[TB + 2 * sl + 1] = ~static_cast<uint32_t>(pos);
+                    }
+                }
+            }
+            lds_barrier();
+            const uint32_t n_t = n_list;
+            const uint32_t k_t = k_rem - gt2;
+            if (n_t > static_cast<uint32_t>(kRegTieCap)) {
+                // a mass of nearly equal scores in the threshold bin: its listed
+                // keys radix-selected (on the composite bits that vary among them)
+                RegTieSrc src{lpair, wc1, kRegRegion, static_cast<int>(listed), scale, off, lo2, scale2, d2};
+                Sink tsink{bm, nullptr, &n_list, k_t};
+                radix_select_spread(src, k_t, lh, wsum, tsink);
+            } else {
+                for (uint32_t j = tid; j < n_t; j += T) {
+                    const uint64_t c = (static_cast<uint64_t>(lh[TB + 2 * j]) << 32) | lh[TB + 2 * j + 1];
+                    uint32_t beat = 0;
+                    for (uint32_t q = 0; q < n_t; ++q)
+                        beat += ((static_cast<uint64_t>(lh[TB + 2 * q]) << 32) | lh[TB + 2 * q + 1]) > c ? 1u : 0u;
+                    if (beat < k_t) {
+                        const int pos = static_cast<int>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
+                        lds_or(&bm[pos >> 5], 1u << (pos & 31));
+                    }
+                }
+            }
+            lds_barrier();                    // every thread has read n_list; the bits are set
+        }
+        Sink sink{bm, nullptr, &n_list, k};
+        write_ordered(sink, nwords, 1, a.k, out, wsum);
+        lds_barrier();                        // the next row reuses the LDS
+        vis = vis_next;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Rows of scores in memory much longer than k (prefill rows past a few
 // thousand keys; dsa_topk over many such rows).  One workgroup per row:
 //   sample  kRcSample order keys of the row -- runs of 16 consecutive keys
@@ -898,13 +1254,15 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     // the early row blocks of a long one) are selected from LDS
     if (vis_max <= kRowLdsMax) {
         if (vis_max > kRowLdsMax / 2) {
-            const void* fn = reinterpret_cast<const void*>(k_topk_row_lds_next);
-            const size_t smem = static_cast<size_t>(kRowLdsMax) * sizeof(uint32_t);
+            const void* fn = DSA_TOPK_ROW_REG ? reinterpret_cast<const void*>(k_topk_row_reg)
+                                              : reinterpret_cast<const void*>(k_topk_row_lds_next);
+            // (the register select holds its row buffer in static LDS)
+            const size_t smem = DSA_TOPK_ROW_REG ? 0 : static_cast<size_t>(kRowLdsMax) * sizeof(uint32_t);
             if ((e = allow_dyn_lds(fn, smem)) != hipSuccess) return e;
             // workgroups the chip holds at once (one per CU at this LDS size)
             static const int per_cu = [fn] {
                 int nb = 0;
-                return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kRowThreads, smem) == hipSuccess && nb > 0
+                return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, DSA_TOPK_ROW_REG ? kRegThreads : kRowThreads, smem) == hipSuccess && nb > 0
                     ? nb : 1;
             }();
             int dev = 0, cus = 0;
@@ -912,7 +1270,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
             if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
             const long long slots = static_cast<long long>(per_cu) * (cus > 0 ? cus : 1);
             const dim3 grid(static_cast<unsigned>(a.rows < slots ? a.rows : slots));
-            hipLaunchKernelGGL(k_topk_row_lds_next, grid, dim3(kRowThreads), smem, st, a);
+            if (DSA_TOPK_ROW_REG)
+                hipLaunchKernelGGL(k_topk_row_reg, grid, dim3(kRegThreads), smem, st, a);
+            else
+                hipLaunchKernelGGL(k_topk_row_lds_next, grid, dim3(kRowThreads), smem, st, a);
             return hipGetLastError();
         }
         const size_t smem = static_cast<size_t>(vis_max) * sizeof(uint32_t);

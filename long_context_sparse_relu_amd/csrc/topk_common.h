@@ -9,6 +9,41 @@
 namespace dsa {
 
 constexpr int kBitmapMaxKeys = 1 << 18;   // rows up to this long are ordered through a bitmap
+// s_waitcnt immediate that waits for every outstanding vector memory access
+// of the wave (vmcnt = 0, the other counters unconstrained).
+constexpr int kWaitVmem = 0x0F70;
+
+// Workgroup barrier for LDS data: the wave's LDS accesses complete
+// (lgkmcnt = 0), then s_barrier.  Unlike __syncthreads it does not wait for
+// the wave's global loads, which may stay in flight across it (including
+// loads straight into LDS, whose target the caller must not touch until it
+// has waited for them).  Global stores made before it are not ordered for
+// other waves.  The helpers below use it: they share only LDS data.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS atomics issued as plain instructions, for kernels that keep loads into
+// LDS in flight: the compiler cannot tell an atomic's target from the loads'
+// and would otherwise wait for all of them before it.  The caller's next
+// lds_barrier completes them; lds_add_rtn waits for its own result.
+__device__ __forceinline__ uint32_t lds_addr(const uint32_t* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint32_t*)p));
+}
+__device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
+    asm volatile("ds_add_u32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_or(uint32_t* p, uint32_t v) {
+    asm volatile("ds_or_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_add_rtn(uint32_t* p, uint32_t v) {
+    uint32_t old;
+    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(lds_addr(p)), "v"(v) : "memory");
+    return old;
+}
 
 // Block-wide search of the threshold bin: the digit d with
 //   count(bins > d) < k_rem <= count(bins >= d).
@@ -32,7 +67,7 @@ __device__ inline void find_threshold_bin(const uint32_t* hist, int nbins, uint3
         if (lane >= o) x += y;
     }
     if (lane == 63) wsum[wave] = x;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0;
     for (int w = 0; w < wave; ++w) before += wsum[w];
     const uint32_t excl = before + x - local;
@@ -44,10 +79,54 @@ __device__ inline void find_threshold_bin(const uint32_t* hist, int nbins, uint3
             run += h;
         }
     }
-    __syncthreads();
+    lds_barrier();
     *digit = static_cast<int>(wsum[nwaves]);
     *gt = wsum[nwaves + 1];
-    __syncthreads();
+    lds_barrier();
+}
+
+// The same search by one wave, for two ranks at once: for r = r1 and r = r2
+// the bin d with count(bins > d) < r <= count(bins >= d), written to LDS as
+// res = {d1, count above d1, d2, count above d2}.  Lane l holds the NB / 64
+// bins from NB - 1 - (NB / 64) l downwards (the top bins in lane 0).  Call
+// from one wave; the caller's barrier publishes res.  Requires
+// 1 <= r <= sum(hist) for both ranks.
+template <int NB>
+__device__ __forceinline__ void wave_find_bins(const uint32_t* hist, uint32_t r1, uint32_t r2, int* res) {
+    constexpr int PER = NB / 64;
+    const int lane = threadIdx.x & 63;
+    const int top = NB - 1 - lane * PER;
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) local += hist[top - j];
+    uint32_t x = local;                          // inclusive scan from the top lane
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    const uint32_t excl = x - local;
+    // the lane holding rank r; then its PER bins, one per lane, scanned again
+    auto find = [&](uint32_t r, int slot) {
+        const uint64_t hit = __ballot(excl < r && x >= r);
+        const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        const uint32_t base = static_cast<uint32_t>(__shfl(static_cast<int>(excl), src));
+        const int btop = NB - 1 - src * PER;
+        const uint32_t h = lane < PER ? hist[btop - lane] : 0u;
+        uint32_t y = h;
+#pragma unroll
+        for (int o = 1; o < PER; o <<= 1) {
+            const uint32_t z = __shfl_up(y, o);
+            if (lane >= o) y += z;
+        }
+        const uint32_t before = base + y - h;
+        if (lane < PER && before < r && before + h >= r) {
+            res[slot] = btop - lane;
+            res[slot + 1] = static_cast<int>(before);
+        }
+    };
+    find(r1, 0);
+    find(r2, 2);
 }
 
 // Block-wide exclusive scan of one value per thread (wave scans, then the
@@ -62,14 +141,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
         if (lane >= o) x += y;
     }
     if (lane == 63) wsum[wave] = x;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0, all = 0;
     for (int w = 0; w < nwaves; ++w) {
         uint32_t t = wsum[w];
         if (w < wave) before += t;
         all += t;
     }
-    __syncthreads();
+    lds_barrier();
     *total = all;
     return before + x - v;
 }
@@ -251,25 +330,25 @@ __device__ void radix_select(const Src& src, uint32_t k_rem, const int* shifts, 
         const int nb = 1 << w;
         const int top = sh + w;
         for (int i = threadIdx.x; i < nb; i += blockDim.x) lh[i] = 0u;
-        __syncthreads();
+        lds_barrier();
         for_each_candidate(src, [&](uint64_t c) {
             const bool hit = top >= 64 || (c >> top) == prefix;
             const uint32_t bin = static_cast<uint32_t>((c >> sh) & (nb - 1));
             if constexpr (AGG) lds_count(lh, hit, bin);
             else if (hit) atomicAdd(&lh[bin], 1u);
         });
-        __syncthreads();
+        lds_barrier();
         int d; uint32_t gt;
         find_threshold_bin(lh, nb, k_rem, wsum, &d, &gt);
         k_rem -= gt;
         prefix = (top >= 64 ? 0ull : (prefix << w)) | static_cast<uint64_t>(d);
         done_shift = sh;
         bool done = lh[d] == k_rem;
-        __syncthreads();
+        lds_barrier();
         if (done) break;
     }
     for_each_candidate(src, [&](uint64_t c) { sink.put_if((c >> done_shift) >= prefix, c); });
-    __syncthreads();
+    lds_barrier();
 }
 
 // radix_select over full 64-bit composites whose digits start below the
@@ -290,13 +369,13 @@ __device__ void radix_select_spread(const Src& src, uint32_t k, uint32_t* lh, ui
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     uint64_t* red = reinterpret_cast<uint64_t*>(lh);        // lh is free until the select
     if (lane == 0) { red[2 * wave] = lo; red[2 * wave + 1] = hi; }
-    __syncthreads();
+    lds_barrier();
     for (int w = 0; w < nwaves; ++w) {
         const uint64_t l2 = red[2 * w], h2 = red[2 * w + 1];
         lo = l2 < lo ? l2 : lo;
         hi = h2 > hi ? h2 : hi;
     }
-    __syncthreads();
+    lds_barrier();
     const uint64_t diff = lo ^ hi;
     const int bits = diff ? 64 - __clzll(static_cast<long long>(diff)) : 1;   // the bits that vary
     int shifts[6], widths[6], np = 0;
@@ -321,9 +400,9 @@ __device__ inline uint32_t lower_bound_rth(const uint32_t* skey, int m, uint32_t
     const int bits = range ? 32 - __clz(static_cast<int>(range)) : 0;
     const int sh1 = bits > 11 ? bits - 11 : 0;
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int j = threadIdx.x; j < m; j += blockDim.x) atomicAdd(&lh[(skey[j] - kmin) >> sh1], 1u);
-    __syncthreads();
+    lds_barrier();
     int d0; uint32_t gt0;
     find_threshold_bin(lh, kTopkBins, r, wsum, &d0, &gt0);
     uint32_t k_low = kmin + (static_cast<uint32_t>(d0) << sh1);
@@ -331,12 +410,12 @@ __device__ inline uint32_t lower_bound_rth(const uint32_t* skey, int m, uint32_t
         const int sh2 = sh1 > 11 ? sh1 - 11 : 0;
         const uint32_t mask2 = (1u << (sh1 - sh2)) - 1u;
         for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-        __syncthreads();
+        lds_barrier();
         for (int j = threadIdx.x; j < m; j += blockDim.x) {
             const uint32_t rel = skey[j] - kmin;
             if (static_cast<int>(rel >> sh1) == d0) atomicAdd(&lh[(rel >> sh2) & mask2], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         int d1; uint32_t gt1;
         find_threshold_bin(lh, kTopkBins, r - gt0, wsum, &d1, &gt1);
         k_low += static_cast<uint32_t>(d1) << sh2;
@@ -379,7 +458,7 @@ __device__ inline void write_ordered(const Sink& sink, int nwords, int kpad, int
                 int32_t x = sorted[lo], y = sorted[hi];
                 if ((x > y) == asc) { sorted[lo] = y; sorted[hi] = x; }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
     for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = sorted[j];

@@ -33,9 +33,6 @@ constexpr int kSFinishThreads = 1024;
 // that falls back is recomputed by all of them, a slice of at least
 // kFinishSliceKeys keys each, up to kFinishPartsMax workgroups.
 constexpr int kFinishSliceKeys = 16384;
-// s_waitcnt immediate that waits for every outstanding vector memory access
-// of the wave (vmcnt = 0, the other counters unconstrained).
-constexpr int kWaitVmem = 0x0F70;
 constexpr int kFinishPartsMax = 64;
 static int finish_parts(int n_k) {
     const int p = (n_k + kFinishSliceKeys - 1) / kFinishSliceKeys;

@@ -409,6 +409,46 @@ def test_topk_long_rows_many_per_workgroup(sinks, window, n_k):
     assert not bad, f"rows {bad[:5]} differ (of {len(bad)})"
 
 
+@pytest.mark.parametrize("k,window", [(2048, 0), (8192, 0), (2048, 12000)])
+def test_topk_sampled_bracket_rows(k, window):
+    """dsa_topk over rows of 16K-32K keys, the register-resident select that
+    brackets the k-th score from a sample of every eighth key.  Rows cycle
+    through: Gaussian scores; rows barely longer than k (the bracket's lower
+    end leaves the sample); a few planted needles far above the rest; scores
+    rounded to 2^-6 (long runs of exact ties inside the bracket); and, with a
+    local window, most keys forced to -inf.  Every row must equal the oracle's
+    selection exactly (ties to the lower position)."""
+    n_q, n_k = 240, 32768
+    sp = custom_spec(name="bracket", n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=k,
+                     q_heads=2, kv_heads=1, d_qk=64, d_v=64, attn_dtype="bf16", window=window)
+    inp = make_inputs(sp, device=DEV, seed=53)
+    g = torch.Generator().manual_seed(53)
+    pos = torch.randint(16384, n_k, (1, n_q), generator=g, dtype=torch.int32)
+    kind = torch.arange(n_q) % 4
+    short = (kind == 1)
+    pos[0, short] = torch.clamp(k + window + torch.randint(1, 200, (int(short.sum()),), generator=g,
+                                                             dtype=torch.int32), max=n_k - 1)
+    pos[0, -1] = n_k - 1
+    sc = torch.randn((n_q, n_k), generator=g)
+    nd = torch.randint(0, n_k, (n_q, 8), generator=g)
+    needles = (kind == 2).unsqueeze(1).expand(n_q, 8)
+    sc[torch.arange(n_q).unsqueeze(1).expand(n_q, 8)[needles], nd[needles]] = 50.0
+    sc[kind == 3] = torch.round(sc[kind == 3] * 64.0) / 64.0
+    scores = sc.unsqueeze(0).float()
+    prob = dsa.make_problem(**_problem_kwargs(inp), q_pos=pos.to(DEV))
+    idx = dsa.topk(prob, scores.to(DEV))
+    torch.cuda.synchronize()
+    s_np = sc.double().numpy()
+    p_np = pos[0].numpy().astype(np.int64)
+    if window:
+        o_idx, _ = oracle.select_backbone(s_np, k, 0, window, p_np)
+    else:
+        o_idx, _ = oracle.topk(s_np, k, p_np)
+    g_idx = idx[0].cpu().numpy()
+    bad = [r for r in range(n_q) if not np.array_equal(g_idx[r], o_idx[r])]
+    assert not bad, f"rows {bad[:5]} (kinds {[int(kind[r]) for r in bad[:5]]}) differ (of {len(bad)})"
+
+
 @pytest.mark.parametrize("n_k", [12000, 24000])
 def test_topk_lds_rows_with_skewed_scores(n_k):
     """dsa_topk over rows selected in LDS (12000 keys: one row per workgroup;
