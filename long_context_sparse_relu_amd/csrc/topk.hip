@@ -671,6 +671,10 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
 #ifndef DSA_TOPK_ROW_REG
 #define DSA_TOPK_ROW_REG 1
 #endif
+// launches whose longest row exceeds this many keys take k_topk_row_reg
+#ifndef DSA_TOPK_ROW_REG_MIN
+#define DSA_TOPK_ROW_REG_MIN (kRowLdsMax / 2)
+#endif
 constexpr int kRegThreads = 1024;
 constexpr int kRegPer = kRowLdsMax / kRegThreads;   // 32 keys per thread
 constexpr int kRegRegion = 128;     // list entries per wave
@@ -1253,7 +1257,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     // rows of at most kRowLdsMax visible keys (all rows of a short prefill,
     // the early row blocks of a long one) are selected from LDS
     if (vis_max <= kRowLdsMax) {
-        if (vis_max > kRowLdsMax / 2) {
+        if (vis_max > (DSA_TOPK_ROW_REG ? DSA_TOPK_ROW_REG_MIN : kRowLdsMax / 2)) {
             const void* fn = DSA_TOPK_ROW_REG ? reinterpret_cast<const void*>(k_topk_row_reg)
                                               : reinterpret_cast<const void*>(k_topk_row_lds_next);
             // (the register select holds its row buffer in static LDS)
