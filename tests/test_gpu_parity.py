@@ -415,16 +415,19 @@ def test_topk_sampled_bracket_rows(k, window):
     brackets the k-th score from a sample of every eighth key.  Rows cycle
     through: Gaussian scores; rows barely longer than k (the bracket's lower
     end leaves the sample); a few planted needles far above the rest; scores
-    rounded to 2^-6 (long runs of exact ties inside the bracket); and, with a
-    local window, most keys forced to -inf.  Every row must equal the oracle's
-    selection exactly (ties to the lower position)."""
-    n_q, n_k = 240, 32768
+    rounded to 2^-6 (long runs of exact ties inside the bracket); and 3k/4
+    distinct keys above 1000 keys tied exactly at the k-th score, everything
+    else far below (the tied block fills one second-level bin, too many to
+    rank by comparison).  With a local window most keys are also forced to
+    -inf.  Every row must equal the oracle's selection exactly (ties to the
+    lower position)."""
+    n_q, n_k = 250, 32768
     sp = custom_spec(name="bracket", n_q=n_q, n_k=n_k, idx_heads=4, idx_dtype="bf16", top_k=k,
                      q_heads=2, kv_heads=1, d_qk=64, d_v=64, attn_dtype="bf16", window=window)
     inp = make_inputs(sp, device=DEV, seed=53)
     g = torch.Generator().manual_seed(53)
     pos = torch.randint(16384, n_k, (1, n_q), generator=g, dtype=torch.int32)
-    kind = torch.arange(n_q) % 4
+    kind = torch.arange(n_q) % 5
     short = (kind == 1)
     pos[0, short] = torch.clamp(k + window + torch.randint(1, 200, (int(short.sum()),), generator=g,
                                                              dtype=torch.int32), max=n_k - 1)
@@ -434,6 +437,13 @@ def test_topk_sampled_bracket_rows(k, window):
     needles = (kind == 2).unsqueeze(1).expand(n_q, 8)
     sc[torch.arange(n_q).unsqueeze(1).expand(n_q, 8)[needles], nd[needles]] = 50.0
     sc[kind == 3] = torch.round(sc[kind == 3] * 64.0) / 64.0
+    n_above, n_tie = 3 * k // 4, 1000
+    for r in torch.nonzero(kind == 4).flatten().tolist():
+        ranked_end = int(pos[0, r]) + 1 - window          # keys past it are the forced window
+        sel = torch.randperm(ranked_end, generator=g)[:n_above + n_tie]
+        sc[r] = torch.randn(n_k, generator=g) - 6.0
+        sc[r, sel[:n_above]] = 1.5 + 0.5 * torch.rand(n_above, generator=g)
+        sc[r, sel[n_above:]] = 1.0
     scores = sc.unsqueeze(0).float()
     prob = dsa.make_problem(**_problem_kwargs(inp), q_pos=pos.to(DEV))
     idx = dsa.topk(prob, scores.to(DEV))
