@@ -612,14 +612,15 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
 // RG groups of 16 query rows with every head's operand in registers (16
 // heads x 8 registers per group); per head and 16 keys one
 // v_mfma_scale_f32_16x16x128_f8f6f4 gives that head's 16 x 16 dot products,
-// lane l holding queries 4(l/16)..4(l/16)+3 of key l%16.  Each lane folds its
+// lane l holding queries 4(l/16)..4(l/16)+3 of one key (column l%16 of key
+// block u is key 4(l%16) + u of the 64-key tile).  Each lane folds its
 // four products with ReLU and the head weight (one integer max and one FMA
 // each) into four running sums, so the sum over heads needs no exchange
 // between lanes and the only vector work per product is those two
 // instructions.  The waves of a workgroup share each 64-key tile staged in
 // LDS.  The head weights times the query scales sit in LDS ([head][query])
-// and are read as one 16-byte broadcast per head and group.  Work split and
-// stores as in k_index_tiled.
+// and are read as one 16-byte broadcast per head and group.  Work split as
+// in k_index_tiled; a lane stores four consecutive keys of a query at once.
 // ---------------------------------------------------------------------------
 #ifndef DSA_Q16_RG
 #define DSA_Q16_RG 1
@@ -634,7 +635,7 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
     constexpr int KSTR = 144;                                // padded LDS stride of a 128-byte key row
     constexpr int PIECES = 64 * 128 / 16 / (kQ16W * 64);     // 16-byte pieces of a key tile per thread
     __shared__ __align__(16) uint8_t k_s[2][64 * KSTR];      // double-buffered key tile
-    __shared__ float ks_s[2][64];
+    __shared__ float ks_s[2][kQ16W * 64];                    // key scales (entries 64.. are never read)
     __shared__ __align__(16) float w_s[16 * kQ16Q];          // [head][query]: w * sq (0 past H or nrows)
 
     const int lane = threadIdx.x & 63;
@@ -705,31 +706,12 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
             return;
         }
 
-        // operands: head h of row r0[g] + col (zero for a missing row or a head
-        // past H); loads issued unconditionally from a valid row
-        v8i a[RG][16];
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int arow = t_first + (nlive[g] > 0 ? r0[g] + min(col, nlive[g] - 1) : 0);
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                a[g][h] = load_split32(static_cast<const uint8_t*>(x.iq) + (static_cast<size_t>(arow) * H + min(h, H - 1)) * 128, kg);
-        }
-        // weights of the block's rows, times their query scales
-        for (int e = tid; e < 16 * kQ16Q; e += kQ16W * 64) {
-            const int h = e / kQ16Q, q = e % kQ16Q;
-            const int lr = qb * kQ16Q + q;
-            const int row = t_first + min(lr, nrows - 1);
-            const float wv = x.iw[static_cast<size_t>(row) * H + min(h, H - 1)] * x.iq_scale[row];
-            w_s[e] = (lr < nrows && h < H) ? wv : 0.0f;
-        }
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                if (!(col < nlive[g] && h < H)) a[g][h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
-        // tile loads: PIECES 16-byte pieces per thread, clamped to the last key
+        // Tile loads: PIECES 16-byte pieces per thread, clamped to the last key.
+        // Key r of a tile goes to LDS row 16 (r % 4) + r / 4, so that the MFMA
+        // column c of key block u (LDS row 16 u + c) is key 4 c + u: each lane
+        // then holds four consecutive keys of its queries and stores them with
+        // one 16-byte store.
         v4i pre[PIECES];
         float pre_s = 0.0f;
         auto fetch = [&](int k0) {
@@ -744,17 +726,22 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
 #pragma unroll
             for (int p = 0; p < PIECES; ++p) {
                 const int e = tid + p * kQ16W * 64, kr = e >> 3, off = (e & 7) * 16;
-                *reinterpret_cast<v4i*>(k_s[nb] + kr * KSTR + off) = pre[p];
+                *reinterpret_cast<v4i*>(k_s[nb] + (16 * (kr & 3) + (kr >> 2)) * KSTR + off) = pre[p];
             }
-            if (tid < 64) ks_s[nb][tid] = pre_s;
+            // every thread writes (threads past the tile's 64 keys to unread
+            // entries), so the scale load is never moved to a branch of its own
+            ks_s[nb][tid < 64 ? 16 * (tid & 3) + (tid >> 2) : tid] = pre_s;
         };
 
         // scores of the previous tile, stored while the next is scored (16 per
-        // group and lane, issued after the next tile's loads)
+        // group and lane: held[g][4u + i] is query 4 kg + i, key 4 col + u;
+        // issued after the next tile's loads)
         float held[RG][16];
-        uint32_t hbase = kNoStore;                           // (k0 + col) * 4 of the held tile
+        uint32_t hbase = kNoStore;                           // (k0 + 4 col) * 4 of the held tile
         uint32_t hmask[RG];                                  // bit 4u + i: store held[g][4u + i]
         bool hall = false;                                   // uniform: store every held value
+        // whole 16-byte stores need 16-byte aligned rows
+        const bool vec_rows = (n_k & 3) == 0 && (reinterpret_cast<uintptr_t>(x.scores) & 15) == 0;
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
             hmask[g] = 0u;
@@ -766,17 +753,17 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
             for (int g = 0; g < RG; ++g) {
                 if (hall) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[g][4 * u + i]), orsrc[g],
-                                                                  static_cast<int>(roff[i] + hbase + 64u * u), 0, 0);
+                    for (int i = 0; i < 4; ++i) {
+                        const v4i q4 = {__float_as_int(held[g][i]), __float_as_int(held[g][4 + i]),
+                                        __float_as_int(held[g][8 + i]), __float_as_int(held[g][12 + i])};
+                        __builtin_amdgcn_raw_buffer_store_b128(q4, orsrc[g], static_cast<int>(roff[i] + hbase), 0, 0);
+                    }
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const uint32_t off = (hmask[g] >> (4 * u + i) & 1u) ? roff[i] + hbase + 64u * u : kNoStore;
+                            const uint32_t off = (hmask[g] >> (4 * u + i) & 1u) ? roff[i] + hbase + 4u * u : kNoStore;
                             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[g][4 * u + i]), orsrc[g],
                                                                   static_cast<int>(off), 0, 0);
                         }
@@ -785,13 +772,53 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
         };
 
         fetch(c0);
+        // The prologue's loads (the block's head weights and query scales, the
+        // query operands, the first key tile) are all issued before any of them
+        // is waited for, so the prologue costs one memory round trip.
+        // Weights: entry e = tid + i * threads of the [head][query] table.
+        constexpr int WPT = 16 * kQ16Q / (kQ16W * 64);
+        static_assert(16 * kQ16Q % (kQ16W * 64) == 0, "whole weight entries per thread");
+        float wl[WPT], sl[WPT];
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int e = tid + i * kQ16W * 64, h = e / kQ16Q, q = e % kQ16Q;
+            const int row = t_first + min(qb * kQ16Q + q, nrows - 1);
+            wl[i] = x.iw[static_cast<size_t>(row) * H + min(h, H - 1)];
+            sl[i] = x.iq_scale[row];
+        }
+        // operands: head h of row r0[g] + col, loaded unconditionally from a
+        // valid row.  A missing row's operand is never zeroed: its scores lie
+        // past the end of the group's store resource and are dropped.  A head
+        // past H repeats head H - 1 with weight 0, so it adds nothing (a NaN
+        // code there is already in head H - 1's own term).
+        v8i a[RG][16];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int arow = t_first + (nlive[g] > 0 ? r0[g] + min(col, nlive[g] - 1) : 0);
+#pragma unroll
+            for (int h = 0; h < 16; ++h)
+                a[g][h] = load_split32(static_cast<const uint8_t*>(x.iq) + (static_cast<size_t>(arow) * H + min(h, H - 1)) * 128, kg);
+        }
+        __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first wait
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int e = tid + i * kQ16W * 64, h = e / kQ16Q, q = e % kQ16Q;
+            w_s[e] = (qb * kQ16Q + q < nrows && h < H) ? wl[i] * sl[i] : 0.0f;
+        }
         stage(0);
-        __builtin_amdgcn_s_waitcnt(0);                       // prologue loads (operands, weights) landed
-        __syncthreads();
+        // The staged tile and weights are visible after this barrier, which
+        // waits for LDS only: the query operands may still be in flight, and
+        // the first tile's products wait for each one as they reach it (the
+        // first tile stores nothing before its products, so those waits count
+        // loads only).
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         int cur = 0;
-        for (int k0 = c0; k0 < cvis; k0 += 64) {
+        auto score_tile = [&](const int k0, auto first_tag) {
             fetch(min(k0 + 64, cvis - 1));                   // in flight while this tile is scored
-            flush();
+            if constexpr (!decltype(first_tag)::value) flush();
             if (k0 <= wmax) {                                // uniform: some row of the wave sees the tile
                 v8i bk[4];
                 float sk[4];
@@ -845,11 +872,12 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
                     dcur = dnext;
                 }
                 const bool fast = k0 + 63 < c1 && k0 + 63 <= wmin;   // uniform: every key of every row
-                hbase = static_cast<uint32_t>(k0 + col) * 4u;
-                hall = fast;
+                hbase = static_cast<uint32_t>(k0 + 4 * col) * 4u;
+                hall = fast && vec_rows;
 #pragma unroll
                 for (int g = 0; g < RG; ++g) {
                     if (fast) {
+                        hmask[g] = 0xFFFFu;                  // for rows not 16-byte aligned
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -860,7 +888,7 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
                         for (int u = 0; u < 4; ++u)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const int sidx = k0 + 16 * u + col;
+                                const int sidx = k0 + 4 * col + u;
                                 const bool vis = sidx <= pos[g][i];
                                 held[g][4 * u + i] = vis ? acc[g][4 * u + i] * sk[u] : -__builtin_inff();
                                 hmask[g] |= (sidx < c1 && (vis || write_future)) ? 1u << (4 * u + i) : 0u;
@@ -868,7 +896,7 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
                     }
                 }
             } else {                                         // no row of the wave sees the tile
-                hbase = static_cast<uint32_t>(k0 + col) * 4u;
+                hbase = static_cast<uint32_t>(k0 + 4 * col) * 4u;
                 hall = false;
 #pragma unroll
                 for (int g = 0; g < RG; ++g) {
@@ -878,7 +906,7 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             held[g][4 * u + i] = -__builtin_inff();
-                            hmask[g] |= (write_future && k0 + 16 * u + col < c1) ? 1u << (4 * u + i) : 0u;
+                            hmask[g] |= (write_future && k0 + 4 * col + u < c1) ? 1u << (4 * u + i) : 0u;
                         }
                 }
             }
@@ -886,7 +914,9 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
             stage(cur ^ 1);
             __syncthreads();
             cur ^= 1;
-        }
+        };
+        score_tile(c0, std::true_type{});                    // c0 < cvis here
+        for (int k0 = c0 + 64; k0 < cvis; k0 += 64) score_tile(k0, std::false_type{});
         flush();
         if (write_future) store_inf(cvis);                   // keys of this segment no query of the block sees
     };
