@@ -730,20 +730,26 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
     };
     // Row lrow's scores into keys[] (completion is awaited at the row's
     // start): instruction u of wave w copies keys [u * T + 64 w, +64), lane l
-    // one key (positions past vis re-read the last visible score).  Each
-    // wave reads only these slices of keys[] (the sample and the classify
-    // below), so chunk u of the next row can follow as soon as the wave has
-    // classified chunk u of the current one.
-    auto load_chunk = [&](const float* sc, int vis, int u, int t0, int wbase) {
-        __builtin_amdgcn_global_load_lds(sc + min(t0 + u * T, vis - 1),
-                                         (__attribute__((address_space(3))) void*)(keys + u * T + wbase), 4, 0, 0);
+    // one key, through a buffer resource over the row's visible scores (a
+    // position past vis reads 0 and is never used; the thread's offset is
+    // fixed and the chunk's is a scalar, so a chunk costs no address
+    // arithmetic).  Each wave reads only these slices of keys[] (the sample
+    // and the classify below), so chunk u of the next row can follow as soon
+    // as the wave has classified chunk u of the current one.
+    auto row_rsrc = [&](int lr, int vis) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.scores + static_cast<size_t>(lr) * a.n_k), 0,
+                                                 vis * 4, kBufferWord3);
+    };
+    auto load_chunk = [&](__amdgpu_buffer_rsrc_t rs, int u, int t0, int wbase) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(keys + u * T + wbase), 4,
+                                                 static_cast<uint32_t>(t0) * 4u, static_cast<uint32_t>(u * T) * 4u, 0, 0);
     };
     auto prefetch = [&](int lrow, int vis) {
-        const float* sc = a.scores + static_cast<size_t>(lrow) * a.n_k;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(lrow, vis);
         const int t0 = fresh_tid();
         const int wbase = __builtin_amdgcn_readfirstlane(t0 & ~63);
 #pragma unroll
-        for (int u = 0; u < P; ++u) load_chunk(sc, vis, u, t0, wbase);
+        for (int u = 0; u < P; ++u) load_chunk(rs, u, t0, wbase);
     };
     int lrow = blockIdx.x;
     int vis = lrow < a.rows ? row_visible(a, a.row0 + lrow) : 0;
@@ -787,11 +793,8 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
                 if (pres) smax = fmaxf(smax, sv);
             }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            smin = fminf(smin, __shfl_xor(smin, o));
-            smax = fmaxf(smax, __shfl_xor(smax, o));
-        }
+        smin = wave_allmin(smin);
+        smax = wave_allmax(smax);
         if (lane == 0) { wmin[wave] = smin; wmax[wave] = smax; wc0[wave] = ns_w; }
         for (int i = tid; i < kTopkBins; i += T) lh[i] = 0u;
         if (tid == 0) n_list = 0;
@@ -837,27 +840,34 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
             int bw = 0;
             const int tc = fresh_tid();
             uint32_t* lreg = lpair + 2 * (tc >> 6) * kRegRegion;   // this wave's region
-            const float* nsc = a.scores + static_cast<size_t>(fetch_next ? next : lrow) * a.n_k;
+            const __amdgpu_buffer_rsrc_t nrs = row_rsrc(fetch_next ? next : lrow, fetch_next ? vis_next : vis);
             const int wbase = __builtin_amdgcn_readfirstlane(tc & ~63);
+            // each chunk's score is read one chunk ahead, so its LDS latency
+            // overlaps the classify of the chunk before (the slots it reads
+            // are not the ones that chunk's next-row load replaces)
+            uint32_t ynext = keys[tc];
 #pragma unroll
             for (int u = 0; u < P; ++u) {
+                const uint32_t y = ynext;
+                if (u + 1 < P && (u + 1) * T < vis) ynext = keys[tc + (u + 1) * T];
                 if (u * T < vis) {
                     // (chunks holding no absent or forced key skip those tests)
-                    float xv;
-                    if (u * T >= a.sinks && (u + 1) * T <= vis - a.window)
-                        xv = __uint_as_float(keys[tc + u * T]);
-                    else
-                        xv = key_at(tc + u * T);
+                    float xv = __uint_as_float(y);
+                    if (!(u * T >= a.sinks && (u + 1) * T <= vis - a.window)) {
+                        const int i = tc + u * T;
+                        xv = i >= vis ? kNaN : (i < a.sinks || i >= vis - a.window) ? -__builtin_inff() : xv;
+                    }
+                    // (the ballots take the compares' lane masks directly)
                     const float t = fmaf(xv, scale, off);
                     const bool ab = t >= th;
-                    const bool tk = t >= tl && !ab;
-                    const uint64_t above = __ballot(ab);
+                    const bool ge = t >= tl;
+                    const uint64_t above = __builtin_amdgcn_ballot_w64(ab);
                     asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(bw) : "s"(static_cast<uint32_t>(above)), "n"(2 * u));
                     asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(bw) : "s"(static_cast<uint32_t>(above >> 32)), "n"(2 * u + 1));
                     n_above += static_cast<uint32_t>(__popcll(above));
-                    const uint64_t take = __ballot(tk);
+                    const uint64_t take = __builtin_amdgcn_ballot_w64(ge) & ~above;
                     if (take) {
-                        if (tk) {
+                        if (ge && !ab) {
                             // (past the region's end every entry lands on its last slot;
                             // the count then exceeds the region and the row takes the
                             // fallback, so those entries are never read)
@@ -875,7 +885,7 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
                 // chunk u follows
                 if (fetch_next) {
                     __builtin_amdgcn_sched_barrier(0);
-                    load_chunk(nsc, vis_next, u, tc, wbase);
+                    load_chunk(nrs, u, tc, wbase);
                 }
             }
             {
@@ -887,12 +897,10 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
             // the waves' counts, one per lane, summed across the wave
             uint32_t c0 = lane < NW ? wc0[lane] : 0u, c1 = lane < NW ? wc1[lane] : 0u;
             uint32_t ovf = c1 > static_cast<uint32_t>(kRegRegion) ? 1u : 0u;
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) {
-                c0 += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c0), o));
-                c1 += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c1), o));
-                ovf |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(ovf), o));
-            }
+            const auto add = [](uint32_t x, uint32_t y) { return x + y; };
+            c0 = wave_allreduce(c0, add);
+            c1 = wave_allreduce(c1, add);
+            ovf = wave_allreduce(ovf, [](uint32_t x, uint32_t y) { return x | y; });
             above_all = __builtin_amdgcn_readfirstlane(c0);
             listed = __builtin_amdgcn_readfirstlane(c1);
             fast = !__builtin_amdgcn_readfirstlane(ovf) && above_all <= k && above_all + listed >= k;

@@ -26,6 +26,49 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// x combined over the whole wave on the VALU: lanes l and l^1, then l^2
+// (quad permutations), then the two halves of each 8-lane group and of each
+// 16-lane row (mirrors), all by DPP, then rows 2r and 2r+1 and the two halves
+// of the wave by v_permlane16/32_swap.  Each step pairs every lane with one
+// lane of the other group, so any commutative and associative op works (sum,
+// min, max, or); every lane gets the result.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t x, Op op) {
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xF, 0xF, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = op(r16[0], r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return op(r32[0], r32[1]);
+}
+__device__ __forceinline__ float wave_allmin(float x) {
+    return __uint_as_float(wave_allreduce(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+__device__ __forceinline__ float wave_allmax(float x) {
+    return __uint_as_float(wave_allreduce(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+
+// Inclusive prefix sum over the wave's lanes on the VALU: lanes l - 1, l - 2,
+// l - 4, l - 8 of the same 16-lane row by DPP row shifts (a lane shifted in
+// from outside the row adds 0), which scans each row; then the last lane of
+// row 0 (of row 2) is broadcast into row 1 (row 3) and the last lane of row 1
+// into rows 2 and 3 (DPP row broadcasts, the other rows left unchanged).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xA, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xC, 0xF, false));
+    return x;
+}
+
 // LDS atomics issued as plain instructions, for kernels that keep loads into
 // LDS in flight: the compiler cannot tell an atomic's target from the loads'
 // and would otherwise wait for all of them before it.  The caller's next
@@ -60,12 +103,7 @@ __device__ inline void find_threshold_bin(const uint32_t* hist, int nbins, uint3
     const int top = nbins - 1 - tid * per;      // this thread's bins: top, top-1, ...
     uint32_t local = 0;
     for (int j = 0; j < per; ++j) local += hist[top - j];
-    uint32_t x = local;                          // inclusive scan inside the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(local);   // inclusive scan inside the wave
     if (lane == 63) wsum[wave] = x;
     lds_barrier();
     uint32_t before = 0;
@@ -99,12 +137,7 @@ __device__ __forceinline__ void wave_find_bins(const uint32_t* hist, uint32_t r1
     uint32_t local = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) local += hist[top - j];
-    uint32_t x = local;                          // inclusive scan from the top lane
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(local);   // inclusive scan from the top lane
     const uint32_t excl = x - local;
     // the lane holding rank r; then its PER bins, one per lane, scanned again
     auto find = [&](uint32_t r, int slot) {
@@ -113,12 +146,7 @@ __device__ __forceinline__ void wave_find_bins(const uint32_t* hist, uint32_t r1
         const uint32_t base = static_cast<uint32_t>(__shfl(static_cast<int>(excl), src));
         const int btop = NB - 1 - src * PER;
         const uint32_t h = lane < PER ? hist[btop - lane] : 0u;
-        uint32_t y = h;
-#pragma unroll
-        for (int o = 1; o < PER; o <<= 1) {
-            const uint32_t z = __shfl_up(y, o);
-            if (lane >= o) y += z;
-        }
+        const uint32_t y = wave_inclusive_sum(h);
         const uint32_t before = base + y - h;
         if (lane < PER && before < r && before + h >= r) {
             res[slot] = btop - lane;
@@ -134,12 +162,7 @@ __device__ __forceinline__ void wave_find_bins(const uint32_t* hist, uint32_t r1
 // prefix; *total gets the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(v);
     if (lane == 63) wsum[wave] = x;
     lds_barrier();
     uint32_t before = 0, all = 0;
