@@ -285,7 +285,7 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
                 const uint32_t kb = static_cast<uint32_t>(__builtin_amdgcn_sbfe(mb, bit, 1));
                 sa[r] = __uint_as_float((__float_as_uint(sa[r]) & ka) | (ninf & ~ka));
                 sb[r] = __uint_as_float((__float_as_uint(sb[r]) & kb) | (ninf & ~kb));
-                bmax = fmaxf(bmax, fmaxf(sa[r], sb[r]));
+                bmax = fmaxf(fmaxf(bmax, sa[r]), sb[r]);   // one v_max3_f32
             }
             bmax = pair32_max(bmax);
             // Everything below runs on every lane (the MFMAs and transposing
