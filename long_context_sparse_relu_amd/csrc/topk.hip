@@ -864,7 +864,6 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
                     const uint64_t above = __builtin_amdgcn_ballot_w64(ab);
                     asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(bw) : "s"(static_cast<uint32_t>(above)), "n"(2 * u));
                     asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(bw) : "s"(static_cast<uint32_t>(above >> 32)), "n"(2 * u + 1));
-                    n_above += static_cast<uint32_t>(__popcll(above));
                     const uint64_t take = __builtin_amdgcn_ballot_w64(ge) & ~above;
                     if (take) {
                         if (ge && !ab) {
@@ -889,8 +888,13 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
                 }
             }
             {
+                // (the above-count is summed from the bitmap words after the
+                // loop, not per chunk: the scalar unit is this loop's limit)
                 const int nchunk = (vis + T - 1) / T;
-                if (lane < 2 * nchunk) bm[(lane >> 1) * (T / 32) + 2 * (tc >> 6) + (lane & 1)] = static_cast<uint32_t>(bw);
+                const bool mine = lane < 2 * nchunk;
+                if (mine) bm[(lane >> 1) * (T / 32) + 2 * (tc >> 6) + (lane & 1)] = static_cast<uint32_t>(bw);
+                n_above = wave_allreduce(mine ? static_cast<uint32_t>(__popc(static_cast<uint32_t>(bw))) : 0u,
+                                         [](uint32_t x, uint32_t y) { return x + y; });
             }
             if (lane == 0) { wc0[wave] = n_above; wc1[wave] = cnt; }
             lds_barrier();
