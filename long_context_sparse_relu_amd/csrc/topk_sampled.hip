@@ -155,9 +155,9 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
 // whole row.
 __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(SampledTopk t) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ uint32_t lh[kTopkBins];
+    __shared__ __align__(16) uint32_t lh[kTopkBins];
     __shared__ uint32_t wsum[kSFinishThreads / 64 + 2];
-    __shared__ uint32_t n_list;
+    __shared__ uint32_t n_list, n_tie;
     __shared__ uint32_t last, win_base;
     const IndexArgs& x = t.ix;
     const int lrow = blockIdx.x, row = x.row0 + lrow;
@@ -218,8 +218,7 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
             cl[i] = c;
             kmax = max(kmax, static_cast<uint32_t>(c >> 32));
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+        kmax = wave_allreduce(kmax, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
         if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = kmax;
         __syncthreads();
         for (int w = 0; w < kSFinishThreads / 64; ++w) kmax = max(kmax, wsum[w]);
@@ -239,8 +238,43 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
             shifts[np] = below;
             widths[np] = w;
         }
-        Cand64Rel src{cl, static_cast<int>(n), static_cast<uint64_t>(k_low) << 32};
-        radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
+        // The first digit's histogram finds the threshold bin.  A bin of at
+        // most kTopkBins / 2 candidates (a few, on a spread-out sample) is
+        // ranked by direct comparison, its composites being distinct; a
+        // larger one goes through the radix passes from the start.
+        const uint64_t base = static_cast<uint64_t>(k_low) << 32;
+        const int sh0 = shifts[0];
+        for (int i = threadIdx.x; i < kTopkBins; i += kSFinishThreads) lh[i] = 0u;
+        if (threadIdx.x == 0) n_tie = 0u;
+        lds_barrier();
+        for (uint32_t i = threadIdx.x; i < n; i += kSFinishThreads)
+            atomicAdd(&lh[static_cast<uint32_t>((cl[i] - base) >> sh0)], 1u);
+        lds_barrier();
+        int d0;
+        uint32_t gt0;
+        find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(k), wsum, &d0, &gt0);
+        const uint32_t n_t = lh[d0], k_t = static_cast<uint32_t>(k) - gt0;
+        lds_barrier();                          // every thread has read lh[d0]
+        if (n_t <= static_cast<uint32_t>(kTopkBins / 2)) {
+            uint64_t* tie = reinterpret_cast<uint64_t*>(lh);      // lh is free now
+            for (uint32_t i = threadIdx.x; i < n; i += kSFinishThreads) {
+                const uint64_t c = cl[i] - base;
+                const int dg = static_cast<int>(c >> sh0);
+                if (dg > d0) sink.put_c(c);
+                else if (dg == d0) tie[atomicAdd(&n_tie, 1u)] = c;
+            }
+            lds_barrier();
+            for (uint32_t j = threadIdx.x; j < n_t; j += kSFinishThreads) {
+                const uint64_t c = tie[j];
+                uint32_t beat = 0;
+                for (uint32_t q = 0; q < n_t; ++q) beat += tie[q] > c ? 1u : 0u;
+                if (beat < k_t) sink.put_c(c);
+            }
+            lds_barrier();
+        } else {
+            Cand64Rel src{cl, static_cast<int>(n), base};
+            radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
+        }
     } else {
         // recompute this row's scores in full, slice `part` of nparts here:
         // each wave scores 128 keys per step with whole-line loads
