@@ -1042,10 +1042,10 @@ __global__ __launch_bounds__(kRcThreads) void k_topk_row_cand(TopkArgs a, int ca
     uint64_t* cl = reinterpret_cast<uint64_t*>(smem);              // [cap] candidates
     uint32_t* skey = reinterpret_cast<uint32_t*>(smem);            // [kRcSample] samples, dead before collection
     uint32_t* tail = reinterpret_cast<uint32_t*>(cl + cap);        // bitmap of the row, or the list of kept keys
-    __shared__ uint32_t lh[kTopkBins];
+    __shared__ __align__(16) uint32_t lh[kTopkBins];
     __shared__ uint32_t wsum[kRcThreads / 64 + 2];
     __shared__ uint32_t wmin[kRcThreads / 64], wmax[kRcThreads / 64];
-    __shared__ uint32_t n_c, n_list;
+    __shared__ uint32_t n_c, n_list, n_tie;
     const int lrow = blockIdx.x, row = a.row0 + lrow;
     const int vis = row_visible(a, row);
     const int k = a.k;
@@ -1156,8 +1156,7 @@ __global__ __launch_bounds__(kRcThreads) void k_topk_row_cand(TopkArgs a, int ca
     if (n >= static_cast<uint32_t>(k) && n <= static_cast<uint32_t>(cap)) {
         uint32_t cmax = 0u;
         for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) cmax = max(cmax, static_cast<uint32_t>(cl[i] >> 32));
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(cmax), o)));
+        cmax = wave_allreduce(cmax, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
         if (lane == 0) wmax[threadIdx.x >> 6] = cmax;
         __syncthreads();
         for (int w = 0; w < kRcThreads / 64; ++w) cmax = max(cmax, wmax[w]);
@@ -1175,8 +1174,7 @@ __global__ __launch_bounds__(kRcThreads) void k_topk_row_cand(TopkArgs a, int ca
             shifts[np] = rest;
             widths[np] = w;
         }
-        Cand64Rel src{cl, static_cast<int>(n), static_cast<uint64_t>(k_low) << 32};
-        radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
+        select_candidates(cl, n, k_low, static_cast<uint32_t>(k), shifts, widths, np, lh, wsum, &n_tie, sink);
     } else {
         // the whole row, on the bits of the composite that vary
         ScoreRow64 src{sc, vis, a.sinks, vis - a.window};

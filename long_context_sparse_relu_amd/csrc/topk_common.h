@@ -411,6 +411,52 @@ __device__ void radix_select_spread(const Src& src, uint32_t k, uint32_t* lh, ui
     radix_select<true>(src, k, shifts, widths, np, bits >= 64 ? 0ull : hi >> bits, lh, wsum, sink);
 }
 
+// The k largest of the n candidate composites cl[0..n) (order key << 32 |
+// ~position, every key at least k_low; LDS) into the sink, with the radix
+// digits of ((key - k_low) << 32 | ~position) in shifts / widths (np of them).
+// The first digit's histogram finds the threshold bin.  A bin of at most
+// kTopkBins / 2 candidates (a few, when the candidates spread over the key
+// range) is then ranked by direct comparison, the composites being distinct;
+// a larger one takes the radix passes from the start.  `lh` (kTopkBins
+// entries, 8-byte aligned), `wsum` and the LDS counter `n_tie` are scratch.
+template <class SinkT>
+__device__ void select_candidates(const uint64_t* cl, uint32_t n, uint32_t k_low, uint32_t k, const int* shifts,
+                                  const int* widths, int np, uint32_t* lh, uint32_t* wsum, uint32_t* n_tie,
+                                  const SinkT& sink) {
+    const uint64_t base = static_cast<uint64_t>(k_low) << 32;
+    const int sh0 = shifts[0];
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+    if (threadIdx.x == 0) *n_tie = 0u;
+    lds_barrier();
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&lh[static_cast<uint32_t>((cl[i] - base) >> sh0)], 1u);
+    lds_barrier();
+    int d0;
+    uint32_t gt0;
+    find_threshold_bin(lh, kTopkBins, k, wsum, &d0, &gt0);
+    const uint32_t n_t = lh[d0], k_t = k - gt0;
+    lds_barrier();                               // every thread has read lh[d0]
+    if (n_t <= static_cast<uint32_t>(kTopkBins / 2)) {
+        uint64_t* tie = reinterpret_cast<uint64_t*>(lh);      // lh is free now
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const uint64_t c = cl[i] - base;
+            const int dg = static_cast<int>(c >> sh0);
+            if (dg > d0) sink.put_c(c);
+            else if (dg == d0) tie[atomicAdd(n_tie, 1u)] = c;
+        }
+        lds_barrier();
+        for (uint32_t j = threadIdx.x; j < n_t; j += blockDim.x) {
+            const uint64_t c = tie[j];
+            uint32_t beat = 0;
+            for (uint32_t q = 0; q < n_t; ++q) beat += tie[q] > c ? 1u : 0u;
+            if (beat < k_t) sink.put_c(c);
+        }
+        lds_barrier();
+    } else {
+        Cand64Rel src{cl, static_cast<int>(n), base};
+        radix_select(src, k, shifts, widths, np, 0ull, lh, wsum, sink);
+    }
+}
+
 // A lower bound on the r-th largest of the m order keys skey[0..m) (LDS),
 // at two 11-bit digits of resolution: digit 0 spans the top 11 bits of the
 // keys' range [kmin, kmax], digit 1 the next 11 below it; the result is kmin

@@ -238,43 +238,7 @@ __global__ __launch_bounds__(kSFinishThreads) void k_topk_finish_sampled(Sampled
             shifts[np] = below;
             widths[np] = w;
         }
-        // The first digit's histogram finds the threshold bin.  A bin of at
-        // most kTopkBins / 2 candidates (a few, on a spread-out sample) is
-        // ranked by direct comparison, its composites being distinct; a
-        // larger one goes through the radix passes from the start.
-        const uint64_t base = static_cast<uint64_t>(k_low) << 32;
-        const int sh0 = shifts[0];
-        for (int i = threadIdx.x; i < kTopkBins; i += kSFinishThreads) lh[i] = 0u;
-        if (threadIdx.x == 0) n_tie = 0u;
-        lds_barrier();
-        for (uint32_t i = threadIdx.x; i < n; i += kSFinishThreads)
-            atomicAdd(&lh[static_cast<uint32_t>((cl[i] - base) >> sh0)], 1u);
-        lds_barrier();
-        int d0;
-        uint32_t gt0;
-        find_threshold_bin(lh, kTopkBins, static_cast<uint32_t>(k), wsum, &d0, &gt0);
-        const uint32_t n_t = lh[d0], k_t = static_cast<uint32_t>(k) - gt0;
-        lds_barrier();                          // every thread has read lh[d0]
-        if (n_t <= static_cast<uint32_t>(kTopkBins / 2)) {
-            uint64_t* tie = reinterpret_cast<uint64_t*>(lh);      // lh is free now
-            for (uint32_t i = threadIdx.x; i < n; i += kSFinishThreads) {
-                const uint64_t c = cl[i] - base;
-                const int dg = static_cast<int>(c >> sh0);
-                if (dg > d0) sink.put_c(c);
-                else if (dg == d0) tie[atomicAdd(&n_tie, 1u)] = c;
-            }
-            lds_barrier();
-            for (uint32_t j = threadIdx.x; j < n_t; j += kSFinishThreads) {
-                const uint64_t c = tie[j];
-                uint32_t beat = 0;
-                for (uint32_t q = 0; q < n_t; ++q) beat += tie[q] > c ? 1u : 0u;
-                if (beat < k_t) sink.put_c(c);
-            }
-            lds_barrier();
-        } else {
-            Cand64Rel src{cl, static_cast<int>(n), base};
-            radix_select(src, static_cast<uint32_t>(k), shifts, widths, np, 0ull, lh, wsum, sink);
-        }
+        select_candidates(cl, n, k_low, static_cast<uint32_t>(k), shifts, widths, np, lh, wsum, &n_tie, sink);
     } else {
         // recompute this row's scores in full, slice `part` of nparts here:
         // each wave scores 128 keys per step with whole-line loads
