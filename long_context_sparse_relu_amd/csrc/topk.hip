@@ -460,11 +460,8 @@ __device__ void select_lds_row_lin(const TopkArgs& a, uint32_t* sbits, int vis, 
             kmin = min(kmin, kk);
             kmax = max(kmax, kk);
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-            kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
-        }
+        kmin = wave_allreduce(kmin, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+        kmax = wave_allreduce(kmax, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
         uint32_t* wred = lh;                      // free until the select clears it
         if ((threadIdx.x & 63) == 0) { wred[2 * (threadIdx.x >> 6)] = kmin; wred[2 * (threadIdx.x >> 6) + 1] = kmax; }
         __syncthreads();
@@ -565,11 +562,8 @@ __global__ __launch_bounds__(T) void k_topk_row_lds(TopkArgs a) {
     const int nwords = (vis + 31) >> 5;
     for (int i = threadIdx.x; i < nwords; i += T) bm[i] = 0u;
     if (threadIdx.x == 0) n_list = 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        smin = fminf(smin, __shfl_xor(smin, o));
-        smax = fmaxf(smax, __shfl_xor(smax, o));
-    }
+    smin = wave_allmin(smin);
+    smax = wave_allmax(smax);
     __shared__ float wmin[T / 64], wmax[T / 64];
     if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = smin; wmax[threadIdx.x >> 6] = smax; }
     __syncthreads();
@@ -626,11 +620,8 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row_lds_next(TopkArgs a) {
             const int nwords = (vis + 31) >> 5;
             for (int i = threadIdx.x; i < nwords; i += kRowThreads) bm[i] = 0u;
             if (threadIdx.x == 0) n_list = 0;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                smin = fminf(smin, __shfl_xor(smin, o));
-                smax = fmaxf(smax, __shfl_xor(smax, o));
-            }
+            smin = wave_allmin(smin);
+            smax = wave_allmax(smax);
             if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = smin; wmax[threadIdx.x >> 6] = smax; }
             __syncthreads();
             for (int w = 0; w < kRowThreads / 64; ++w) { smin = fminf(smin, wmin[w]); smax = fmaxf(smax, wmax[w]); }
@@ -934,11 +925,8 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
                 }
             }
             for (int i = tid; i < nwords; i += T) bm[i] = 0u;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                rmin = fminf(rmin, __shfl_xor(rmin, o));
-                rmax = fmaxf(rmax, __shfl_xor(rmax, o));
-            }
+            rmin = wave_allmin(rmin);
+            rmax = wave_allmax(rmax);
             __syncthreads();                  // every thread has read the sample's range
             if (lane == 0) { wmin[wave] = rmin; wmax[wave] = rmax; }
             if (tid == 0) n_list = 0;
@@ -1080,11 +1068,8 @@ __global__ __launch_bounds__(kRcThreads) void k_topk_row_cand(TopkArgs a, int ca
             }
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
-    }
+    kmin = wave_allreduce(kmin, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+    kmax = wave_allreduce(kmax, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
     if (lane == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
     __syncthreads();
     for (int w = 0; w < kRcThreads / 64; ++w) { kmin = min(kmin, wmin[w]); kmax = max(kmax, wmax[w]); }

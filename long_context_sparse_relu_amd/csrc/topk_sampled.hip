@@ -129,11 +129,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_topk_sample_bound(SampledTop
         const int j = threadIdx.x + u * kSampleThreads;
         if (j < m) { skey[j] = v[u]; kmin = min(kmin, v[u]); kmax = max(kmax, v[u]); }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
-    }
+    kmin = wave_allreduce(kmin, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+    kmax = wave_allreduce(kmax, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
     __shared__ uint32_t wmin[kSampleThreads / 64], wmax[kSampleThreads / 64];
     if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = kmin; wmax[threadIdx.x >> 6] = kmax; }
     __syncthreads();
