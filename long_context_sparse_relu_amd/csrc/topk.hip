@@ -825,6 +825,9 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
                 d_lo = fres[2];
                 if (d_lo > 0) tl = static_cast<float>(d_lo);
             }
+            // the second level's bins, cleared here (the first level is done
+            // with lh; the barrier after the classify orders this)
+            for (int i = tid; i < kRegBins2; i += T) lh[i] = 0u;
             // classify: lane 2u (2u + 1) of bw gathers the low (high) bitmap
             // word of this wave's 64 keys of chunk u
             uint32_t n_above = 0, cnt = 0;
@@ -948,14 +951,12 @@ __global__ __launch_bounds__(kRegThreads) void k_topk_row_reg(TopkArgs a) {
             // compiler sees that they do not overlap the loads in flight)
             const int lb = 2 * wave * kRegRegion;
             const int mine = static_cast<int>(wc1[wave]);     // this wave's region
-            for (int i = tid; i < kRegBins2; i += T) lh[i] = 0u;
-            lds_barrier();
             for (int j = lane; j < mine; j += 64) lds_add(&lh[digit2(lpair[lb + 2 * j])], 1u);
             lds_barrier();
-            if (wave == 0) wave_find_bins<kRegBins2>(lh, k_rem, k_rem, fres);
-            lds_barrier();
-            const int d2 = fres[0];
-            const uint32_t gt2 = static_cast<uint32_t>(fres[1]);
+            // every wave finds the threshold bin itself (no barrier to publish it)
+            int d2;
+            uint32_t gt2;
+            wave_find_bin_reg<kRegBins2>(lh, k_rem, &d2, &gt2);
             // the threshold bin's keys: (order key, ~position) word pairs in lh past the bins
             constexpr int TB = kRegBins2;
             for (int j = lane; j < mine; j += 64) {

@@ -157,6 +157,35 @@ __device__ __forceinline__ void wave_find_bins(const uint32_t* hist, uint32_t r1
     find(r2, 2);
 }
 
+// The same search for one rank r, by every wave that calls it, with the
+// result in registers (no LDS write and no barrier): the bin d with
+// count(bins > d) < r <= count(bins >= d) and that count above it.  Lane l
+// holds the NB / 64 bins from NB - 1 - (NB / 64) l downwards; the lane whose
+// range holds rank r walks its own bins.  Requires 1 <= r <= sum(hist).
+template <int NB>
+__device__ __forceinline__ void wave_find_bin_reg(const uint32_t* hist, uint32_t r, int* d, uint32_t* gt) {
+    constexpr int PER = NB / 64;
+    const int lane = threadIdx.x & 63;
+    const int top = NB - 1 - lane * PER;
+    uint32_t h[PER], local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) { h[j] = hist[top - j]; local += h[j]; }
+    const uint32_t x = wave_inclusive_sum(local);
+    const uint32_t excl = x - local;
+    int dl = top;
+    uint32_t gl = excl, run = excl;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (!found && run + h[j] >= r) { dl = top - j; gl = run; found = true; }
+        run += h[j];
+    }
+    const uint64_t hit = __ballot(excl < r && x >= r);
+    const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    *d = __builtin_amdgcn_readlane(dl, src);
+    *gt = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(gl), src));
+}
+
 // Block-wide exclusive scan of one value per thread (wave scans, then the
 // wave totals); `wsum` holds one LDS slot per wave.  Returns the exclusive
 // prefix; *total gets the block sum.
