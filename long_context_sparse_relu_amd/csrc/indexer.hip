@@ -299,9 +299,14 @@ __host__ __device__ inline int tiled_block_tiles(int j, int nrows, int kTQ, long
 // inclusive prefix, and the first lane whose prefix passes the target walks
 // its own blocks.  Every wave does this and gets the same answer.  Returns
 // false when the workgroup has no work.
+// With PRO > 0 the runs are cut over a sequence in which every block with
+// tiles starts with PRO units of no work, the cost of the prologue (query
+// operands and weights) that a workgroup pays again when its run crosses
+// into the next block: such a run then takes PRO fewer tiles, and the
+// runs end together.
 struct TiledWork { int qb, t0, tj, ta, tb, piece; };
 
-template <int kTQ>
+template <int kTQ, int PRO = 0>
 __device__ __forceinline__ bool tiled_work_start(int lane, int nrows, long long base, int n_k, bool all_keys,
                                                  int piece, long long total, TiledWork& w) {
     const int nqb = (nrows + kTQ - 1) / kTQ;
@@ -311,7 +316,7 @@ __device__ __forceinline__ bool tiled_work_start(int lane, int nrows, long long 
     if (runs && target >= g_end) return false;               // uniform over the workgroup
     auto units = [&](int j) {
         const int tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
-        return runs ? tj : (tj + piece - 1) / piece;
+        return runs ? (tj > 0 ? tj + PRO : 0) : (tj + piece - 1) / piece;
     };
     const int m = (nqb + 63) / 64;
     long long lsum = 0;
@@ -337,11 +342,20 @@ __device__ __forceinline__ bool tiled_work_start(int lane, int nrows, long long 
     w.tj = __builtin_amdgcn_readfirstlane(tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys));
     const int into = __builtin_amdgcn_readfirstlane(static_cast<int>(target - acc));
     w.piece = piece;
-    w.t0 = runs ? into : into * piece;
     w.ta = w.tb = 0;
     if (runs) {
-        w.ta = static_cast<int>(min(static_cast<long long>(w.tj - w.t0), g_end - target));
-        w.tb = static_cast<int>(g_end - target - w.ta);
+        // the run's units: the block's prologue units it covers, then tiles
+        // of block qb, then (prologue units and) tiles of block qb + 1
+        const int skip = into < PRO ? PRO - into : 0;
+        w.t0 = into < PRO ? 0 : into - PRO;
+        const long long budget = g_end - target - skip;
+        w.ta = static_cast<int>(max(0ll, min(static_cast<long long>(w.tj - w.t0), budget)));
+        const long long rest = budget - w.ta - PRO;
+        w.tb = rest > 0 ? static_cast<int>(min(rest, static_cast<long long>(
+                              tiled_block_tiles(w.qb + 1, nrows, kTQ, base, n_k, all_keys))))
+                        : 0;
+    } else {
+        w.t0 = into * piece;
     }
     return true;
 }
@@ -628,6 +642,12 @@ __global__ __launch_bounds__(TiledShape<DT>::TW * 64) void k_index_tiled(IndexAr
 constexpr int kQ16RG = DSA_Q16_RG;                   // groups of 16 query rows per wave
 constexpr int kQ16W = kQ16RG == 1 ? 8 : 4;           // waves per workgroup (one workgroup per CU)
 constexpr int kQ16Q = 16 * kQ16RG * kQ16W;           // query rows per workgroup (block)
+// a block's prologue (256 KiB of query operands and the weights, ~10 us)
+// counted as this many tiles (~3.5 us each) when runs are cut
+#ifndef DSA_Q16_PRO
+#define DSA_Q16_PRO 3
+#endif
+constexpr int kQ16Pro = DSA_Q16_PRO;
 
 __global__ __launch_bounds__(kQ16W * 64) __attribute__((amdgpu_waves_per_eu(kQ16W / 4)))
 void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long total, int write_future) {
@@ -922,7 +942,7 @@ void k_index_fp8_q16(IndexArgs x, int t_first, int nrows, int piece, long long t
     };
 
     TiledWork w;
-    if (!tiled_work_start<kQ16Q>(lane, nrows, base, n_k, all_keys, piece, total, w)) return;
+    if (!tiled_work_start<kQ16Q, kQ16Pro>(lane, nrows, base, n_k, all_keys, piece, total, w)) return;
     if (w.piece > 0) {
         run_segment(w.qb, 64 * w.t0, min(64 * min(w.t0 + w.piece, w.tj), n_k));
         return;
@@ -954,7 +974,8 @@ bool index_tiled_path(const IndexArgs& a) {
 // k_index_fp8_q16, which take the same arguments.
 typedef void (*TiledKernel)(IndexArgs, int, int, int, long long, int);
 
-static hipError_t launch_tiled(TiledKernel fn, int kTQ, int threads, int& per_cu_cache, const IndexArgs& a,
+// `pro`: the kernel's prologue units per block (tiled_work_start's PRO)
+static hipError_t launch_tiled(TiledKernel fn, int kTQ, int threads, int pro, int& per_cu_cache, const IndexArgs& a,
                                bool write_future, hipStream_t st) {
     // workgroups the chip holds at once
     if (per_cu_cache == 0) {
@@ -976,8 +997,12 @@ static hipError_t launch_tiled(TiledKernel fn, int kTQ, int threads, int& per_cu
         const long long base = static_cast<long long>(a.n_k) - a.n_q + r % a.n_q;
         const bool all_keys = a.q_pos != nullptr;
         const int nqb = (n + kTQ - 1) / kTQ;
+        // (runs are cut over tiles plus `pro` prologue units per block with tiles)
         long long total = 0;
-        for (int j = 0; j < nqb; ++j) total += tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys);
+        for (int j = 0; j < nqb; ++j) {
+            const int tj = tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys);
+            total += tj > 0 ? tj + pro : 0;
+        }
         if (total > 0) {
             // Few blocks (a fused row block): equal runs, one per resident
             // workgroup, when no block with keys is shorter than a run (a run
@@ -989,7 +1014,7 @@ static hipError_t launch_tiled(TiledKernel fn, int kTQ, int threads, int& per_cu
             int shortest = INT_MAX;
             for (int j = 0; j < nqb; ++j) {
                 const int tj = tiled_block_tiles(j, n, kTQ, base, a.n_k, all_keys);
-                if (tj > 0 && tj < shortest) shortest = tj;
+                if (tj > 0 && tj + pro < shortest) shortest = tj + pro;
             }
             long long piece = 0;
             if (nqb * 2 > slots || run > shortest) {
@@ -1017,12 +1042,12 @@ hipError_t launch_index_tiled(const IndexArgs& a, bool write_future, hipStream_t
     static int occ_q16 = 0, occ_f8 = 0, occ_bf = 0;
     if (a.dtype == E4M3) {
         if (DSA_TILED_FP8_Q16)
-            return launch_tiled(k_index_fp8_q16, kQ16Q, kQ16W * 64, occ_q16, a, write_future, st);
+            return launch_tiled(k_index_fp8_q16, kQ16Q, kQ16W * 64, kQ16Pro, occ_q16, a, write_future, st);
         constexpr int tw = TiledShape<E4M3>::TW;
-        return launch_tiled(k_index_tiled<E4M3>, TiledShape<E4M3>::QPW * tw, tw * 64, occ_f8, a, write_future, st);
+        return launch_tiled(k_index_tiled<E4M3>, TiledShape<E4M3>::QPW * tw, tw * 64, 0, occ_f8, a, write_future, st);
     }
     constexpr int tw = TiledShape<BF16>::TW;
-    return launch_tiled(k_index_tiled<BF16>, TiledShape<BF16>::QPW * tw, tw * 64, occ_bf, a, write_future, st);
+    return launch_tiled(k_index_tiled<BF16>, TiledShape<BF16>::QPW * tw, tw * 64, 0, occ_bf, a, write_future, st);
 }
 
 // ---------------------------------------------------------------------------
