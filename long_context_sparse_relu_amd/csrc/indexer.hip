@@ -10,6 +10,7 @@
 #include <type_traits>
 #include "dsa_kernels.h"
 #include "fp8_index.h"
+#include "topk_common.h"
 
 namespace dsa {
 
@@ -318,20 +319,17 @@ __device__ __forceinline__ bool tiled_work_start(int lane, int nrows, long long 
         const int tj = tiled_block_tiles(j, nrows, kTQ, base, n_k, all_keys);
         return runs ? (tj > 0 ? tj + PRO : 0) : (tj + piece - 1) / piece;
     };
+    // (a launch's units stay far below 2^31: the prefix scan is 32-bit, on DPP)
     const int m = (nqb + 63) / 64;
-    long long lsum = 0;
+    uint32_t lsum = 0;
     for (int i = 0; i < m; ++i) {
         const int j = lane * m + i;
-        if (j < nqb) lsum += units(j);
+        if (j < nqb) lsum += static_cast<uint32_t>(units(j));
     }
-    long long incl = lsum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const long long v = __shfl_up(incl, d);
-        if (lane >= d) incl += v;
-    }
+    const uint32_t incl32 = wave_inclusive_sum(lsum);
+    const long long incl = incl32;
     const int L = __ffsll(static_cast<long long>(__ballot(target < incl))) - 1;   // target < all units
-    long long acc = __shfl(incl - lsum, L);
+    long long acc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl32 - lsum), L));
     int j = L * m;
     int u = units(j);
     while (acc + u <= target) {
