@@ -169,8 +169,10 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
     const int last = __builtin_amdgcn_readfirstlane(last_all);
     // this workgroup's key tiles [t0, t1) of the block's walk
     const int ntiles = last < 0 ? 0 : last / kKB + 1;
-    const int t0 = split * tps;
-    const int t1 = min(ntiles, t0 + tps);
+    // (held in scalar registers, so the tile loop, its buffer index and the
+    // tile offsets below are scalar work)
+    const int t0 = __builtin_amdgcn_readfirstlane(split * tps);
+    const int t1 = __builtin_amdgcn_readfirstlane(min(ntiles, t0 + tps));
 
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     const uint16_t* vp = static_cast<const uint16_t*>(a.v);
@@ -190,8 +192,8 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
     const int lcol = (threadIdx.x & 15) * 8;    // bf16 offset within the 128-wide row
     const int row_bytes = static_cast<int>(rstride) * 2;
     const int kv_bytes = __builtin_amdgcn_readfirstlane((a.n_k - 1) * row_bytes + 256);
-    const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
-    const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
+    const unsigned char* kbytes = static_cast<const unsigned char*>(uniform_ptr(kbase));
+    const unsigned char* vbytes = static_cast<const unsigned char*>(uniform_ptr(vbase));
     int voff[kLoadRows];
 #pragma unroll
     for (int r = 0; r < kLoadRows; ++r) voff[r] = (lrow + kLoadStride * r) * row_bytes + lcol * 2;
@@ -202,9 +204,9 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2))) v
         const int toff = __builtin_amdgcn_readfirstlane(tile * kKB * row_bytes);
         const int rem = __builtin_amdgcn_readfirstlane(kv_bytes - toff);
         const __amdgpu_buffer_rsrc_t kr =
-            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kbytes + toff), 0, rem, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbytes + toff), 0, rem, kBufferWord3);
         const __amdgpu_buffer_rsrc_t vr =
-            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vbytes + toff), 0, rem, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbytes + toff), 0, rem, kBufferWord3);
 #pragma unroll
         for (int r = 0; r < kLoadRows; ++r) {
             const v4i xk = __builtin_amdgcn_raw_buffer_load_b128(kr, voff[r], 0, 0);
