@@ -33,6 +33,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -267,6 +269,53 @@ def _sweep_ladder(dsa, torch, dev, lengths, ks, reps):
     return 0
 
 
+def _sweep_compress(dsa, torch, dev, reps):
+    """Importance compression of whole caches: one JSON line per cache shape.
+
+    The cut is the pages' operating point: an 8K recent window and half of the
+    older tokens kept.  Bytes per call = importance read once (4 B per token)
+    + every kept token's rows read and written + its position written; the
+    call's time is the median of HIP-event-timed calls on the launch stream,
+    each after a 1 GiB read that flushes the caches.
+    """
+    from dsa_inputs import importance_scores, kv_args, make_inputs, spec
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for name in ("decode_1m", "decode_128k", "decode_128k_fp8kv"):
+        s = spec(name)
+        print(f"[bench] compress: generating {name} inputs", file=sys.stderr, flush=True)
+        inp = make_inputs(s, device=dev, seed=0)
+        B, N, window = s["B"], s["n_k"], 8192
+        keep_old = (N - window) // 2
+        imp = importance_scores(B, N, "normal", device=dev, seed=0)
+        prob = dsa.make_problem(iq=inp["iq"], ik=inp["ik"], iw=inp["iw"], top_k=s["top_k"], q=inp["q"],
+                                iq_scale=inp["iq_scale"], ik_scale=inp["ik_scale"], **kv_args(inp))
+        ws = torch.empty(dsa.workspace_bytes(dsa.OP_COMPRESS_KV, prob), dtype=torch.uint8, device=dev)
+        res = dsa.compress_kv(prob, imp, window, keep_old, workspace=ws, stream=stream)
+        n_keep = res["pos"].shape[1]
+        row = sum(t[0, 0].numel() * t.element_size() for t in (res["k"], res["v"], res["ik"], res["ik_scale"])
+                  if t is not None)
+        times = []
+        for _ in range(reps):
+            flush.add_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsa.compress_kv(prob, imp, window, keep_old, out=res, workspace=ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(1e3 * e0.elapsed_time(e1))
+        us = float(np.median(times))
+        nbytes = B * N * 4 + B * n_keep * (2 * row + 4)
+        print(json.dumps({"sweep": "compress", "cache": name, "batch": B, "tokens": N, "window": window,
+                          "keep_old": keep_old, "kept": n_keep, "cache_cut": round(1 - n_keep / N, 4),
+                          "row_bytes": row, "us": round(us, 1), "bytes": nbytes,
+                          "tb_s": round(nbytes / us / 1e6, 3), "frac_hbm": round(nbytes / us / 1e6 / 8.0, 3)}),
+              flush=True)
+        del inp, imp, prob, ws, res
+        torch.cuda.empty_cache()
+    return 0
+
+
 def _cpu_model():
     """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
     try:
@@ -326,10 +375,10 @@ def main(argv=None):
                          "at 0, so a decode row overflows its sampled candidate list and is recomputed in full "
                          "(times that fallback; the workload is then not the benchmark's)")
     ap.add_argument("--phase-reps", type=int, default=10)
-    ap.add_argument("--sweep", choices=["mask", "ladder"], default=None,
+    ap.add_argument("--sweep", choices=["mask", "ladder", "compress"], default=None,
                     help="instead of the step benchmark: 'mask' = masked vs gather attention and DSA vs dense "
                          "attention in prefill; 'ladder' = decode time and bytes against context length and k "
-                         "(JSON line per point)")
+                         "(JSON line per point); 'compress' = importance compression of whole caches")
     ap.add_argument("--lengths", default="4096,16384,65536,131072,262144,524288,1048576")
     ap.add_argument("--ladder-ks", default="256,512,2048")
     ap.add_argument("--ladder", default="1024,2048,4096,8192,16384,32768,65536,131072")
@@ -351,6 +400,8 @@ def main(argv=None):
     if args.sweep == "ladder":
         return _sweep_ladder(dsa, torch, dev, [int(x) for x in args.lengths.split(",")],
                              [int(x) for x in args.ladder_ks.split(",")], max(3, args.steps // 4))
+    if args.sweep == "compress":
+        return _sweep_compress(dsa, torch, dev, max(3, args.steps // 4))
     if args.sweep == "mask":
         return _sweep_mask(dsa, torch, dev, [int(x) for x in args.ladder.split(",")],
                            [int(x) for x in args.ks.split(",")], [int(x) for x in args.chunks.split(",")],

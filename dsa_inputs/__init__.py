@@ -74,7 +74,8 @@ CONFIGS["decode_128k_backbone"] = dict(CONFIGS["decode_128k"], sinks=4, window=4
 CONFIGS["decode_1m_window"] = dict(CONFIGS["decode_1m"], window=8192)
 
 _TORCH_STORE = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
-_TENSOR_IDS = {"iq": 1, "ik": 2, "iw": 3, "q": 4, "k": 5, "v": 6, "needle": 7, "outlier": 8}
+_TENSOR_IDS = {"iq": 1, "ik": 2, "iw": 3, "q": 4, "k": 5, "v": 6, "needle": 7, "outlier": 8,
+               "importance": 9}
 
 
 def spec(name: str, **overrides) -> dict:
@@ -297,3 +298,29 @@ def oracle_view(inp: dict, seqs=None) -> dict:
         res[name] = stored_numpy(t.index_select(0, sel.to(t.device)))
     res["seq_ids"] = seqs
     return res
+
+
+def importance_scores(B: int, n_k: int, kind: str = "normal", device="cpu", seed: int = 0) -> torch.Tensor:
+    """Per-token importance [B, n_k] fp32 for cache compression.
+
+    kind "normal": standard normal draws; "ties": integers in [-3, 3] with every
+    zero's sign drawn at random (many equal values, -0.0 beside +0.0); "const":
+    all zeros, half of them -0.0 (every token ties).
+    """
+    rows = []
+    for b in range(B):
+        g = _gen("cpu", seed, "importance", b)
+        if kind == "normal":
+            x = torch.randn(n_k, generator=g, dtype=torch.float32)
+        elif kind == "ties":
+            x = torch.randint(-3, 4, (n_k,), generator=g).to(torch.float32)
+            neg = torch.randint(0, 2, (n_k,), generator=g).bool() & (x == 0)
+            x = torch.where(neg, torch.full_like(x, -0.0), x)
+        elif kind == "const":
+            x = torch.zeros(n_k, dtype=torch.float32)
+            x[1::2] = -0.0
+        else:
+            raise ValueError(f"unknown importance kind {kind!r}")
+        rows.append(x)
+    return torch.stack(rows).to(device)
+

@@ -80,7 +80,7 @@ extern "C" {
 /* Same typedef as HIP's own header, so both may be included together. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 /* Bytes of one token's record in an FP8 (DSA_FP8_E4M3) k or v cache with
  * `heads` kv heads of `dim` entries: bytes [0, heads*dim) are the E4M3 codes,
@@ -109,7 +109,8 @@ typedef enum {
     DSA_OP_SPARSE_ATTN = 2,
     DSA_OP_PREFILL = 3,
     DSA_OP_DECODE = 4,
-    DSA_OP_DENSE_ATTN = 5
+    DSA_OP_DENSE_ATTN = 5,
+    DSA_OP_COMPRESS_KV = 6
 } dsa_op_t;
 
 /* How the attention over the kept rows is computed; every mode gives the same
@@ -237,6 +238,47 @@ dsa_status_t dsa_decode_noalloc(const dsa_problem_t *p, void *out, float *lse, i
  * bytes (partial results when the key walk is split; may be 0). */
 dsa_status_t dsa_dense_attn(const dsa_problem_t *p, void *out, float *lse,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Importance compression of the cached tokens, as "DeepSeek-V4 百万 token
+ * 上下文的工程实现" (blog.hotdry.top), section "滑动窗口 KV Cache 与混合策略",
+ * describes it: the most recent tokens keep their full K/V and the older ones
+ * are cut down by an importance score to the ones that matter.  The pages give
+ * no rule for the score or the cut; read here as a selection of whole tokens.
+ * Per sequence b, with W = min(window, n_k) and n_old = n_k - W:
+ *   - the last W tokens (positions n_old .. n_k-1) are kept;
+ *   - of the old tokens 0 .. n_old-1, the min(keep_old, n_old) with the
+ *     highest importance[b][s] are kept; among equal importance the lower
+ *     position wins, and -0.0 equals +0.0 (NaN importance is unsupported:
+ *     which of those tokens are kept is unspecified);
+ *   - the kept tokens, in ascending position order, are written to slots
+ *     0 .. n_keep-1 of the outputs, n_keep = dsa_compress_kept(n_k, window,
+ *     keep_old) = W + min(keep_old, n_old), the same for every sequence.
+ * Each kept token's rows are copied bit for bit: its k row (or FP8 record),
+ * its v row (or record) unless kv_latent, its indexer key row ik and, for an
+ * FP8 indexer, its ik_scale.  The outputs use the input layouts with n_k
+ * replaced by n_keep, so a problem over the compressed cache (n_k = n_keep,
+ * the same head counts and dtypes) runs through every other entry point.
+ * importance: [B, n_k] fp32 device memory, any per-token score the caller
+ * keeps (for example the indexer scores I of recent queries, or their sum).
+ * Uses batch, n_k, kv_heads, d_qk, d_v, kv_latent, kv_dtype, k, v, idx_dim,
+ * idx_dtype, ik and ik_scale of p (n_q and the query fields are ignored; ik
+ * may be NULL, then no indexer rows are copied).  out->pos: [B, n_keep] int32,
+ * the original positions.  Requires batch * n_k < 2^31 and a workspace of
+ * dsa_workspace_bytes(DSA_OP_COMPRESS_KV, p) bytes.  Rows are copied 16 or 4
+ * bytes at a time: each row size and its input and output pointers must be
+ * multiples of 4 (else DSA_E_UNSUPPORTED).  When n_keep is 0 nothing is
+ * enqueued. */
+typedef struct {
+    void *k;                  /* [B, n_keep] rows in p->k's layout and dtype */
+    void *v;                  /* [B, n_keep] rows in p->v's layout; NULL when kv_latent */
+    void *ik;                 /* [B, n_keep, idx_dim] in idx_dtype; NULL when p->ik is NULL */
+    float *ik_scale;          /* [B, n_keep]; required when p->ik_scale is given, else NULL */
+    int32_t *pos;             /* [B, n_keep] original positions, ascending per sequence */
+} dsa_kv_compressed_t;
+int32_t dsa_compress_kept(int32_t n_k, int32_t window, int32_t keep_old);
+dsa_status_t dsa_compress_kv(const dsa_problem_t *p, const float *importance, int32_t window, int32_t keep_old,
+                             const dsa_kv_compressed_t *out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Phase timing of the fused entry points, for profiling.
  * dsa_phase_timing(1) makes every later dsa_prefill / dsa_decode call record

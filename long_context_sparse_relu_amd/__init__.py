@@ -23,15 +23,16 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE = 0, -1, -2, -3, -4
 F32, BF16, FP8_E4M3 = 0, 1, 2
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE_ATTN = 0, 1, 2, 3, 4, 5
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE_ATTN, OP_COMPRESS_KV = 0, 1, 2, 3, 4, 5, 6
 ATTN_AUTO, ATTN_GATHER, ATTN_MASKED = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
 EXPORTED = ("dsa_abi_version", "dsa_workspace_bytes", "dsa_index_scores", "dsa_topk",
             "dsa_sparse_attn", "dsa_prefill", "dsa_decode", "dsa_decode_noalloc", "dsa_dense_attn",
-            "dsa_phase_timing", "dsa_phase_times", "dsa_status_str", "dsa_last_error")
+            "dsa_phase_timing", "dsa_phase_times", "dsa_status_str", "dsa_last_error",
+            "dsa_compress_kept", "dsa_compress_kv")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 # dsa_phase_t, in order
 PHASES = ("prep", "index", "topk", "attn")
@@ -95,6 +96,10 @@ def load_library(path: str = LIB_PATH):
     lib.dsa_dense_attn.restype = ctypes.c_int
     lib.dsa_dense_attn.argtypes = [P, vp, vp, vp, sz, vp]
     lib.dsa_phase_timing.restype = ctypes.c_int
+    lib.dsa_compress_kept.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.dsa_compress_kept.restype = ctypes.c_int32
+    lib.dsa_compress_kv.argtypes = [P, vp, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(KVCompressed), vp, sz, vp]
+    lib.dsa_compress_kv.restype = ctypes.c_int
     lib.dsa_phase_timing.argtypes = [ctypes.c_int]
     lib.dsa_phase_times.restype = ctypes.c_int
     lib.dsa_phase_times.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -352,6 +357,43 @@ def dense_attn(prob: DSAProblem, out=None, lse=None, workspace=None, stream=None
     _check(load_library().dsa_dense_attn(prob.ref(), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                          _stream(stream)))
     return out, lse
+
+
+class KVCompressed(ctypes.Structure):
+    """dsa_kv_compressed_t: output pointers of dsa_compress_kv."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("ik", ctypes.c_void_p),
+                ("ik_scale", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+def compress_kept(n_k: int, window: int, keep_old: int) -> int:
+    """Tokens per sequence that dsa_compress_kv keeps."""
+    return int(load_library().dsa_compress_kept(n_k, window, keep_old))
+
+
+def compress_kv(prob: DSAProblem, importance, window: int, keep_old: int, out=None, workspace=None, stream=None):
+    """Importance compression of the cache `prob` points at (see dsa_compress_kv).
+
+    Returns a dict of the compressed cache: k, v (None when latent), ik and
+    ik_scale (None when the problem has none) with n_k replaced by n_keep, and
+    pos [B, n_keep] int32, the kept tokens' original positions.
+    """
+    s = prob.struct
+    t = prob.tensors
+    importance = _contig("importance", importance, prob.device, (torch.float32,))
+    n_keep = compress_kept(s.n_k, window, keep_old)
+
+    def like(x):
+        return None if x is None else torch.empty((x.shape[0], n_keep, *x.shape[2:]), dtype=x.dtype,
+                                                  device=prob.device)
+    if out is None:
+        out = dict(k=like(t.get("k")), v=like(t.get("v")), ik=like(t.get("ik")), ik_scale=like(t.get("ik_scale")),
+                   pos=torch.empty((s.batch, n_keep), dtype=torch.int32, device=prob.device))
+    o = KVCompressed(*(None if out.get(n) is None else out[n].data_ptr()
+                       for n in ("k", "v", "ik", "ik_scale", "pos")))
+    ws = _workspace(OP_COMPRESS_KV, prob, workspace)
+    _check(load_library().dsa_compress_kv(prob.ref(), _ptr(importance), int(window), int(keep_old),
+                                          ctypes.byref(o), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def phase_timing(enable: bool):

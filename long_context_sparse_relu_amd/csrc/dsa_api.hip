@@ -159,6 +159,34 @@ dsa_status_t check_attn(const dsa_problem_t* p) {
     return DSA_OK;
 }
 
+// The cached-token fields dsa_compress_kv reads.
+dsa_status_t check_cache(const dsa_problem_t* p) {
+    if (p->kv_heads < 1) return fail(DSA_E_INVALID, "kv_heads must be >= 1 (got %d)", p->kv_heads);
+    if (p->kv_dtype != DSA_F32 && p->kv_dtype != DSA_BF16 && p->kv_dtype != DSA_FP8_E4M3)
+        return fail(DSA_E_INVALID, "kv_dtype %d is not a dsa_dtype_t", p->kv_dtype);
+    if (p->d_qk < 1 || p->d_qk > 576 || p->d_v < 1 || p->d_v > 512)
+        return fail(DSA_E_UNSUPPORTED, "need 1 <= d_qk <= 576 and 1 <= d_v <= 512 (got %d, %d)", p->d_qk, p->d_v);
+    if (!p->k) return fail(DSA_E_INVALID, "k is required");
+    if (p->kv_latent ? p->kv_heads != 1 : !p->v)
+        return fail(DSA_E_INVALID, "latent rows need kv_heads == 1; otherwise v is required");
+    if (p->ik) {
+        if (p->idx_dim != 128) return fail(DSA_E_UNSUPPORTED, "idx_dim must be 128 (got %d)", p->idx_dim);
+        if (p->idx_dtype != DSA_F32 && p->idx_dtype != DSA_BF16 && p->idx_dtype != DSA_FP8_E4M3)
+            return fail(DSA_E_INVALID, "idx_dtype %d is not a dsa_dtype_t", p->idx_dtype);
+        if (p->idx_dtype == DSA_FP8_E4M3 && !p->ik_scale)
+            return fail(DSA_E_INVALID, "FP8 indexer keys need ik_scale");
+    }
+    if (static_cast<int64_t>(p->batch) * p->n_k >= (int64_t(1) << 31))
+        return fail(DSA_E_UNSUPPORTED, "batch * n_k must be below 2^31");
+    return DSA_OK;
+}
+
+// Bytes per token of a k (or v) cache row of `dim` entries.
+int cache_row_bytes(const dsa_problem_t* p, int dim) {
+    if (p->kv_dtype == DSA_FP8_E4M3) return DSA_FP8_KV_RECORD_BYTES(p->kv_heads, dim);
+    return p->kv_heads * dim * (p->kv_dtype == DSA_F32 ? 4 : 2);
+}
+
 int rows_of(const dsa_problem_t* p) { return p->batch * p->n_q; }
 
 // Entries of a selection row: the k picks plus a backbone's forced keys.
@@ -446,6 +474,9 @@ size_t dsa_workspace_bytes(int op, const dsa_problem_t* p) {
                 return static_cast<size_t>(-1);
             }
             return fused_layout(p, true).total;
+        case DSA_OP_COMPRESS_KV:
+            if (check_cache(p) != DSA_OK) return static_cast<size_t>(-1);
+            return dsa::compress_workspace_bytes(p->batch, p->n_k);
         case DSA_OP_DENSE_ATTN:
             if (check_attn(p) != DSA_OK) return static_cast<size_t>(-1);
             if (!masked_shape(p)) {
@@ -600,5 +631,71 @@ const char* dsa_status_str(dsa_status_t status) {
 }
 
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+
+int32_t dsa_compress_kept(int32_t n_k, int32_t window, int32_t keep_old) {
+    if (n_k < 0 || window < 0 || keep_old < 0) return 0;
+    const int32_t w = window < n_k ? window : n_k;
+    const int32_t n_old = n_k - w;
+    return w + (keep_old < n_old ? keep_old : n_old);
+}
+
+dsa_status_t dsa_compress_kv(const dsa_problem_t* p, const float* importance, int32_t window, int32_t keep_old,
+                             const dsa_kv_compressed_t* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (!p) return fail(DSA_E_INVALID, "problem pointer is NULL");
+    if (p->batch < 1 || p->n_k < 1)
+        return fail(DSA_E_INVALID, "batch and n_k must be >= 1 (got %d, %d)", p->batch, p->n_k);
+    if (p->n_k > kMaxNk) return fail(DSA_E_UNSUPPORTED, "n_k %d exceeds %d", p->n_k, kMaxNk);
+    dsa_status_t s = check_cache(p);
+    if (s != DSA_OK) return s;
+    if (window < 0 || keep_old < 0)
+        return fail(DSA_E_INVALID, "window and keep_old must be >= 0 (got %d, %d)", window, keep_old);
+    if (!importance || !out || !out->k || !out->pos) return fail(DSA_E_INVALID, "importance, out, out->k and out->pos are required");
+    if (!p->kv_latent && !out->v) return fail(DSA_E_INVALID, "out->v is required unless kv_latent");
+    if (p->kv_latent && out->v) return fail(DSA_E_INVALID, "out->v must be NULL when kv_latent");
+    if (!p->ik != !out->ik) return fail(DSA_E_INVALID, "out->ik must be given exactly when p->ik is");
+    const bool with_scale = p->ik && p->idx_dtype == DSA_FP8_E4M3;
+    if (with_scale != (out->ik_scale != nullptr))
+        return fail(DSA_E_INVALID, "out->ik_scale must be given exactly when FP8 indexer keys are copied");
+    const size_t need = dsa::compress_workspace_bytes(p->batch, p->n_k);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    const int n_keep = dsa_compress_kept(p->n_k, window, keep_old);
+    if (n_keep == 0) return DSA_OK;
+
+    dsa::CompressArgs a{};
+    a.B = p->batch;
+    a.n_k = p->n_k;
+    a.window = window < p->n_k ? window : p->n_k;
+    a.keep = n_keep - a.window;
+    a.n_keep = n_keep;
+    a.nch = dsa::compress_chunks(p->n_k);
+    a.imp = importance;
+    // rows move 16 bytes at a time where the row size and both pointers allow
+    // it, else 4; anything else is refused before a launch
+    auto add = [&](const char* name, const void* src, void* dst, int bytes) -> bool {
+        const uintptr_t al = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+        const int unit = (bytes % 16 == 0 && al % 16 == 0) ? 16 : ((bytes % 4 == 0 && al % 4 == 0) ? 4 : 0);
+        if (!unit) {
+            fail(DSA_E_UNSUPPORTED, "%s rows of %d bytes (or their pointers) are not 4-byte aligned", name, bytes);
+            return false;
+        }
+        a.src[a.nrow] = static_cast<const uint8_t*>(src);
+        a.dst[a.nrow] = static_cast<uint8_t*>(dst);
+        a.bytes[a.nrow] = bytes;
+        a.unit[a.nrow] = unit;
+        ++a.nrow;
+        return true;
+    };
+    if (!add("k", p->k, out->k, cache_row_bytes(p, p->d_qk))) return DSA_E_UNSUPPORTED;
+    if (!p->kv_latent && !add("v", p->v, out->v, cache_row_bytes(p, p->d_v))) return DSA_E_UNSUPPORTED;
+    if (p->ik && !add("ik", p->ik, out->ik, 128 * (p->idx_dtype == DSA_F32 ? 4 : (p->idx_dtype == DSA_BF16 ? 2 : 1))))
+        return DSA_E_UNSUPPORTED;
+    if (with_scale && !add("ik_scale", p->ik_scale, out->ik_scale, 4)) return DSA_E_UNSUPPORTED;
+    a.pos_out = out->pos;
+    a.ws = static_cast<uint32_t*>(workspace);
+    return device_status(dsa::launch_compress(a, stream), "compress launch");
+}
 
 }  // extern "C"

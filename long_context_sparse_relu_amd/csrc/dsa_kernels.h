@@ -173,4 +173,23 @@ hipError_t launch_attn_wide(const AttnArgs& a, float* part, hipStream_t st);
 // sum, unnormalised O[dv]) into out and lse (bf16 out).
 hipError_t launch_attn_merge(const AttnArgs& a, int nsplit, const float* part, hipStream_t st);
 
+// Importance compression of cached tokens (compress.hip): per sequence the
+// last `window` tokens and the `keep` older tokens of highest importance
+// (lower position first among equal importance) are copied, in position
+// order, into [B, n_keep] outputs.  Rows are opaque bytes (a multiple of 4).
+struct CompressArgs {
+    int B, n_k, window, keep, n_keep, nch;   // window <= n_k, keep <= n_k - window, n_keep = window + keep
+    const float* imp;                        // [B, n_k]
+    int nrow;                                // row arrays to copy (<= 4)
+    const uint8_t* src[4];
+    uint8_t* dst[4];
+    int bytes[4];                            // bytes per token of each array
+    int unit[4];                             // 16 or 4: bytes per vector load and store
+    int32_t* pos_out;                        // [B, n_keep] original positions
+    uint32_t* ws;                            // compress_workspace_bytes(B, n_k)
+};
+int compress_chunks(int n_k);
+size_t compress_workspace_bytes(int batch, int n_k);
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+
 }  // namespace dsa

@@ -242,3 +242,47 @@ def test_phase_timer_without_a_timed_call(lib):
     assert lib.dsa_phase_timing(1) == dsa.OK
     assert lib.dsa_phase_times(buf) == dsa.E_INVALID
     assert lib.dsa_phase_timing(0) == dsa.OK
+
+
+def test_compress_kept_counts(lib):
+    assert dsa.compress_kept(12, 3, 4) == 7
+    assert dsa.compress_kept(12, 20, 4) == 12
+    assert dsa.compress_kept(12, 3, 100) == 12
+    assert dsa.compress_kept(12, 0, 0) == 0
+    assert dsa.compress_kept(1 << 20, 8192, ((1 << 20) - 8192) // 2) == 8192 + ((1 << 20) - 8192) // 2
+
+
+def test_compress_validation(lib):
+    p = _problem()
+    need = lib.dsa_workspace_bytes(dsa.OP_COMPRESS_KV, ctypes.byref(p))
+    assert 0 < need != ctypes.c_size_t(-1).value
+    good = dsa.KVCompressed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+
+    def call(prob=p, imp=FAKE, window=8, keep=16, out=good, ws=FAKE, nbytes=need):
+        return lib.dsa_compress_kv(ctypes.byref(prob), imp, window, keep, None if out is None else ctypes.byref(out),
+                                   ws, nbytes, None)
+    assert call(imp=None) == dsa.E_INVALID
+    assert call(out=None) == dsa.E_INVALID
+    assert call(window=-1) == dsa.E_INVALID
+    assert call(keep=-1) == dsa.E_INVALID
+    assert call(nbytes=need - 1) == dsa.E_WORKSPACE
+    assert call(ws=None) == dsa.E_WORKSPACE
+    assert call(out=dsa.KVCompressed(FAKE.value, None, FAKE.value, FAKE.value, FAKE.value)) == dsa.E_INVALID
+    assert call(out=dsa.KVCompressed(FAKE.value, FAKE.value, FAKE.value, None, FAKE.value)) == dsa.E_INVALID
+    assert call(out=dsa.KVCompressed(FAKE.value, FAKE.value, None, FAKE.value, FAKE.value)) == dsa.E_INVALID
+    assert call(prob=_problem(kv_heads=0)) == dsa.E_INVALID
+    assert call(prob=_problem(k=None)) == dsa.E_INVALID
+    assert call(prob=_problem(kv_latent=1)) == dsa.E_INVALID          # latent with 4 kv heads
+    assert call(prob=_problem(batch=1024, n_k=1 << 24)) == dsa.E_UNSUPPORTED
+    assert lib.dsa_workspace_bytes(dsa.OP_COMPRESS_KV, ctypes.byref(_problem(kv_heads=0))) == \
+        ctypes.c_size_t(-1).value
+    # nothing to keep: valid, and nothing is enqueued (no device needed)
+    assert call(window=0, keep=0) == dsa.OK
+
+
+def test_compress_rejects_rows_not_a_multiple_of_four_bytes(lib):
+    p = _problem(d_qk=63, d_v=63, kv_heads=1, q_heads=1)      # bf16 rows of 126 bytes
+    need = lib.dsa_workspace_bytes(dsa.OP_COMPRESS_KV, ctypes.byref(p))
+    out = dsa.KVCompressed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    st = lib.dsa_compress_kv(ctypes.byref(p), FAKE, 8, 16, ctypes.byref(out), FAKE, need, None)
+    assert st == dsa.E_UNSUPPORTED and "aligned" in dsa.last_error()

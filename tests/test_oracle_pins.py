@@ -483,3 +483,75 @@ def test_fp8_latent_value_uses_key_scale():
             z = 0.25 * kd[sel, 0, :] @ q[t, h].astype(np.float64)
             p = np.exp(z - z.max()); p /= p.sum()
             np.testing.assert_allclose(out[t, h], p @ kd[sel, 0, :dv], rtol=1e-11, atol=1e-13)
+
+
+# ---- importance compression of the cache ------------------------------------
+
+def _golden_importance(vals):
+    return np.array([-0.0 if v == "-0.0" else float(v) for v in vals], dtype=np.float32)
+
+
+def test_compress_hand_worked_example():
+    with open(os.path.join(GOLDEN, "compress_worked_example.json")) as f:
+        g = json.load(f)
+    imp = _golden_importance(g["importance"])
+    assert np.signbit(imp[5]) and imp[5] == 0.0
+    for case in g["cases"]:
+        got = oracle.compress_select(imp, case["window"], case["keep_old"])
+        assert got.tolist() == case["kept"], case
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_compress_brute_force_over_subsets(seed):
+    # the kept old set is the unique subset of its size that no swap improves:
+    # every kept token beats every dropped one (higher importance, or equal
+    # importance and a lower position)
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 11))
+    imp = rng.integers(-2, 3, n).astype(np.float32)
+    imp[rng.random(n) < 0.3] = -0.0
+    for window in range(0, n + 2):
+        n_old = max(0, n - window)
+        for keep in range(0, n_old + 2):
+            m = min(keep, n_old)
+            valid = []
+            for sub in itertools.combinations(range(n_old), m):
+                kept = set(sub)
+                if all(imp[s] > imp[d] or (imp[s] == imp[d] and s < d)
+                       for s in kept for d in range(n_old) if d not in kept):
+                    valid.append(sorted(sub) + list(range(n_old, n)))
+            assert len(valid) == 1
+            assert oracle.compress_select(imp, window, keep).tolist() == valid[0]
+
+
+def test_compress_degenerate_cases():
+    imp = np.zeros(1000, dtype=np.float32)
+    imp[1::2] = -0.0
+    # every token ties: the lowest old positions win
+    assert oracle.compress_select(imp, 100, 300).tolist() == list(range(300)) + list(range(900, 1000))
+    # a strictly increasing importance keeps the newest old tokens
+    inc = np.arange(1000, dtype=np.float32)
+    assert oracle.compress_select(inc, 10, 5).tolist() == list(range(985, 1000))
+    assert oracle.compress_select(inc, 0, 0).tolist() == []
+    assert oracle.compress_select(-inf_row(7), 2, 1).tolist() == [0, 5, 6]
+
+
+def inf_row(n):
+    r = np.full(n, np.inf, dtype=np.float32)
+    r[0] = -r[0]
+    return r
+
+
+def test_compress_matches_the_pages_memory_cut():
+    # the pages: an 8K window plus importance compression cuts the KV cache by
+    # 45-55 % at 1M tokens; keeping half of the older tokens lands inside that
+    n = 1 << 20
+    imp = np.random.default_rng(0).standard_normal(n).astype(np.float32)
+    kept = oracle.compress_select(imp, 8192, (n - 8192) // 2)
+    cut = 1.0 - kept.size / n
+    assert 0.45 <= cut <= 0.55
+    assert np.all(np.diff(kept) > 0) and kept[-8192:].tolist() == list(range(n - 8192, n))
+    # every kept old token's importance is at least every dropped one's
+    old = np.zeros(n - 8192, dtype=bool)
+    old[kept[:-8192]] = True
+    assert imp[:n - 8192][old].min() >= imp[:n - 8192][~old].max()
