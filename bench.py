@@ -281,6 +281,22 @@ def _sweep_compress(dsa, torch, dev, reps):
     from dsa_inputs import importance_scores, kv_args, make_inputs, spec
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # the ceiling a plain device copy reaches (bytes read + written)
+    a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    c = torch.empty_like(a)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        c.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(1e3 * e0.elapsed_time(e1))
+    us = float(np.median(times))
+    print(json.dumps({"sweep": "compress", "cache": "plain_copy_4GiB", "us": round(us, 1), "bytes": 2 * a.numel(),
+                      "tb_s": round(2 * a.numel() / us / 1e6, 3), "frac_hbm": round(2 * a.numel() / us / 8e6, 3)}),
+          flush=True)
+    del a, c
     for name in ("decode_1m", "decode_128k", "decode_128k_fp8kv"):
         s = spec(name)
         print(f"[bench] compress: generating {name} inputs", file=sys.stderr, flush=True)

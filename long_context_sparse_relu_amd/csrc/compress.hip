@@ -30,6 +30,7 @@ constexpr int kCmpBins = 2048;          // 11-bit digits: passes over bits 31..2
 constexpr int kCmpHistKeys = 16384;     // old tokens per histogram workgroup
 constexpr int kCmpChunk = 4096;         // tokens per count / write workgroup (16 per thread)
 constexpr int kCmpThreads = 256;
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -207,22 +208,51 @@ __global__ __launch_bounds__(kCmpThreads) void k_cmp_scan(CompressArgs a) {
     }
 }
 
+// Copies the chunk's nk kept rows of one array.  Their output slots are
+// consecutive, so piece j of the chunk's output goes to dst + j * UNIT and the
+// stores are contiguous.  A thread moves U pieces per step and loads the next
+// step's pieces before it stores the current ones, so up to 2U loads are in
+// flight.
 template <int UNIT>
-__device__ __forceinline__ void copy_rows(const uint8_t* src, uint8_t* dst, int bytes, const int* ls, const int* ld,
-                                          int nk) {
-    using V = typename std::conditional<UNIT == 16, uint4, uint32_t>::type;
+__device__ __forceinline__ void copy_rows(const uint8_t* src, uint8_t* dst, int bytes, const int* ls, int nk) {
+    using V = typename std::conditional<UNIT == 16, v4u32, uint32_t>::type;
+    constexpr int U = 8;
+    constexpr int STEP = U * kCmpThreads;
     const int per = bytes / UNIT;
     const int total = nk * per;
-    for (int j = threadIdx.x; j < total; j += kCmpThreads) {
-        const int r = j / per, piece = j - r * per;
-        const V x = *reinterpret_cast<const V*>(src + static_cast<size_t>(ls[r]) * bytes + piece * UNIT);
-        *reinterpret_cast<V*>(dst + static_cast<size_t>(ld[r]) * bytes + piece * UNIT) = x;
+    auto load = [&](int j0, V* x) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * kCmpThreads;
+            if (j < total) {
+                const int r = j / per, piece = j - r * per;
+                x[u] = *reinterpret_cast<const V*>(src + static_cast<size_t>(ls[r]) * bytes + piece * UNIT);
+            }
+        }
+    };
+    V cur[U];
+    int j0 = threadIdx.x;
+    if (j0 >= total) return;
+    load(j0, cur);
+    while (true) {
+        V nxt[U];
+        const bool more = j0 + STEP < total;
+        if (more) load(j0 + STEP, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * kCmpThreads;
+            if (j < total) __builtin_nontemporal_store(cur[u], reinterpret_cast<V*>(dst + static_cast<size_t>(j) * UNIT));
+        }
+        if (!more) break;
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        j0 += STEP;
     }
 }
 
 __global__ __launch_bounds__(kCmpThreads) void k_cmp_write(CompressArgs a) {
     __shared__ uint32_t sh[kCmpThreads];
-    __shared__ int lsrc[kCmpChunk], ldst[kCmpChunk];
+    __shared__ int lsrc[kCmpChunk];
     const int b = blockIdx.y, c = blockIdx.x;
     const SeqWs w = seq_ws(a.ws, b, a.nch);
     const float* imp = a.imp + static_cast<size_t>(b) * a.n_k;
@@ -252,15 +282,15 @@ __global__ __launch_bounds__(kCmpThreads) void k_cmp_write(CompressArgs a) {
             const int i = __builtin_ctz(m);
             m &= m - 1u;
             lsrc[j] = b * a.n_k + s0 + i;
-            ldst[j] = static_cast<int>(b * n_keep + first + j);
             a.pos_out[b * n_keep + first + j] = s0 + i;
             ++j;
         }
     }
     __syncthreads();
     for (int r = 0; r < a.nrow; ++r) {
-        if (a.unit[r] == 16) copy_rows<16>(a.src[r], a.dst[r], a.bytes[r], lsrc, ldst, static_cast<int>(nk));
-        else copy_rows<4>(a.src[r], a.dst[r], a.bytes[r], lsrc, ldst, static_cast<int>(nk));
+        uint8_t* d = a.dst[r] + (b * n_keep + first) * static_cast<size_t>(a.bytes[r]);
+        if (a.unit[r] == 16) copy_rows<16>(a.src[r], d, a.bytes[r], lsrc, static_cast<int>(nk));
+        else copy_rows<4>(a.src[r], d, a.bytes[r], lsrc, static_cast<int>(nk));
     }
 }
 
