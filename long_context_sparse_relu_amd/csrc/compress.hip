@@ -14,7 +14,7 @@
 //   1. a three-pass radix select over the old tokens' order keys finds the
 //      keep-th largest key T and how many keys equal to T are kept (k_cmp_hist
 //      over many workgroups, k_cmp_pick for the bin);
-//   2. k_cmp_count counts, per 4096-token chunk, the keys above T, equal to T
+//   2. k_cmp_count counts, per 1024-token chunk, the keys above T, equal to T
 //      and in the window; k_cmp_scan turns that into each chunk's first output
 //      slot and the number of T-keys before it;
 //   3. k_cmp_write ranks the chunk's kept tokens and copies their rows with
@@ -28,8 +28,12 @@ namespace {
 
 constexpr int kCmpBins = 2048;          // 11-bit digits: passes over bits 31..21, 20..10, 9..0
 constexpr int kCmpHistKeys = 16384;     // old tokens per histogram workgroup
-constexpr int kCmpChunk = 4096;         // tokens per count / write workgroup (16 per thread)
+// Tokens per count / write workgroup.  Chunks of the recent window keep every
+// token and the others about half; 1024-token chunks give several workgroups
+// per CU slot over a launch, so the heavier ones are spread as slots free up.
+constexpr int kCmpChunk = 1024;
 constexpr int kCmpThreads = 256;
+constexpr int kCmpPer = kCmpChunk / kCmpThreads;   // tokens per thread
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -144,7 +148,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
     return incl - v;
 }
 
-// Which tokens of [s0, s0 + 16) the thread's flags describe.
+// Which tokens of [s0, s0 + kCmpPer) the thread's flags describe.
 struct Flags {
     uint32_t fixed;   // bit i: kept whatever the tie rank (window, key > T, or every old token kept)
     uint32_t eq;      // bit i: an old token with key == T (kept if its rank among them is small enough)
@@ -154,7 +158,7 @@ __device__ __forceinline__ Flags token_flags(const CompressArgs& a, const float*
     const int n_old = a.n_k - a.window;
     Flags f{0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kCmpPer; ++i) {
         const int s = s0 + i;
         if (s >= a.n_k) break;
         if (s >= n_old || a.keep == n_old) {
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(kCmpThreads) void k_cmp_count(CompressArgs a) {
     const int b = blockIdx.y, c = blockIdx.x;
     const SeqWs w = seq_ws(a.ws, b, a.nch);
     const float* imp = a.imp + static_cast<size_t>(b) * a.n_k;
-    const Flags f = token_flags(a, imp, w.state[0], c * kCmpChunk + 16 * static_cast<int>(threadIdx.x));
+    const Flags f = token_flags(a, imp, w.state[0], c * kCmpChunk + kCmpPer * static_cast<int>(threadIdx.x));
     uint32_t nf = 0u, ne = 0u;
     block_excl_scan(static_cast<uint32_t>(__builtin_popcount(f.fixed)), sh, nf);
     block_excl_scan(static_cast<uint32_t>(__builtin_popcount(f.eq)), sh, ne);
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kCmpThreads) void k_cmp_write(CompressArgs a) {
     const int b = blockIdx.y, c = blockIdx.x;
     const SeqWs w = seq_ws(a.ws, b, a.nch);
     const float* imp = a.imp + static_cast<size_t>(b) * a.n_k;
-    const int s0 = c * kCmpChunk + 16 * static_cast<int>(threadIdx.x);
+    const int s0 = c * kCmpChunk + kCmpPer * static_cast<int>(threadIdx.x);
     const Flags f = token_flags(a, imp, w.state[0], s0);
     const uint32_t take = w.state[1];
     uint32_t etot = 0u;
